@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused LayerNorm forward + mix-order backward on one MI355X.
+
+A step is one pass of the whole path over one batch: ln_fwd (bias + residual
++ LayerNorm; y, residual_out, mean, rstd, amax) followed by ln_bwd on its
+outputs (dx, dgamma, dbeta in bf16), at M = 1152 * 500 = 576000 rows by
+N = 384, bf16 tensors, fp32 arithmetic.  Inputs are seeded synthetic
+Gaussians (x, residual, dy ~ N(0,1); bias, beta ~ N(0, 0.1); gamma ~ 1 +
+N(0, 0.1)) resident in HBM before timing starts.
+
+value = algorithmic bytes of a step / time of a step (GB/s): each [M, N]
+tensor read or written once plus the fp32 per-row statistics (forward
+8N + 8 bytes per row, backward 6N + 8).  Prints ONE JSON line on stdout;
+progress goes to stderr.
+
+Also reported: the roofline of the dominant kernel (the forward), timed with
+HIP events around each forward launch inside the timed loop; a per-case
+breakdown (each case timed alone with a 512 MiB cache flush between calls);
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0  # MI355X HBM3E
+M_BIG, N_BIG = 1152 * 500, 384
+FLUSH_BYTES = 512 << 20
+KERNEL_SOURCES = ("normalization_ln_fwd_amd/csrc/kernels.hpp",
+                  "normalization_ln_fwd_amd/csrc/device.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_ln_bf16_576000x384_traffic.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_bytes(M, N, es=2, stats=2, io_tensors=4):
+    return M * (io_tensors * N * es + 4 * stats)
+
+
+def bwd_bytes(M, N, es=2, stats=2):
+    return M * (3 * N * es + 4 * stats)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per forward launch from the committed counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--breakdown-iters", type=int, default=20)
+    ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=M_BIG,
+                    help="rows of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (the path has no multi-GPU "
+              "component); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import normalization_ln_fwd_amd as nf
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    nf.library()  # fails loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    M, N = M_BIG, N_BIG
+    t0 = time.time()
+    h = synth.make_inputs(M, N, dtype=synth.BF16, seed=0,
+                          names=("x", "residual", "bias", "gamma", "beta", "dy"))
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    d = {k: to_dev(v) for k, v in h.items()}
+    y = torch.empty_like(d["x"])
+    res_out = torch.empty_like(d["x"])
+    mean = torch.empty(M, dtype=torch.float32, device=dev)
+    rstd = torch.empty(M, dtype=torch.float32, device=dev)
+    amax = torch.empty(1, dtype=torch.float32, device=dev)
+    dx = torch.empty_like(d["x"])
+    dgamma = torch.empty(N, dtype=torch.bfloat16, device=dev)
+    dbeta = torch.empty(N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(4, nf.bwd_workspace_size(M, N, torch.bfloat16)), dtype=torch.uint8,
+                     device=dev)
+    fwd_out = {"y": y, "residual_out": res_out, "mean": mean, "rstd": rstd, "amax": amax}
+    bwd_out = {"dx": dx, "dgamma": dgamma, "dbeta": dbeta}
+
+    def fwd():
+        nf.ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 1e-5,
+                  want_amax=True, out=fwd_out)
+
+    def bwd():
+        nf.ln_bwd(d["dy"], res_out, d["gamma"], mean, rstd, dparam_dtype=torch.bfloat16,
+                  workspace=ws, out=bwd_out)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record()
+        fwd()
+        ev[k][1].record()
+        bwd()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = ev[0][0].elapsed_time(ev[K - 1][2]) / K
+    fwd_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]
+    bwd_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]
+    step_bytes = fwd_bytes(M, N) + bwd_bytes(M, N)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"timed {K} steps: {ms_step:.4f} ms/step (wall {wall / K * 1e3:.4f} ms/step), "
+        f"{value:.1f} GB/s")
+
+    fwd_avg = statistics.fmean(fwd_ms)
+    fwd_gbs = fwd_bytes(M, N) / (fwd_avg * 1e-3) / 1e9
+    traffic = recorded_traffic()
+    roofline = {"bound": "hbm", "achieved": round(fwd_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(fwd_gbs / PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "fwd_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 16, LayerNorm>",
+                "bytes_per_launch": fwd_bytes(M, N), "avg_launch_us": round(fwd_avg * 1e3, 2),
+                "kernel_source_hash": kernel_source_hash()}
+    bwd_avg = statistics.fmean(bwd_ms)
+
+    result = {
+        "metric": "achieved HBM GB/s (% of MI355X peak) for fused LN/RMSNorm fwd and bwd",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "fused bias+residual LayerNorm fwd (y, residual_out, mean, rstd, "
+                               "amax) + mix-order LayerNorm bwd (dx, dgamma, dbeta), "
+                               "M=576000 (1152x500) x N=384",
+                   "M": M, "N": N, "io_dtype": "bf16", "compute_dtype": "f32",
+                   "step_bytes": step_bytes, "frac_of_peak": round(value / PEAK_GBS, 4),
+                   "fwd_us": round(fwd_avg * 1e3, 2), "bwd_us": round(bwd_avg * 1e3, 2)},
+        "roofline": roofline,
+    }
+
+    if args.calib_copy:
+        src = torch.empty(FLUSH_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = 2 * src.numel() * src.element_size()
+        log("calibration copies done")
+
+    if not args.no_breakdown:
+        result["breakdown"] = breakdown(args.breakdown_iters, nf, torch, np, synth, d, h, dev,
+                                        fwd_out, ws)
+
+    # free the device copies before the CPU leg
+    del d
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(h, args.cpu_rows)
+
+    print(json.dumps(result), flush=True)
+
+
+def time_calls(fn, iters, torch, flush_buf):
+    """Median / min microseconds of fn(), each call after a cache flush."""
+    times = []
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(iters + 3):
+        flush_buf.zero_()
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            times.append(s.elapsed_time(e) * 1e3)
+    return statistics.median(times), min(times)
+
+
+def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    out = {}
+
+    def rec(name, fn, nbytes, gated):
+        med, mn = time_calls(fn, iters, torch, flush)
+        gbs = nbytes / (med * 1e-6) / 1e9
+        out[name] = {"us_median": round(med, 2), "us_min": round(mn, 2), "bytes": nbytes,
+                     "GB_s": round(gbs, 1), "frac_peak": round(gbs / PEAK_GBS, 4),
+                     "gated_70pct": gated}
+        log(f"  {name}: {med:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_GBS:.1f}% of peak)")
+
+    M, N = M_BIG, N_BIG
+    rec("ln_fwd_576000x384", lambda: nf.ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"],
+                                                d["beta"], 1e-5, want_amax=True, out=fwd_out),
+        fwd_bytes(M, N), True)
+    rms_out = {"y": fwd_out["y"], "residual_out": fwd_out["residual_out"],
+               "rstd": fwd_out["rstd"], "amax": fwd_out["amax"]}
+    rec("rms_fwd_576000x384", lambda: nf.rms_fwd(d["x"], d["bias"], d["residual"], d["gamma"],
+                                                  None, 1e-6, want_amax=True, out=rms_out),
+        fwd_bytes(M, N, stats=1), False)
+    # configs 3 and 4: backward on x = N(0,1) (the generator's x), dy
+    dx = torch.empty_like(d["x"])
+    dg = torch.empty(N, dtype=torch.bfloat16, device=dev)
+    db = torch.empty(N, dtype=torch.bfloat16, device=dev)
+    nf.ln_fwd(d["x"], None, None, None, None, 1e-5, out=fwd_out)  # mean / rstd of x
+    rec("rms_bwd_576000x384_recompute", lambda: nf.rms_bwd(
+        d["dy"], d["x"], d["gamma"], None, 1e-6, dparam_dtype=torch.bfloat16, workspace=ws,
+        out={"dx": dx, "dgamma": dg}), bwd_bytes(M, N, stats=0), True)
+    rec("ln_bwd_576000x384", lambda: nf.ln_bwd(
+        d["dy"], d["x"], d["gamma"], fwd_out["mean"], fwd_out["rstd"],
+        dparam_dtype=torch.bfloat16, workspace=ws, out={"dx": dx, "dgamma": dg, "dbeta": db}),
+        bwd_bytes(M, N), True)
+    del dx
+    # config 2 (launch-bound size)
+    M2 = 4096
+    sub = {k: (v[:M2] if v.dim() == 2 else v) for k, v in d.items()}
+    rec("ln_fwd_4096x384_amax", lambda: nf.ln_fwd(sub["x"], sub["bias"], sub["residual"],
+                                                   sub["gamma"], sub["beta"], 1e-5,
+                                                   want_amax=True),
+        fwd_bytes(M2, N), False)
+    # config 5: 8192 x 4096, residual + LayerNorm, 1% outliers
+    M5, N5 = 8192, 4096
+    g5 = synth.make_inputs(M5, N5, dtype=synth.BF16, seed=0, outlier_p=0.01,
+                           names=("x", "residual", "gamma", "beta", "dy"))
+    d5 = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev)
+          for k, v in g5.items()}
+    o5 = nf.ln_fwd(d5["x"], None, d5["residual"], d5["gamma"], d5["beta"], 1e-5)
+    ws5 = torch.empty(max(4, nf.bwd_workspace_size(M5, N5, torch.bfloat16)), dtype=torch.uint8,
+                      device=dev)
+    rec("ln_fwd_8192x4096", lambda: nf.ln_fwd(d5["x"], None, d5["residual"], d5["gamma"],
+                                               d5["beta"], 1e-5, out=o5),
+        fwd_bytes(M5, N5), True)
+    b5 = {"dx": torch.empty_like(d5["x"]),
+          "dgamma": torch.empty(N5, dtype=torch.bfloat16, device=dev),
+          "dbeta": torch.empty(N5, dtype=torch.bfloat16, device=dev)}
+    rec("ln_bwd_8192x4096", lambda: nf.ln_bwd(d5["dy"], o5["residual_out"], d5["gamma"],
+                                               o5["mean"], o5["rstd"],
+                                               dparam_dtype=torch.bfloat16, workspace=ws5,
+                                               out=b5), bwd_bytes(M5, N5), True)
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(h, rows):
+    """The oracle (double precision, unchanged) on the first `rows` rows of
+    the same workload: forward then backward, all host threads."""
+    import oracle
+
+    R = min(rows, M_BIG)
+    sub = {k: (v[:R] if v.ndim == 2 else v) for k, v in h.items()}
+    threads = oracle.default_threads()
+    oracle._load()
+    t0 = time.perf_counter()
+    f = oracle.norm_fwd(sub["x"], sub["bias"], sub["residual"], sub["gamma"], sub["beta"], 1e-5,
+                        nthreads=threads)
+    oracle.norm_bwd(sub["dy"], f["u"], sub["gamma"], f["mean"], f["rstd"], 1e-5,
+                    nthreads=threads)
+    sec = time.perf_counter() - t0
+    nbytes = fwd_bytes(R, N_BIG) + bwd_bytes(R, N_BIG)
+    log(f"cpu oracle: {R} rows in {sec:.2f}s on {threads} threads")
+    return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {R} of {M_BIG} rows of the same workload (fwd + bwd), "
+                      f"{sec:.2f} s wall, same algorithmic-byte accounting"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * normfuse.h -- C ABI of the fused LayerNorm / RMSNorm library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operations
+ *  ln_fwd / rms_fwd : fused (bias +) residual + LayerNorm / RMSNorm forward
+ *      with an optional FP8-scaling amax of the normalised output.  The
+ *      operation is the one spelled out in nvFuser issue #1660 ("performance
+ *      optimization for moving distributive reduction operation across
+ *      broadcast dimensions"), layernorm + amax comment:
+ *          out1 = (x + bias) + residual, viewed as rows of the hidden size N
+ *          out2 = layer_norm(out1, gamma, beta, eps)
+ *          amax = max |out2|, overwriting the amax tensor.
+ *      The same comment asks for the amax to be split so that its first
+ *      stage runs inside the normalisation kernel; IREE issue #9139
+ *      ("Investigate a fusion opportunity on Layer Normalization") asks for
+ *      mean, variance and normalisation to read the source data once.  Both
+ *      hold here: every [M, N] input is read once and every output written
+ *      once, in one kernel.
+ *  ln_bwd / rms_bwd : backward.  PyTorch PR #165370 (Inductor mix-order
+ *      reduction), PR description: the dx reduction runs over the hidden
+ *      dimension and the dgamma / dbeta reduction over all B x T rows; both
+ *      read dy and x, which are loaded once here, and the outer reduction
+ *      ends with a down-cast when dgamma / dbeta are low precision.
+ *
+ * Definitions (the pages call PyTorch's layer_norm; these are its semantics)
+ *   u      = round_io((x + bias) + residual)          (absent terms are 0)
+ *   LN     : mean = sum(u)/N, var = sum((u-mean)^2)/N, rstd = 1/sqrt(var+eps)
+ *            y = (u - mean) * rstd * gamma + beta
+ *   RMS    : rstd = 1/sqrt(sum(u^2)/N + eps),  y = u * rstd * gamma (+ beta)
+ *   amax   = max over all elements of |y| as stored (after rounding)
+ *   bwd    : xhat = (x-mean)*rstd (LN) or x*rstd (RMS), g = dy*gamma,
+ *            dx = rstd*(g - mean_j(g) - xhat*mean_j(g*xhat))   (LN)
+ *            dx = rstd*(g - xhat*mean_j(g*xhat))                (RMS)
+ *            dgamma_j = sum_i dy_ij*xhat_ij,  dbeta_j = sum_i dy_ij
+ *   Arithmetic is fp32 throughout; round_io rounds to the I/O dtype to
+ *   nearest, ties to even.  The normalisation reads the rounded u, which is
+ *   also what residual_out holds.
+ *
+ * Conventions shared by every entry point
+ *   Layout   : [M, N] tensors are dense row-major (row stride N elements);
+ *              M is every leading dimension flattened.  [N] vectors (bias,
+ *              gamma, beta, dgamma, dbeta) are dense.  mean / rstd are fp32
+ *              [M].
+ *   Memory   : every pointer is device memory owned by the caller.  The
+ *              library allocates nothing, frees nothing and keeps no pointer
+ *              after a call returns.  ln_bwd / rms_bwd take a caller-owned
+ *              workspace whose size norm_bwd_workspace_size reports.
+ *   Streams  : all work is enqueued on `stream` (a hipStream_t; NULL is the
+ *              default stream) and the call returns without synchronising.
+ *              Work of one call is ordered by that stream.
+ *   Errors   : arguments are checked before anything is enqueued; on an
+ *              error the call returns a status other than NORM_OK and
+ *              enqueues nothing.  NORM_ERR_LAUNCH reports a failed launch;
+ *              faults during execution appear at the caller's next
+ *              synchronisation, as in HIP.
+ *   Aliasing : outputs must not overlap inputs or each other.
+ *   Threads  : calls are thread-safe; the library keeps only a per-device
+ *              cache of device properties.
+ *   Results  : deterministic: the same inputs on the same device give
+ *              bit-identical outputs (the column sums use a fixed grid and a
+ *              fixed summation order).
+ *   Alignment: pointers must be aligned to their element size.  16-byte
+ *              aligned [M, N] / [N] pointers with N a multiple of 16 bytes'
+ *              worth of elements take the vectorised kernels; anything else
+ *              takes a correct element-wise path.
+ *   Sizes    : 0 <= M; 1 <= N <= NORM_N_MAX.  M = 0 enqueues only what
+ *              defines the outputs (amax = 0, dgamma = dbeta = 0), and then
+ *              the [M, N] and [M] pointers may be NULL.
+ */
+#ifndef NORMFUSE_H
+#define NORMFUSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of tensors (the "I/O dtype") and of dgamma / dbeta. */
+#define NORM_F32 0  /* IEEE binary32 */
+#define NORM_BF16 1 /* bfloat16 (upper half of a binary32) */
+
+/* Status codes. */
+typedef int32_t norm_status_t;
+#define NORM_OK 0
+#define NORM_ERR_NULL 1      /* a required pointer is NULL */
+#define NORM_ERR_SHAPE 2     /* M < 0, N < 1 or N > NORM_N_MAX */
+#define NORM_ERR_ARG 3       /* eps negative or NaN, or an argument the op does not take */
+#define NORM_ERR_DTYPE 4     /* unknown dtype code */
+#define NORM_ERR_ALIGN 5     /* a pointer is not aligned to its element size */
+#define NORM_ERR_WORKSPACE 6 /* workspace NULL or smaller than norm_bwd_workspace_size */
+#define NORM_ERR_LAUNCH 7    /* a kernel launch failed */
+#define NORM_ERR_DEVICE 8    /* no usable HIP device, or a device query failed */
+
+/* Largest row length any entry point accepts. */
+#define NORM_N_MAX 16384
+
+/*
+ * ln_fwd -- fused (bias +) residual + LayerNorm forward.
+ *   x            [M,N] dtype   required
+ *   bias         [N]   dtype   optional (NULL: no bias)
+ *   residual     [M,N] dtype   optional (NULL: no residual)
+ *   gamma        [N]   dtype   optional (NULL: 1)
+ *   beta         [N]   dtype   optional (NULL: 0)
+ *   eps          >= 0, finite
+ *   y            [M,N] dtype   required
+ *   residual_out [M,N] dtype   optional: u, the rounded sum that was normalised
+ *   mean, rstd   [M]   fp32    optional
+ *   amax         [1]   fp32    optional: overwritten with max |y| (0 when M = 0)
+ *   stream       hipStream_t
+ */
+norm_status_t ln_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
+                     const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
+                     void *residual_out, float *mean, float *rstd, float *amax, void *stream);
+
+/*
+ * rms_fwd -- fused (bias +) residual + RMSNorm forward.  Arguments as ln_fwd;
+ * `mean` must be NULL (RMSNorm has no mean; NORM_ERR_ARG otherwise).  beta is
+ * an optional additive shift after the scale.
+ */
+norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
+                      const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
+                      void *residual_out, float *mean, float *rstd, float *amax, void *stream);
+
+/*
+ * norm_bwd_workspace_size -- bytes of device workspace ln_bwd / rms_bwd need
+ * for an [M, N] problem of the given dtype on the current device (the
+ * per-workgroup dgamma / dbeta column partials).  Writes 0 when none is
+ * needed.  The workspace needs no initialisation and may be reused by calls
+ * ordered on one stream.
+ */
+norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_t *bytes);
+
+/*
+ * ln_bwd -- LayerNorm backward with the mix-order (one-load) reduction.
+ *   dy           [M,N] dtype   required
+ *   x            [M,N] dtype   required: the tensor that was normalised
+ *                              (the forward's residual_out when it fused an add)
+ *   gamma        [N]   dtype   optional (NULL: 1)
+ *   mean, rstd   [M]   fp32    required (as saved by ln_fwd)
+ *   dx           [M,N] dtype   required
+ *   dgamma       [N]   dparam_dtype  optional
+ *   dbeta        [N]   dparam_dtype  optional
+ *   dparam_dtype NORM_F32 or NORM_BF16: dgamma / dbeta are summed in fp32
+ *                and rounded (to nearest, ties to even) to this type
+ *   workspace    device memory of at least norm_bwd_workspace_size bytes
+ *                (may be NULL when that size is 0)
+ */
+norm_status_t ln_bwd(const void *dy, const void *x, const void *gamma, const float *mean,
+                     const float *rstd, int64_t M, int64_t N, int32_t dtype, void *dx,
+                     void *dgamma, void *dbeta, int32_t dparam_dtype, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/*
+ * rms_bwd -- RMSNorm backward with the mix-order reduction.  Arguments as
+ * ln_bwd, except: no mean; rstd [M] fp32 is optional -- NULL recomputes it
+ * from x with `eps` inside the same pass (eps is ignored when rstd is given);
+ * dbeta (optional) is the gradient of the optional shift beta.
+ */
+norm_status_t rms_bwd(const void *dy, const void *x, const void *gamma, const float *rstd,
+                      float eps, int64_t M, int64_t N, int32_t dtype, void *dx, void *dgamma,
+                      void *dbeta, int32_t dparam_dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *norm_status_string(norm_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NORMFUSE_H */

@@ -1,0 +1,217 @@
+"""Fused LayerNorm / RMSNorm for AMD MI355X (gfx950): Python binding.
+
+Thin ctypes layer over ``libnormfuse.so`` (the C ABI of ``include/normfuse.h``).
+It only marshals arguments: torch supplies device memory (``data_ptr``) and
+the stream (``torch.cuda.current_stream()``); every step of the computation
+runs in the library's HIP kernels.  There is no fallback: without the built
+library, importing works but every call raises ``NormLibraryMissing``.
+
+Operations (definitions in ``include/normfuse.h``):
+  ln_fwd / rms_fwd   fused (bias +) residual + LayerNorm / RMSNorm forward
+                     with optional residual_out, mean / rstd and amax
+  ln_bwd / rms_bwd   backward: dx plus dgamma / dbeta from one read of dy, x
+"""
+import ctypes
+import os
+
+import torch
+
+from .build import LIB as _LIB_PATH
+
+__all__ = ["ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "bwd_workspace_size", "NormError",
+           "NormLibraryMissing", "library", "F32", "BF16", "N_MAX"]
+
+F32 = 0
+BF16 = 1
+N_MAX = 16384
+STATUS = {0: "NORM_OK", 1: "NORM_ERR_NULL", 2: "NORM_ERR_SHAPE", 3: "NORM_ERR_ARG",
+          4: "NORM_ERR_DTYPE", 5: "NORM_ERR_ALIGN", 6: "NORM_ERR_WORKSPACE", 7: "NORM_ERR_LAUNCH",
+          8: "NORM_ERR_DEVICE"}
+EXPORTS = ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "norm_bwd_workspace_size",
+           "norm_status_string")
+
+
+class NormLibraryMissing(RuntimeError):
+    pass
+
+
+class NormError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+_lib = None
+
+
+def library():
+    """The loaded ``libnormfuse.so`` (ctypes), with argument types set."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise NormLibraryMissing(
+                f"{_LIB_PATH} is not built; run normalization_ln_fwd_amd/build.py "
+                "(or __graft_entry__.build()) first")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_float, ctypes.c_size_t)
+        fwd = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+        lib.ln_fwd.argtypes = fwd
+        lib.rms_fwd.argtypes = fwd
+        lib.ln_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, i32, vp, sz, vp]
+        lib.rms_bwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, i32, vp, sz, vp]
+        lib.norm_bwd_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
+        lib.norm_status_string.argtypes = [i32]
+        lib.norm_status_string.restype = ctypes.c_char_p
+        for name in ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "norm_bwd_workspace_size"):
+            getattr(lib, name).restype = i32
+        _lib = lib
+    return _lib
+
+
+def _check(fn, st):
+    if st != 0:
+        raise NormError(fn, st, library().norm_status_string(st).decode())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t, name, dtype=None, numel=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, want_rstd,
+         want_amax, stream, out):
+    lib = library()
+    N = x.shape[-1]
+    M = x.numel() // N if N else 0
+    dt = x.dtype
+    out = dict(out or {})
+    y = out.get("y")
+    if y is None:
+        y = torch.empty_like(x)
+    res_out = out.get("residual_out")
+    if res_out is None and want_residual_out:
+        res_out = torch.empty_like(x)
+    mean = out.get("mean")
+    if mean is None and want_mean:
+        mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    rstd = out.get("rstd")
+    if rstd is None and want_rstd:
+        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    amax = out.get("amax")
+    if amax is None and want_amax:
+        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    st = getattr(lib, fn)(
+        _ptr(x, "x"), _ptr(bias, "bias", dt, N), _ptr(residual, "residual", dt, M * N),
+        _ptr(gamma, "gamma", dt, N), _ptr(beta, "beta", dt, N), float(eps), M, N,
+        _dtype_code(x), _ptr(y, "y", dt, M * N), _ptr(res_out, "residual_out", dt, M * N),
+        _ptr(mean, "mean", torch.float32, M), _ptr(rstd, "rstd", torch.float32, M),
+        _ptr(amax, "amax", torch.float32, 1), _stream(stream))
+    _check(fn, st)
+    return {"y": y, "residual_out": res_out, "mean": mean, "rstd": rstd, "amax": amax}
+
+
+def ln_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, *,
+           want_residual_out=None, want_stats=True, want_amax=False, stream=None, out=None):
+    """Fused (bias +) residual + LayerNorm over the last dimension of ``x``.
+
+    Returns a dict with ``y``, ``residual_out`` (when bias or residual is given,
+    unless disabled), ``mean`` / ``rstd`` (fp32, when ``want_stats``) and
+    ``amax`` (1-element fp32, when ``want_amax``).  ``out`` may supply any of
+    these tensors preallocated.
+    """
+    if want_residual_out is None:
+        want_residual_out = bias is not None or residual is not None
+    return _fwd("ln_fwd", x, bias, residual, gamma, beta, eps, want_residual_out, want_stats,
+                want_stats, want_amax, stream, out)
+
+
+def rms_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-6, *,
+            want_residual_out=None, want_stats=True, want_amax=False, stream=None, out=None):
+    """Fused (bias +) residual + RMSNorm; as :func:`ln_fwd` without ``mean``."""
+    if want_residual_out is None:
+        want_residual_out = bias is not None or residual is not None
+    return _fwd("rms_fwd", x, bias, residual, gamma, beta, eps, want_residual_out, False,
+                want_stats, want_amax, stream, out)
+
+
+def bwd_workspace_size(M, N, dtype):
+    """Workspace bytes ln_bwd / rms_bwd need for an [M, N] problem."""
+    lib = library()
+    n = ctypes.c_size_t(0)
+    code = dtype if isinstance(dtype, int) else (F32 if dtype == torch.float32 else BF16)
+    _check("norm_bwd_workspace_size", lib.norm_bwd_workspace_size(M, N, code, ctypes.byref(n)))
+    return n.value
+
+
+def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbeta, workspace,
+         stream, out):
+    lib = library()
+    N = x.shape[-1]
+    M = x.numel() // N if N else 0
+    dt = x.dtype
+    out = dict(out or {})
+    dx = out.get("dx")
+    if dx is None:
+        dx = torch.empty_like(x)
+    pdt = dt if dparam_dtype is None else dparam_dtype
+    dgamma = out.get("dgamma")
+    if dgamma is None and want_dgamma:
+        dgamma = torch.empty(N, dtype=pdt, device=x.device)
+    dbeta = out.get("dbeta")
+    if dbeta is None and want_dbeta:
+        dbeta = torch.empty(N, dtype=pdt, device=x.device)
+    need = bwd_workspace_size(M, N, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    pcode = F32 if pdt == torch.float32 else BF16
+    args = [_ptr(dy, "dy", dt, M * N), _ptr(x, "x"), _ptr(gamma, "gamma", dt, N)]
+    if fn == "ln_bwd":
+        args += [_ptr(mean, "mean", torch.float32, M), _ptr(rstd, "rstd", torch.float32, M)]
+    else:
+        args += [_ptr(rstd, "rstd", torch.float32, M), float(eps)]
+    args += [M, N, _dtype_code(x), _ptr(dx, "dx", dt, M * N),
+             _ptr(dgamma, "dgamma", pdt, N), _ptr(dbeta, "dbeta", pdt, N), pcode,
+             _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+             _stream(stream)]
+    _check(fn, getattr(lib, fn)(*args))
+    return {"dx": dx, "dgamma": dgamma, "dbeta": dbeta}
+
+
+def ln_bwd(dy, x, gamma, mean, rstd, *, dparam_dtype=None, want_dgamma=True, want_dbeta=True,
+           workspace=None, stream=None, out=None):
+    """LayerNorm backward (dx, dgamma, dbeta) from one read of dy and x.
+    ``dparam_dtype`` (default: x's dtype) is the type of dgamma / dbeta."""
+    return _bwd("ln_bwd", dy, x, gamma, mean, rstd, 0.0, dparam_dtype, want_dgamma, want_dbeta,
+                workspace, stream, out)
+
+
+def rms_bwd(dy, x, gamma, rstd=None, eps=1e-6, *, dparam_dtype=None, want_dgamma=True,
+            want_dbeta=False, workspace=None, stream=None, out=None):
+    """RMSNorm backward; ``rstd=None`` recomputes it from ``x`` and ``eps``."""
+    return _bwd("rms_bwd", dy, x, gamma, None, rstd, eps, dparam_dtype, want_dgamma, want_dbeta,
+                workspace, stream, out)

@@ -1,0 +1,177 @@
+// device.hpp -- gfx950 device helpers shared by the normalisation kernels:
+// 16-byte vector I/O of fp32 / bf16 rows with fp32 compute, bf16 rounding to
+// nearest-even through the hardware converter, and wave64 group reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nf {
+
+// bf16 storage tag: the upper half of a binary32 pattern.
+struct bf16 {
+    uint16_t bits;
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest, ties to even; v_cvt_pk_bf16_f32),
+// element `a` in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// Vector I/O.  VecIO<T, VEC> moves VEC consecutive elements of type T between
+// memory and float registers.  VEC = 16 / sizeof(T) is one 16-byte access per
+// lane (the caller guarantees 16-byte alignment); VEC = 1 is element-wise.
+// `Raw` is the packed register form, kept for values reused across rows.
+// store() rounds to T; round() returns the values as they were stored.
+// ---------------------------------------------------------------------------
+template <typename T, int VEC>
+struct VecIO;
+
+template <>
+struct VecIO<bf16, 8> {
+    using Raw = uint4;
+    static __device__ __forceinline__ Raw load_raw(const void *base, int64_t idx)
+    {
+        return *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + idx);
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *f)
+    {
+        f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
+        f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+        f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
+        f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+    }
+    static __device__ __forceinline__ Raw pack(const float *f)
+    {
+        return uint4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+    }
+    static __device__ __forceinline__ void store_raw(void *base, int64_t idx, const Raw &r)
+    {
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + idx) = r;
+    }
+};
+
+template <>
+struct VecIO<bf16, 1> {
+    using Raw = uint32_t; // pattern in the upper half, i.e. the float's bits
+    static __device__ __forceinline__ Raw load_raw(const void *base, int64_t idx)
+    {
+        return uint32_t(static_cast<const uint16_t *>(base)[idx]) << 16;
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *f) { f[0] = __uint_as_float(r); }
+    static __device__ __forceinline__ Raw pack(const float *f) { return pack_bf16x2(f[0], 0.f) << 16; }
+    static __device__ __forceinline__ void store_raw(void *base, int64_t idx, const Raw &r)
+    {
+        static_cast<uint16_t *>(base)[idx] = uint16_t(r >> 16);
+    }
+};
+
+template <>
+struct VecIO<float, 4> {
+    using Raw = float4;
+    static __device__ __forceinline__ Raw load_raw(const void *base, int64_t idx)
+    {
+        return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *f)
+    {
+        f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
+    }
+    static __device__ __forceinline__ Raw pack(const float *f) { return float4{f[0], f[1], f[2], f[3]}; }
+    static __device__ __forceinline__ void store_raw(void *base, int64_t idx, const Raw &r)
+    {
+        *reinterpret_cast<float4 *>(static_cast<float *>(base) + idx) = r;
+    }
+};
+
+template <>
+struct VecIO<float, 1> {
+    using Raw = float;
+    static __device__ __forceinline__ Raw load_raw(const void *base, int64_t idx)
+    {
+        return static_cast<const float *>(base)[idx];
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *f) { f[0] = r; }
+    static __device__ __forceinline__ Raw pack(const float *f) { return f[0]; }
+    static __device__ __forceinline__ void store_raw(void *base, int64_t idx, const Raw &r)
+    {
+        static_cast<float *>(base)[idx] = r;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Group reductions over aligned groups of W lanes of a wave64 (W a power of
+// two, 1..64).  Every lane of a group receives the same bits: each step
+// combines a lane with its partner by a commutative operation.
+//   W <= 16 : DPP within a row of 16 lanes (quad_perm xor 1 / xor 2,
+//             row_half_mirror, row_mirror)
+//   W  = 32 : + v_permlane16_swap (rows 0<->1, 2<->3)
+//   W  = 64 : + v_permlane32_swap (lanes 0-31 <-> 32-63)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+struct OpSum {
+    static __device__ __forceinline__ float apply(float a, float b) { return a + b; }
+};
+struct OpMax {
+    static __device__ __forceinline__ float apply(float a, float b) { return fmaxf(a, b); }
+};
+
+template <class Op>
+__device__ __forceinline__ float xor16_combine(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return Op::apply(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <class Op>
+__device__ __forceinline__ float xor32_combine(float v)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return Op::apply(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int W, class Op>
+__device__ __forceinline__ float group_reduce(float v)
+{
+    static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+    if constexpr (W >= 2) v = Op::apply(v, dpp<0xB1>(v));  // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v = Op::apply(v, dpp<0x4E>(v));  // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v = Op::apply(v, dpp<0x141>(v)); // row_half_mirror
+    if constexpr (W >= 16) v = Op::apply(v, dpp<0x140>(v)); // row_mirror
+    if constexpr (W >= 32) v = xor16_combine<Op>(v);
+    if constexpr (W >= 64) v = xor32_combine<Op>(v);
+    return v;
+}
+
+// Combine the values of lanes l, l + W, l + 2W, ... (W < 64) so that every
+// lane holds the sum over the lanes of the wave that share (lane mod W).
+// Used to fold teams of W lanes that cover the same columns.
+template <int W>
+__device__ __forceinline__ float fold_teams_sum(float v)
+{
+    static_assert(W >= 1 && W <= 64, "team width");
+    if constexpr (W <= 8) v += __shfl_xor(v, 8);
+    if constexpr (W <= 4) v += __shfl_xor(v, 4);
+    if constexpr (W <= 2) v += __shfl_xor(v, 2);
+    if constexpr (W <= 1) v += __shfl_xor(v, 1);
+    if constexpr (W <= 16) v = xor16_combine<OpSum>(v);
+    if constexpr (W <= 32) v = xor32_combine<OpSum>(v);
+    return v;
+}
+
+} // namespace nf

@@ -1,0 +1,74 @@
+// internal.hpp -- host/device interface between the C-ABI layer (api.cpp)
+// and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nf {
+
+// Arguments of one forward call (pointers are device memory; optional ones
+// may be null).
+struct FwdArgs {
+    const void *x, *bias, *res, *gamma, *beta;
+    void *y, *res_out;
+    float *mean, *rstd;
+    unsigned *amax; // bit pattern of a non-negative float, combined with atomicMax
+    int64_t M;
+    int N;
+    float eps;
+};
+
+// Arguments of one backward stage-1 call.  `ws` holds the per-workgroup
+// column partials: dgamma partials [grid][N], then dbeta partials [grid][N].
+struct BwdArgs {
+    const void *dy, *x, *gamma;
+    const float *mean, *rstd; // rstd null (RMSNorm only): recompute from x
+    void *dx;
+    float *ws;
+    int64_t M;
+    int N;
+    float eps;
+};
+
+typedef hipError_t (*FwdLaunch)(const FwdArgs &, int grid, hipStream_t);
+typedef hipError_t (*BwdLaunch)(const BwdArgs &, int grid, hipStream_t);
+// Resident workgroups per CU of a kernel (HIP occupancy query on the
+// current device).
+typedef int (*OccFn)();
+
+// One row-kernel shape: a team of `lpr` lanes owns a row; each lane holds
+// `vpl` vectors of `vec` elements; a workgroup holds `teams` teams.
+// `capacity` = lpr * vpl * vec is the longest row the shape covers.
+struct RowShape {
+    int lpr, vpl, teams, vec;
+    int capacity() const { return lpr * vpl * vec; }
+    int threads() const { return lpr * teams; }
+};
+
+struct FwdEntry {
+    RowShape shape;
+    FwdLaunch ln, rms;
+    OccFn occ_ln, occ_rms;
+};
+struct BwdEntry {
+    RowShape shape;
+    BwdLaunch ln, rms;
+    OccFn occ_ln, occ_rms;
+};
+
+// Tables of instantiated shapes, ordered by capacity; vectorised = 16-byte
+// accesses (else element-wise).  One translation unit per dtype/direction.
+const FwdEntry *fwd_table_f32(bool vectorised, int *count);
+const FwdEntry *fwd_table_bf16(bool vectorised, int *count);
+const BwdEntry *bwd_table_f32(bool vectorised, int *count);
+const BwdEntry *bwd_table_bf16(bool vectorised, int *count);
+
+// Small kernels.
+hipError_t launch_zero_u32(unsigned *p, hipStream_t s);
+// Column sums of the stage-1 partials; writes dgamma / dbeta (each optional)
+// in fp32 (out_dtype 0) or bf16 (1).  grid_parts = 0 writes zeros.
+hipError_t launch_colsum(const float *ws, int grid_parts, int N, void *dgamma, void *dbeta,
+                         int out_dtype, hipStream_t s);
+
+} // namespace nf

@@ -1,0 +1,35 @@
+// shapes.hpp -- the row-kernel shapes instantiated for each dtype, as
+// X(T, VEC, LPR, VPL, TEAMS) lists ordered by row capacity LPR * VPL * VEC.
+// The host picks the first shape whose capacity covers N.
+//
+// 16-byte path (VEC = 16 / sizeof(T)); workgroups of 256 threads, or one
+// team of LPR threads when LPR > 256:
+//   bf16 capacities: 64 128 256 384 512 768 1024 1536 2048 4096 8192 16384
+//   fp32 capacities: 32 64 128 192 256 384 512 768 1024 2048 4096 8192 16384
+// Element-wise path (VEC = 1), for rows that are not whole 16-byte vectors
+// or pointers that are not 16-byte aligned: 256 512 1024 4096 16384.
+#pragma once
+
+#define NF_SHAPES_COMMON(X, T, VEC)                                                              \
+    X(T, VEC, 8, 1, 32)                                                                          \
+    X(T, VEC, 16, 1, 16)                                                                         \
+    X(T, VEC, 16, 2, 16)                                                                         \
+    X(T, VEC, 16, 3, 16)                                                                         \
+    X(T, VEC, 16, 4, 16)                                                                         \
+    X(T, VEC, 32, 3, 8)                                                                          \
+    X(T, VEC, 32, 4, 8)                                                                          \
+    X(T, VEC, 64, 3, 4)                                                                          \
+    X(T, VEC, 64, 4, 4)                                                                          \
+    X(T, VEC, 128, 4, 2)                                                                         \
+    X(T, VEC, 256, 4, 1)                                                                         \
+    X(T, VEC, 512, 4, 1)
+
+#define NF_SHAPES_BF16_VEC(X) NF_SHAPES_COMMON(X, bf16, 8)
+#define NF_SHAPES_F32_VEC(X) NF_SHAPES_COMMON(X, float, 4) X(float, 4, 1024, 4, 1)
+
+#define NF_SHAPES_ELEM(X, T)                                                                     \
+    X(T, 1, 64, 4, 4)                                                                            \
+    X(T, 1, 64, 8, 4)                                                                            \
+    X(T, 1, 64, 16, 4)                                                                           \
+    X(T, 1, 256, 16, 1)                                                                          \
+    X(T, 1, 1024, 16, 1)

@@ -51,7 +51,7 @@ def _load():
                                         vp, vp, vp, vp, vp]
         lib.oracle_norm_fwd.restype = ci
         lib.oracle_norm_bwd.argtypes = [ci, vp, vp, vp, vp, vp, dbl, i64, i64, ci, ci,
-                                        vp, vp, vp, vp, vp]
+                                        vp, vp, vp, vp, vp, vp]
         lib.oracle_norm_bwd.restype = ci
         lib.oracle_round_to_dtype.argtypes = [vp, i64, ci, vp]
         lib.oracle_round_to_dtype.restype = ci
@@ -118,7 +118,8 @@ def norm_bwd(dy, x, gamma=None, mean=None, rstd=None, eps=1e-5, *, rms=False,
     ``mean`` / ``rstd`` are per-row arrays (any float dtype, widened exactly
     to float64); RMSNorm takes ``rstd=None`` to recompute it from ``x``.
     Returns a dict of float64 arrays: ``dx`` (M, N), ``dgamma``, ``dbeta``,
-    ``dgamma_l2``, ``dbeta_l2`` (N,), all unrounded.
+    ``dgamma_l2``, ``dbeta_l2`` (N,), all unrounded, and ``rstd`` (M,), the
+    rstd the gradients used.
     """
     lib = _load()
     dy = _in(dy, dtype, name="dy")
@@ -130,13 +131,15 @@ def norm_bwd(dy, x, gamma=None, mean=None, rstd=None, eps=1e-5, *, rms=False,
     dx = np.empty((M, N), np.float64) if want_dx else None
     out = {k: (np.empty(N, np.float64) if want_params else None)
            for k in ("dgamma", "dbeta", "dgamma_l2", "dbeta_l2")}
+    rstd_used = np.empty(M, np.float64)
     rc = lib.oracle_norm_bwd(int(rms), _ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd),
                              float(eps), M, N, dtype, nthreads or default_threads(), _ptr(dx),
                              _ptr(out["dgamma"]), _ptr(out["dbeta"]), _ptr(out["dgamma_l2"]),
-                             _ptr(out["dbeta_l2"]))
+                             _ptr(out["dbeta_l2"]), _ptr(rstd_used))
     if rc != 0:
         raise ValueError("oracle_norm_bwd rejected its arguments")
     out["dx"] = dx
+    out["rstd"] = rstd_used
     return out
 
 

@@ -358,13 +358,14 @@ static void bwd_col_sums(void *vctx, int64_t j0, int64_t j1)
  *            (NULL = 1); LayerNorm needs mean [M] and rstd [M]; RMSNorm takes
  *            rstd [M] or NULL to recompute it from x with eps.
  *   outputs (each optional): dx [M,N], dgamma [N], dbeta [N] in double,
- *            unrounded; dgamma_l2 / dbeta_l2 [N] = 2-norm of the summed terms.
+ *            unrounded; dgamma_l2 / dbeta_l2 [N] = 2-norm of the summed terms;
+ *            rstd_out [M] = the rstd used (given or recomputed).
  * Returns 0, or -1 on a bad argument.
  */
 int oracle_norm_bwd(int is_rms, const void *dy, const void *x, const void *gamma,
                     const double *mean, const double *rstd, double eps, int64_t M, int64_t N,
                     int dtype, int nthreads, double *dx, double *dgamma, double *dbeta,
-                    double *dgamma_l2, double *dbeta_l2)
+                    double *dgamma_l2, double *dbeta_l2, double *rstd_out)
 {
     if (!dy || !x || M < 0 || N <= 0 || (dtype != OR_F32 && dtype != OR_BF16))
         return -1;
@@ -382,6 +383,8 @@ int oracle_norm_bwd(int is_rms, const void *dy, const void *x, const void *gamma
         parallel_ranges(nthreads, M, bwd_dx_rows, &c);
     if (dgamma || dbeta || dgamma_l2 || dbeta_l2)
         parallel_ranges(nthreads, N, bwd_col_sums, &c);
+    if (rstd_out && M > 0)
+        memcpy(rstd_out, rstd_used, (size_t)M * sizeof(double));
     free(rstd_used);
     return 0;
 }

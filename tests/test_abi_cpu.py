@@ -1,0 +1,162 @@
+"""The C ABI on the CPU: the library loads, exports what include/normfuse.h
+declares, and rejects bad arguments before touching a device.
+
+No call here reaches a kernel launch: every call has exactly one fault that
+the argument checks catch first (fake pointers are never dereferenced).  The
+one check of a fault-free call (NORM_ERR_DEVICE) runs only where no GPU is
+visible.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import normalization_ln_fwd_amd as nf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "normfuse.h")
+
+# Fake, suitably aligned device addresses; never dereferenced.
+P = 0x7F0000000000
+BAD2 = P + 2    # aligned to 2, not 4
+BAD1 = P + 1    # not aligned to 2
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(\w+)\s*\(", text, re.M)) - {"if"})
+
+
+def header_defines():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"#define\s+(NORM_\w+)\s+(\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return nf.library()
+    except nf.NormLibraryMissing as e:
+        pytest.fail(str(e))
+
+
+def test_exports_every_declared_function(lib):
+    funcs = header_functions()
+    assert set(funcs) == set(nf.EXPORTS), funcs
+    for name in funcs:
+        assert hasattr(lib, name), name
+
+
+def test_binding_constants_match_header():
+    d = header_defines()
+    assert d["NORM_F32"] == nf.F32 and d["NORM_BF16"] == nf.BF16
+    assert d["NORM_N_MAX"] == nf.N_MAX
+    for code, name in nf.STATUS.items():
+        assert d[name] == code
+
+
+def test_status_strings(lib):
+    for code in list(nf.STATUS) + [99]:
+        s = lib.norm_status_string(code).decode()
+        assert s and isinstance(s, str)
+    assert lib.norm_status_string(0).decode() == "ok"
+
+
+def fwd_args(**over):
+    a = dict(x=P, bias=None, residual=None, gamma=P, beta=P, eps=1e-5, M=4, N=64, dtype=1,
+             y=P, residual_out=None, mean=P, rstd=P, amax=None, stream=None)
+    a.update(over)
+    return [a[k] for k in ("x", "bias", "residual", "gamma", "beta", "eps", "M", "N", "dtype",
+                           "y", "residual_out", "mean", "rstd", "amax", "stream")]
+
+
+@pytest.mark.parametrize("fn", ["ln_fwd", "rms_fwd"])
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=2), 4), (dict(dtype=-1), 4),
+    (dict(x=None), 1), (dict(y=None), 1),
+    (dict(M=-1), 2), (dict(N=0), 2), (dict(N=16385), 2), (dict(N=-5), 2),
+    (dict(M=2**62), 2),
+    (dict(eps=-1e-3), 3), (dict(eps=math.nan), 3), (dict(eps=math.inf), 3),
+    (dict(x=BAD1), 5), (dict(gamma=BAD1), 5), (dict(y=BAD1), 5),
+    (dict(dtype=0, x=BAD2), 5), (dict(dtype=0, residual=BAD2), 5),
+    (dict(rstd=BAD2), 5), (dict(amax=BAD2), 5),
+])
+def test_forward_rejects(lib, fn, over, code):
+    if fn == "rms_fwd":
+        over = dict(over, mean=None)
+    assert getattr(lib, fn)(*fwd_args(**over)) == code
+
+
+def test_no_rows_allows_null_row_tensors(lib):
+    # validation passes (M = 0, NULL x / y), so the call only fails on the
+    # missing device -- only checked where no GPU is visible
+    if _gpu_visible():
+        pytest.skip("would launch")
+    assert lib.ln_fwd(*fwd_args(M=0, x=None, y=None, mean=None, rstd=None)) == 8
+    assert lib.ln_bwd(*bwd_args("ln_bwd", M=0, dy=None, x=None, dx=None, mean=None,
+                                rstd=None)) == 8
+
+
+def test_rms_forward_takes_no_mean(lib):
+    assert lib.rms_fwd(*fwd_args(mean=P)) == 3
+
+
+def bwd_args(fn, **over):
+    a = dict(dy=P, x=P, gamma=P, mean=P, rstd=P, eps=1e-6, M=4, N=64, dtype=1, dx=P,
+             dgamma=P, dbeta=P, pdtype=0, ws=P, ws_bytes=1 << 20, stream=None)
+    a.update(over)
+    keys = ["dy", "x", "gamma"] + (["mean", "rstd"] if fn == "ln_bwd" else ["rstd", "eps"]) + [
+        "M", "N", "dtype", "dx", "dgamma", "dbeta", "pdtype", "ws", "ws_bytes", "stream"]
+    return [a[k] for k in keys]
+
+
+@pytest.mark.parametrize("fn", ["ln_bwd", "rms_bwd"])
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=3), 4), (dict(pdtype=7), 4),
+    (dict(dy=None), 1), (dict(x=None), 1), (dict(dx=None), 1),
+    (dict(M=-2), 2), (dict(N=0), 2), (dict(N=16385), 2),
+    (dict(dy=BAD1), 5), (dict(dx=BAD1), 5), (dict(rstd=BAD2), 5), (dict(ws=BAD2), 5),
+    (dict(pdtype=0, dgamma=BAD2), 5), (dict(pdtype=1, dbeta=BAD1), 5),
+])
+def test_backward_rejects(lib, fn, over, code):
+    assert getattr(lib, fn)(*bwd_args(fn, **over)) == code
+
+
+def test_ln_backward_needs_stats(lib):
+    assert lib.ln_bwd(*bwd_args("ln_bwd", mean=None)) == 1
+    assert lib.ln_bwd(*bwd_args("ln_bwd", rstd=None)) == 1
+
+
+def test_rms_backward_eps_only_checked_when_recomputing(lib):
+    assert lib.rms_bwd(*bwd_args("rms_bwd", rstd=None, eps=-1.0)) == 3
+    assert lib.rms_bwd(*bwd_args("rms_bwd", rstd=None, eps=math.nan)) == 3
+
+
+def test_workspace_size_rejects(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.norm_bwd_workspace_size(4, 64, 1, None) == 1
+    assert lib.norm_bwd_workspace_size(4, 64, 9, ctypes.byref(n)) == 4
+    assert lib.norm_bwd_workspace_size(4, 0, 1, ctypes.byref(n)) == 2
+    assert lib.norm_bwd_workspace_size(-1, 64, 1, ctypes.byref(n)) == 2
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful without a GPU (would launch)")
+def test_valid_call_without_device_reports_device_error(lib):
+    assert lib.ln_fwd(*fwd_args()) == 8
+    n = ctypes.c_size_t(0)
+    assert lib.norm_bwd_workspace_size(4, 64, 1, ctypes.byref(n)) == 8
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    """The Python layer has no fallback: a missing library is an error."""
+    monkeypatch.setattr(nf, "_lib", None)
+    monkeypatch.setattr(nf, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(nf.NormLibraryMissing):
+        nf.library()

@@ -1,0 +1,159 @@
+"""GPU parity of the mix-order backward (ln_bwd / rms_bwd) against the oracle.
+
+Both sides consume the same inputs: dy, x, gamma, and for LayerNorm the
+fp32 mean / rstd that the oracle forward produced (rounded to fp32), so the
+comparison isolates the backward.  dx is checked row by row (one bf16 ulp or
+1e-5 of the row scale), dgamma / dbeta against the oracle's exact column
+sums relative to max(|sum|, ||terms||_2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import normalization_ln_fwd_amd as nf
+import oracle
+import synth
+from gpu_util import BF16, F32, f64, from_dev, require_gpu, to_dev
+from tolerance import assert_colsums_close, assert_rows_close, dx_term_scale
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520), (64, 1000),
+          (33, 1024), (17, 1536), (9, 2000), (40, 4096), (5, 5000), (3, 16384), (2, 16383),
+          (2500, 384), (1100, 1024)]
+# column sums over at most a few thousand rows in fp32: far inside 1e-5 of
+# the terms' 2-norm
+COLSUM_REL_SMALL = 1e-5
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def make_case(M, N, dtype, rms, seed, outlier_p=0.0, eps=None):
+    inp = synth.make_inputs(M, N, dtype=dtype, seed=seed, names=("x", "dy", "gamma"),
+                            outlier_p=outlier_p)
+    eps = (1e-6 if rms else 1e-5) if eps is None else eps
+    f = oracle.norm_fwd(inp["x"], eps=eps, rms=rms, dtype=dtype, want_u=False, want_y=False)
+    inp["mean"] = f["mean"].astype(np.float32)
+    inp["rstd"] = f["rstd"].astype(np.float32)
+    return inp, eps
+
+
+def run_bwd(rms, inp, dtype, eps, misalign=False, recompute=False, dparam_dtype=None,
+            want_dbeta=True):
+    dy = to_dev(inp["dy"], dtype, misalign)
+    x = to_dev(inp["x"], dtype)
+    g = to_dev(inp["gamma"], dtype)
+    rstd = None if recompute else torch.from_numpy(inp["rstd"]).cuda()
+    if rms:
+        out = nf.rms_bwd(dy, x, g, rstd, eps, dparam_dtype=dparam_dtype, want_dbeta=want_dbeta)
+    else:
+        mean = torch.from_numpy(inp["mean"]).cuda()
+        out = nf.ln_bwd(dy, x, g, mean, rstd, dparam_dtype=dparam_dtype, want_dbeta=want_dbeta)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_bwd(rms, inp, dtype, eps, recompute=False, rows=None):
+    sl = slice(None) if rows is None else rows
+    return oracle.norm_bwd(inp["dy"][sl], inp["x"][sl], inp["gamma"],
+                           None if rms else inp["mean"][sl],
+                           None if recompute else inp["rstd"][sl], eps, rms=rms, dtype=dtype)
+
+
+@pytest.mark.parametrize("M,N", SHAPES)
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("misalign", [False, True], ids=["vec", "elem"])
+def test_bwd_matches_oracle(M, N, rms, dtype, misalign):
+    inp, eps = make_case(M, N, dtype, rms, seed=M * 31 + N)
+    out = run_bwd(rms, inp, dtype, eps, misalign, dparam_dtype=torch.float32)
+    ref = oracle_bwd(rms, inp, dtype, eps)
+    assert_rows_close(f64(out["dx"]), ref["dx"], dtype, "dx",
+                      scale=dx_term_scale(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+    assert_colsums_close(f64(out["dgamma"]), ref["dgamma"], ref["dgamma_l2"], COLSUM_REL_SMALL,
+                         "dgamma")
+    assert_colsums_close(f64(out["dbeta"]), ref["dbeta"], ref["dbeta_l2"], COLSUM_REL_SMALL,
+                         "dbeta")
+
+
+@pytest.mark.parametrize("N", [7, 384, 4096])
+def test_rms_bwd_recomputes_rstd(N):
+    M = 300
+    inp, eps = make_case(M, N, BF16, True, seed=N)
+    out = run_bwd(True, inp, BF16, eps, recompute=True, dparam_dtype=torch.float32)
+    ref = oracle_bwd(True, inp, BF16, eps, recompute=True)
+    assert_rows_close(f64(out["dx"]), ref["dx"], BF16, "dx",
+                      scale=dx_term_scale(inp["dy"], inp["gamma"], ref["rstd"], BF16))
+    assert_colsums_close(f64(out["dgamma"]), ref["dgamma"], ref["dgamma_l2"], COLSUM_REL_SMALL,
+                         "dgamma")
+
+
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+def test_bwd_bf16_params_are_rounded_sums(rms):
+    """dgamma / dbeta requested in bf16: the fp32 column sums rounded to
+    nearest-even, i.e. within one bf16 ulp of the exact sums."""
+    inp, eps = make_case(2000, 384, BF16, rms, seed=77)
+    out = run_bwd(rms, inp, BF16, eps, dparam_dtype=torch.bfloat16)
+    out32 = run_bwd(rms, inp, BF16, eps, dparam_dtype=torch.float32)
+    ref = oracle_bwd(rms, inp, BF16, eps)
+    for k in ("dgamma", "dbeta"):
+        assert out[k].dtype == torch.bfloat16
+        assert torch.equal(out[k], out32[k].to(torch.bfloat16)), k
+        assert_colsums_close(f64(out[k]), ref[k], ref[k + "_l2"], COLSUM_REL_SMALL, k, dtype=BF16)
+
+
+def test_bwd_gamma_absent_means_one():
+    inp, eps = make_case(200, 256, BF16, False, seed=4)
+    x, dy = to_dev(inp["x"], BF16), to_dev(inp["dy"], BF16)
+    mean, rstd = torch.from_numpy(inp["mean"]).cuda(), torch.from_numpy(inp["rstd"]).cuda()
+    out = nf.ln_bwd(dy, x, None, mean, rstd, dparam_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.norm_bwd(inp["dy"], inp["x"], None, inp["mean"], inp["rstd"], eps)
+    assert_rows_close(f64(out["dx"]), ref["dx"], BF16, "dx",
+                      scale=dx_term_scale(inp["dy"], None, ref["rstd"], BF16))
+    assert_colsums_close(f64(out["dgamma"]), ref["dgamma"], ref["dgamma_l2"], COLSUM_REL_SMALL,
+                         "dgamma")
+
+
+def test_bwd_outliers_wide_rows():
+    inp, eps = make_case(256, 4096, BF16, False, seed=5, outlier_p=0.01)
+    out = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32)
+    ref = oracle_bwd(False, inp, BF16, eps)
+    assert_rows_close(f64(out["dx"]), ref["dx"], BF16, "dx",
+                      scale=dx_term_scale(inp["dy"], inp["gamma"], ref["rstd"], BF16))
+    assert_colsums_close(f64(out["dgamma"]), ref["dgamma"], ref["dgamma_l2"], COLSUM_REL_SMALL,
+                         "dgamma")
+
+
+def test_bwd_empty_rows_zero_params():
+    x = torch.empty((0, 384), dtype=torch.bfloat16, device="cuda")
+    st = torch.empty((0,), dtype=torch.float32, device="cuda")
+    dg = torch.full((384,), 7.0, device="cuda")
+    db = torch.full((384,), 7.0, device="cuda")
+    out = nf.ln_bwd(x, x, None, st, st, dparam_dtype=torch.float32,
+                    out={"dgamma": dg, "dbeta": db})
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out["dgamma"]) == 0 and torch.count_nonzero(out["dbeta"]) == 0
+
+
+def test_bwd_rejects_small_workspace():
+    M, N = 1000, 384
+    need = nf.bwd_workspace_size(M, N, torch.bfloat16)
+    assert need > 0
+    x = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    st = torch.ones((M,), dtype=torch.float32, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(nf.NormError) as e:
+        nf.ln_bwd(x, x, None, st, st, workspace=ws)
+    assert e.value.status == 6
+
+
+def test_bwd_is_deterministic():
+    inp, eps = make_case(20000, 384, BF16, False, seed=8)
+    a = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32)
+    b = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32)
+    for k in ("dx", "dgamma", "dbeta"):
+        assert torch.equal(a[k], b[k]), k

@@ -1,0 +1,160 @@
+"""GPU parity of the fused forward (ln_fwd / rms_fwd) against the oracle.
+
+Staged, so that a rare one-ulp difference in the fused sum does not show up
+as a normalisation failure: residual_out against the oracle's rounded exact sum
+(one ulp of the I/O dtype plus the rounding bound of the two fp32 additions), then y / mean / rstd against the oracle run on
+the GPU's own residual_out, then amax bit-exact against the brute-force
+max |y| of the GPU's stored y.  End-to-end y is also checked (two ulps).
+Sizes span several workgroups and a ragged tail; misaligned inputs force
+the element-wise kernels, aligned ones the 16-byte kernels.
+"""
+import numpy as np
+import pytest
+import torch
+
+import normalization_ln_fwd_amd as nf
+import oracle
+import synth
+from gpu_util import BF16, F32, f64, from_dev, require_gpu, to_dev
+from tolerance import assert_fused_add_close, assert_rows_close, assert_within_ulps
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520), (64, 1000),
+          (33, 1024), (17, 1536), (9, 2000), (40, 4096), (5, 5000), (3, 16384), (2, 16383)]
+
+
+def run_fwd(rms, inp, dtype, eps, misalign=False, want_amax=True, parts=None):
+    parts = parts or ("x", "bias", "residual", "gamma", "beta")
+    dev = {k: to_dev(inp[k], dtype, misalign and k == "x") if k in parts else None
+           for k in ("x", "bias", "residual", "gamma", "beta")}
+    fn = nf.rms_fwd if rms else nf.ln_fwd
+    out = fn(dev["x"], dev["bias"], dev["residual"], dev["gamma"], dev["beta"], eps,
+             want_residual_out=True, want_amax=want_amax)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_fwd(rms, inp, dtype, eps, out, parts=("x", "bias", "residual", "gamma", "beta")):
+    g = {k: (inp[k] if k in parts else None) for k in ("x", "bias", "residual", "gamma", "beta")}
+    ref = oracle.norm_fwd(g["x"], g["bias"], g["residual"], g["gamma"], g["beta"], eps, rms=rms,
+                          dtype=dtype)
+    u_gpu = from_dev(out["residual_out"], dtype)
+    # 1. fused add
+    assert_fused_add_close(u_gpu, ref["u"], g, dtype, "residual_out")
+    # 2. normalisation of the GPU's residual_out
+    st = oracle.norm_fwd(u_gpu, None, None, g["gamma"], g["beta"], eps, rms=rms, dtype=dtype)
+    y_gpu = f64(out["y"])
+    assert_rows_close(y_gpu, st["y"], dtype, "y (staged)")
+    if not rms:
+        s = np.maximum(np.max(np.abs(synth.to_f64(u_gpu, dtype)), axis=1), 1e-30)
+        assert np.all(np.abs(f64(out["mean"]) - st["mean"]) <= 1e-5 * s), "mean"
+    rel = np.abs(f64(out["rstd"]) - st["rstd"]) / st["rstd"]
+    assert np.all(rel <= 1e-5), f"rstd: max rel err {rel.max():.3e}"
+    # 3. amax: bit-exact against max |stored y|; and within an ulp of the oracle's
+    if out["amax"] is not None:
+        brute = float(np.max(np.abs(y_gpu))) if y_gpu.size else 0.0
+        assert float(out["amax"].item()) == brute, (out["amax"].item(), brute)
+        assert_within_ulps(np.array([brute]), np.array([ref["amax"]]), dtype, "amax vs oracle")
+    # end to end
+    assert_rows_close(y_gpu, ref["y"], dtype, "y (end to end)", ulps=2.0)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("M,N", SHAPES)
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("misalign", [False, True], ids=["vec", "elem"])
+def test_fwd_matches_oracle(M, N, rms, dtype, misalign):
+    inp = synth.make_inputs(M, N, dtype=dtype, seed=M * 7919 + N)
+    eps = 1e-6 if rms else 1e-5
+    out = run_fwd(rms, inp, dtype, eps, misalign)
+    check_fwd(rms, inp, dtype, eps, out)
+
+
+@pytest.mark.parametrize("parts", [("x",), ("x", "residual"), ("x", "bias"), ("x", "gamma"),
+                                   ("x", "residual", "gamma", "beta")],
+                         ids=["x", "x+res", "x+bias", "x+gamma", "x+res+affine"])
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+def test_fwd_optional_inputs(parts, rms):
+    M, N = 129, 384
+    inp = synth.make_inputs(M, N, dtype=BF16, seed=21)
+    out = run_fwd(rms, inp, BF16, 1e-5, parts=parts)
+    check_fwd(rms, inp, BF16, 1e-5, out, parts=parts)
+
+
+def test_fwd_outlier_rows_variance_precision():
+    """Rows with 1% of elements scaled by 100 (a wide dynamic range)."""
+    M, N = 96, 4096
+    inp = synth.make_inputs(M, N, dtype=BF16, seed=5, outlier_p=0.01)
+    out = run_fwd(False, inp, BF16, 1e-5)
+    check_fwd(False, inp, BF16, 1e-5, out)
+
+
+def test_fwd_large_mean_rows_fp32():
+    """fp32 rows 1000 + N(0,1): a one-pass E[x^2] - E[x]^2 in fp32 would lose
+    the variance here; the two-pass statistics keep it."""
+    M, N = 64, 768
+    rng = np.random.default_rng(3)
+    x = (1000.0 + rng.standard_normal((M, N))).astype(np.float32)
+    inp = {"x": x, "bias": None, "residual": None, "gamma": None, "beta": None}
+    out = run_fwd(False, inp, F32, 1e-5, parts=("x",))
+    check_fwd(False, inp, F32, 1e-5, out, parts=("x",))
+
+
+def test_fwd_constant_rows_and_tiny_n():
+    """Zero-variance rows give y = beta exactly; N = 1 likewise."""
+    for N in (1, 8, 384):
+        M = 20
+        x = np.full((M, N), 0.75, np.float32)
+        beta = synth.make_inputs(1, N, dtype=F32, seed=1, names=("beta",))["beta"]
+        inp = {"x": synth.f32_to_bf16_bits(x), "beta": synth.f32_to_bf16_bits(beta)}
+        dev_x, dev_b = to_dev(inp["x"], BF16), to_dev(inp["beta"], BF16)
+        out = nf.ln_fwd(dev_x, None, None, None, dev_b, 1e-5, want_amax=True)
+        y = from_dev(out["y"], BF16)
+        assert np.array_equal(y, np.broadcast_to(inp["beta"], (M, N)))
+
+
+def test_fwd_empty_rows_sets_amax_zero():
+    x = torch.empty((0, 384), dtype=torch.bfloat16, device="cuda")
+    amax = torch.full((1,), 123.0, device="cuda")
+    out = nf.ln_fwd(x, None, None, None, None, 1e-5, want_amax=True, out={"amax": amax})
+    torch.cuda.synchronize()
+    assert out["amax"].item() == 0.0
+    assert out["y"].shape == (0, 384)
+
+
+def test_fwd_amax_overwrites_previous_value():
+    inp = synth.make_inputs(64, 384, dtype=BF16, seed=2)
+    amax = torch.full((1,), 1e9, device="cuda")
+    out = nf.ln_fwd(to_dev(inp["x"], BF16), None, None, None, None, 1e-5, want_amax=True,
+                    out={"amax": amax})
+    torch.cuda.synchronize()
+    assert out["amax"].item() == float(np.max(np.abs(f64(out["y"]))))
+
+
+def test_fwd_is_deterministic():
+    M, N = 5000, 384
+    inp = synth.make_inputs(M, N, dtype=BF16, seed=9)
+    a = run_fwd(False, inp, BF16, 1e-5)
+    b = run_fwd(False, inp, BF16, 1e-5)
+    for k in ("y", "residual_out", "mean", "rstd", "amax"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_fwd_on_a_side_stream():
+    """Work is enqueued on the stream given, not the default one."""
+    inp = synth.make_inputs(1000, 384, dtype=BF16, seed=4)
+    x = to_dev(inp["x"], BF16)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = nf.ln_fwd(x, None, None, None, None, 1e-5, want_amax=True, stream=s)
+    s.synchronize()
+    ref = nf.ln_fwd(x, None, None, None, None, 1e-5, want_amax=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out["y"], ref["y"]) and torch.equal(out["amax"], ref["amax"])
