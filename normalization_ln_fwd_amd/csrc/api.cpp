@@ -1,5 +1,5 @@
 // api.cpp -- the C ABI declared in include/normfuse.h: argument checks,
-// choice of kernel shape, persistent-grid sizing and launches on the
+// choice of kernel shape, row-group walk sizing and launches on the
 // caller's stream.  Nothing here allocates device memory.
 #include "normfuse.h"
 
@@ -8,9 +8,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "internal.hpp"
 
@@ -19,80 +16,79 @@ namespace {
 using namespace nf;
 
 // ---------------------------------------------------------------- device
-constexpr int kMaxDevices = 64;
-std::once_flag g_cu_once[kMaxDevices];
-int g_cus[kMaxDevices];
-
-norm_status_t current_device(int *dev, int *cus)
+norm_status_t check_device()
 {
-    if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= kMaxDevices)
+    int dev = -1, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
         return NORM_ERR_DEVICE;
-    const int d = *dev;
-    std::call_once(g_cu_once[d], [d] {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess)
-            n = 0;
-        g_cus[d] = n;
-    });
-    if (g_cus[d] <= 0)
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
         return NORM_ERR_DEVICE;
-    *cus = g_cus[d];
     return NORM_OK;
 }
 
-// Resident workgroups per CU of one kernel on one device, cached.
-int resident_per_cu(OccFn fn, int dev)
-{
-    static std::mutex mu;
-    static std::map<std::pair<OccFn, int>, int> cache;
-    std::lock_guard<std::mutex> lock(mu);
-    auto key = std::make_pair(fn, dev);
-    auto it = cache.find(key);
-    if (it != cache.end())
-        return it->second;
-    const int n = fn();
-    cache[key] = n;
-    return n;
-}
-
 // ------------------------------------------------------ optional tuning knobs
-// NORMFUSE_{FWD,BWD}_WG_PER_CU : cap on workgroups per CU of the persistent grid
-// NORMFUSE_{FWD,BWD}_SHAPE     : "LPRxVPL" -- use that instantiated shape when it
-//                                covers the row (tests use it to cross-check shapes)
+// NORMFUSE_{FWD,BWD}_SHAPE          : "LPRxVPL" or "LPRxVPLxTEAMS" -- use that
+//                                     instantiated shape when it covers the row
+// NORMFUSE_{FWD,BWD}_GROUPS_PER_WG  : row groups per workgroup (K)
+// NORMFUSE_{FWD,BWD}_INTERLEAVE     : workgroups per interleave block (A)
+// Read on every call (a few getenv lookups, far below launch cost), so a
+// process can change them between calls; tests use them to cross-check
+// shapes and groupings against each other.
+constexpr int kFwdGroupsPerWg = 2;
+constexpr int kBwdGroupsPerWg = 4;
+constexpr int kFwdInterleave = 1024;
+constexpr int kBwdInterleave = 256;
+
 struct Knobs {
-    int fwd_wg_per_cu = 0, bwd_wg_per_cu = 0;
-    int fwd_lpr = 0, fwd_vpl = 0, bwd_lpr = 0, bwd_vpl = 0;
+    int fwd_lpr = 0, fwd_vpl = 0, bwd_lpr = 0, bwd_vpl = 0, fwd_teams = 0, bwd_teams = 0;
+    int fwd_k = kFwdGroupsPerWg, bwd_k = kBwdGroupsPerWg;
+    int fwd_a = kFwdInterleave, bwd_a = kBwdInterleave;
 };
 
-void parse_shape(const char *s, int *lpr, int *vpl)
+// "LPRxVPL" or "LPRxVPLxTEAMS"
+void parse_shape(const char *s, int *lpr, int *vpl, int *teams)
 {
-    if (s && std::sscanf(s, "%dx%d", lpr, vpl) != 2) {
+    if (!s)
+        return;
+    const int n = std::sscanf(s, "%dx%dx%d", lpr, vpl, teams);
+    if (n < 2) {
         *lpr = 0;
         *vpl = 0;
     }
+    if (n < 3)
+        *teams = 0;
 }
 
-const Knobs &knobs()
+void parse_positive(const char *s, int *out)
 {
-    static Knobs k = [] {
-        Knobs r;
-        if (const char *s = std::getenv("NORMFUSE_FWD_WG_PER_CU"))
-            r.fwd_wg_per_cu = std::atoi(s);
-        if (const char *s = std::getenv("NORMFUSE_BWD_WG_PER_CU"))
-            r.bwd_wg_per_cu = std::atoi(s);
-        parse_shape(std::getenv("NORMFUSE_FWD_SHAPE"), &r.fwd_lpr, &r.fwd_vpl);
-        parse_shape(std::getenv("NORMFUSE_BWD_SHAPE"), &r.bwd_lpr, &r.bwd_vpl);
-        return r;
-    }();
-    return k;
+    if (s) {
+        const int v = std::atoi(s);
+        if (v > 0)
+            *out = v;
+    }
+}
+
+Knobs knobs()
+{
+    Knobs r;
+    parse_shape(std::getenv("NORMFUSE_FWD_SHAPE"), &r.fwd_lpr, &r.fwd_vpl, &r.fwd_teams);
+    parse_shape(std::getenv("NORMFUSE_BWD_SHAPE"), &r.bwd_lpr, &r.bwd_vpl, &r.bwd_teams);
+    parse_positive(std::getenv("NORMFUSE_FWD_GROUPS_PER_WG"), &r.fwd_k);
+    parse_positive(std::getenv("NORMFUSE_BWD_GROUPS_PER_WG"), &r.bwd_k);
+    parse_positive(std::getenv("NORMFUSE_FWD_INTERLEAVE"), &r.fwd_a);
+    parse_positive(std::getenv("NORMFUSE_BWD_INTERLEAVE"), &r.bwd_a);
+    return r;
 }
 
 template <class Entry>
-const Entry *pick_shape(const Entry *tab, int n, int N, int force_lpr, int force_vpl)
+const Entry *pick_shape(const Entry *tab, int n, int N, int force_lpr, int force_vpl,
+                        int force_teams)
 {
     if (force_lpr > 0) {
         for (int i = 0; i < n; ++i)
             if (tab[i].shape.lpr == force_lpr && tab[i].shape.vpl == force_vpl &&
+                (force_teams == 0 || tab[i].shape.teams == force_teams) &&
                 tab[i].shape.capacity() >= N)
                 return &tab[i];
     }
@@ -102,29 +98,35 @@ const Entry *pick_shape(const Entry *tab, int n, int N, int force_lpr, int force
     return nullptr;
 }
 
-const FwdEntry *fwd_entry(int dtype, bool vec, int N)
+const FwdEntry *fwd_entry(int dtype, bool vec, int N, const Knobs &k)
 {
     int n = 0;
     const FwdEntry *tab = dtype == NORM_F32 ? fwd_table_f32(vec, &n) : fwd_table_bf16(vec, &n);
-    return pick_shape(tab, n, N, knobs().fwd_lpr, knobs().fwd_vpl);
+    return pick_shape(tab, n, N, k.fwd_lpr, k.fwd_vpl, k.fwd_teams);
 }
 
-const BwdEntry *bwd_entry(int dtype, bool vec, int N)
+const BwdEntry *bwd_entry(int dtype, bool vec, int N, const Knobs &k)
 {
     int n = 0;
     const BwdEntry *tab = dtype == NORM_F32 ? bwd_table_f32(vec, &n) : bwd_table_bf16(vec, &n);
-    return pick_shape(tab, n, N, knobs().bwd_lpr, knobs().bwd_vpl);
+    return pick_shape(tab, n, N, k.bwd_lpr, k.bwd_vpl, k.bwd_teams);
 }
 
-// Persistent grid: as many workgroups as are resident at once, but no more
-// than there are row groups.
-int64_t persistent_grid(int64_t M, int teams, int cus, int per_cu, int cap_per_cu)
+// Grid of a row-group walk: n_groups groups of `teams` rows, K per workgroup.
+struct Walk {
+    int64_t n_groups = 0, grid = 0;
+    int K = 1, A = 1;
+};
+
+norm_status_t plan_walk(int64_t M, int teams, int K, int A, Walk *w)
 {
-    if (cap_per_cu > 0 && cap_per_cu < per_cu)
-        per_cu = cap_per_cu;
-    const int64_t want = (M + teams - 1) / teams;
-    const int64_t have = int64_t(cus) * per_cu;
-    return want < have ? want : have;
+    w->n_groups = (M + teams - 1) / teams;
+    w->K = K;
+    w->A = A;
+    w->grid = (w->n_groups + K - 1) / K;
+    if (w->grid > INT32_MAX)
+        return NORM_ERR_SHAPE;
+    return NORM_OK;
 }
 
 // ------------------------------------------------------------- validation
@@ -181,13 +183,16 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
         if (p && !aligned(p, 4))
             return NORM_ERR_ALIGN;
 
-    int dev = 0, cus = 0;
-    if (norm_status_t st = current_device(&dev, &cus))
+    if (norm_status_t st = check_device())
         return st;
+    const Knobs kn = knobs();
     const bool vec = vectorisable(N, dtype, {x, bias, residual, gamma, beta, y, residual_out});
-    const FwdEntry *e = fwd_entry(dtype, vec, int(N));
+    const FwdEntry *e = fwd_entry(dtype, vec, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
+    Walk w;
+    if (norm_status_t st = plan_walk(M, e->shape.teams, kn.fwd_k, kn.fwd_a, &w))
+        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     unsigned *amax_bits = reinterpret_cast<unsigned *>(amax);
@@ -197,8 +202,6 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     if (M == 0)
         return NORM_OK;
 
-    const int per_cu = resident_per_cu(rms ? e->occ_rms : e->occ_ln, dev);
-    const int64_t grid = persistent_grid(M, e->shape.teams, cus, per_cu, knobs().fwd_wg_per_cu);
     FwdArgs a;
     a.x = x;
     a.bias = bias;
@@ -211,26 +214,31 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     a.rstd = rstd;
     a.amax = amax_bits;
     a.M = M;
+    a.n_groups = w.n_groups;
     a.N = int(N);
+    a.K = w.K;
+    a.A = w.A;
     a.eps = eps;
-    return launched((rms ? e->rms : e->ln)(a, int(grid), s));
+    return launched((rms ? e->rms : e->ln)(a, int(w.grid), s));
 }
 
 // ----------------------------------------------------------------- backward
-// Stage-1 grid of the backward for the shape used on these pointers.
-norm_status_t bwd_plan(bool rms, int64_t M, int64_t N, int32_t dtype, bool vec, int dev, int cus,
-                       const BwdEntry **entry, int64_t *grid)
+// Stage-1 walk of the backward for the shape used on these pointers, and
+// the workspace it needs: the stage-1 partials (two blocks of `grid` rows of
+// N floats) and, for many partial rows, the second summation level.
+norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, const Knobs &kn,
+                       const BwdEntry **entry, Walk *w, size_t *ws_bytes)
 {
-    const BwdEntry *e = bwd_entry(dtype, vec, int(N));
+    const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    const int per_cu = resident_per_cu(rms ? e->occ_rms : e->occ_ln, dev);
+    if (norm_status_t st = plan_walk(M, e->shape.teams, kn.bwd_k, kn.bwd_a, w))
+        return st;
     *entry = e;
-    *grid = M == 0 ? 0 : persistent_grid(M, e->shape.teams, cus, per_cu, knobs().bwd_wg_per_cu);
+    const size_t rows = size_t(w->grid) + size_t(colsum_level2_rows(w->grid));
+    *ws_bytes = 2 * rows * size_t(N) * sizeof(float);
     return NORM_OK;
 }
-
-size_t ws_bytes_for(int64_t grid, int64_t N) { return size_t(2) * size_t(grid) * size_t(N) * 4; }
 
 norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *gamma,
                          const float *mean, const float *rstd, float eps, int64_t M, int64_t N,
@@ -257,18 +265,19 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         if (p && !aligned(p, ps))
             return NORM_ERR_ALIGN;
 
-    int dev = 0, cus = 0;
-    if (norm_status_t st = current_device(&dev, &cus))
+    if (norm_status_t st = check_device())
         return st;
+    const Knobs kn = knobs();
     const bool vec = vectorisable(N, dtype, {dy, x, gamma, dx});
     const BwdEntry *e = nullptr;
-    int64_t grid = 0;
-    if (norm_status_t st = bwd_plan(rms, M, N, dtype, vec, dev, cus, &e, &grid))
+    Walk w;
+    size_t need = 0;
+    if (norm_status_t st = bwd_plan(M, N, dtype, vec, kn, &e, &w, &need))
         return st;
-    const size_t need = ws_bytes_for(grid, N);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return NORM_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    float *ws = static_cast<float *>(workspace);
 
     if (M > 0) {
         BwdArgs a;
@@ -278,15 +287,18 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         a.mean = mean;
         a.rstd = rstd;
         a.dx = dx;
-        a.ws = static_cast<float *>(workspace);
+        a.ws = ws;
         a.M = M;
+        a.n_groups = w.n_groups;
         a.N = int(N);
+        a.K = w.K;
+        a.A = w.A;
         a.eps = eps;
-        if (norm_status_t st = launched((rms ? e->rms : e->ln)(a, int(grid), s)))
+        if (norm_status_t st = launched((rms ? e->rms : e->ln)(a, int(w.grid), s)))
             return st;
     }
-    return launched(launch_colsum(static_cast<const float *>(workspace), int(grid), int(N), dgamma,
-                                  dbeta, dparam_dtype, s));
+    float *level2 = ws ? ws + 2 * size_t(w.grid) * size_t(N) : nullptr;
+    return launched(launch_colsum(ws, int(w.grid), int(N), dgamma, dbeta, dparam_dtype, level2, s));
 }
 
 } // namespace
@@ -317,25 +329,23 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
         return NORM_ERR_DTYPE;
     if (norm_status_t st = check_shape(M, N))
         return st;
-    int dev = 0, cus = 0;
-    if (norm_status_t st = current_device(&dev, &cus))
+    if (norm_status_t st = check_device())
         return st;
     // Largest need over the kernels a call of this shape may take (the
-    // 16-byte path or the element-wise one, LayerNorm or RMSNorm).
+    // 16-byte path or the element-wise one).
+    const Knobs kn = knobs();
     size_t best = 0;
     const int vec = int(16 / elem_size(dtype));
     for (int v = 0; v < 2; ++v) {
         if (v == 1 && N % vec != 0)
             continue;
-        for (int rms = 0; rms < 2; ++rms) {
-            const BwdEntry *e = nullptr;
-            int64_t grid = 0;
-            if (norm_status_t st = bwd_plan(rms != 0, M, N, dtype, v == 1, dev, cus, &e, &grid))
-                return st;
-            const size_t b = ws_bytes_for(grid, N);
-            if (b > best)
-                best = b;
-        }
+        const BwdEntry *e = nullptr;
+        Walk w;
+        size_t b = 0;
+        if (norm_status_t st = bwd_plan(M, N, dtype, v == 1, kn, &e, &w, &b))
+            return st;
+        if (b > best)
+            best = b;
     }
     *bytes = best;
     return NORM_OK;

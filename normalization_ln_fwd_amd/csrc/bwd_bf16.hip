@@ -7,9 +7,7 @@ namespace nf {
 #define NF_ENTRY(T, VEC, LPR, VPL, TEAMS)                                                          \
     {{LPR, VPL, TEAMS, VEC},                                                                     \
      &launch_bwd<T, VEC, LPR, VPL, TEAMS, false>,                                                 \
-     &launch_bwd<T, VEC, LPR, VPL, TEAMS, true>,                                                  \
-     &occupancy_bwd<T, VEC, LPR, VPL, TEAMS, false>,                                              \
-     &occupancy_bwd<T, VEC, LPR, VPL, TEAMS, true>},
+     &launch_bwd<T, VEC, LPR, VPL, TEAMS, true>},
 
 static const BwdEntry k_vec[] = {NF_SHAPES_BF16_VEC(NF_ENTRY)};
 static const BwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, bf16)};

@@ -16,17 +16,31 @@ hipError_t launch_zero_u32(unsigned *p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_colsum(const float *ws, int grid_parts, int N, void *dgamma, void *dbeta,
-                         int out_dtype, hipStream_t s)
+hipError_t launch_colsum(const float *ws, int parts, int N, void *dgamma, void *dbeta,
+                         int out_dtype, float *level2, hipStream_t s)
 {
     if (dgamma == nullptr && dbeta == nullptr)
         return hipSuccess;
-    const dim3 grid((N + COLSUM_COLS - 1) / COLSUM_COLS, 2);
-    const dim3 block(COLSUM_COLS * COLSUM_SLICES);
+    const unsigned tiles = unsigned((N + COLSUM_COLS - 1) / COLSUM_COLS);
+    const dim3 block(COLSUM_COLS * COLSUM_SUB);
+    const float *src = ws;
+    int rows = parts;
+    const int s2 = colsum_level2_rows(parts);
+    if (s2 > 0) {
+        const int span = (parts + s2 - 1) / s2;
+        hipLaunchKernelGGL((colsum_kernel<false, false>), dim3(tiles, s2, 2), block, 0, s, ws,
+                           parts, N, span, level2, nullptr, nullptr);
+        if (hipError_t e = hipGetLastError())
+            return e;
+        src = level2;
+        rows = s2;
+    }
     if (out_dtype == 1)
-        hipLaunchKernelGGL(colsum_kernel<true>, grid, block, 0, s, ws, grid_parts, N, dgamma, dbeta);
+        hipLaunchKernelGGL((colsum_kernel<true, true>), dim3(tiles, 1, 2), block, 0, s, src, rows,
+                           N, rows, nullptr, dgamma, dbeta);
     else
-        hipLaunchKernelGGL(colsum_kernel<false>, grid, block, 0, s, ws, grid_parts, N, dgamma, dbeta);
+        hipLaunchKernelGGL((colsum_kernel<true, false>), dim3(tiles, 1, 2), block, 0, s, src,
+                           rows, N, rows, nullptr, dgamma, dbeta);
     return hipGetLastError();
 }
 

@@ -30,18 +30,36 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Vector I/O.  VecIO<T, VEC> moves VEC consecutive elements of type T between
 // memory and float registers.  VEC = 16 / sizeof(T) is one 16-byte access per
 // lane (the caller guarantees 16-byte alignment); VEC = 1 is element-wise.
-// `Raw` is the packed register form, kept for values reused across rows.
-// store() rounds to T; round() returns the values as they were stored.
+// `Raw` is the packed register form.  load/store are ordinary cached accesses
+// (for the per-column vectors, reused by every row); load_stream /
+// store_stream carry the nontemporal hint, for [M, N] tensors that cross HBM
+// once.  pack() rounds to T (nearest, ties to even); unpack() widens exactly.
 // ---------------------------------------------------------------------------
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 template <typename T, int VEC>
 struct VecIO;
 
 template <>
 struct VecIO<bf16, 8> {
-    using Raw = uint4;
-    static __device__ __forceinline__ Raw load_raw(const void *base, int64_t idx)
+    using Raw = u32x4_t;
+    static __device__ __forceinline__ const Raw *at(const void *b, int64_t i)
     {
-        return *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + idx);
+        return reinterpret_cast<const Raw *>(static_cast<const uint16_t *>(b) + i);
+    }
+    static __device__ __forceinline__ Raw *at(void *b, int64_t i)
+    {
+        return reinterpret_cast<Raw *>(static_cast<uint16_t *>(b) + i);
+    }
+    static __device__ __forceinline__ Raw load(const void *b, int64_t i) { return *at(b, i); }
+    static __device__ __forceinline__ Raw load_stream(const void *b, int64_t i)
+    {
+        return __builtin_nontemporal_load(at(b, i));
+    }
+    static __device__ __forceinline__ void store_stream(void *b, int64_t i, Raw r)
+    {
+        __builtin_nontemporal_store(r, at(b, i));
     }
     static __device__ __forceinline__ void unpack(const Raw &r, float *f)
     {
@@ -52,62 +70,94 @@ struct VecIO<bf16, 8> {
     }
     static __device__ __forceinline__ Raw pack(const float *f)
     {
-        return uint4{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                     pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])};
+        return Raw{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                   pack_bf16x2(f[6], f[7])};
     }
-    static __device__ __forceinline__ void store_raw(void *base, int64_t idx, const Raw &r)
-    {
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(base) + idx) = r;
-    }
+    static __device__ __forceinline__ Raw zero() { return Raw{0u, 0u, 0u, 0u}; }
 };
 
 template <>
 struct VecIO<bf16, 1> {
-    using Raw = uint32_t; // pattern in the upper half, i.e. the float's bits
-    static __device__ __forceinline__ Raw load_raw(const void *base, int64_t idx)
+    using Raw = uint16_t;
+    static __device__ __forceinline__ Raw load(const void *b, int64_t i)
     {
-        return uint32_t(static_cast<const uint16_t *>(base)[idx]) << 16;
+        return static_cast<const uint16_t *>(b)[i];
     }
-    static __device__ __forceinline__ void unpack(const Raw &r, float *f) { f[0] = __uint_as_float(r); }
-    static __device__ __forceinline__ Raw pack(const float *f) { return pack_bf16x2(f[0], 0.f) << 16; }
-    static __device__ __forceinline__ void store_raw(void *base, int64_t idx, const Raw &r)
+    static __device__ __forceinline__ Raw load_stream(const void *b, int64_t i)
     {
-        static_cast<uint16_t *>(base)[idx] = uint16_t(r >> 16);
+        return __builtin_nontemporal_load(static_cast<const uint16_t *>(b) + i);
     }
+    static __device__ __forceinline__ void store_stream(void *b, int64_t i, Raw r)
+    {
+        __builtin_nontemporal_store(r, static_cast<uint16_t *>(b) + i);
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float *f)
+    {
+        f[0] = __uint_as_float(uint32_t(r) << 16);
+    }
+    static __device__ __forceinline__ Raw pack(const float *f)
+    {
+        return uint16_t(pack_bf16x2(f[0], 0.f) & 0xffffu);
+    }
+    static __device__ __forceinline__ Raw zero() { return 0; }
 };
 
 template <>
 struct VecIO<float, 4> {
-    using Raw = float4;
-    static __device__ __forceinline__ Raw load_raw(const void *base, int64_t idx)
+    using Raw = f32x4_t;
+    static __device__ __forceinline__ const Raw *at(const void *b, int64_t i)
     {
-        return *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + idx);
+        return reinterpret_cast<const Raw *>(static_cast<const float *>(b) + i);
+    }
+    static __device__ __forceinline__ Raw *at(void *b, int64_t i)
+    {
+        return reinterpret_cast<Raw *>(static_cast<float *>(b) + i);
+    }
+    static __device__ __forceinline__ Raw load(const void *b, int64_t i) { return *at(b, i); }
+    static __device__ __forceinline__ Raw load_stream(const void *b, int64_t i)
+    {
+        return __builtin_nontemporal_load(at(b, i));
+    }
+    static __device__ __forceinline__ void store_stream(void *b, int64_t i, Raw r)
+    {
+        __builtin_nontemporal_store(r, at(b, i));
     }
     static __device__ __forceinline__ void unpack(const Raw &r, float *f)
     {
         f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
     }
-    static __device__ __forceinline__ Raw pack(const float *f) { return float4{f[0], f[1], f[2], f[3]}; }
-    static __device__ __forceinline__ void store_raw(void *base, int64_t idx, const Raw &r)
-    {
-        *reinterpret_cast<float4 *>(static_cast<float *>(base) + idx) = r;
-    }
+    static __device__ __forceinline__ Raw pack(const float *f) { return Raw{f[0], f[1], f[2], f[3]}; }
+    static __device__ __forceinline__ Raw zero() { return Raw{0.f, 0.f, 0.f, 0.f}; }
 };
 
 template <>
 struct VecIO<float, 1> {
     using Raw = float;
-    static __device__ __forceinline__ Raw load_raw(const void *base, int64_t idx)
+    static __device__ __forceinline__ Raw load(const void *b, int64_t i)
     {
-        return static_cast<const float *>(base)[idx];
+        return static_cast<const float *>(b)[i];
+    }
+    static __device__ __forceinline__ Raw load_stream(const void *b, int64_t i)
+    {
+        return __builtin_nontemporal_load(static_cast<const float *>(b) + i);
+    }
+    static __device__ __forceinline__ void store_stream(void *b, int64_t i, Raw r)
+    {
+        __builtin_nontemporal_store(r, static_cast<float *>(b) + i);
     }
     static __device__ __forceinline__ void unpack(const Raw &r, float *f) { f[0] = r; }
     static __device__ __forceinline__ Raw pack(const float *f) { return f[0]; }
-    static __device__ __forceinline__ void store_raw(void *base, int64_t idx, const Raw &r)
-    {
-        static_cast<float *>(base)[idx] = r;
-    }
+    static __device__ __forceinline__ Raw zero() { return 0.f; }
 };
+
+// Opaque to the optimiser: after this the compiler must assume `r` changed,
+// so values computed from it before (e.g. unpacked floats) are recomputed
+// afterwards instead of being kept live.  Emits no instruction.
+template <typename R>
+__device__ __forceinline__ void reload_barrier(R &r)
+{
+    asm volatile("" : "+v"(r));
+}
 
 // ---------------------------------------------------------------------------
 // Group reductions over aligned groups of W lanes of a wave64 (W a power of
@@ -155,6 +205,45 @@ __device__ __forceinline__ float group_reduce(float v)
     if constexpr (W >= 16) v = Op::apply(v, dpp<0x140>(v)); // row_mirror
     if constexpr (W >= 32) v = xor16_combine<Op>(v);
     if constexpr (W >= 64) v = xor32_combine<Op>(v);
+    return v;
+}
+
+// fp64 group sum over aligned groups of W lanes: the same exchange pattern
+// applied to both 32-bit halves of each value.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo));
+}
+
+__device__ __forceinline__ double join_f64(uint32_t lo, uint32_t hi)
+{
+    return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+template <int W>
+__device__ __forceinline__ double group_sum_f64(double v)
+{
+    static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+    if constexpr (W >= 2) v += dpp_f64<0xB1>(v);
+    if constexpr (W >= 4) v += dpp_f64<0x4E>(v);
+    if constexpr (W >= 8) v += dpp_f64<0x141>(v);
+    if constexpr (W >= 16) v += dpp_f64<0x140>(v);
+    if constexpr (W >= 32) {
+        const uint64_t b = __builtin_bit_cast(uint64_t, v);
+        auto lo = __builtin_amdgcn_permlane16_swap(uint32_t(b), uint32_t(b), false, false);
+        auto hi = __builtin_amdgcn_permlane16_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
+        v = join_f64(lo[0], hi[0]) + join_f64(lo[1], hi[1]);
+    }
+    if constexpr (W >= 64) {
+        const uint64_t b = __builtin_bit_cast(uint64_t, v);
+        auto lo = __builtin_amdgcn_permlane32_swap(uint32_t(b), uint32_t(b), false, false);
+        auto hi = __builtin_amdgcn_permlane32_swap(uint32_t(b >> 32), uint32_t(b >> 32), false, false);
+        v = join_f64(lo[0], hi[0]) + join_f64(lo[1], hi[1]);
+    }
     return v;
 }
 

@@ -7,9 +7,7 @@ namespace nf {
 #define NF_ENTRY(T, VEC, LPR, VPL, TEAMS)                                                          \
     {{LPR, VPL, TEAMS, VEC},                                                                     \
      &launch_fwd<T, VEC, LPR, VPL, TEAMS, false>,                                                 \
-     &launch_fwd<T, VEC, LPR, VPL, TEAMS, true>,                                                  \
-     &occupancy_fwd<T, VEC, LPR, VPL, TEAMS, false>,                                              \
-     &occupancy_fwd<T, VEC, LPR, VPL, TEAMS, true>},
+     &launch_fwd<T, VEC, LPR, VPL, TEAMS, true>},
 
 static const FwdEntry k_vec[] = {NF_SHAPES_BF16_VEC(NF_ENTRY)};
 static const FwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, bf16)};

@@ -9,13 +9,17 @@ namespace nf {
 
 // Arguments of one forward call (pointers are device memory; optional ones
 // may be null).
+// Rows are visited in row groups of `teams` rows; a workgroup takes K row
+// groups, interleaved over blocks of A workgroups (see GroupWalk).
 struct FwdArgs {
     const void *x, *bias, *res, *gamma, *beta;
     void *y, *res_out;
     float *mean, *rstd;
     unsigned *amax; // bit pattern of a non-negative float, combined with atomicMax
     int64_t M;
+    int64_t n_groups;
     int N;
+    int K, A;
     float eps;
 };
 
@@ -27,15 +31,14 @@ struct BwdArgs {
     void *dx;
     float *ws;
     int64_t M;
+    int64_t n_groups;
     int N;
+    int K, A;
     float eps;
 };
 
 typedef hipError_t (*FwdLaunch)(const FwdArgs &, int grid, hipStream_t);
 typedef hipError_t (*BwdLaunch)(const BwdArgs &, int grid, hipStream_t);
-// Resident workgroups per CU of a kernel (HIP occupancy query on the
-// current device).
-typedef int (*OccFn)();
 
 // One row-kernel shape: a team of `lpr` lanes owns a row; each lane holds
 // `vpl` vectors of `vec` elements; a workgroup holds `teams` teams.
@@ -49,12 +52,10 @@ struct RowShape {
 struct FwdEntry {
     RowShape shape;
     FwdLaunch ln, rms;
-    OccFn occ_ln, occ_rms;
 };
 struct BwdEntry {
     RowShape shape;
     BwdLaunch ln, rms;
-    OccFn occ_ln, occ_rms;
 };
 
 // Tables of instantiated shapes, ordered by capacity; vectorised = 16-byte
@@ -66,9 +67,17 @@ const BwdEntry *bwd_table_bf16(bool vectorised, int *count);
 
 // Small kernels.
 hipError_t launch_zero_u32(unsigned *p, hipStream_t s);
-// Column sums of the stage-1 partials; writes dgamma / dbeta (each optional)
-// in fp32 (out_dtype 0) or bf16 (1).  grid_parts = 0 writes zeros.
-hipError_t launch_colsum(const float *ws, int grid_parts, int N, void *dgamma, void *dbeta,
-                         int out_dtype, hipStream_t s);
+// Column sums of the stage-1 partials (two blocks of `parts` rows of N
+// floats at ws); writes dgamma / dbeta (each optional) in fp32 (out_dtype 0)
+// or bf16 (1).  parts = 0 writes zeros.  More than COLSUM_ONE_LEVEL_MAX parts
+// are summed in two levels through `level2` (colsum_level2_rows(parts) rows
+// per block).
+constexpr int COLSUM_ONE_LEVEL_MAX = 256;
+inline int colsum_level2_rows(int64_t parts)
+{
+    return parts <= COLSUM_ONE_LEVEL_MAX ? 0 : int((parts + COLSUM_ONE_LEVEL_MAX - 1) / COLSUM_ONE_LEVEL_MAX);
+}
+hipError_t launch_colsum(const float *ws, int parts, int N, void *dgamma, void *dbeta,
+                         int out_dtype, float *level2, hipStream_t s);
 
 } // namespace nf

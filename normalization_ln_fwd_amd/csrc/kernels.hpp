@@ -1,25 +1,55 @@
 // kernels.hpp -- fused LayerNorm / RMSNorm kernels for gfx950.
 //
-// Row ownership.  A "team" of LPR lanes owns one row at a time; lane `tl` of
-// the team holds VPL vectors of VEC consecutive elements, vector k covering
-// columns [(k*LPR + tl)*VEC, +VEC).  For one k the team's lanes therefore
-// touch one contiguous span of LPR*VEC elements: every access instruction is
-// fully coalesced.  LPR <= 64 packs 64/LPR teams (rows) into a wave and
-// reduces with DPP / permlane inside the wave; LPR > 64 spans LPR/64 waves
-// and finishes its reductions through LDS.  A workgroup holds TEAMS teams
-// and walks rows with a grid-stride loop over a persistent grid, so the
-// per-column vectors (bias, gamma, beta) are loaded once per team and stay
-// in registers.
+// Row ownership.  A "team" of LPR lanes owns one row; lane `tl` of the team
+// holds VPL vectors of VEC consecutive elements, vector k covering columns
+// [(k*LPR + tl)*VEC, +VEC).  For one k the team's lanes touch one contiguous
+// span of LPR*VEC elements, so every access instruction is fully coalesced.
+// LPR <= 64 packs 64/LPR teams (rows) into a wave and reduces with DPP /
+// permlane inside the wave; LPR > 64 spans LPR/64 waves and finishes its
+// reductions through LDS.  A workgroup holds TEAMS teams, i.e. it covers a
+// "row group" of TEAMS consecutive rows at a time.
 //
 // The whole row stays in registers between the statistics and the
 // normalisation (or between the two reductions of the backward): every
-// [M, N] tensor crosses HBM exactly once.
+// [M, N] tensor crosses HBM exactly once, with nontemporal loads and stores.
+//
+// Grid.  Streaming on this GPU is fastest when each workgroup covers a small
+// contiguous piece and exits, so that the workgroups in flight always sweep
+// one compact window of memory: the forward gives each workgroup one row
+// group.  The backward gives each workgroup K row groups (GroupWalk) so that
+// its dgamma / dbeta column partials are written once per K groups.
 #pragma once
+
+#include <type_traits>
 
 #include "device.hpp"
 #include "internal.hpp"
 
+// Whether a workgroup walking several row groups issues the next group's
+// loads before working on the current one (two groups in flight per wave, at
+// the cost of the registers that hold them).
+#ifndef NORMFUSE_PREFETCH
+#define NORMFUSE_PREFETCH 0
+#endif
+
 namespace nf {
+
+// Row groups of workgroup b = q*A + r (A_q = min(A, grid - q*A) workgroups in
+// its block of A): groups q*A*K + k*A_q + r for k < K.  The workgroups of one
+// block sweep K contiguous windows of A_q groups, one window per k, and with
+// grid = ceil(n_groups / K) every group is visited exactly once.
+struct GroupWalk {
+    int64_t base, step;
+    __device__ __forceinline__ GroupWalk(int K, int A)
+    {
+        // grid and A fit 31 bits: 32-bit division (uniform, scalar unit)
+        const uint32_t b = blockIdx.x, q = b / uint32_t(A), r = b - q * uint32_t(A);
+        const uint32_t left = gridDim.x - q * uint32_t(A);
+        step = left < uint32_t(A) ? left : uint32_t(A);
+        base = int64_t(q) * A * K + r;
+    }
+    __device__ __forceinline__ int64_t group(int k) const { return base + k * step; }
+};
 
 // Sum over a team.  LPR <= 64: inside the wave.  LPR > 64: wave partials
 // meet in LDS (double-buffered by `parity`, so one barrier per reduction
@@ -61,6 +91,29 @@ struct TeamLds {
     static constexpr int size = LPR > 64 ? 2 * TEAMS * (LPR / 64) * NV : 1;
 };
 
+// fp64 sum over a team (same scheme as team_sum, one value).
+template <int LPR, int TEAMS>
+__device__ __forceinline__ double team_sum_f64(double v, double *lds, int &parity, int team,
+                                               int wave_in_team, int lane)
+{
+    if constexpr (LPR <= 64) {
+        return group_sum_f64<LPR>(v);
+    } else {
+        constexpr int WPT = LPR / 64;
+        v = group_sum_f64<64>(v);
+        double *b = lds + parity * (TEAMS * WPT);
+        if (lane == 0)
+            b[team * WPT + wave_in_team] = v;
+        __syncthreads();
+        double s = b[team * WPT];
+#pragma unroll
+        for (int w = 1; w < WPT; ++w)
+            s += b[team * WPT + w];
+        parity ^= 1;
+        return s;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Forward: t = (x + bias) + residual (fp32), u = round(t) -> residual_out,
 // statistics of u, y = normalise(u) * gamma + beta -> y, running max |y|.
@@ -72,11 +125,11 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     using Raw = typename IO::Raw;
     constexpr int E = VPL * VEC;
     constexpr int WG = LPR * TEAMS;
-    constexpr int NW = WG / 64;
     static_assert(WG % 64 == 0, "workgroup of whole waves");
 
     __shared__ float red_lds[TeamLds<LPR, TEAMS, 1>::size];
-    __shared__ float max_lds[NW];
+    __shared__ double red_lds_f64[TeamLds<LPR, TEAMS, 1>::size];
+    __shared__ float max_lds[WG / 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -89,121 +142,175 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     const bool has_gamma = a.gamma != nullptr, has_beta = a.beta != nullptr;
     const bool fused_add = has_bias || has_res;
 
-    // Column validity and the per-column vectors, once per team.
     bool cvalid[VPL];
-    Raw bias_r[VPL], gamma_r[VPL], beta_r[VPL];
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int c0 = (k * LPR + tl) * VEC;
-        cvalid[k] = c0 < N; // VEC > 1 implies N % VEC == 0: whole vector valid
-        float zero[VEC] = {};
-        bias_r[k] = (has_bias && cvalid[k]) ? IO::load_raw(a.bias, c0) : IO::pack(zero);
-        gamma_r[k] = (has_gamma && cvalid[k]) ? IO::load_raw(a.gamma, c0) : IO::pack(zero);
-        beta_r[k] = (has_beta && cvalid[k]) ? IO::load_raw(a.beta, c0) : IO::pack(zero);
-    }
+    for (int k = 0; k < VPL; ++k)
+        cvalid[k] = (k * LPR + tl) * VEC < N; // VEC > 1: N % VEC == 0, whole vector valid
 
     float lane_max = 0.f;
     int parity = 0;
-    const int64_t stride = (int64_t)gridDim.x * TEAMS;
-    for (int64_t base = (int64_t)blockIdx.x * TEAMS; base < a.M; base += stride) {
-        const int64_t row = base + team;
+    const GroupWalk walk(a.K, a.A);
+
+    // x and residual of a row group, nontemporal; zeros outside the matrix.
+    // With NORMFUSE_PREFETCH the next group's loads are issued before the
+    // current group is worked on.
+    Raw xn[VPL], rn[VPL];
+    auto issue = [&](int64_t g) {
+        const int64_t row = g * TEAMS + team;
+        const bool rv = g < a.n_groups && row < a.M;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int64_t idx = row * (int64_t)N + (k * LPR + tl) * VEC;
+            const bool ok = rv && cvalid[k];
+            xn[k] = ok ? IO::load_stream(a.x, idx) : IO::zero();
+            rn[k] = (ok && has_res) ? IO::load_stream(a.res, idx) : IO::zero();
+        }
+    };
+    if (NORMFUSE_PREFETCH)
+        issue(walk.group(0));
+
+    for (int kk = 0; kk < a.K; ++kk) {
+        const int64_t grp = walk.group(kk);
+        if (grp >= a.n_groups)
+            break; // uniform over the workgroup; later groups are larger
+        const int64_t row = grp * TEAMS + team;
         const bool rv = row < a.M;
         const int64_t roff = row * (int64_t)N;
+        if (!NORMFUSE_PREFETCH)
+            issue(grp);
 
-        // fused add; u = value actually normalised (rounded to the I/O dtype)
-        float u[E];
+        // Fused add.  ur holds u, the value actually normalised, in its
+        // packed I/O form (exact: u is rounded to T); every later pass
+        // unpacks it again rather than keeping a float copy live.
+        Raw ur[VPL], rr[VPL], br[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            ur[k] = xn[k];
+            rr[k] = rn[k];
+            br[k] = (cvalid[k] && has_bias) ? IO::load(a.bias, (k * LPR + tl) * VEC) : IO::zero();
+        }
+        if (NORMFUSE_PREFETCH && kk + 1 < a.K)
+            issue(walk.group(kk + 1));
+        // fused add; u = round_T((x + bias) + residual), and the row sum of
+        // u for LayerNorm (fp32 for bf16 rows, whose sums of values of
+        // similar magnitude are exact in fp32; fp64 for fp32 rows).
+        using Acc = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
+        Acc sum = Acc(0);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float t[VEC];
+            IO::unpack(ur[k], t);
+            if (fused_add) {
+                float bv[VEC], rv_[VEC];
+                IO::unpack(br[k], bv);
+                IO::unpack(rr[k], rv_);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    t[e] = (t[e] + bv[e]) + rv_[e];
+                ur[k] = IO::pack(t);
+                IO::unpack(ur[k], t);
+            }
+            if constexpr (!RMS) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    sum += Acc(t[e]); // invalid columns hold 0
+            }
+        }
+        if (a.res_out) {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k)
+                if (rv && cvalid[k])
+                    IO::store_stream(a.res_out, roff + (k * LPR + tl) * VEC, ur[k]);
+        }
+        // per-column scale and shift, in flight during the reductions
+        Raw gr[VPL], betar[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
-            const bool ok = rv && cvalid[k];
-            float *uk = &u[k * VEC];
-            Raw xr;
-            if (ok) {
-                xr = IO::load_raw(a.x, roff + c0);
-            } else {
-                float zero[VEC] = {};
-                xr = IO::pack(zero);
-            }
-            IO::unpack(xr, uk);
-            if (fused_add) {
-                if (has_bias) {
-                    float bv[VEC];
-                    IO::unpack(bias_r[k], bv);
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        uk[e] += bv[e];
-                }
-                if (has_res) {
-                    float rvv[VEC] = {};
-                    if (ok)
-                        IO::unpack(IO::load_raw(a.res, roff + c0), rvv);
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        uk[e] += rvv[e];
-                }
-                xr = IO::pack(uk);
-                IO::unpack(xr, uk);
-            }
-            if (a.res_out && ok)
-                IO::store_raw(a.res_out, roff + c0, xr);
+            gr[k] = (cvalid[k] && has_gamma) ? IO::load(a.gamma, c0) : IO::zero();
+            betar[k] = (cvalid[k] && has_beta) ? IO::load(a.beta, c0) : IO::zero();
         }
 
-        // statistics (two passes over registers for LayerNorm)
-        float mean = 0.f, rstd;
+        // Statistics.  LayerNorm keeps its mean as an fp32 pair mean + lo
+        // (lo = the rounding error of the fp32 mean), so that centring stays
+        // accurate when the mean is large next to the spread: d = u - mean is
+        // exact near the mean, sum(d^2) = N var + N lo^2, and the normalised
+        // value is d * rstd - lo * rstd.
+        float mean = 0.f, lo = 0.f, rstd;
         if constexpr (!RMS) {
-            float s[1] = {0.f};
+            if constexpr (std::is_same<T, float>::value) {
+                const double sd =
+                    team_sum_f64<LPR, TEAMS>(sum, red_lds_f64, parity, team, wave_in_team, lane);
+                const double mean_d = sd / double(N);
+                mean = float(mean_d);
+                lo = float(mean_d - double(mean));
+            } else {
+                float sv[1] = {sum};
+                team_sum<LPR, TEAMS, 1>(sv, red_lds, parity, team, wave_in_team, lane);
+                mean = sv[0] / float(N);
+                lo = fmaf(-mean, float(N), sv[0]) / float(N);
+            }
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                s[0] += u[e]; // invalid columns hold 0
-            team_sum<LPR, TEAMS, 1>(s, red_lds, parity, team, wave_in_team, lane);
-            mean = s[0] / float(N);
-            float d[1] = {0.f};
+            for (int k = 0; k < VPL; ++k)
+                reload_barrier(ur[k]);
+            float d2[1] = {0.f};
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
                 if (cvalid[k]) {
+                    float u[VEC];
+                    IO::unpack(ur[k], u);
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        const float z = u[k * VEC + e] - mean;
-                        d[0] += z * z;
+                        const float d = u[e] - mean;
+                        d2[0] = fmaf(d, d, d2[0]);
                     }
                 }
             }
-            team_sum<LPR, TEAMS, 1>(d, red_lds, parity, team, wave_in_team, lane);
-            rstd = rsqrtf(d[0] / float(N) + a.eps);
+            team_sum<LPR, TEAMS, 1>(d2, red_lds, parity, team, wave_in_team, lane);
+            const float var = fmaxf(d2[0] / float(N) - lo * lo, 0.f);
+            rstd = rsqrtf(var + a.eps);
         } else {
-            float s[1] = {0.f};
+            float s2[1] = {0.f};
 #pragma unroll
-            for (int e = 0; e < E; ++e)
-                s[0] += u[e] * u[e];
-            team_sum<LPR, TEAMS, 1>(s, red_lds, parity, team, wave_in_team, lane);
-            rstd = rsqrtf(s[0] / float(N) + a.eps);
+            for (int k = 0; k < VPL; ++k) {
+                float u[VEC];
+                IO::unpack(ur[k], u);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    s2[0] = fmaf(u[e], u[e], s2[0]);
+            }
+            team_sum<LPR, TEAMS, 1>(s2, red_lds, parity, team, wave_in_team, lane);
+            rstd = rsqrtf(s2[0] / float(N) + a.eps);
         }
+        const float lo_r = -lo * rstd;
 
-        // normalise, affine, store, amax
+        // normalise, affine, store; amax over |y| before rounding (rounding
+        // to nearest is monotone, so max |round(y)| = round(max |y|))
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+            reload_barrier(ur[k]);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
             const bool ok = rv && cvalid[k];
-            float gv[VEC], bv[VEC], yv[VEC];
-            IO::unpack(gamma_r[k], gv);
-            IO::unpack(beta_r[k], bv);
+            float u[VEC], gv[VEC], bv[VEC], yv[VEC];
+            IO::unpack(ur[k], u);
+            IO::unpack(gr[k], gv);
+            IO::unpack(betar[k], bv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                float n = (u[k * VEC + e] - mean) * rstd;
+                float n = fmaf(u[e] - mean, rstd, lo_r);
                 if (has_gamma)
-                    n *= gv[e];
-                if (has_beta)
+                    n = has_beta ? fmaf(n, gv[e], bv[e]) : n * gv[e];
+                else if (has_beta)
                     n += bv[e];
                 yv[e] = n;
             }
-            const Raw yr = IO::pack(yv);
             if (ok) {
-                IO::store_raw(a.y, roff + c0, yr);
-                float ys[VEC];
-                IO::unpack(yr, ys);
+                IO::store_stream(a.y, roff + c0, IO::pack(yv));
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    lane_max = fmaxf(lane_max, fabsf(ys[e]));
+                    lane_max = fmaxf(lane_max, fabsf(yv[e]));
             }
         }
         if (tl == 0 && rv) {
@@ -214,9 +321,11 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         }
     }
 
-    // amax, first stage: wave max, then the workgroup's waves through LDS;
-    // second stage: one atomicMax per workgroup on the float's bit pattern
-    // (non-negative floats order like their unsigned patterns).
+    // amax, first stage: wave max through DPP / permlane, then the
+    // workgroup's waves through LDS; second stage: one atomicMax per
+    // workgroup on the float's bit pattern (non-negative floats order like
+    // their unsigned patterns).  Atomics on one address serialise, which is
+    // one reason a workgroup covers several row groups.
     if (a.amax) {
         const float m = group_reduce<64, OpMax>(lane_max);
         if (lane == 0)
@@ -225,18 +334,20 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         if (tid == 0) {
             float mm = max_lds[0];
 #pragma unroll
-            for (int w = 1; w < NW; ++w)
+            for (int w = 1; w < WG / 64; ++w)
                 mm = fmaxf(mm, max_lds[w]);
-            atomicMax(a.amax, __float_as_uint(mm));
+            float r[1] = {mm};
+            VecIO<T, 1>::unpack(VecIO<T, 1>::pack(r), r); // max of the stored y
+            atomicMax(a.amax, __float_as_uint(r[0]));
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Backward stage 1 (mix-order): per row, one load of dy and x; the row
-// reduction gives dx; the column reduction is accumulated in registers across
-// the team's rows, folded over the workgroup in a fixed order and written as
-// this workgroup's partial row of the workspace.
+// reduction gives dx; the column reduction is accumulated in registers over
+// the workgroup's rows, folded over the workgroup in a fixed order and
+// written as this workgroup's partial row of the workspace.
 // ---------------------------------------------------------------------------
 template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS>
 __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
@@ -269,8 +380,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     for (int k = 0; k < VPL; ++k) {
         const int c0 = (k * LPR + tl) * VEC;
         cvalid[k] = c0 < N;
-        float zero[VEC] = {};
-        gamma_r[k] = (has_gamma && cvalid[k]) ? IO::load_raw(a.gamma, c0) : IO::pack(zero);
+        gamma_r[k] = (has_gamma && cvalid[k]) ? IO::load(a.gamma, c0) : IO::zero();
     }
 
     float acc_g[E], acc_b[E];
@@ -281,90 +391,115 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     }
 
     int parity = 0;
-    const int64_t stride = (int64_t)gridDim.x * TEAMS;
-    for (int64_t base = (int64_t)blockIdx.x * TEAMS; base < a.M; base += stride) {
-        const int64_t row = base + team;
+    const GroupWalk walk(a.K, a.A);
+
+    // x, dy and the row statistics of a row group (with NORMFUSE_PREFETCH the
+    // next group's loads are issued before the current group is worked on).
+    Raw xn[VPL], dn[VPL];
+    float mean_n = 0.f, rstd_n = 0.f;
+    auto issue = [&](int64_t g) {
+        const int64_t row = g * TEAMS + team;
+        const bool rv = g < a.n_groups && row < a.M;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int64_t idx = row * (int64_t)N + (k * LPR + tl) * VEC;
+            const bool ok = rv && cvalid[k];
+            xn[k] = ok ? IO::load_stream(a.x, idx) : IO::zero();
+            dn[k] = ok ? IO::load_stream(a.dy, idx) : IO::zero();
+        }
+        mean_n = (rv && !RMS) ? a.mean[row] : 0.f;
+        rstd_n = (rv && !recompute) ? a.rstd[row] : 0.f;
+    };
+    if (NORMFUSE_PREFETCH)
+        issue(walk.group(0));
+
+    for (int kk = 0; kk < a.K; ++kk) {
+        const int64_t grp = walk.group(kk);
+        if (grp >= a.n_groups)
+            break; // uniform over the workgroup; later groups are larger
+        const int64_t row = grp * TEAMS + team;
         const bool rv = row < a.M;
         const int64_t roff = row * (int64_t)N;
+        if (!NORMFUSE_PREFETCH)
+            issue(grp);
 
-        float xv[E], dyv[E], g[E];
+        Raw xr[VPL], dr[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            const int c0 = (k * LPR + tl) * VEC;
-            const bool ok = rv && cvalid[k];
-            float *xk = &xv[k * VEC], *dk = &dyv[k * VEC];
-            if (ok) {
-                IO::unpack(IO::load_raw(a.x, roff + c0), xk);
-                IO::unpack(IO::load_raw(a.dy, roff + c0), dk);
-            } else {
+            xr[k] = xn[k];
+            dr[k] = dn[k];
+            reload_barrier(gamma_r[k]); // unpack gamma here, not once outside the loop
+        }
+        float mean = mean_n, rstd = rstd_n;
+        if (NORMFUSE_PREFETCH && kk + 1 < a.K)
+            issue(walk.group(kk + 1));
+
+        // g = dy * gamma; the rows stay packed and are unpacked per pass
+        float c1, c2 = 0.f;
+        {
+            float s[2] = {0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                float xv[VEC], dv[VEC], gv[VEC];
+                IO::unpack(xr[k], xv);
+                IO::unpack(dr[k], dv);
+                IO::unpack(gamma_r[k], gv);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    xk[e] = 0.f;
-                    dk[e] = 0.f;
+                    const float g = has_gamma ? dv[e] * gv[e] : dv[e]; // invalid: 0
+                    if constexpr (!RMS) {
+                        s[0] += g * ((xv[e] - mean) * rstd);
+                        s[1] += g;
+                    } else {
+                        if (recompute) {
+                            // rstd from the same load: sum x^2 and sum g*x
+                            // reduce together; mean(g*xhat) = rstd * mean(g*x)
+                            s[0] += xv[e] * xv[e];
+                            s[1] += g * xv[e];
+                        } else {
+                            s[0] += g * (xv[e] * rstd);
+                        }
+                    }
                 }
             }
-            float gv[VEC];
-            IO::unpack(gamma_r[k], gv);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                g[k * VEC + e] = has_gamma ? dk[e] * gv[e] : dk[e];
-        }
-
-        float mean = 0.f, rstd = 0.f, c1, c2 = 0.f;
-        if constexpr (!RMS) {
-            if (rv) {
-                mean = a.mean[row];
-                rstd = a.rstd[row];
-            }
-            float s[2] = {0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                s[0] += g[e] * ((xv[e] - mean) * rstd); // invalid: g = 0
-                s[1] += g[e];
-            }
             team_sum<LPR, TEAMS, 2>(s, red_lds, parity, team, wave_in_team, lane);
-            c1 = s[0] / float(N);
-            c2 = s[1] / float(N);
-        } else if (!recompute) {
-            if (rv)
-                rstd = a.rstd[row];
-            float s[2] = {0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                s[0] += g[e] * (xv[e] * rstd);
-            team_sum<LPR, TEAMS, 2>(s, red_lds, parity, team, wave_in_team, lane);
-            c1 = s[0] / float(N);
-        } else {
-            // rstd from the same load: sum x^2 and sum g*x reduce together,
-            // and mean(g*xhat) = rstd * mean(g*x)
-            float s[2] = {0.f, 0.f};
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                s[0] += xv[e] * xv[e];
-                s[1] += g[e] * xv[e];
+            if constexpr (!RMS) {
+                c1 = s[0] / float(N);
+                c2 = s[1] / float(N);
+            } else if (recompute) {
+                rstd = rsqrtf(s[0] / float(N) + a.eps);
+                c1 = rstd * (s[1] / float(N));
+            } else {
+                c1 = s[0] / float(N);
             }
-            team_sum<LPR, TEAMS, 2>(s, red_lds, parity, team, wave_in_team, lane);
-            rstd = rsqrtf(s[0] / float(N) + a.eps);
-            c1 = rstd * (s[1] / float(N));
         }
 
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
+            reload_barrier(xr[k]);
+            reload_barrier(dr[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
             const bool ok = rv && cvalid[k];
-            float dxv[VEC];
+            float xv[VEC], dv[VEC], gv[VEC], dxv[VEC];
+            IO::unpack(xr[k], xv);
+            IO::unpack(dr[k], dv);
+            IO::unpack(gamma_r[k], gv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const int i = k * VEC + e;
-                const float xh = RMS ? xv[i] * rstd : (xv[i] - mean) * rstd;
-                dxv[e] = rstd * (g[i] - c2 - xh * c1);
+                const float g = has_gamma ? dv[e] * gv[e] : dv[e];
+                const float xh = RMS ? xv[e] * rstd : (xv[e] - mean) * rstd;
+                dxv[e] = rstd * (g - c2 - xh * c1);
                 if (ok) {
-                    acc_g[i] += dyv[i] * xh;
-                    acc_b[i] += dyv[i];
+                    acc_g[i] += dv[e] * xh;
+                    acc_b[i] += dv[e];
                 }
             }
             if (ok)
-                IO::store_raw(a.dx, roff + c0, IO::pack(dxv));
+                IO::store_stream(a.dx, roff + c0, IO::pack(dxv));
         }
     }
 
@@ -421,42 +556,54 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Backward stage 2: dgamma_j = sum_g partial[g][j] (g ascending within each of
-// 32 interleaved slices, slices added in order), then the down-cast.
+// Backward stage 2: column sums of the partial rows.  src holds two blocks
+// (dgamma, dbeta) of `rows` rows of N floats.  Workgroup (column tile, slice
+// s, block) adds rows [s*span, min(rows, (s+1)*span)): thread (c, t) takes
+// rows t, t + 4, ... of the slice in ascending order, and the four threads of
+// a column are added in order t = 0..3.  FINAL: one slice, the down-cast and
+// the store to dgamma / dbeta; otherwise slice s writes row s of dst (two
+// blocks of `gridDim.y` rows), the input of the next level.
 // ---------------------------------------------------------------------------
-constexpr int COLSUM_COLS = 32;
-constexpr int COLSUM_SLICES = 32;
+constexpr int COLSUM_COLS = 64;
+constexpr int COLSUM_SUB = 4;
 
-template <bool BF16_OUT>
-__global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SLICES)
-    colsum_kernel(const float *ws, int G, int N, void *dgamma, void *dbeta)
+template <bool FINAL, bool BF16_OUT>
+__global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SUB)
+    colsum_kernel(const float *src, int rows, int N, int span, float *dst, void *dgamma,
+                  void *dbeta)
 {
     const int tx = threadIdx.x % COLSUM_COLS;
     const int ty = threadIdx.x / COLSUM_COLS;
-    const int which = blockIdx.y;
-    void *out = which == 0 ? dgamma : dbeta;
-    if (out == nullptr)
+    const int which = blockIdx.z;
+    if (FINAL && (which == 0 ? dgamma : dbeta) == nullptr)
         return; // uniform over the block
     const int j = blockIdx.x * COLSUM_COLS + tx;
-    const float *part = ws + (int64_t)which * G * N;
-    float s = 0.f;
+    const int s = blockIdx.y;
+    const int r0 = s * span;
+    const int r1 = min(rows, r0 + span);
+    const float *part = src + (int64_t)which * rows * N;
+    float acc = 0.f;
     if (j < N) {
 #pragma unroll 8
-        for (int g = ty; g < G; g += COLSUM_SLICES)
-            s += part[(int64_t)g * N + j];
+        for (int r = r0 + ty; r < r1; r += COLSUM_SUB)
+            acc += part[(int64_t)r * N + j];
     }
-    __shared__ float sl[COLSUM_SLICES][COLSUM_COLS];
-    sl[ty][tx] = s;
+    __shared__ float sl[COLSUM_SUB][COLSUM_COLS];
+    sl[ty][tx] = acc;
     __syncthreads();
     if (ty == 0 && j < N) {
         float t = sl[0][tx];
 #pragma unroll
-        for (int q = 1; q < COLSUM_SLICES; ++q)
+        for (int q = 1; q < COLSUM_SUB; ++q)
             t += sl[q][tx];
-        if constexpr (BF16_OUT)
-            static_cast<uint16_t *>(out)[j] = uint16_t(pack_bf16x2(t, 0.f) & 0xffffu);
-        else
-            static_cast<float *>(out)[j] = t;
+        if constexpr (!FINAL) {
+            dst[((int64_t)which * gridDim.y + s) * N + j] = t;
+        } else if constexpr (BF16_OUT) {
+            static_cast<uint16_t *>(which == 0 ? dgamma : dbeta)[j] =
+                uint16_t(pack_bf16x2(t, 0.f) & 0xffffu);
+        } else {
+            static_cast<float *>(which == 0 ? dgamma : dbeta)[j] = t;
+        }
     }
 }
 
@@ -474,28 +621,6 @@ hipError_t launch_bwd(const BwdArgs &a, int grid, hipStream_t s)
     hipLaunchKernelGGL((bwd_kernel<T, VEC, LPR, VPL, TEAMS, RMS>), dim3(grid), dim3(LPR * TEAMS),
                        0, s, a);
     return hipGetLastError();
-}
-
-template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS>
-int occupancy_fwd()
-{
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&fwd_kernel<T, VEC, LPR, VPL, TEAMS, RMS>),
-            LPR * TEAMS, 0) != hipSuccess)
-        return 1;
-    return n > 0 ? n : 1;
-}
-
-template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS>
-int occupancy_bwd()
-{
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, reinterpret_cast<const void *>(&bwd_kernel<T, VEC, LPR, VPL, TEAMS, RMS>),
-            LPR * TEAMS, 0) != hipSuccess)
-        return 1;
-    return n > 0 ? n : 1;
 }
 
 } // namespace nf

@@ -15,6 +15,8 @@
     X(T, VEC, 16, 1, 16)                                                                         \
     X(T, VEC, 16, 2, 16)                                                                         \
     X(T, VEC, 16, 3, 16)                                                                         \
+    X(T, VEC, 16, 3, 32)                                                                         \
+    X(T, VEC, 16, 3, 64)                                                                         \
     X(T, VEC, 16, 4, 16)                                                                         \
     X(T, VEC, 32, 3, 8)                                                                          \
     X(T, VEC, 32, 4, 8)                                                                          \
