@@ -164,7 +164,7 @@ def main():
     traffic = recorded_traffic()
     roofline = {"bound": "hbm", "achieved": round(fwd_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(fwd_gbs / PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "fwd_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 16, LayerNorm>",
+                "kernel": "fwd_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 32, LayerNorm>",
                 "bytes_per_launch": fwd_bytes(M, N), "avg_launch_us": round(fwd_avg * 1e3, 2),
                 "kernel_source_hash": kernel_source_hash()}
     bwd_avg = statistics.fmean(bwd_ms)

@@ -35,8 +35,8 @@ norm_status_t check_device()
 // Read on every call (a few getenv lookups, far below launch cost), so a
 // process can change them between calls; tests use them to cross-check
 // shapes and groupings against each other.
-constexpr int kFwdGroupsPerWg = 2;
-constexpr int kBwdGroupsPerWg = 4;
+constexpr int kFwdGroupsPerWg = 0; // 0: chosen per call (see fwd_common)
+constexpr int kBwdGroupsPerWg = 3;
 constexpr int kFwdInterleave = 1024;
 constexpr int kBwdInterleave = 256;
 
@@ -75,6 +75,8 @@ Knobs knobs()
     parse_shape(std::getenv("NORMFUSE_FWD_SHAPE"), &r.fwd_lpr, &r.fwd_vpl, &r.fwd_teams);
     parse_shape(std::getenv("NORMFUSE_BWD_SHAPE"), &r.bwd_lpr, &r.bwd_vpl, &r.bwd_teams);
     parse_positive(std::getenv("NORMFUSE_FWD_GROUPS_PER_WG"), &r.fwd_k);
+    if (r.fwd_k <= 0)
+        r.fwd_k = 0;
     parse_positive(std::getenv("NORMFUSE_BWD_GROUPS_PER_WG"), &r.bwd_k);
     parse_positive(std::getenv("NORMFUSE_FWD_INTERLEAVE"), &r.fwd_a);
     parse_positive(std::getenv("NORMFUSE_BWD_INTERLEAVE"), &r.bwd_a);
@@ -98,11 +100,28 @@ const Entry *pick_shape(const Entry *tab, int n, int N, int force_lpr, int force
     return nullptr;
 }
 
-const FwdEntry *fwd_entry(int dtype, bool vec, int N, const Knobs &k)
+// Forward workgroups.  The forward's amax combines one atomicMax per
+// workgroup on a single address; such atomics serialise, and past about
+// kMaxAmaxWgs workgroups per launch they start to cost more than the kernel
+// hides.  Bigger workgroups (twice the teams) reach that bound with less
+// walking, and are used when they still leave kMinWideGroups workgroups.
+constexpr int64_t kMaxAmaxWgs = 20000;
+constexpr int64_t kMinWideGroups = 2048;
+
+const FwdEntry *fwd_entry(int dtype, bool vec, int64_t M, int N, const Knobs &k)
 {
     int n = 0;
     const FwdEntry *tab = dtype == NORM_F32 ? fwd_table_f32(vec, &n) : fwd_table_bf16(vec, &n);
-    return pick_shape(tab, n, N, k.fwd_lpr, k.fwd_vpl, k.fwd_teams);
+    const FwdEntry *e = pick_shape(tab, n, N, k.fwd_lpr, k.fwd_vpl, k.fwd_teams);
+    if (!e || k.fwd_lpr > 0)
+        return e;
+    for (int i = 0; i < n; ++i) {
+        const RowShape &w = tab[i].shape;
+        if (w.lpr == e->shape.lpr && w.vpl == e->shape.vpl && w.teams == 2 * e->shape.teams &&
+            (M + w.teams - 1) / w.teams >= kMinWideGroups)
+            return &tab[i];
+    }
+    return e;
 }
 
 const BwdEntry *bwd_entry(int dtype, bool vec, int N, const Knobs &k)
@@ -187,11 +206,18 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
         return st;
     const Knobs kn = knobs();
     const bool vec = vectorisable(N, dtype, {x, bias, residual, gamma, beta, y, residual_out});
-    const FwdEntry *e = fwd_entry(dtype, vec, int(N), kn);
+    const FwdEntry *e = fwd_entry(dtype, vec, M, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
+    int K = kn.fwd_k;
+    if (K == 0) {
+        const int64_t groups = (M + e->shape.teams - 1) / e->shape.teams;
+        K = amax ? int((groups + kMaxAmaxWgs - 1) / kMaxAmaxWgs) : 1;
+        if (K < 1)
+            K = 1;
+    }
     Walk w;
-    if (norm_status_t st = plan_walk(M, e->shape.teams, kn.fwd_k, kn.fwd_a, &w))
+    if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -225,9 +251,15 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
 // ----------------------------------------------------------------- backward
 // Stage-1 walk of the backward for the shape used on these pointers, and
 // the workspace it needs: the stage-1 partials (two blocks of `grid` rows of
-// N floats) and, for many partial rows, the second summation level.
+// N floats), then for many partial rows the second summation level (two
+// blocks of colsum_slices(grid) rows).
+struct BwdLayout {
+    size_t level2_off = 0, bytes = 0; // in bytes
+    bool two_level = false;
+};
+
 norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, const Knobs &kn,
-                       const BwdEntry **entry, Walk *w, size_t *ws_bytes)
+                       const BwdEntry **entry, Walk *w, BwdLayout *lay)
 {
     const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
     if (!e)
@@ -235,8 +267,10 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, const Knob
     if (norm_status_t st = plan_walk(M, e->shape.teams, kn.bwd_k, kn.bwd_a, w))
         return st;
     *entry = e;
-    const size_t rows = size_t(w->grid) + size_t(colsum_level2_rows(w->grid));
-    *ws_bytes = 2 * rows * size_t(N) * sizeof(float);
+    const int slices = colsum_slices(w->grid);
+    lay->two_level = slices > 1;
+    lay->level2_off = 2 * size_t(w->grid) * size_t(N) * sizeof(float);
+    lay->bytes = lay->level2_off + (lay->two_level ? 2 * size_t(slices) * size_t(N) * sizeof(float) : 0);
     return NORM_OK;
 }
 
@@ -271,9 +305,10 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
     const bool vec = vectorisable(N, dtype, {dy, x, gamma, dx});
     const BwdEntry *e = nullptr;
     Walk w;
-    size_t need = 0;
-    if (norm_status_t st = bwd_plan(M, N, dtype, vec, kn, &e, &w, &need))
+    BwdLayout lay;
+    if (norm_status_t st = bwd_plan(M, N, dtype, vec, kn, &e, &w, &lay))
         return st;
+    const size_t need = lay.bytes;
     if (need > 0 && (!workspace || workspace_bytes < need))
         return NORM_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -297,7 +332,9 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         if (norm_status_t st = launched((rms ? e->rms : e->ln)(a, int(w.grid), s)))
             return st;
     }
-    float *level2 = ws ? ws + 2 * size_t(w.grid) * size_t(N) : nullptr;
+    float *level2 =
+        lay.two_level ? reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.level2_off)
+                      : nullptr;
     return launched(launch_colsum(ws, int(w.grid), int(N), dgamma, dbeta, dparam_dtype, level2, s));
 }
 
@@ -341,11 +378,11 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
             continue;
         const BwdEntry *e = nullptr;
         Walk w;
-        size_t b = 0;
-        if (norm_status_t st = bwd_plan(M, N, dtype, v == 1, kn, &e, &w, &b))
+        BwdLayout lay;
+        if (norm_status_t st = bwd_plan(M, N, dtype, v == 1, kn, &e, &w, &lay))
             return st;
-        if (b > best)
-            best = b;
+        if (lay.bytes > best)
+            best = lay.bytes;
     }
     *bytes = best;
     return NORM_OK;

@@ -25,15 +25,14 @@ hipError_t launch_colsum(const float *ws, int parts, int N, void *dgamma, void *
     const dim3 block(COLSUM_COLS * COLSUM_SUB);
     const float *src = ws;
     int rows = parts;
-    const int s2 = colsum_level2_rows(parts);
-    if (s2 > 0) {
-        const int span = (parts + s2 - 1) / s2;
-        hipLaunchKernelGGL((colsum_kernel<false, false>), dim3(tiles, s2, 2), block, 0, s, ws,
-                           parts, N, span, level2, nullptr, nullptr);
+    const int slices = colsum_slices(parts);
+    if (slices > 1) {
+        hipLaunchKernelGGL((colsum_kernel<false, false>), dim3(tiles, slices, 2), block, 0, s, ws,
+                           parts, N, COLSUM_SPAN, level2, nullptr, nullptr);
         if (hipError_t e = hipGetLastError())
             return e;
         src = level2;
-        rows = s2;
+        rows = slices;
     }
     if (out_dtype == 1)
         hipLaunchKernelGGL((colsum_kernel<true, true>), dim3(tiles, 1, 2), block, 0, s, src, rows,

@@ -150,6 +150,96 @@ struct VecIO<float, 1> {
     static __device__ __forceinline__ Raw zero() { return 0.f; }
 };
 
+// ---------------------------------------------------------------------------
+// Buffer I/O for streamed [M, N] tensors.  A buffer descriptor covers the
+// valid bytes of one row group (uniform, scalar registers); each lane adds a
+// 32-bit byte offset.  Accesses beyond the descriptor's range read 0 and
+// write nothing, so rows past M and columns past N need no predication: such
+// lanes use an offset past the range (BUF_OOB).  Loads and stores carry the
+// nontemporal hint.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t BUF_OOB = 0x80000000u; // above any row group's byte range
+constexpr int BUF_NT = 2;                 // cache policy: nontemporal
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    // raw buffer: stride 0, num_records in bytes, gfx9 word-3 format bits
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), 0x00020000);
+}
+
+template <typename T, int VEC>
+struct BufIO;
+
+template <>
+struct BufIO<bf16, 8> {
+    using Raw = u32x4_t;
+    static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, BUF_NT);
+    }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, BUF_NT);
+    }
+};
+template <>
+struct BufIO<float, 4> {
+    using Raw = f32x4_t;
+    static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, BUF_NT));
+    }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, int(off), 0, BUF_NT);
+    }
+};
+template <>
+struct BufIO<bf16, 1> {
+    using Raw = uint16_t;
+    static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, int(off), 0, BUF_NT);
+    }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, int(off), 0, BUF_NT);
+    }
+};
+template <>
+struct BufIO<float, 1> {
+    using Raw = float;
+    static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, BUF_NT));
+    }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, int(off), 0, BUF_NT);
+    }
+};
+
+// VEC floats from LDS (16-byte reads when VEC is a multiple of 4).
+template <int VEC>
+__device__ __forceinline__ void lds_read(const float *p, float *out)
+{
+    if constexpr (VEC % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < VEC; i += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(p + i);
+            out[i] = v.x;
+            out[i + 1] = v.y;
+            out[i + 2] = v.z;
+            out[i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+            out[i] = p[i];
+    }
+}
+
 // Opaque to the optimiser: after this the compiler must assume `r` changed,
 // so values computed from it before (e.g. unpacked floats) are recomputed
 // afterwards instead of being kept live.  Emits no instruction.

@@ -69,13 +69,13 @@ const BwdEntry *bwd_table_bf16(bool vectorised, int *count);
 hipError_t launch_zero_u32(unsigned *p, hipStream_t s);
 // Column sums of the stage-1 partials (two blocks of `parts` rows of N
 // floats at ws); writes dgamma / dbeta (each optional) in fp32 (out_dtype 0)
-// or bf16 (1).  parts = 0 writes zeros.  More than COLSUM_ONE_LEVEL_MAX parts
-// are summed in two levels through `level2` (colsum_level2_rows(parts) rows
-// per block).
-constexpr int COLSUM_ONE_LEVEL_MAX = 256;
-inline int colsum_level2_rows(int64_t parts)
+// or bf16 (1).  parts = 0 writes zeros.  More than COLSUM_SPAN parts are
+// summed in two launches: colsum_slices(parts) slice sums go to `level2`
+// (two blocks of that many rows of N floats), then a final launch adds them.
+constexpr int COLSUM_SPAN = 128;
+inline int colsum_slices(int64_t parts)
 {
-    return parts <= COLSUM_ONE_LEVEL_MAX ? 0 : int((parts + COLSUM_ONE_LEVEL_MAX - 1) / COLSUM_ONE_LEVEL_MAX);
+    return parts <= COLSUM_SPAN ? 1 : int((parts + COLSUM_SPAN - 1) / COLSUM_SPAN);
 }
 hipError_t launch_colsum(const float *ws, int parts, int N, void *dgamma, void *dbeta,
                          int out_dtype, float *level2, hipStream_t s);

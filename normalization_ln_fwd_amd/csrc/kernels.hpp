@@ -25,13 +25,6 @@
 #include "device.hpp"
 #include "internal.hpp"
 
-// Whether a workgroup walking several row groups issues the next group's
-// loads before working on the current one (two groups in flight per wave, at
-// the cost of the registers that hold them).
-#ifndef NORMFUSE_PREFETCH
-#define NORMFUSE_PREFETCH 0
-#endif
-
 namespace nf {
 
 // Row groups of workgroup b = q*A + r (A_q = min(A, grid - q*A) workgroups in
@@ -115,6 +108,46 @@ __device__ __forceinline__ double team_sum_f64(double v, double *lds, int &parit
 }
 
 // ---------------------------------------------------------------------------
+// Per-column vectors (bias, gamma, beta).  For rows up to PARAMS_LDS_MAX
+// elements a workgroup converts them once to fp32 in LDS, with the neutral
+// value (0, 1, 0) where a vector is absent or beyond N, so the row loops read
+// them with LDS loads and no unpacking or selects.  Wider rows read them
+// from global memory (cached) for each row group.
+// ---------------------------------------------------------------------------
+constexpr int PARAMS_LDS_MAX = 2048;
+
+template <typename T>
+__device__ __forceinline__ void stage_param(float *dst, const void *src, int N, int cap,
+                                            float neutral, int tid, int nthreads)
+{
+    for (int c = tid; c < cap; c += nthreads) {
+        float v = neutral;
+        if (src != nullptr && c < N)
+            VecIO<T, 1>::unpack(VecIO<T, 1>::load(src, c), &v);
+        dst[c] = v;
+    }
+}
+
+// VEC values of a per-column vector at column c0: from LDS when staged, else
+// from global memory (neutral where absent or invalid).
+template <typename T, int VEC, bool IN_LDS>
+__device__ __forceinline__ void param_vec(const float *lds, const void *src, int c0, bool valid,
+                                          float neutral, float *out)
+{
+    if constexpr (IN_LDS) {
+        lds_read<VEC>(lds + c0, out);
+    } else {
+        if (src != nullptr && valid) {
+            VecIO<T, VEC>::unpack(VecIO<T, VEC>::load(src, c0), out);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                out[e] = neutral;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Forward: t = (x + bias) + residual (fp32), u = round(t) -> residual_out,
 // statistics of u, y = normalise(u) * gamma + beta -> y, running max |y|.
 // ---------------------------------------------------------------------------
@@ -122,14 +155,17 @@ template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS>
 __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
 {
     using IO = VecIO<T, VEC>;
+    using BIO = BufIO<T, VEC>;
     using Raw = typename IO::Raw;
-    constexpr int E = VPL * VEC;
     constexpr int WG = LPR * TEAMS;
+    constexpr int CAP = LPR * VPL * VEC;
+    constexpr bool PLDS = CAP <= PARAMS_LDS_MAX;
     static_assert(WG % 64 == 0, "workgroup of whole waves");
 
     __shared__ float red_lds[TeamLds<LPR, TEAMS, 1>::size];
     __shared__ double red_lds_f64[TeamLds<LPR, TEAMS, 1>::size];
     __shared__ float max_lds[WG / 64];
+    __shared__ __attribute__((aligned(16))) float par[PLDS ? 3 * CAP : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -137,60 +173,51 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     const int tl = tid % LPR;
     const int wave_in_team = LPR > 64 ? tl / 64 : 0;
     const int N = a.N;
+    const bool has_res = a.res != nullptr;
+    const bool fused_add = a.bias != nullptr || has_res;
 
-    const bool has_bias = a.bias != nullptr, has_res = a.res != nullptr;
-    const bool has_gamma = a.gamma != nullptr, has_beta = a.beta != nullptr;
-    const bool fused_add = has_bias || has_res;
+    if constexpr (PLDS) {
+        stage_param<T>(par, a.bias, N, CAP, 0.f, tid, WG);
+        stage_param<T>(par + CAP, a.gamma, N, CAP, 1.f, tid, WG);
+        stage_param<T>(par + 2 * CAP, a.beta, N, CAP, 0.f, tid, WG);
+        __syncthreads();
+    }
 
     bool cvalid[VPL];
+    uint32_t off[VPL]; // this lane's byte offset of vector k inside a row group
 #pragma unroll
-    for (int k = 0; k < VPL; ++k)
+    for (int k = 0; k < VPL; ++k) {
         cvalid[k] = (k * LPR + tl) * VEC < N; // VEC > 1: N % VEC == 0, whole vector valid
+        off[k] = cvalid[k] ? uint32_t(team * N + (k * LPR + tl) * VEC) * uint32_t(sizeof(T))
+                           : BUF_OOB;
+    }
 
     float lane_max = 0.f;
     int parity = 0;
     const GroupWalk walk(a.K, a.A);
-
-    // x and residual of a row group, nontemporal; zeros outside the matrix.
-    // With NORMFUSE_PREFETCH the next group's loads are issued before the
-    // current group is worked on.
-    Raw xn[VPL], rn[VPL];
-    auto issue = [&](int64_t g) {
-        const int64_t row = g * TEAMS + team;
-        const bool rv = g < a.n_groups && row < a.M;
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            const int64_t idx = row * (int64_t)N + (k * LPR + tl) * VEC;
-            const bool ok = rv && cvalid[k];
-            xn[k] = ok ? IO::load_stream(a.x, idx) : IO::zero();
-            rn[k] = (ok && has_res) ? IO::load_stream(a.res, idx) : IO::zero();
-        }
-    };
-    if (NORMFUSE_PREFETCH)
-        issue(walk.group(0));
-
     for (int kk = 0; kk < a.K; ++kk) {
         const int64_t grp = walk.group(kk);
         if (grp >= a.n_groups)
             break; // uniform over the workgroup; later groups are larger
         const int64_t row = grp * TEAMS + team;
         const bool rv = row < a.M;
-        const int64_t roff = row * (int64_t)N;
-        if (!NORMFUSE_PREFETCH)
-            issue(grp);
+        // descriptors over the valid rows of this group
+        const int64_t rows = a.M - grp * TEAMS < TEAMS ? a.M - grp * TEAMS : TEAMS;
+        const uint32_t bytes = uint32_t(rows * N) * uint32_t(sizeof(T));
+        const int64_t gbyte = grp * TEAMS * int64_t(N) * int64_t(sizeof(T));
+        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + gbyte, bytes);
+        const rsrc_t rs = make_rsrc(has_res ? static_cast<const char *>(a.res) + gbyte : nullptr,
+                                    has_res ? bytes : 0u);
 
-        // Fused add.  ur holds u, the value actually normalised, in its
-        // packed I/O form (exact: u is rounded to T); every later pass
-        // unpacks it again rather than keeping a float copy live.
-        Raw ur[VPL], rr[VPL], br[VPL];
+        // Loads.  ur holds u, the value actually normalised, in its packed I/O
+        // form (exact: u is rounded to T); every later pass unpacks it again.
+        Raw ur[VPL], rr[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            ur[k] = xn[k];
-            rr[k] = rn[k];
-            br[k] = (cvalid[k] && has_bias) ? IO::load(a.bias, (k * LPR + tl) * VEC) : IO::zero();
+            ur[k] = BIO::load(xs, off[k]);
+            rr[k] = has_res ? BIO::load(rs, off[k]) : IO::zero();
         }
-        if (NORMFUSE_PREFETCH && kk + 1 < a.K)
-            issue(walk.group(kk + 1));
+
         // fused add; u = round_T((x + bias) + residual), and the row sum of
         // u for LayerNorm (fp32 for bf16 rows, whose sums of values of
         // similar magnitude are exact in fp32; fp64 for fp32 rows).
@@ -198,11 +225,12 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         Acc sum = Acc(0);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
+            const int c0 = (k * LPR + tl) * VEC;
             float t[VEC];
             IO::unpack(ur[k], t);
             if (fused_add) {
                 float bv[VEC], rv_[VEC];
-                IO::unpack(br[k], bv);
+                param_vec<T, VEC, PLDS>(par, a.bias, c0, cvalid[k], 0.f, bv);
                 IO::unpack(rr[k], rv_);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
@@ -217,18 +245,10 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
             }
         }
         if (a.res_out) {
+            const rsrc_t os = make_rsrc(static_cast<char *>(a.res_out) + gbyte, bytes);
 #pragma unroll
             for (int k = 0; k < VPL; ++k)
-                if (rv && cvalid[k])
-                    IO::store_stream(a.res_out, roff + (k * LPR + tl) * VEC, ur[k]);
-        }
-        // per-column scale and shift, in flight during the reductions
-        Raw gr[VPL], betar[VPL];
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            const int c0 = (k * LPR + tl) * VEC;
-            gr[k] = (cvalid[k] && has_gamma) ? IO::load(a.gamma, c0) : IO::zero();
-            betar[k] = (cvalid[k] && has_beta) ? IO::load(a.beta, c0) : IO::zero();
+                BIO::store(os, off[k], ur[k]);
         }
 
         // Statistics.  LayerNorm keeps its mean as an fp32 pair mean + lo
@@ -289,25 +309,19 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
 #pragma unroll
         for (int k = 0; k < VPL; ++k)
             reload_barrier(ur[k]);
+        const rsrc_t ys = make_rsrc(static_cast<char *>(a.y) + gbyte, bytes);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
-            const bool ok = rv && cvalid[k];
             float u[VEC], gv[VEC], bv[VEC], yv[VEC];
             IO::unpack(ur[k], u);
-            IO::unpack(gr[k], gv);
-            IO::unpack(betar[k], bv);
+            param_vec<T, VEC, PLDS>(par + CAP, a.gamma, c0, cvalid[k], 1.f, gv);
+            param_vec<T, VEC, PLDS>(par + 2 * CAP, a.beta, c0, cvalid[k], 0.f, bv);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                float n = fmaf(u[e] - mean, rstd, lo_r);
-                if (has_gamma)
-                    n = has_beta ? fmaf(n, gv[e], bv[e]) : n * gv[e];
-                else if (has_beta)
-                    n += bv[e];
-                yv[e] = n;
-            }
-            if (ok) {
-                IO::store_stream(a.y, roff + c0, IO::pack(yv));
+            for (int e = 0; e < VEC; ++e)
+                yv[e] = fmaf(fmaf(u[e] - mean, rstd, lo_r), gv[e], bv[e]);
+            BIO::store(ys, off[k], IO::pack(yv));
+            if (rv && cvalid[k]) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     lane_max = fmaxf(lane_max, fabsf(yv[e]));
@@ -324,8 +338,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     // amax, first stage: wave max through DPP / permlane, then the
     // workgroup's waves through LDS; second stage: one atomicMax per
     // workgroup on the float's bit pattern (non-negative floats order like
-    // their unsigned patterns).  Atomics on one address serialise, which is
-    // one reason a workgroup covers several row groups.
+    // their unsigned patterns).  Atomics on one address serialise: the host
+    // keeps the number of workgroups that issue them bounded.
     if (a.amax) {
         const float m = group_reduce<64, OpMax>(lane_max);
         if (lane == 0)
@@ -353,17 +367,20 @@ template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS>
 __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 {
     using IO = VecIO<T, VEC>;
+    using BIO = BufIO<T, VEC>;
     using Raw = typename IO::Raw;
     constexpr int E = VPL * VEC;
     constexpr int WG = LPR * TEAMS;
     constexpr int NW = WG / 64;
     constexpr int CAP = LPR * VPL * VEC;
+    constexpr bool PLDS = CAP <= PARAMS_LDS_MAX;
     // partial slots to fold in LDS: waves (LPR <= 64) or teams (LPR > 64)
     constexpr int SLOTS = LPR <= 64 ? NW : TEAMS;
     static_assert(WG % 64 == 0, "workgroup of whole waves");
 
     __shared__ float red_lds[TeamLds<LPR, TEAMS, 2>::size];
     __shared__ float col_lds[SLOTS > 1 ? 2 * CAP : 1];
+    __shared__ __attribute__((aligned(16))) float par[PLDS ? CAP : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -371,16 +388,19 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     const int tl = tid % LPR;
     const int wave_in_team = LPR > 64 ? tl / 64 : 0;
     const int N = a.N;
-    const bool has_gamma = a.gamma != nullptr;
     const bool recompute = RMS && a.rstd == nullptr;
 
+    if constexpr (PLDS) {
+        stage_param<T>(par, a.gamma, N, CAP, 1.f, tid, WG);
+        __syncthreads();
+    }
     bool cvalid[VPL];
-    Raw gamma_r[VPL];
+    uint32_t off[VPL];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
-        const int c0 = (k * LPR + tl) * VEC;
-        cvalid[k] = c0 < N;
-        gamma_r[k] = (has_gamma && cvalid[k]) ? IO::load(a.gamma, c0) : IO::zero();
+        cvalid[k] = (k * LPR + tl) * VEC < N;
+        off[k] = cvalid[k] ? uint32_t(team * N + (k * LPR + tl) * VEC) * uint32_t(sizeof(T))
+                           : BUF_OOB;
     }
 
     float acc_g[E], acc_b[E];
@@ -392,114 +412,88 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 
     int parity = 0;
     const GroupWalk walk(a.K, a.A);
-
-    // x, dy and the row statistics of a row group (with NORMFUSE_PREFETCH the
-    // next group's loads are issued before the current group is worked on).
-    Raw xn[VPL], dn[VPL];
-    float mean_n = 0.f, rstd_n = 0.f;
-    auto issue = [&](int64_t g) {
-        const int64_t row = g * TEAMS + team;
-        const bool rv = g < a.n_groups && row < a.M;
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            const int64_t idx = row * (int64_t)N + (k * LPR + tl) * VEC;
-            const bool ok = rv && cvalid[k];
-            xn[k] = ok ? IO::load_stream(a.x, idx) : IO::zero();
-            dn[k] = ok ? IO::load_stream(a.dy, idx) : IO::zero();
-        }
-        mean_n = (rv && !RMS) ? a.mean[row] : 0.f;
-        rstd_n = (rv && !recompute) ? a.rstd[row] : 0.f;
-    };
-    if (NORMFUSE_PREFETCH)
-        issue(walk.group(0));
-
     for (int kk = 0; kk < a.K; ++kk) {
         const int64_t grp = walk.group(kk);
         if (grp >= a.n_groups)
             break; // uniform over the workgroup; later groups are larger
         const int64_t row = grp * TEAMS + team;
         const bool rv = row < a.M;
-        const int64_t roff = row * (int64_t)N;
-        if (!NORMFUSE_PREFETCH)
-            issue(grp);
+        const int64_t rows = a.M - grp * TEAMS < TEAMS ? a.M - grp * TEAMS : TEAMS;
+        const uint32_t bytes = uint32_t(rows * N) * uint32_t(sizeof(T));
+        const int64_t gbyte = grp * TEAMS * int64_t(N) * int64_t(sizeof(T));
+        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + gbyte, bytes);
+        const rsrc_t ds = make_rsrc(static_cast<const char *>(a.dy) + gbyte, bytes);
 
         Raw xr[VPL], dr[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            xr[k] = xn[k];
-            dr[k] = dn[k];
-            reload_barrier(gamma_r[k]); // unpack gamma here, not once outside the loop
+            xr[k] = BIO::load(xs, off[k]);
+            dr[k] = BIO::load(ds, off[k]);
         }
-        float mean = mean_n, rstd = rstd_n;
-        if (NORMFUSE_PREFETCH && kk + 1 < a.K)
-            issue(walk.group(kk + 1));
+        float mean = 0.f, rstd = 0.f;
+        if (rv && !recompute) {
+            if (!RMS)
+                mean = a.mean[row];
+            rstd = a.rstd[row];
+        }
 
-        // g = dy * gamma; the rows stay packed and are unpacked per pass
-        float c1, c2 = 0.f;
-        {
-            float s[2] = {0.f, 0.f};
+        // Row sums, g = dy * gamma (invalid elements hold 0):
+        //   LN : s0 = sum g (x - mean), s1 = sum g  ->  mean(g xhat) = rstd s0 / N
+        //   RMS: s0 = sum g x                      ->  mean(g xhat) = rstd s0 / N
+        //   RMS without rstd: s1 = sum x^2 gives rstd from the same load.
+        float s[2] = {0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < VPL; ++k) {
-                float xv[VEC], dv[VEC], gv[VEC];
-                IO::unpack(xr[k], xv);
-                IO::unpack(dr[k], dv);
-                IO::unpack(gamma_r[k], gv);
+        for (int k = 0; k < VPL; ++k) {
+            const int c0 = (k * LPR + tl) * VEC;
+            float xv[VEC], dv[VEC], gv[VEC];
+            IO::unpack(xr[k], xv);
+            IO::unpack(dr[k], dv);
+            param_vec<T, VEC, PLDS>(par, a.gamma, c0, cvalid[k], 1.f, gv);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const float g = has_gamma ? dv[e] * gv[e] : dv[e]; // invalid: 0
-                    if constexpr (!RMS) {
-                        s[0] += g * ((xv[e] - mean) * rstd);
-                        s[1] += g;
-                    } else {
-                        if (recompute) {
-                            // rstd from the same load: sum x^2 and sum g*x
-                            // reduce together; mean(g*xhat) = rstd * mean(g*x)
-                            s[0] += xv[e] * xv[e];
-                            s[1] += g * xv[e];
-                        } else {
-                            s[0] += g * (xv[e] * rstd);
-                        }
-                    }
+            for (int e = 0; e < VEC; ++e) {
+                const float g = dv[e] * gv[e];
+                if constexpr (!RMS) {
+                    s[0] = fmaf(g, xv[e] - mean, s[0]);
+                    s[1] += g;
+                } else {
+                    s[0] = fmaf(g, xv[e], s[0]);
+                    if (recompute)
+                        s[1] = fmaf(xv[e], xv[e], s[1]);
                 }
             }
-            team_sum<LPR, TEAMS, 2>(s, red_lds, parity, team, wave_in_team, lane);
-            if constexpr (!RMS) {
-                c1 = s[0] / float(N);
-                c2 = s[1] / float(N);
-            } else if (recompute) {
-                rstd = rsqrtf(s[0] / float(N) + a.eps);
-                c1 = rstd * (s[1] / float(N));
-            } else {
-                c1 = s[0] / float(N);
-            }
         }
+        team_sum<LPR, TEAMS, 2>(s, red_lds, parity, team, wave_in_team, lane);
+        if (recompute)
+            rstd = rsqrtf(s[1] / float(N) + a.eps);
+        // dx = rstd (g - c2 - xhat c1) = fma(xhat, -rstd c1, fma(g, rstd, -rstd c2))
+        const float c1 = rstd * (s[0] / float(N));
+        const float c2 = RMS ? 0.f : s[1] / float(N);
+        const float k1 = -rstd * c1, k2 = -rstd * c2;
 
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             reload_barrier(xr[k]);
             reload_barrier(dr[k]);
         }
+        const rsrc_t dxs = make_rsrc(static_cast<char *>(a.dx) + gbyte, bytes);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
-            const bool ok = rv && cvalid[k];
             float xv[VEC], dv[VEC], gv[VEC], dxv[VEC];
             IO::unpack(xr[k], xv);
             IO::unpack(dr[k], dv);
-            IO::unpack(gamma_r[k], gv);
+            param_vec<T, VEC, PLDS>(par, a.gamma, c0, cvalid[k], 1.f, gv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const int i = k * VEC + e;
-                const float g = has_gamma ? dv[e] * gv[e] : dv[e];
                 const float xh = RMS ? xv[e] * rstd : (xv[e] - mean) * rstd;
-                dxv[e] = rstd * (g - c2 - xh * c1);
-                if (ok) {
-                    acc_g[i] += dv[e] * xh;
+                dxv[e] = fmaf(xh, k1, fmaf(dv[e] * gv[e], rstd, k2));
+                if (rv) { // rows past M read zeros; columns past N too
+                    acc_g[i] = fmaf(dv[e], xh, acc_g[i]);
                     acc_b[i] += dv[e];
                 }
             }
-            if (ok)
-                IO::store_stream(a.dx, roff + c0, IO::pack(dxv));
+            BIO::store(dxs, off[k], IO::pack(dxv));
         }
     }
 
@@ -531,8 +525,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     } else {
         const int slot = LPR <= 64 ? (tid >> 6) : team;
         const bool holder = LPR < 64 ? lane < LPR : true;
-        for (int s = 0; s < SLOTS; ++s) {
-            if (slot == s && holder) {
+        for (int sl = 0; sl < SLOTS; ++sl) {
+            if (slot == sl && holder) {
 #pragma unroll
                 for (int k = 0; k < VPL; ++k) {
                     const int c0 = (k * LPR + tl) * VEC;
@@ -540,8 +534,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) {
                             const int c = c0 + e;
-                            col_lds[c] = (s == 0 ? 0.f : col_lds[c]) + acc_g[k * VEC + e];
-                            col_lds[CAP + c] = (s == 0 ? 0.f : col_lds[CAP + c]) + acc_b[k * VEC + e];
+                            col_lds[c] = (sl == 0 ? 0.f : col_lds[c]) + acc_g[k * VEC + e];
+                            col_lds[CAP + c] = (sl == 0 ? 0.f : col_lds[CAP + c]) + acc_b[k * VEC + e];
                         }
                     }
                 }
@@ -558,11 +552,15 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 // ---------------------------------------------------------------------------
 // Backward stage 2: column sums of the partial rows.  src holds two blocks
 // (dgamma, dbeta) of `rows` rows of N floats.  Workgroup (column tile, slice
-// s, block) adds rows [s*span, min(rows, (s+1)*span)): thread (c, t) takes
-// rows t, t + 4, ... of the slice in ascending order, and the four threads of
-// a column are added in order t = 0..3.  FINAL: one slice, the down-cast and
-// the store to dgamma / dbeta; otherwise slice s writes row s of dst (two
-// blocks of `gridDim.y` rows), the input of the next level.
+// s, block) adds rows [s*span, min(rows, (s+1)*span)) of its 64 columns:
+// thread (c, t) takes rows t, t + 4, ... of the slice in ascending order, and
+// the four threads of a column are added in order t = 0..3.  FINAL: one
+// slice; down-cast and store to dgamma / dbeta.  Otherwise slice s stores its
+// sums as row s of dst (two blocks of gridDim.y rows), which a FINAL launch
+// then adds the same way.  Every addition happens in a fixed order.
+// (A one-launch variant that lets the last workgroup finish needs a
+// device-scope release per workgroup, i.e. an L2 write-back each, which
+// costs more than the second launch.)
 // ---------------------------------------------------------------------------
 constexpr int COLSUM_COLS = 64;
 constexpr int COLSUM_SUB = 4;

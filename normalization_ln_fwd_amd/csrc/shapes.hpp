@@ -3,7 +3,7 @@
 // The host picks the first shape whose capacity covers N.
 //
 // 16-byte path (VEC = 16 / sizeof(T)); workgroups of 256 threads, or one
-// team of LPR threads when LPR > 256:
+// team of LPR threads when LPR > 256 (the forward adds 512-thread variants):
 //   bf16 capacities: 64 128 256 384 512 768 1024 1536 2048 4096 8192 16384
 //   fp32 capacities: 32 64 128 192 256 384 512 768 1024 2048 4096 8192 16384
 // Element-wise path (VEC = 1), for rows that are not whole 16-byte vectors
@@ -15,8 +15,6 @@
     X(T, VEC, 16, 1, 16)                                                                         \
     X(T, VEC, 16, 2, 16)                                                                         \
     X(T, VEC, 16, 3, 16)                                                                         \
-    X(T, VEC, 16, 3, 32)                                                                         \
-    X(T, VEC, 16, 3, 64)                                                                         \
     X(T, VEC, 16, 4, 16)                                                                         \
     X(T, VEC, 32, 3, 8)                                                                          \
     X(T, VEC, 32, 4, 8)                                                                          \
@@ -28,6 +26,19 @@
 
 #define NF_SHAPES_BF16_VEC(X) NF_SHAPES_COMMON(X, bf16, 8)
 #define NF_SHAPES_F32_VEC(X) NF_SHAPES_COMMON(X, float, 4) X(float, 4, 1024, 4, 1)
+
+// Forward only: the same team shapes in 512-thread workgroups (twice the
+// rows per workgroup), preferred when there are rows enough to fill the GPU.
+#define NF_SHAPES_WIDE_WG(X, T, VEC)                                                             \
+    X(T, VEC, 8, 1, 64)                                                                          \
+    X(T, VEC, 16, 1, 32)                                                                         \
+    X(T, VEC, 16, 2, 32)                                                                         \
+    X(T, VEC, 16, 3, 32)                                                                         \
+    X(T, VEC, 16, 4, 32)                                                                         \
+    X(T, VEC, 32, 3, 16)                                                                         \
+    X(T, VEC, 32, 4, 16)                                                                         \
+    X(T, VEC, 64, 3, 8)                                                                          \
+    X(T, VEC, 64, 4, 8)
 
 #define NF_SHAPES_ELEM(X, T)                                                                     \
     X(T, 1, 64, 4, 4)                                                                            \
