@@ -36,7 +36,14 @@ norm_status_t check_device()
 // process can change them between calls; tests use them to cross-check
 // shapes and groupings against each other.
 constexpr int kFwdGroupsPerWg = 0; // 0: chosen per call (see fwd_common)
-constexpr int kBwdGroupsPerWg = 3;
+constexpr int kBwdGroupsPerWg = 0; // 0: chosen per shape (see bwd_plan)
+// Row groups per workgroup.  Teams of several waves (wide rows) have few
+// rows in flight per CU; walking several groups per workgroup, with the next
+// group prefetched, keeps the loads going.  The backward's count also sets
+// how many rows one column partial covers.
+constexpr int kFwdGroupsWide = 4;
+constexpr int kBwdGroupsNarrow = 3;
+constexpr int kBwdGroupsWide = 8;
 constexpr int kFwdInterleave = 1024;
 constexpr int kBwdInterleave = 256;
 
@@ -213,6 +220,8 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     if (K == 0) {
         const int64_t groups = (M + e->shape.teams - 1) / e->shape.teams;
         K = amax ? int((groups + kMaxAmaxWgs - 1) / kMaxAmaxWgs) : 1;
+        if (e->shape.lpr >= WIDE_LPR && K < kFwdGroupsWide)
+            K = kFwdGroupsWide;
         if (K < 1)
             K = 1;
     }
@@ -264,7 +273,9 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, const Knob
     const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    if (norm_status_t st = plan_walk(M, e->shape.teams, kn.bwd_k, kn.bwd_a, w))
+    const int K = kn.bwd_k > 0 ? kn.bwd_k
+                               : (e->shape.lpr >= WIDE_LPR ? kBwdGroupsWide : kBwdGroupsNarrow);
+    if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.bwd_a, w))
         return st;
     *entry = e;
     const int slices = colsum_slices(w->grid);

@@ -178,6 +178,10 @@ struct BufIO<bf16, 8> {
     {
         return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, BUF_NT);
     }
+    static __device__ __forceinline__ Raw load_cached(rsrc_t r, uint32_t off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+    }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
     {
         __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, BUF_NT);
@@ -189,6 +193,10 @@ struct BufIO<float, 4> {
     static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
     {
         return __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, BUF_NT));
+    }
+    static __device__ __forceinline__ Raw load_cached(rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
     }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
     {
@@ -202,6 +210,10 @@ struct BufIO<bf16, 1> {
     {
         return __builtin_amdgcn_raw_buffer_load_b16(r, int(off), 0, BUF_NT);
     }
+    static __device__ __forceinline__ Raw load_cached(rsrc_t r, uint32_t off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, int(off), 0, 0);
+    }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
     {
         __builtin_amdgcn_raw_buffer_store_b16(v, r, int(off), 0, BUF_NT);
@@ -213,6 +225,10 @@ struct BufIO<float, 1> {
     static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
     {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, BUF_NT));
+    }
+    static __device__ __forceinline__ Raw load_cached(rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
     }
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
     {

@@ -65,6 +65,11 @@ const FwdEntry *fwd_table_bf16(bool vectorised, int *count);
 const BwdEntry *bwd_table_f32(bool vectorised, int *count);
 const BwdEntry *bwd_table_bf16(bool vectorised, int *count);
 
+// Teams of at least WIDE_LPR lanes (several waves per row) hold few rows per
+// CU: their kernels prefetch the next row group, and the host gives their
+// workgroups more row groups to walk.
+constexpr int WIDE_LPR = 128;
+
 // Small kernels.
 hipError_t launch_zero_u32(unsigned *p, hipStream_t s);
 // Column sums of the stage-1 partials (two blocks of `parts` rows of N
@@ -72,7 +77,7 @@ hipError_t launch_zero_u32(unsigned *p, hipStream_t s);
 // or bf16 (1).  parts = 0 writes zeros.  More than COLSUM_SPAN parts are
 // summed in two launches: colsum_slices(parts) slice sums go to `level2`
 // (two blocks of that many rows of N floats), then a final launch adds them.
-constexpr int COLSUM_SPAN = 128;
+constexpr int COLSUM_SPAN = 512;
 inline int colsum_slices(int64_t parts)
 {
     return parts <= COLSUM_SPAN ? 1 : int((parts + COLSUM_SPAN - 1) / COLSUM_SPAN);

@@ -44,6 +44,20 @@ struct GroupWalk {
     __device__ __forceinline__ int64_t group(int k) const { return base + k * step; }
 };
 
+// Bytes of row group g: it starts byte0 bytes into an [M, N] tensor and holds
+// `bytes` valid bytes (fewer rows in the last group).
+struct RowGroup {
+    int64_t byte0;
+    uint32_t bytes;
+    __device__ __forceinline__ RowGroup(int64_t g, int teams, int64_t M, int N, int elem)
+    {
+        const int64_t r0 = g * teams;
+        const int64_t rows = M - r0 < teams ? (M - r0 > 0 ? M - r0 : 0) : teams;
+        byte0 = r0 * int64_t(N) * elem;
+        bytes = uint32_t(rows * N) * uint32_t(elem);
+    }
+};
+
 // Sum over a team.  LPR <= 64: inside the wave.  LPR > 64: wave partials
 // meet in LDS (double-buffered by `parity`, so one barrier per reduction
 // suffices) and are added in wave order.  NV values are reduced together.
@@ -111,40 +125,83 @@ __device__ __forceinline__ double team_sum_f64(double v, double *lds, int &parit
 // Per-column vectors (bias, gamma, beta).  For rows up to PARAMS_LDS_MAX
 // elements a workgroup converts them once to fp32 in LDS, with the neutral
 // value (0, 1, 0) where a vector is absent or beyond N, so the row loops read
-// them with LDS loads and no unpacking or selects.  Wider rows read them
-// from global memory (cached) for each row group.
+// them with LDS loads and no unpacking or selects.  For wider rows each lane
+// keeps its own columns in registers in the packed I/O form, loaded once per
+// workgroup (zeros beyond N or where absent, ones for an absent gamma), so
+// the row walk issues no memory reads besides its rows.
 // ---------------------------------------------------------------------------
-constexpr int PARAMS_LDS_MAX = 2048;
+constexpr int PARAMS_LDS_MAX = 4096;
 
-template <typename T>
-__device__ __forceinline__ void stage_param(float *dst, const void *src, int N, int cap,
-                                            float neutral, int tid, int nthreads)
-{
-    for (int c = tid; c < cap; c += nthreads) {
-        float v = neutral;
-        if (src != nullptr && c < N)
-            VecIO<T, 1>::unpack(VecIO<T, 1>::load(src, c), &v);
-        dst[c] = v;
+// Staging of one per-column vector into LDS (fp32, `neutral` beyond N or
+// where absent) in two phases, so that the workgroup's first row loads go out
+// between them: fetch() issues this thread's loads, put() converts and
+// stores.  VEC > 1 kernels have 16-byte aligned vectors and N % VEC == 0.
+template <typename T, int VEC, int CAP, int WG>
+struct ParamStage {
+    using Raw = typename VecIO<T, VEC>::Raw;
+    static constexpr int SI = (CAP + WG * VEC - 1) / (WG * VEC);
+    Raw r[SI];
+
+    __device__ __forceinline__ void fetch(const void *src, int N, int tid)
+    {
+        const rsrc_t rs = make_rsrc(src, src ? uint32_t(N) * uint32_t(sizeof(T)) : 0u);
+#pragma unroll
+        for (int i = 0; i < SI; ++i) {
+            const int c = (tid + i * WG) * VEC;
+            r[i] = BufIO<T, VEC>::load_cached(rs, c < CAP ? uint32_t(c) * uint32_t(sizeof(T))
+                                                          : BUF_OOB);
+        }
     }
+    __device__ __forceinline__ void put(float *dst, const void *src, int N, float neutral,
+                                        int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < SI; ++i) {
+            const int c = (tid + i * WG) * VEC;
+            if (c < CAP) {
+                float v[VEC];
+                VecIO<T, VEC>::unpack(r[i], v);
+                const bool ok = src != nullptr && c < N;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    dst[c + e] = ok ? v[e] : neutral;
+            }
+        }
+    }
+};
+
+// This lane's VPL vectors of a per-column vector (registers, packed).
+template <typename T, int VEC, int VPL>
+__device__ __forceinline__ void load_param_regs(typename VecIO<T, VEC>::Raw (&dst)[VPL],
+                                                const void *src, int N, const uint32_t (&poff)[VPL],
+                                                bool ones_if_absent)
+{
+    using IO = VecIO<T, VEC>;
+    if (src == nullptr && ones_if_absent) {
+        float one[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            one[e] = 1.f;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+            dst[k] = IO::pack(one);
+        return;
+    }
+    const rsrc_t r = make_rsrc(src, src ? uint32_t(N) * uint32_t(sizeof(T)) : 0u);
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+        dst[k] = BufIO<T, VEC>::load_cached(r, poff[k]);
 }
 
 // VEC values of a per-column vector at column c0: from LDS when staged, else
-// from global memory (neutral where absent or invalid).
-template <typename T, int VEC, bool IN_LDS>
-__device__ __forceinline__ void param_vec(const float *lds, const void *src, int c0, bool valid,
-                                          float neutral, float *out)
+// unpacked from this lane's registers.
+template <typename T, int VEC, bool IN_LDS, typename Raw>
+__device__ __forceinline__ void param_vec(const float *lds, const Raw &reg, int c0, float *out)
 {
-    if constexpr (IN_LDS) {
+    if constexpr (IN_LDS)
         lds_read<VEC>(lds + c0, out);
-    } else {
-        if (src != nullptr && valid) {
-            VecIO<T, VEC>::unpack(VecIO<T, VEC>::load(src, c0), out);
-        } else {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                out[e] = neutral;
-        }
-    }
+    else
+        VecIO<T, VEC>::unpack(reg, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -160,6 +217,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     constexpr int WG = LPR * TEAMS;
     constexpr int CAP = LPR * VPL * VEC;
     constexpr bool PLDS = CAP <= PARAMS_LDS_MAX;
+    constexpr bool PREFETCH = LPR >= WIDE_LPR;
     static_assert(WG % 64 == 0, "workgroup of whole waves");
 
     __shared__ float red_lds[TeamLds<LPR, TEAMS, 1>::size];
@@ -176,13 +234,6 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     const bool has_res = a.res != nullptr;
     const bool fused_add = a.bias != nullptr || has_res;
 
-    if constexpr (PLDS) {
-        stage_param<T>(par, a.bias, N, CAP, 0.f, tid, WG);
-        stage_param<T>(par + CAP, a.gamma, N, CAP, 1.f, tid, WG);
-        stage_param<T>(par + 2 * CAP, a.beta, N, CAP, 0.f, tid, WG);
-        __syncthreads();
-    }
-
     bool cvalid[VPL];
     uint32_t off[VPL]; // this lane's byte offset of vector k inside a row group
 #pragma unroll
@@ -192,31 +243,87 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
                            : BUF_OOB;
     }
 
+    // x and residual of row group g (zeros outside the matrix).  Wide teams
+    // walk their row groups with the next group's loads in flight while the
+    // current one is worked on (PREFETCH).
+    Raw xn[VPL], rn[VPL];
+    auto issue = [&](int64_t g) {
+        const RowGroup rg(g, TEAMS, a.M, N, sizeof(T));
+        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + rg.byte0, rg.bytes);
+        const rsrc_t rs = make_rsrc(has_res ? static_cast<const char *>(a.res) + rg.byte0 : nullptr,
+                                    has_res ? rg.bytes : 0u);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            xn[k] = BIO::load(xs, off[k]);
+            rn[k] = has_res ? BIO::load(rs, off[k]) : IO::zero();
+        }
+    };
+    const GroupWalk walk(a.K, a.A);
+
+    // Parameters: their loads first, then the first row group's, so that the
+    // wait for the parameters does not include the rows.
+    constexpr int PR = PLDS ? 1 : VPL;
+    Raw pbias[PR], pgam[PR], pbeta[PR];
+    if constexpr (PLDS) {
+        ParamStage<T, VEC, CAP, WG> sb, sg, se;
+        sb.fetch(a.bias, N, tid);
+        sg.fetch(a.gamma, N, tid);
+        se.fetch(a.beta, N, tid);
+        if (PREFETCH)
+            issue(walk.group(0));
+        sb.put(par, a.bias, N, 0.f, tid);
+        sg.put(par + CAP, a.gamma, N, 1.f, tid);
+        se.put(par + 2 * CAP, a.beta, N, 0.f, tid);
+        __syncthreads();
+    } else {
+        uint32_t poff[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+            poff[k] = cvalid[k] ? uint32_t((k * LPR + tl) * VEC) * uint32_t(sizeof(T)) : BUF_OOB;
+        load_param_regs<T, VEC, VPL>(pbias, a.bias, N, poff, false);
+        load_param_regs<T, VEC, VPL>(pgam, a.gamma, N, poff, true);
+        load_param_regs<T, VEC, VPL>(pbeta, a.beta, N, poff, false);
+        if (PREFETCH)
+            issue(walk.group(0));
+    }
+
     float lane_max = 0.f;
     int parity = 0;
-    const GroupWalk walk(a.K, a.A);
+
     for (int kk = 0; kk < a.K; ++kk) {
         const int64_t grp = walk.group(kk);
         if (grp >= a.n_groups)
             break; // uniform over the workgroup; later groups are larger
         const int64_t row = grp * TEAMS + team;
         const bool rv = row < a.M;
-        // descriptors over the valid rows of this group
-        const int64_t rows = a.M - grp * TEAMS < TEAMS ? a.M - grp * TEAMS : TEAMS;
-        const uint32_t bytes = uint32_t(rows * N) * uint32_t(sizeof(T));
-        const int64_t gbyte = grp * TEAMS * int64_t(N) * int64_t(sizeof(T));
-        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + gbyte, bytes);
-        const rsrc_t rs = make_rsrc(has_res ? static_cast<const char *>(a.res) + gbyte : nullptr,
-                                    has_res ? bytes : 0u);
+        const RowGroup rgp(grp, TEAMS, a.M, N, sizeof(T));
+        const uint32_t bytes = rgp.bytes;
+        const int64_t gbyte = rgp.byte0;
+        if (!PREFETCH)
+            issue(grp);
+        if constexpr (!PLDS) {
+            // keep the parameters packed: unpacking them once for the whole
+            // walk would cost more registers than the unpacking per group
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                reload_barrier(pbias[k]);
+                reload_barrier(pgam[k]);
+                reload_barrier(pbeta[k]);
+            }
+        }
 
-        // Loads.  ur holds u, the value actually normalised, in its packed I/O
-        // form (exact: u is rounded to T); every later pass unpacks it again.
+        // ur holds u, the value actually normalised, in its packed I/O form
+        // (exact: u is rounded to T); every later pass unpacks it again.
         Raw ur[VPL], rr[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            ur[k] = BIO::load(xs, off[k]);
-            rr[k] = has_res ? BIO::load(rs, off[k]) : IO::zero();
+            ur[k] = xn[k];
+            rr[k] = rn[k];
         }
+        const int64_t next = walk.group(kk + 1);
+        const bool has_next = kk + 1 < a.K && next < a.n_groups;
+        if (PREFETCH && has_next)
+            issue(next); // early: in flight during this group's work
 
         // fused add; u = round_T((x + bias) + residual), and the row sum of
         // u for LayerNorm (fp32 for bf16 rows, whose sums of values of
@@ -230,7 +337,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
             IO::unpack(ur[k], t);
             if (fused_add) {
                 float bv[VEC], rv_[VEC];
-                param_vec<T, VEC, PLDS>(par, a.bias, c0, cvalid[k], 0.f, bv);
+                param_vec<T, VEC, PLDS>(par, pbias[PLDS ? 0 : k], c0, bv);
                 IO::unpack(rr[k], rv_);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
@@ -315,8 +422,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
             const int c0 = (k * LPR + tl) * VEC;
             float u[VEC], gv[VEC], bv[VEC], yv[VEC];
             IO::unpack(ur[k], u);
-            param_vec<T, VEC, PLDS>(par + CAP, a.gamma, c0, cvalid[k], 1.f, gv);
-            param_vec<T, VEC, PLDS>(par + 2 * CAP, a.beta, c0, cvalid[k], 0.f, bv);
+            param_vec<T, VEC, PLDS>(par + CAP, pgam[PLDS ? 0 : k], c0, gv);
+            param_vec<T, VEC, PLDS>(par + 2 * CAP, pbeta[PLDS ? 0 : k], c0, bv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 yv[e] = fmaf(fmaf(u[e] - mean, rstd, lo_r), gv[e], bv[e]);
@@ -374,6 +481,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     constexpr int NW = WG / 64;
     constexpr int CAP = LPR * VPL * VEC;
     constexpr bool PLDS = CAP <= PARAMS_LDS_MAX;
+    constexpr bool PREFETCH = LPR >= WIDE_LPR;
     // partial slots to fold in LDS: waves (LPR <= 64) or teams (LPR > 64)
     constexpr int SLOTS = LPR <= 64 ? NW : TEAMS;
     static_assert(WG % 64 == 0, "workgroup of whole waves");
@@ -390,10 +498,6 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     const int N = a.N;
     const bool recompute = RMS && a.rstd == nullptr;
 
-    if constexpr (PLDS) {
-        stage_param<T>(par, a.gamma, N, CAP, 1.f, tid, WG);
-        __syncthreads();
-    }
     bool cvalid[VPL];
     uint32_t off[VPL];
 #pragma unroll
@@ -403,39 +507,82 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
                            : BUF_OOB;
     }
 
+    // x, dy and the row statistics of row group g; wide teams prefetch the
+    // next group while working on the current one.
+    Raw xn[VPL], dn[VPL];
+    float mean_n = 0.f, rstd_n = 0.f;
+    auto issue = [&](int64_t g) {
+        const RowGroup rg(g, TEAMS, a.M, N, sizeof(T));
+        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + rg.byte0, rg.bytes);
+        const rsrc_t ds = make_rsrc(static_cast<const char *>(a.dy) + rg.byte0, rg.bytes);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            xn[k] = BIO::load(xs, off[k]);
+            dn[k] = BIO::load(ds, off[k]);
+        }
+        const int64_t row = g * TEAMS + team;
+        const bool rv = row < a.M;
+        mean_n = (rv && !RMS) ? a.mean[row] : 0.f;
+        rstd_n = (rv && !recompute) ? a.rstd[row] : 0.f;
+    };
+    const GroupWalk walk(a.K, a.A);
+
+    // gamma's loads first, then the first row group's (see the forward)
+    constexpr int PR = PLDS ? 1 : VPL;
+    Raw pgam[PR];
+    if constexpr (PLDS) {
+        ParamStage<T, VEC, CAP, WG> sg;
+        sg.fetch(a.gamma, N, tid);
+        if (PREFETCH)
+            issue(walk.group(0));
+        sg.put(par, a.gamma, N, 1.f, tid);
+        __syncthreads();
+    } else {
+        uint32_t poff[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+            poff[k] = cvalid[k] ? uint32_t((k * LPR + tl) * VEC) * uint32_t(sizeof(T)) : BUF_OOB;
+        load_param_regs<T, VEC, VPL>(pgam, a.gamma, N, poff, true);
+        if (PREFETCH)
+            issue(walk.group(0));
+    }
+
     float acc_g[E], acc_b[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         acc_g[e] = 0.f;
         acc_b[e] = 0.f;
     }
-
     int parity = 0;
-    const GroupWalk walk(a.K, a.A);
+
     for (int kk = 0; kk < a.K; ++kk) {
         const int64_t grp = walk.group(kk);
         if (grp >= a.n_groups)
             break; // uniform over the workgroup; later groups are larger
         const int64_t row = grp * TEAMS + team;
         const bool rv = row < a.M;
-        const int64_t rows = a.M - grp * TEAMS < TEAMS ? a.M - grp * TEAMS : TEAMS;
-        const uint32_t bytes = uint32_t(rows * N) * uint32_t(sizeof(T));
-        const int64_t gbyte = grp * TEAMS * int64_t(N) * int64_t(sizeof(T));
-        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + gbyte, bytes);
-        const rsrc_t ds = make_rsrc(static_cast<const char *>(a.dy) + gbyte, bytes);
+        const RowGroup rgp(grp, TEAMS, a.M, N, sizeof(T));
+        const uint32_t bytes = rgp.bytes;
+        const int64_t gbyte = rgp.byte0;
+        if (!PREFETCH)
+            issue(grp);
+        if constexpr (!PLDS) {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k)
+                reload_barrier(pgam[k]); // unpacked per group, not held unpacked
+        }
 
         Raw xr[VPL], dr[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            xr[k] = BIO::load(xs, off[k]);
-            dr[k] = BIO::load(ds, off[k]);
+            xr[k] = xn[k];
+            dr[k] = dn[k];
         }
-        float mean = 0.f, rstd = 0.f;
-        if (rv && !recompute) {
-            if (!RMS)
-                mean = a.mean[row];
-            rstd = a.rstd[row];
-        }
+        float mean = mean_n, rstd = rstd_n;
+        const int64_t next = walk.group(kk + 1);
+        const bool has_next = kk + 1 < a.K && next < a.n_groups;
+        if (PREFETCH && has_next)
+            issue(next); // early: in flight during this group's work
 
         // Row sums, g = dy * gamma (invalid elements hold 0):
         //   LN : s0 = sum g (x - mean), s1 = sum g  ->  mean(g xhat) = rstd s0 / N
@@ -448,7 +595,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
             float xv[VEC], dv[VEC], gv[VEC];
             IO::unpack(xr[k], xv);
             IO::unpack(dr[k], dv);
-            param_vec<T, VEC, PLDS>(par, a.gamma, c0, cvalid[k], 1.f, gv);
+            param_vec<T, VEC, PLDS>(par, pgam[PLDS ? 0 : k], c0, gv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const float g = dv[e] * gv[e];
@@ -482,7 +629,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
             float xv[VEC], dv[VEC], gv[VEC], dxv[VEC];
             IO::unpack(xr[k], xv);
             IO::unpack(dr[k], dv);
-            param_vec<T, VEC, PLDS>(par, a.gamma, c0, cvalid[k], 1.f, gv);
+            param_vec<T, VEC, PLDS>(par, pgam[PLDS ? 0 : k], c0, gv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const int i = k * VEC + e;
@@ -553,8 +700,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 // Backward stage 2: column sums of the partial rows.  src holds two blocks
 // (dgamma, dbeta) of `rows` rows of N floats.  Workgroup (column tile, slice
 // s, block) adds rows [s*span, min(rows, (s+1)*span)) of its 64 columns:
-// thread (c, t) takes rows t, t + 4, ... of the slice in ascending order, and
-// the four threads of a column are added in order t = 0..3.  FINAL: one
+// thread (c, t) takes rows t, t + 16, ... of the slice in ascending order,
+// and the sixteen threads of a column are added in order t = 0..15.  FINAL: one
 // slice; down-cast and store to dgamma / dbeta.  Otherwise slice s stores its
 // sums as row s of dst (two blocks of gridDim.y rows), which a FINAL launch
 // then adds the same way.  Every addition happens in a fixed order.
@@ -563,7 +710,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 // costs more than the second launch.)
 // ---------------------------------------------------------------------------
 constexpr int COLSUM_COLS = 64;
-constexpr int COLSUM_SUB = 4;
+constexpr int COLSUM_SUB = 16;
 
 template <bool FINAL, bool BF16_OUT>
 __global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SUB)

@@ -2,15 +2,17 @@
 // X(T, VEC, LPR, VPL, TEAMS) lists ordered by row capacity LPR * VPL * VEC.
 // The host picks the first shape whose capacity covers N.
 //
-// 16-byte path (VEC = 16 / sizeof(T)); workgroups of 256 threads, or one
-// team of LPR threads when LPR > 256 (the forward adds 512-thread variants):
+// 16-byte path (VEC = 16 / sizeof(T)); narrow rows in workgroups of 256
+// threads (the forward adds 512-thread variants), wide rows in teams of 256
+// or 512 threads:
 //   bf16 capacities: 64 128 256 384 512 768 1024 1536 2048 4096 8192 16384
 //   fp32 capacities: 32 64 128 192 256 384 512 768 1024 2048 4096 8192 16384
 // Element-wise path (VEC = 1), for rows that are not whole 16-byte vectors
 // or pointers that are not 16-byte aligned: 256 512 1024 4096 16384.
 #pragma once
 
-#define NF_SHAPES_COMMON(X, T, VEC)                                                              \
+// Teams of at most one wave per row (bf16 rows <= 2048, fp32 <= 1024).
+#define NF_SHAPES_NARROW(X, T, VEC)                                                              \
     X(T, VEC, 8, 1, 32)                                                                          \
     X(T, VEC, 16, 1, 16)                                                                         \
     X(T, VEC, 16, 2, 16)                                                                         \
@@ -19,17 +21,32 @@
     X(T, VEC, 32, 3, 8)                                                                          \
     X(T, VEC, 32, 4, 8)                                                                          \
     X(T, VEC, 64, 3, 4)                                                                          \
-    X(T, VEC, 64, 4, 4)                                                                          \
-    X(T, VEC, 128, 4, 2)                                                                         \
+    X(T, VEC, 64, 4, 4)
+
+// Wide rows, several waves per row.  At twice the narrow capacity the forward
+// runs teams of 512 lanes holding one vector each (two rows per workgroup)
+// and the backward teams of 256 lanes holding two (four rows per workgroup,
+// so each workgroup's column partial covers more rows); beyond that both
+// use one team per workgroup.
+#define NF_SHAPES_WIDE_FWD(X, T, VEC)                                                            \
+    X(T, VEC, 512, 1, 2)                                                                         \
+    X(T, VEC, 256, 4, 1)                                                                         \
+    X(T, VEC, 512, 4, 1)
+#define NF_SHAPES_WIDE_BWD(X, T, VEC)                                                            \
+    X(T, VEC, 256, 2, 4)                                                                         \
     X(T, VEC, 256, 4, 1)                                                                         \
     X(T, VEC, 512, 4, 1)
 
-#define NF_SHAPES_BF16_VEC(X) NF_SHAPES_COMMON(X, bf16, 8)
-#define NF_SHAPES_F32_VEC(X) NF_SHAPES_COMMON(X, float, 4) X(float, 4, 1024, 4, 1)
+#define NF_SHAPES_BF16_FWD_VEC(X) NF_SHAPES_NARROW(X, bf16, 8) NF_SHAPES_WIDE_FWD(X, bf16, 8)
+#define NF_SHAPES_BF16_BWD_VEC(X) NF_SHAPES_NARROW(X, bf16, 8) NF_SHAPES_WIDE_BWD(X, bf16, 8)
+#define NF_SHAPES_F32_FWD_VEC(X)                                                                 \
+    NF_SHAPES_NARROW(X, float, 4) NF_SHAPES_WIDE_FWD(X, float, 4) X(float, 4, 1024, 4, 1)
+#define NF_SHAPES_F32_BWD_VEC(X)                                                                 \
+    NF_SHAPES_NARROW(X, float, 4) NF_SHAPES_WIDE_BWD(X, float, 4) X(float, 4, 1024, 4, 1)
 
 // Forward only: the same team shapes in 512-thread workgroups (twice the
 // rows per workgroup), preferred when there are rows enough to fill the GPU.
-#define NF_SHAPES_WIDE_WG(X, T, VEC)                                                             \
+#define NF_SHAPES_NARROW_2X(X, T, VEC)                                                             \
     X(T, VEC, 8, 1, 64)                                                                          \
     X(T, VEC, 16, 1, 32)                                                                         \
     X(T, VEC, 16, 2, 32)                                                                         \
