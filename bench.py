@@ -13,17 +13,17 @@ tensor read or written once plus the fp32 per-row statistics (forward
 8N + 8 bytes per row, backward 6N + 8).  Prints ONE JSON line on stdout;
 progress goes to stderr.
 
-Also reported: the roofline of the dominant kernel (the forward), timed with
-HIP events around each forward launch inside the timed loop; a per-case
-breakdown (each case timed alone with a 512 MiB cache flush between calls);
-and the CPU oracle timed on a bounded sample of the same workload.
+Also reported: the roofline of the dominant kernel (the forward): its
+algorithmic bytes over the per-launch duration of K forward calls run back
+to back between two HIP events; a per-case breakdown (each case timed the
+same way, cycling through buffers that together exceed the last-level
+cache); and the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
 import json
 import os
 import re
-import statistics
 import sys
 import time
 
@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0  # MI355X HBM3E
 M_BIG, N_BIG = 1152 * 500, 384
-FLUSH_BYTES = 512 << 20
+CALIB_BYTES = 512 << 20
 KERNEL_SOURCES = ("normalization_ln_fwd_amd/csrc/kernels.hpp",
                   "normalization_ln_fwd_amd/csrc/device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_ln_bf16_576000x384_traffic.md")
@@ -72,12 +72,57 @@ def recorded_traffic():
     return float(val.group(1))
 
 
+class HipEvents:
+    """n timing events of the HIP runtime, recorded on a given stream.
+
+    Created with hipEventDisableSystemFence: recording a default event ends
+    with a system-scope release (cache write-back) that costs several
+    microseconds and lands inside the interval being timed; these events only
+    take timestamps.  The runtime is the one already loaded in this process
+    (by torch and the library)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.ev = [ctypes.c_void_p() for _ in range(n)]
+        for e in self.ev:
+            self._check(self.hip.hipEventCreateWithFlags(ctypes.byref(e),
+                                                         ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)))
+
+    def _check(self, rc):
+        if rc != 0:
+            raise RuntimeError(f"HIP event call failed with status {rc}")
+
+    def record(self, i, stream):
+        self._check(self.hip.hipEventRecord(self.ev[i], self.ct.c_void_p(stream)))
+
+    def elapsed_ms(self, i, j):
+        ms = self.ct.c_float()
+        self._check(self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[i], self.ev[j]))
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--breakdown-iters", type=int, default=20)
+    ap.add_argument("--breakdown-iters", type=int, default=50)
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=M_BIG,
                     help="rows of the workload the CPU oracle is timed on")
@@ -139,35 +184,40 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
+    # Timed region: K steps on the current stream (the binding launches on
+    # it), one event before and one after: recording an event costs a few
+    # microseconds of idle GPU, so none is recorded between the steps.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents(2)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    ev.record(0, stream)
     for k in range(K):
-        ev[k][0].record()
         fwd()
-        ev[k][1].record()
         bwd()
-        ev[k][2].record()
+    ev.record(1, stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_step = ev[0][0].elapsed_time(ev[K - 1][2]) / K
-    fwd_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(K)]
-    bwd_ms = [ev[k][1].elapsed_time(ev[k][2]) for k in range(K)]
+    ms_step = ev.elapsed_ms(0, 1) / K
+    ev.close()
     step_bytes = fwd_bytes(M, N) + bwd_bytes(M, N)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"timed {K} steps: {ms_step:.4f} ms/step (wall {wall / K * 1e3:.4f} ms/step), "
         f"{value:.1f} GB/s")
 
-    fwd_avg = statistics.fmean(fwd_ms)
-    fwd_gbs = fwd_bytes(M, N) / (fwd_avg * 1e-3) / 1e9
+    # Per-launch durations of the two halves of the step: K forward calls back
+    # to back between two events, then K backward calls.  A forward call is
+    # the amax reset (one tiny kernel) and the forward kernel.
+    fwd_avg = time_calls([fwd], K, torch)[2]
+    bwd_avg = time_calls([bwd], K, torch)[2]
+    fwd_gbs = fwd_bytes(M, N) / (fwd_avg * 1e-6) / 1e9
     traffic = recorded_traffic()
     roofline = {"bound": "hbm", "achieved": round(fwd_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(fwd_gbs / PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "fwd_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 32, LayerNorm>",
-                "bytes_per_launch": fwd_bytes(M, N), "avg_launch_us": round(fwd_avg * 1e3, 2),
+                "bytes_per_launch": fwd_bytes(M, N), "avg_launch_us": round(fwd_avg, 2),
                 "kernel_source_hash": kernel_source_hash()}
-    bwd_avg = statistics.fmean(bwd_ms)
 
     result = {
         "metric": "achieved HBM GB/s (% of MI355X peak) for fused LN/RMSNorm fwd and bwd",
@@ -179,12 +229,12 @@ def main():
                                "M=576000 (1152x500) x N=384",
                    "M": M, "N": N, "io_dtype": "bf16", "compute_dtype": "f32",
                    "step_bytes": step_bytes, "frac_of_peak": round(value / PEAK_GBS, 4),
-                   "fwd_us": round(fwd_avg * 1e3, 2), "bwd_us": round(bwd_avg * 1e3, 2)},
+                   "fwd_us": round(fwd_avg, 2), "bwd_us": round(bwd_avg, 2)},
         "roofline": roofline,
     }
 
     if args.calib_copy:
-        src = torch.empty(FLUSH_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1)
+        src = torch.empty(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev).fill_(1)
         dst = torch.empty_like(src)
         for _ in range(5):
             dst.copy_(src)
@@ -204,29 +254,39 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def time_calls(fn, iters, torch, flush_buf):
-    """Median / min microseconds of fn(), each call after a cache flush."""
-    times = []
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for i in range(iters + 3):
-        flush_buf.zero_()
-        s.record()
-        fn()
-        e.record()
-        torch.cuda.synchronize()
-        if i >= 3:
-            times.append(s.elapsed_time(e) * 1e3)
-    return statistics.median(times), min(times)
+def time_calls(fns, iters, torch):
+    """Microseconds per call in steady state: after 3 untimed calls, `iters`
+    calls run back to back between two events, cycling through fns (the same
+    operation on different buffers, so that small cases do not run out of
+    the 256 MB last-level cache).  Returns (per call over the whole run, best
+    of 5 equal slices, per call of the run)."""
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(3):
+        fns[i % len(fns)]()
+    slices = 5
+    per = max(1, iters // slices)
+    ev = HipEvents(slices + 1)
+    torch.cuda.synchronize()
+    ev.record(0, stream)
+    for j in range(slices):
+        for i in range(per):
+            fns[(j * per + i) % len(fns)]()
+        ev.record(j + 1, stream)
+    torch.cuda.synchronize()
+    sl = [ev.elapsed_ms(j, j + 1) * 1e3 / per for j in range(slices)]
+    total = ev.elapsed_ms(0, slices) * 1e3 / (per * slices)
+    ev.close()
+    return total, min(sl), total
 
 
 def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     out = {}
 
     def rec(name, fn, nbytes, gated):
-        med, mn = time_calls(fn, iters, torch, flush)
+        fns = fn if isinstance(fn, list) else [fn]
+        med, mn, _ = time_calls(fns, iters, torch)
         gbs = nbytes / (med * 1e-6) / 1e9
-        out[name] = {"us_median": round(med, 2), "us_min": round(mn, 2), "bytes": nbytes,
+        out[name] = {"us_per_call": round(med, 2), "us_best_slice": round(mn, 2), "bytes": nbytes,
                      "GB_s": round(gbs, 1), "frac_peak": round(gbs / PEAK_GBS, 4),
                      "gated_70pct": gated}
         log(f"  {name}: {med:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_GBS:.1f}% of peak)")
@@ -253,32 +313,40 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
         dparam_dtype=torch.bfloat16, workspace=ws, out={"dx": dx, "dgamma": dg, "dbeta": db}),
         bwd_bytes(M, N), True)
     del dx
-    # config 2 (launch-bound size)
+    # config 2 (launch-bound size): consecutive calls take consecutive
+    # 4096-row slices of the large tensors
     M2 = 4096
-    sub = {k: (v[:M2] if v.dim() == 2 else v) for k, v in d.items()}
-    rec("ln_fwd_4096x384_amax", lambda: nf.ln_fwd(sub["x"], sub["bias"], sub["residual"],
-                                                   sub["gamma"], sub["beta"], 1e-5,
-                                                   want_amax=True),
-        fwd_bytes(M2, N), False)
-    # config 5: 8192 x 4096, residual + LayerNorm, 1% outliers
+    subs = [{k: (v[i * M2:(i + 1) * M2] if v.dim() == 2 else v) for k, v in d.items()}
+            for i in range(M // M2)]
+    rec("ln_fwd_4096x384_amax", [
+        (lambda s=s: nf.ln_fwd(s["x"], s["bias"], s["residual"], s["gamma"], s["beta"], 1e-5,
+                               want_amax=True)) for s in subs], fwd_bytes(M2, N), False)
+    # config 5: 8192 x 4096, residual + LayerNorm, 1% outliers; two buffer
+    # sets alternate (512 MB working set)
     M5, N5 = 8192, 4096
-    g5 = synth.make_inputs(M5, N5, dtype=synth.BF16, seed=0, outlier_p=0.01,
-                           names=("x", "residual", "gamma", "beta", "dy"))
-    d5 = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev)
-          for k, v in g5.items()}
-    o5 = nf.ln_fwd(d5["x"], None, d5["residual"], d5["gamma"], d5["beta"], 1e-5)
+    sets = []
+    for seed in (0, 1):
+        g5 = synth.make_inputs(M5, N5, dtype=synth.BF16, seed=seed, outlier_p=0.01,
+                               names=("x", "residual", "gamma", "beta", "dy"))
+        d5 = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev)
+              for k, v in g5.items()}
+        o5 = nf.ln_fwd(d5["x"], None, d5["residual"], d5["gamma"], d5["beta"], 1e-5)
+        b5 = {"dx": torch.empty_like(d5["x"]),
+              "dgamma": torch.empty(N5, dtype=torch.bfloat16, device=dev),
+              "dbeta": torch.empty(N5, dtype=torch.bfloat16, device=dev)}
+        sets.append((d5, o5, b5))
     ws5 = torch.empty(max(4, nf.bwd_workspace_size(M5, N5, torch.bfloat16)), dtype=torch.uint8,
                       device=dev)
-    rec("ln_fwd_8192x4096", lambda: nf.ln_fwd(d5["x"], None, d5["residual"], d5["gamma"],
-                                               d5["beta"], 1e-5, out=o5),
+    rec("ln_fwd_8192x4096", [
+        (lambda d5=d5, o5=o5: nf.ln_fwd(d5["x"], None, d5["residual"], d5["gamma"], d5["beta"],
+                                        1e-5, out=o5)) for d5, o5, _ in sets],
         fwd_bytes(M5, N5), True)
-    b5 = {"dx": torch.empty_like(d5["x"]),
-          "dgamma": torch.empty(N5, dtype=torch.bfloat16, device=dev),
-          "dbeta": torch.empty(N5, dtype=torch.bfloat16, device=dev)}
-    rec("ln_bwd_8192x4096", lambda: nf.ln_bwd(d5["dy"], o5["residual_out"], d5["gamma"],
+    rec("ln_bwd_8192x4096", [
+        (lambda d5=d5, o5=o5, b5=b5: nf.ln_bwd(d5["dy"], o5["residual_out"], d5["gamma"],
                                                o5["mean"], o5["rstd"],
                                                dparam_dtype=torch.bfloat16, workspace=ws5,
-                                               out=b5), bwd_bytes(M5, N5), True)
+                                               out=b5)) for d5, o5, b5 in sets],
+        bwd_bytes(M5, N5), True)
     torch.cuda.synchronize()
     return out
 
