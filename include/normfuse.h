@@ -55,11 +55,17 @@
  *              faults during execution appear at the caller's next
  *              synchronisation, as in HIP.
  *   Aliasing : outputs must not overlap inputs or each other.
- *   Threads  : calls are thread-safe; the library keeps only a per-device
- *              cache of device properties.
- *   Results  : deterministic: the same inputs on the same device give
- *              bit-identical outputs (the column sums use a fixed grid and a
- *              fixed summation order).
+ *   Threads  : calls are thread-safe; the library keeps no state between
+ *              calls.
+ *   Results  : deterministic: the same inputs give bit-identical outputs.
+ *              The kernel shape, the grid and every summation order follow
+ *              from M, N, the dtypes and the pointers' alignment alone.
+ *   Tuning   : the environment variables NORMFUSE_FWD_SHAPE / _BWD_SHAPE
+ *              ("LPRxVPL[xTEAMS]"), NORMFUSE_FWD_GROUPS_PER_WG /
+ *              _BWD_GROUPS_PER_WG and NORMFUSE_FWD_INTERLEAVE /
+ *              _BWD_INTERLEAVE, read at every call, override those choices
+ *              among the compiled shapes (for tuning; results stay within
+ *              the same tolerances, but column sums may round differently).
  *   Alignment: pointers must be aligned to their element size.  16-byte
  *              aligned [M, N] / [N] pointers with N a multiple of 16 bytes'
  *              worth of elements take the vectorised kernels; anything else
