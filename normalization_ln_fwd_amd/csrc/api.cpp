@@ -3,6 +3,7 @@
 // caller's stream.  Nothing here allocates device memory.
 #include "normfuse.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -39,11 +40,12 @@ constexpr int kFwdGroupsPerWg = 0; // 0: chosen per call (see fwd_common)
 constexpr int kBwdGroupsPerWg = 0; // 0: chosen per shape (see bwd_plan)
 // Row groups per workgroup.  Teams of several waves (wide rows) have few
 // rows in flight per CU; walking several groups per workgroup, with the next
-// group prefetched, keeps the loads going.  The backward's count also sets
-// how many rows one column partial covers.
+// group's loads in flight, keeps the loads going.  The backward's count also
+// sets how many rows one column partial covers: for wide rows a workgroup
+// walks kBwdRowsWide rows.
 constexpr int kFwdGroupsWide = 4;
 constexpr int kBwdGroupsNarrow = 3;
-constexpr int kBwdGroupsWide = 8;
+constexpr int kBwdRowsWide = 32;
 constexpr int kFwdInterleave = 1024;
 constexpr int kBwdInterleave = 256;
 
@@ -273,8 +275,9 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, const Knob
     const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    const int K = kn.bwd_k > 0 ? kn.bwd_k
-                               : (e->shape.lpr >= WIDE_LPR ? kBwdGroupsWide : kBwdGroupsNarrow);
+    int K = kn.bwd_k;
+    if (K == 0)
+        K = e->shape.lpr >= WIDE_LPR ? std::max(1, kBwdRowsWide / e->shape.teams) : kBwdGroupsNarrow;
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.bwd_a, w))
         return st;
     *entry = e;

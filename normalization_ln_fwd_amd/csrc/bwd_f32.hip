@@ -9,7 +9,7 @@ namespace nf {
      &launch_bwd<T, VEC, LPR, VPL, TEAMS, false>,                                                 \
      &launch_bwd<T, VEC, LPR, VPL, TEAMS, true>},
 
-static const BwdEntry k_vec[] = {NF_SHAPES_F32_BWD_VEC(NF_ENTRY)};
+static const BwdEntry k_vec[] = {NF_SHAPES_F32_VEC(NF_ENTRY)};
 static const BwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, float)};
 
 const BwdEntry *bwd_table_f32(bool vectorised, int *count)

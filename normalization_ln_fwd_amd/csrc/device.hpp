@@ -265,6 +265,15 @@ __device__ __forceinline__ void reload_barrier(R &r)
     asm volatile("" : "+v"(r));
 }
 
+// Uses `r` (so the compiler first waits for the load that writes it) and
+// keeps every memory access after this point from moving above it.  Emits no
+// instruction.
+template <typename R>
+__device__ __forceinline__ void order_after_arrival(R &r)
+{
+    asm volatile("" : "+v"(r) : : "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Group reductions over aligned groups of W lanes of a wave64 (W a power of
 // two, 1..64).  Every lane of a group receives the same bits: each step

@@ -9,7 +9,7 @@ namespace nf {
      &launch_fwd<T, VEC, LPR, VPL, TEAMS, false>,                                                 \
      &launch_fwd<T, VEC, LPR, VPL, TEAMS, true>},
 
-static const FwdEntry k_vec[] = {NF_SHAPES_BF16_FWD_VEC(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, bf16, 8)};
+static const FwdEntry k_vec[] = {NF_SHAPES_BF16_VEC(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, bf16, 8)};
 static const FwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, bf16)};
 
 const FwdEntry *fwd_table_bf16(bool vectorised, int *count)

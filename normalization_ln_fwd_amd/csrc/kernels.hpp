@@ -47,16 +47,27 @@ struct GroupWalk {
 // Bytes of row group g: it starts byte0 bytes into an [M, N] tensor and holds
 // `bytes` valid bytes (fewer rows in the last group).
 struct RowGroup {
-    int64_t byte0;
-    uint32_t bytes;
+    int64_t r0 = 0, byte0 = 0;
+    uint32_t rows = 0, bytes = 0;
+    RowGroup() = default;
     __device__ __forceinline__ RowGroup(int64_t g, int teams, int64_t M, int N, int elem)
     {
-        const int64_t r0 = g * teams;
-        const int64_t rows = M - r0 < teams ? (M - r0 > 0 ? M - r0 : 0) : teams;
+        r0 = g * teams;
+        const int64_t left = M - r0;
+        rows = uint32_t(left < teams ? (left > 0 ? left : 0) : teams);
         byte0 = r0 * int64_t(N) * elem;
-        bytes = uint32_t(rows * N) * uint32_t(elem);
+        bytes = rows * uint32_t(N) * uint32_t(elem);
     }
 };
+
+// Element `team` of a per-row fp32 vector over row group rg (0 past M or
+// when v is absent).  A buffer load: no branch, so the compiler can count
+// it exactly among the loads in flight.
+__device__ __forceinline__ float row_stat(const float *v, const RowGroup &rg, int team)
+{
+    const rsrc_t r = make_rsrc(v ? v + rg.r0 : nullptr, v ? rg.rows * 4u : 0u);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, team * 4, 0, 0));
+}
 
 // Sum over a team.  LPR <= 64: inside the wave.  LPR > 64: wave partials
 // meet in LDS (double-buffered by `parity`, so one barrier per reduction
@@ -464,6 +475,24 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     }
 }
 
+// Whether the backward pipelines its row walk (wide teams, see bwd_kernel):
+// two groups' packed rows, one group's packed dx, the column accumulators and
+// the unpacked working values (about 4E + 24 registers) must fit the wave's
+// share of the 512 VGPRs of a SIMD.  Narrow teams hold several rows per
+// wave and keep enough loads in flight without it; fp32 rows (twice the
+// registers per element) do not pipeline.
+template <typename T, int VEC, int LPR, int VPL, int TEAMS>
+constexpr bool bwd_pipelined()
+{
+    constexpr int raw = VEC * int(sizeof(T)) >= 4 ? VEC * int(sizeof(T)) / 4 : 1;
+    constexpr int slot = 2 * VPL * raw; // x and dy of one group, packed
+    constexpr int E = VPL * VEC;
+    constexpr int waves_per_simd = (LPR * TEAMS / 64 + 3) / 4;
+    constexpr int share = 512 / waves_per_simd;
+    constexpr int budget = share >= 256 ? share - 16 : share;
+    return sizeof(T) == 2 && LPR >= WIDE_LPR && 2 * slot + VPL * raw + 4 * E + 24 <= budget;
+}
+
 // ---------------------------------------------------------------------------
 // Backward stage 1 (mix-order): per row, one load of dy and x; the row
 // reduction gives dx; the column reduction is accumulated in registers over
@@ -481,7 +510,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     constexpr int NW = WG / 64;
     constexpr int CAP = LPR * VPL * VEC;
     constexpr bool PLDS = CAP <= PARAMS_LDS_MAX;
-    constexpr bool PREFETCH = LPR >= WIDE_LPR;
+    constexpr bool PIPE = bwd_pipelined<T, VEC, LPR, VPL, TEAMS>();
     // partial slots to fold in LDS: waves (LPR <= 64) or teams (LPR > 64)
     constexpr int SLOTS = LPR <= 64 ? NW : TEAMS;
     static_assert(WG % 64 == 0, "workgroup of whole waves");
@@ -507,34 +536,45 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
                            : BUF_OOB;
     }
 
-    // x, dy and the row statistics of row group g; wide teams prefetch the
-    // next group while working on the current one.
-    Raw xn[VPL], dn[VPL];
-    float mean_n = 0.f, rstd_n = 0.f;
-    auto issue = [&](int64_t g) {
+    // x, dy and the row statistics of one row group, as loaded.
+    struct Slot {
+        Raw x[VPL], d[VPL];
+        float mean, rstd;
+    };
+    auto issue = [&](int64_t g, Slot &sl) {
         const RowGroup rg(g, TEAMS, a.M, N, sizeof(T));
         const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + rg.byte0, rg.bytes);
         const rsrc_t ds = make_rsrc(static_cast<const char *>(a.dy) + rg.byte0, rg.bytes);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            xn[k] = BIO::load(xs, off[k]);
-            dn[k] = BIO::load(ds, off[k]);
+            sl.x[k] = BIO::load(xs, off[k]);
+            sl.d[k] = BIO::load(ds, off[k]);
         }
-        const int64_t row = g * TEAMS + team;
-        const bool rv = row < a.M;
-        mean_n = (rv && !RMS) ? a.mean[row] : 0.f;
-        rstd_n = (rv && !recompute) ? a.rstd[row] : 0.f;
+        if constexpr (PIPE) {
+            sl.mean = RMS ? 0.f : row_stat(a.mean, rg, team);
+            sl.rstd = recompute ? 0.f : row_stat(a.rstd, rg, team);
+        } else {
+            const int64_t row = g * TEAMS + team;
+            const bool rv = row < a.M;
+            sl.mean = (rv && !RMS) ? a.mean[row] : 0.f;
+            sl.rstd = (rv && !recompute) ? a.rstd[row] : 0.f;
+        }
     };
     const GroupWalk walk(a.K, a.A);
+    auto valid = [&](int kk) { return kk < a.K && walk.group(kk) < a.n_groups; };
 
-    // gamma's loads first, then the first row group's (see the forward)
+    // Slot A holds the group being worked on; pipelined walks load the next
+    // group into slot B meanwhile (the two alternate).
+    Slot A, B;
+
+    // gamma's loads first, then the first row groups' (see the forward)
     constexpr int PR = PLDS ? 1 : VPL;
     Raw pgam[PR];
     if constexpr (PLDS) {
         ParamStage<T, VEC, CAP, WG> sg;
         sg.fetch(a.gamma, N, tid);
-        if (PREFETCH)
-            issue(walk.group(0));
+        if (PIPE)
+            issue(walk.group(0), A);
         sg.put(par, a.gamma, N, 1.f, tid);
         __syncthreads();
     } else {
@@ -543,8 +583,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
         for (int k = 0; k < VPL; ++k)
             poff[k] = cvalid[k] ? uint32_t((k * LPR + tl) * VEC) * uint32_t(sizeof(T)) : BUF_OOB;
         load_param_regs<T, VEC, VPL>(pgam, a.gamma, N, poff, true);
-        if (PREFETCH)
-            issue(walk.group(0));
+        if (PIPE)
+            issue(walk.group(0), A);
     }
 
     float acc_g[E], acc_b[E];
@@ -555,34 +595,24 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     }
     int parity = 0;
 
-    for (int kk = 0; kk < a.K; ++kk) {
-        const int64_t grp = walk.group(kk);
-        if (grp >= a.n_groups)
-            break; // uniform over the workgroup; later groups are larger
+    // dx of the last group worked on, held back by pipelined walks
+    Raw dxh[VPL];
+    RowGroup hrg;
+    bool held = false;
+
+    // The work on row group grp, whose rows and statistics are in sl; dx is
+    // stored, or held in dxh when `hold`.
+    auto work = [&](int64_t grp, Slot &sl, bool hold) {
         const int64_t row = grp * TEAMS + team;
         const bool rv = row < a.M;
         const RowGroup rgp(grp, TEAMS, a.M, N, sizeof(T));
-        const uint32_t bytes = rgp.bytes;
-        const int64_t gbyte = rgp.byte0;
-        if (!PREFETCH)
-            issue(grp);
         if constexpr (!PLDS) {
 #pragma unroll
             for (int k = 0; k < VPL; ++k)
                 reload_barrier(pgam[k]); // unpacked per group, not held unpacked
         }
-
-        Raw xr[VPL], dr[VPL];
-#pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            xr[k] = xn[k];
-            dr[k] = dn[k];
-        }
-        float mean = mean_n, rstd = rstd_n;
-        const int64_t next = walk.group(kk + 1);
-        const bool has_next = kk + 1 < a.K && next < a.n_groups;
-        if (PREFETCH && has_next)
-            issue(next); // early: in flight during this group's work
+        const float mean = sl.mean;
+        float rstd = sl.rstd;
 
         // Row sums, g = dy * gamma (invalid elements hold 0):
         //   LN : s0 = sum g (x - mean), s1 = sum g  ->  mean(g xhat) = rstd s0 / N
@@ -593,8 +623,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
         for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
             float xv[VEC], dv[VEC], gv[VEC];
-            IO::unpack(xr[k], xv);
-            IO::unpack(dr[k], dv);
+            IO::unpack(sl.x[k], xv);
+            IO::unpack(sl.d[k], dv);
             param_vec<T, VEC, PLDS>(par, pgam[PLDS ? 0 : k], c0, gv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -619,16 +649,16 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            reload_barrier(xr[k]);
-            reload_barrier(dr[k]);
+            reload_barrier(sl.x[k]);
+            reload_barrier(sl.d[k]);
         }
-        const rsrc_t dxs = make_rsrc(static_cast<char *>(a.dx) + gbyte, bytes);
+        const rsrc_t dxs = make_rsrc(static_cast<char *>(a.dx) + rgp.byte0, rgp.bytes);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
             float xv[VEC], dv[VEC], gv[VEC], dxv[VEC];
-            IO::unpack(xr[k], xv);
-            IO::unpack(dr[k], dv);
+            IO::unpack(sl.x[k], xv);
+            IO::unpack(sl.d[k], dv);
             param_vec<T, VEC, PLDS>(par, pgam[PLDS ? 0 : k], c0, gv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -640,7 +670,66 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
                     acc_b[i] += dv[e];
                 }
             }
-            BIO::store(dxs, off[k], IO::pack(dxv));
+            if (hold)
+                dxh[k] = IO::pack(dxv);
+            else
+                BIO::store(dxs, off[k], IO::pack(dxv));
+        }
+        if (hold) {
+            hrg = rgp;
+            held = true;
+        }
+    };
+
+    if constexpr (PIPE) {
+        // Two-stage pipeline.  As soon as a group's rows have arrived, the
+        // next group's loads and the previous group's dx stores are issued;
+        // then the group is worked on and its dx held.  Each wait thus finds
+        // only loads and stores issued a whole group earlier.  (A wait for a
+        // load while any store is outstanding waits for all of them, so a
+        // store issued just before the wait would put its latency on every
+        // group's path.)
+        auto arrive = [&](Slot &sl) {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                order_after_arrival(sl.x[k]);
+                order_after_arrival(sl.d[k]);
+            }
+            order_after_arrival(sl.mean);
+            order_after_arrival(sl.rstd);
+        };
+        auto flush = [&]() {
+            if (held) {
+                const rsrc_t dxs = make_rsrc(static_cast<char *>(a.dx) + hrg.byte0, hrg.bytes);
+#pragma unroll
+                for (int k = 0; k < VPL; ++k)
+                    BIO::store(dxs, off[k], dxh[k]);
+            }
+        };
+        for (int kk = 0; kk < a.K; kk += 2) {
+            if (!valid(kk))
+                break;
+            arrive(A);
+            if (valid(kk + 1))
+                issue(walk.group(kk + 1), B);
+            flush();
+            work(walk.group(kk), A, true);
+            if (!valid(kk + 1))
+                break;
+            arrive(B);
+            if (valid(kk + 2))
+                issue(walk.group(kk + 2), A);
+            flush();
+            work(walk.group(kk + 1), B, true);
+        }
+        flush();
+    } else {
+        for (int kk = 0; kk < a.K; ++kk) {
+            const int64_t grp = walk.group(kk);
+            if (grp >= a.n_groups)
+                break; // uniform over the workgroup; later groups are larger
+            issue(grp, A);
+            work(grp, A, false);
         }
     }
 
@@ -729,7 +818,7 @@ __global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SUB)
     const float *part = src + (int64_t)which * rows * N;
     float acc = 0.f;
     if (j < N) {
-#pragma unroll 8
+#pragma unroll 16
         for (int r = r0 + ty; r < r1; r += COLSUM_SUB)
             acc += part[(int64_t)r * N + j];
     }

@@ -23,26 +23,17 @@
     X(T, VEC, 64, 3, 4)                                                                          \
     X(T, VEC, 64, 4, 4)
 
-// Wide rows, several waves per row.  At twice the narrow capacity the forward
-// runs teams of 512 lanes holding one vector each (two rows per workgroup)
-// and the backward teams of 256 lanes holding two (four rows per workgroup,
-// so each workgroup's column partial covers more rows); beyond that both
-// use one team per workgroup.
-#define NF_SHAPES_WIDE_FWD(X, T, VEC)                                                            \
+// Wide rows, several waves per row.  At twice the narrow capacity both
+// directions run teams of 512 lanes holding one vector each, two rows per
+// workgroup; beyond that one team per workgroup.
+#define NF_SHAPES_WIDE(X, T, VEC)                                                                \
     X(T, VEC, 512, 1, 2)                                                                         \
     X(T, VEC, 256, 4, 1)                                                                         \
     X(T, VEC, 512, 4, 1)
-#define NF_SHAPES_WIDE_BWD(X, T, VEC)                                                            \
-    X(T, VEC, 256, 2, 4)                                                                         \
-    X(T, VEC, 256, 4, 1)                                                                         \
-    X(T, VEC, 512, 4, 1)
 
-#define NF_SHAPES_BF16_FWD_VEC(X) NF_SHAPES_NARROW(X, bf16, 8) NF_SHAPES_WIDE_FWD(X, bf16, 8)
-#define NF_SHAPES_BF16_BWD_VEC(X) NF_SHAPES_NARROW(X, bf16, 8) NF_SHAPES_WIDE_BWD(X, bf16, 8)
-#define NF_SHAPES_F32_FWD_VEC(X)                                                                 \
-    NF_SHAPES_NARROW(X, float, 4) NF_SHAPES_WIDE_FWD(X, float, 4) X(float, 4, 1024, 4, 1)
-#define NF_SHAPES_F32_BWD_VEC(X)                                                                 \
-    NF_SHAPES_NARROW(X, float, 4) NF_SHAPES_WIDE_BWD(X, float, 4) X(float, 4, 1024, 4, 1)
+#define NF_SHAPES_BF16_VEC(X) NF_SHAPES_NARROW(X, bf16, 8) NF_SHAPES_WIDE(X, bf16, 8)
+#define NF_SHAPES_F32_VEC(X)                                                                     \
+    NF_SHAPES_NARROW(X, float, 4) NF_SHAPES_WIDE(X, float, 4) X(float, 4, 1024, 4, 1)
 
 // Forward only: the same team shapes in 512-thread workgroups (twice the
 // rows per workgroup), preferred when there are rows enough to fill the GPU.
