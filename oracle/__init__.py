@@ -15,6 +15,10 @@ Parity status of each function (what pins it, in ``tests/test_oracle.py``):
   norm_bwd (both)       -- pinned: central finite differences of the forward,
                            the closed-form row invariants of dx, special cases,
                            float64 autograd, brute-force column sums.
+  norm_bwd dbias        -- pinned: central finite differences of the forward
+                           with respect to bias, float64 autograd through
+                           (x + bias) + residual, and (LayerNorm) the closed
+                           form sum_j dbias_j = 0.
   round_to_dtype        -- pinned: exhaustive checks against exactly
                            representable neighbours and ties.
 
@@ -51,7 +55,7 @@ def _load():
                                         vp, vp, vp, vp, vp]
         lib.oracle_norm_fwd.restype = ci
         lib.oracle_norm_bwd.argtypes = [ci, vp, vp, vp, vp, vp, dbl, i64, i64, ci, ci,
-                                        vp, vp, vp, vp, vp, vp]
+                                        vp, vp, vp, vp, vp, vp, vp, vp]
         lib.oracle_norm_bwd.restype = ci
         lib.oracle_round_to_dtype.argtypes = [vp, i64, ci, vp]
         lib.oracle_round_to_dtype.restype = ci
@@ -112,14 +116,15 @@ def norm_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, *,
 
 
 def norm_bwd(dy, x, gamma=None, mean=None, rstd=None, eps=1e-5, *, rms=False,
-             dtype=BF16, nthreads=None, want_dx=True, want_params=True):
+             dtype=BF16, nthreads=None, want_dx=True, want_params=True, want_dbias=False):
     """Backward on an (M, N) matrix.
 
     ``mean`` / ``rstd`` are per-row arrays (any float dtype, widened exactly
     to float64); RMSNorm takes ``rstd=None`` to recompute it from ``x``.
     Returns a dict of float64 arrays: ``dx`` (M, N), ``dgamma``, ``dbeta``,
     ``dgamma_l2``, ``dbeta_l2`` (N,), all unrounded, and ``rstd`` (M,), the
-    rstd the gradients used.
+    rstd the gradients used; with ``want_dbias`` also ``dbias`` (N,), the
+    gradient of the forward's bias (column sums of dx), and ``dbias_l2``.
     """
     lib = _load()
     dy = _in(dy, dtype, name="dy")
@@ -131,11 +136,14 @@ def norm_bwd(dy, x, gamma=None, mean=None, rstd=None, eps=1e-5, *, rms=False,
     dx = np.empty((M, N), np.float64) if want_dx else None
     out = {k: (np.empty(N, np.float64) if want_params else None)
            for k in ("dgamma", "dbeta", "dgamma_l2", "dbeta_l2")}
+    for k in ("dbias", "dbias_l2"):
+        out[k] = np.empty(N, np.float64) if want_dbias else None
     rstd_used = np.empty(M, np.float64)
     rc = lib.oracle_norm_bwd(int(rms), _ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd),
                              float(eps), M, N, dtype, nthreads or default_threads(), _ptr(dx),
                              _ptr(out["dgamma"]), _ptr(out["dbeta"]), _ptr(out["dgamma_l2"]),
-                             _ptr(out["dbeta_l2"]), _ptr(rstd_used))
+                             _ptr(out["dbeta_l2"]), _ptr(rstd_used), _ptr(out["dbias"]),
+                             _ptr(out["dbias_l2"]))
     if rc != 0:
         raise ValueError("oracle_norm_bwd rejected its arguments")
     out["dx"] = dx

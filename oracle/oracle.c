@@ -25,6 +25,9 @@
  *              with a down-cast to fp16/bf16.  The pages do not write the
  *              gradient formulas out; they are the exact derivatives of the
  *              forward definition (standard calculus), stated where used.
+ *              The gradient of the forward's bias (the column sums of dx) is
+ *              the backward of the fused add that the nvFuser comment's
+ *              forward starts with.
  *
  * Readings where the pages are silent (each is also listed in the design
  * notes of the repository):
@@ -273,6 +276,7 @@ typedef struct {
     double *rstd; /* per-row rstd actually used (given or recomputed) */
     double *dx;
     double *dgamma, *dbeta, *dgamma_l2, *dbeta_l2;
+    double *dbias, *dbias_l2;
 } bwd_ctx;
 
 static double xhat_of(const bwd_ctx *c, int64_t i, int64_t j)
@@ -352,6 +356,30 @@ static void bwd_col_sums(void *vctx, int64_t j0, int64_t j1)
     }
 }
 
+/* dbias_j = sum_i dx_ij, rows in order, and the 2-norm of its terms.  The
+ * forward adds bias to every row before normalising (nvFuser issue #1660,
+ * layernorm + amax comment: out1 = (x + bias) + residual), so the gradient
+ * of the loss with respect to bias_j is the column sum of the gradient with
+ * respect to out1, which is dx; x and residual each receive dx itself.  A
+ * third reduction over the B x T rows, of the kind PyTorch PR #165370
+ * (description) computes next to dw/db. */
+static void bwd_dbias_cols(void *vctx, int64_t j0, int64_t j1)
+{
+    bwd_ctx *c = (bwd_ctx *)vctx;
+    for (int64_t j = j0; j < j1; ++j) {
+        double s = 0.0, q = 0.0;
+        for (int64_t i = 0; i < c->M; ++i) {
+            double t = c->dx[i * c->N + j];
+            s += t;
+            q += t * t;
+        }
+        if (c->dbias)
+            c->dbias[j] = s;
+        if (c->dbias_l2)
+            c->dbias_l2[j] = sqrt(q);
+    }
+}
+
 /*
  * LayerNorm (is_rms = 0) or RMSNorm (is_rms = 1) backward.
  *   inputs : dy [M,N], x [M,N] (the tensor that was normalised), gamma [N]
@@ -359,13 +387,16 @@ static void bwd_col_sums(void *vctx, int64_t j0, int64_t j1)
  *            rstd [M] or NULL to recompute it from x with eps.
  *   outputs (each optional): dx [M,N], dgamma [N], dbeta [N] in double,
  *            unrounded; dgamma_l2 / dbeta_l2 [N] = 2-norm of the summed terms;
- *            rstd_out [M] = the rstd used (given or recomputed).
+ *            rstd_out [M] = the rstd used (given or recomputed); dbias [N] =
+ *            the gradient of the forward's bias (column sums of dx) and
+ *            dbias_l2 [N] the 2-norm of its terms.
  * Returns 0, or -1 on a bad argument.
  */
 int oracle_norm_bwd(int is_rms, const void *dy, const void *x, const void *gamma,
                     const double *mean, const double *rstd, double eps, int64_t M, int64_t N,
                     int dtype, int nthreads, double *dx, double *dgamma, double *dbeta,
-                    double *dgamma_l2, double *dbeta_l2, double *rstd_out)
+                    double *dgamma_l2, double *dbeta_l2, double *rstd_out, double *dbias,
+                    double *dbias_l2)
 {
     if (!dy || !x || M < 0 || N <= 0 || (dtype != OR_F32 && dtype != OR_BF16))
         return -1;
@@ -376,15 +407,29 @@ int oracle_norm_bwd(int is_rms, const void *dy, const void *x, const void *gamma
     double *rstd_used = (double *)malloc((size_t)(M > 0 ? M : 1) * sizeof(double));
     if (!rstd_used)
         return -1;
+    /* dbias needs dx: a scratch copy when the caller does not want dx */
+    const int want_db = dbias || dbias_l2;
+    double *dx_buf = dx;
+    if (want_db && !dx_buf) {
+        dx_buf = (double *)malloc((size_t)(M > 0 ? M * N : 1) * sizeof(double));
+        if (!dx_buf) {
+            free(rstd_used);
+            return -1;
+        }
+    }
     bwd_ctx c = {is_rms, dtype, dy, x, gamma, mean, rstd, eps, M, N,
-                 rstd_used, dx, dgamma, dbeta, dgamma_l2, dbeta_l2};
+                 rstd_used, dx_buf, dgamma, dbeta, dgamma_l2, dbeta_l2, dbias, dbias_l2};
     parallel_ranges(nthreads, M, bwd_rstd_rows, &c);
-    if (dx)
+    if (dx_buf)
         parallel_ranges(nthreads, M, bwd_dx_rows, &c);
     if (dgamma || dbeta || dgamma_l2 || dbeta_l2)
         parallel_ranges(nthreads, N, bwd_col_sums, &c);
+    if (want_db)
+        parallel_ranges(nthreads, N, bwd_dbias_cols, &c);
     if (rstd_out && M > 0)
         memcpy(rstd_out, rstd_used, (size_t)M * sizeof(double));
+    if (dx_buf != dx)
+        free(dx_buf);
     free(rstd_used);
     return 0;
 }

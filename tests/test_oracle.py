@@ -281,6 +281,83 @@ def test_backward_matches_autograd_float64(oracle_mod, rms):
 
 
 @pytest.mark.parametrize("rms", [False, True])
+@pytest.mark.parametrize("N", [1, 3, 8, 17])
+def test_dbias_finite_differences(oracle_mod, rms, N):
+    """dbias = dL/dbias for L = sum(dy * y(x + bias + residual)): central
+    differences in bias through the oracle forward (fp32 I/O; every perturbed
+    sum is exact in fp32), Richardson-extrapolated."""
+    rng = np.random.default_rng(300 + N)
+    M, eps = 4, 0.02
+    x = dyadic(rng, (M, N))
+    res = dyadic(rng, (M, N))
+    bias = dyadic(rng, (N,))
+    gamma = dyadic(rng, (N,), 64, 384)
+    beta = dyadic(rng, (N,))
+    dy = f32(rng.standard_normal((M, N)))
+    fwd = oracle_mod.norm_fwd(x, bias, res, gamma, beta, eps, rms=rms, dtype=F32)
+    b = oracle_mod.norm_bwd(dy, fwd["u"], gamma, None if rms else fwd["mean"], fwd["rstd"], eps,
+                            rms=rms, dtype=F32, want_dbias=True)
+
+    def loss(bb):
+        r = oracle_mod.norm_fwd(x, f32(bb), res, gamma, beta, eps, rms=rms, dtype=F32)
+        return float(np.sum(dy.astype(np.float64) * r["y"]))
+
+    def fd(h):
+        g = np.zeros(N)
+        for j in range(N):
+            hi = bias.astype(np.float64).copy()
+            lo = hi.copy()
+            hi[j] += h
+            lo[j] -= h
+            g[j] = (loss(hi) - loss(lo)) / (2 * h)
+        return g
+
+    est = (4 * fd(2.0**-11) - fd(2.0**-10)) / 3
+    scale = max(1.0, float(np.max(fwd["rstd"])))
+    np.testing.assert_allclose(b["dbias"], est, rtol=0, atol=4e-8 * scale * M)
+
+
+@pytest.mark.parametrize("rms", [False, True])
+def test_dbias_matches_autograd_float64(oracle_mod, rms):
+    """The gradient of the bias through u = (x + bias) + residual, by float64
+    autograd (x, residual and bias dyadic, so u is exact in fp32)."""
+    M, N = 13, 40
+    rng = np.random.default_rng(11)
+    x, res, bias = dyadic(rng, (M, N)), dyadic(rng, (M, N)), dyadic(rng, (N,))
+    gamma = f32(1 + 0.1 * rng.standard_normal(N))
+    beta = f32(0.1 * rng.standard_normal(N))
+    dy = f32(rng.standard_normal((M, N)))
+    eps = 1e-6 if rms else 1e-5
+    bt = t64(bias).requires_grad_()
+    u = t64(x) + bt + t64(res)
+    y = (F.rms_norm(u, (N,), t64(gamma), eps) + t64(beta)) if rms else \
+        F.layer_norm(u, (N,), t64(gamma), t64(beta), eps)
+    (y * t64(dy)).sum().backward()
+    fwd = oracle_mod.norm_fwd(x, bias, res, gamma, beta, eps, rms=rms, dtype=F32)
+    assert np.array_equal(fwd["u"].astype(np.float64), u.detach().numpy())
+    b = oracle_mod.norm_bwd(dy, fwd["u"], gamma, None if rms else fwd["mean"],
+                            None if rms else fwd["rstd"], eps, rms=rms, dtype=F32,
+                            want_dbias=True)
+    np.testing.assert_allclose(b["dbias"], bt.grad.numpy(), rtol=1e-10, atol=1e-10)
+
+
+def test_dbias_layernorm_sums_to_zero(oracle_mod):
+    """LayerNorm's dx sums to zero over every row, so the column sums of dx
+    (dbias) sum to zero over the columns; their 2-norm scale is the root of
+    the column sums of dx^2."""
+    M, N = 37, 96
+    inp = synth.make_inputs(M, N, dtype=BF16, seed=12, names=("x", "gamma", "dy"))
+    fwd = oracle_mod.norm_fwd(inp["x"], eps=1e-5, dtype=BF16)
+    b = oracle_mod.norm_bwd(inp["dy"], inp["x"], inp["gamma"], fwd["mean"], fwd["rstd"], 1e-5,
+                            want_dbias=True)
+    assert abs(float(np.sum(b["dbias"]))) <= 1e-10 * float(np.sum(b["dbias_l2"]))
+    np.testing.assert_allclose(b["dbias_l2"], np.sqrt(np.sum(b["dx"] ** 2, axis=0)), rtol=1e-12)
+    c = oracle_mod.norm_bwd(inp["dy"], inp["x"], inp["gamma"], fwd["mean"], fwd["rstd"], 1e-5,
+                            want_dbias=True, want_dx=False)
+    assert np.array_equal(c["dbias"], b["dbias"])
+
+
+@pytest.mark.parametrize("rms", [False, True])
 def test_dx_row_invariants(oracle_mod, rms):
     """LayerNorm: sum_j dx_j = 0 and sum_j dx_j xhat_j = eps rstd^3 sum_j g_j xhat_j.
     RMSNorm: sum_j dx_j x_j = eps rstd^3 sum_j g_j x_j (g = dy * gamma)."""

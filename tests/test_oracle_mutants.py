@@ -49,6 +49,10 @@ MUTANTS = [
     ("RMS recompute drops eps", "c->rstd[i] = 1.0 / sqrt(s / (double)c->N + c->eps);",
      "c->rstd[i] = 1.0 / sqrt(s / (double)c->N);"),
     ("xhat ignores the mean", "(xv - c->mean[i]) * c->rstd[i]", "xv * c->rstd[i]"),
+    ("dbias sums dy instead of dx", "double t = c->dx[i * c->N + j];",
+     "double t = elem(c->dy, c->dtype, i * c->N + j);"),
+    ("dbias skips the last row", "for (int64_t i = 0; i < c->M; ++i) {\n            double t = c->dx",
+     "for (int64_t i = 0; i + 1 < c->M; ++i) {\n            double t = c->dx"),
 ]
 
 
