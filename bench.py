@@ -312,6 +312,11 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
         d["dy"], d["x"], d["gamma"], fwd_out["mean"], fwd_out["rstd"],
         dparam_dtype=torch.bfloat16, workspace=ws, out={"dx": dx, "dgamma": dg, "dbeta": db}),
         bwd_bytes(M, N), True)
+    dbias = torch.empty(N, dtype=torch.bfloat16, device=dev)
+    rec("ln_bwd_576000x384_dbias", lambda: nf.ln_bwd(
+        d["dy"], d["x"], d["gamma"], fwd_out["mean"], fwd_out["rstd"],
+        dparam_dtype=torch.bfloat16, workspace=ws,
+        out={"dx": dx, "dgamma": dg, "dbeta": db, "dbias": dbias}), bwd_bytes(M, N), False)
     del dx
     # config 2 (launch-bound size): consecutive calls take consecutive
     # 4096-row slices of the large tensors

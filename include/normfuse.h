@@ -21,7 +21,10 @@
  *      reduction), PR description: the dx reduction runs over the hidden
  *      dimension and the dgamma / dbeta reduction over all B x T rows; both
  *      read dy and x, which are loaded once here, and the outer reduction
- *      ends with a down-cast when dgamma / dbeta are low precision.
+ *      ends with a down-cast when dgamma / dbeta are low precision.  The
+ *      optional dbias is the backward of the forward's fused add (the
+ *      nvFuser comment's out1 = (x + bias) + residual): a third reduction
+ *      over the rows, of dx, in the same pass; x and residual receive dx.
  *
  * Definitions (the pages call PyTorch's layer_norm; these are its semantics)
  *   u      = round_io((x + bias) + residual)          (absent terms are 0)
@@ -32,7 +35,8 @@
  *   bwd    : xhat = (x-mean)*rstd (LN) or x*rstd (RMS), g = dy*gamma,
  *            dx = rstd*(g - mean_j(g) - xhat*mean_j(g*xhat))   (LN)
  *            dx = rstd*(g - xhat*mean_j(g*xhat))                (RMS)
- *            dgamma_j = sum_i dy_ij*xhat_ij,  dbeta_j = sum_i dy_ij
+ *            dgamma_j = sum_i dy_ij*xhat_ij,  dbeta_j = sum_i dy_ij,
+ *            dbias_j = sum_i dx_ij (dx before rounding)
  *   Arithmetic is fp32 throughout; round_io rounds to the I/O dtype to
  *   nearest, ties to even.  The normalisation reads the rounded u, which is
  *   also what residual_out holds.
@@ -71,7 +75,7 @@
  *              worth of elements take the vectorised kernels; anything else
  *              takes a correct element-wise path.
  *   Sizes    : 0 <= M; 1 <= N <= NORM_N_MAX.  M = 0 enqueues only what
- *              defines the outputs (amax = 0, dgamma = dbeta = 0), and then
+ *              defines the outputs (amax = 0, dgamma = dbeta = dbias = 0), and then
  *              the [M, N] and [M] pointers may be NULL.
  */
 #ifndef NORMFUSE_H
@@ -133,9 +137,9 @@ norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, con
 /*
  * norm_bwd_workspace_size -- bytes of device workspace ln_bwd / rms_bwd need
  * for an [M, N] problem of the given dtype on the current device (the
- * per-workgroup dgamma / dbeta column partials).  Writes 0 when none is
- * needed.  The workspace needs no initialisation and may be reused by calls
- * ordered on one stream.
+ * per-workgroup dgamma / dbeta / dbias column partials; the size covers a
+ * call that asks for dbias).  Writes 0 when none is needed.  The workspace
+ * needs no initialisation and may be reused by calls ordered on one stream.
  */
 norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_t *bytes);
 
@@ -149,15 +153,19 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
  *   dx           [M,N] dtype   required
  *   dgamma       [N]   dparam_dtype  optional
  *   dbeta        [N]   dparam_dtype  optional
- *   dparam_dtype NORM_F32 or NORM_BF16: dgamma / dbeta are summed in fp32
- *                and rounded (to nearest, ties to even) to this type
+ *   dbias        [N]   dparam_dtype  optional: gradient of the bias of a
+ *                              forward that fused (x + bias) + residual (the
+ *                              column sums of dx); x and residual both
+ *                              receive dx itself
+ *   dparam_dtype NORM_F32 or NORM_BF16: dgamma / dbeta / dbias are summed in
+ *                fp32 and rounded (to nearest, ties to even) to this type
  *   workspace    device memory of at least norm_bwd_workspace_size bytes
  *                (may be NULL when that size is 0)
  */
 norm_status_t ln_bwd(const void *dy, const void *x, const void *gamma, const float *mean,
                      const float *rstd, int64_t M, int64_t N, int32_t dtype, void *dx,
-                     void *dgamma, void *dbeta, int32_t dparam_dtype, void *workspace,
-                     size_t workspace_bytes, void *stream);
+                     void *dgamma, void *dbeta, void *dbias, int32_t dparam_dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * rms_bwd -- RMSNorm backward with the mix-order reduction.  Arguments as
@@ -167,7 +175,7 @@ norm_status_t ln_bwd(const void *dy, const void *x, const void *gamma, const flo
  */
 norm_status_t rms_bwd(const void *dy, const void *x, const void *gamma, const float *rstd,
                       float eps, int64_t M, int64_t N, int32_t dtype, void *dx, void *dgamma,
-                      void *dbeta, int32_t dparam_dtype, void *workspace,
+                      void *dbeta, void *dbias, int32_t dparam_dtype, void *workspace,
                       size_t workspace_bytes, void *stream);
 
 /* Static text for a status code. */

@@ -9,7 +9,8 @@ library, importing works but every call raises ``NormLibraryMissing``.
 Operations (definitions in ``include/normfuse.h``):
   ln_fwd / rms_fwd   fused (bias +) residual + LayerNorm / RMSNorm forward
                      with optional residual_out, mean / rstd and amax
-  ln_bwd / rms_bwd   backward: dx plus dgamma / dbeta from one read of dy, x
+  ln_bwd / rms_bwd   backward: dx plus dgamma / dbeta (and optionally dbias)
+                     from one read of dy, x
 """
 import ctypes
 import os
@@ -58,8 +59,9 @@ def library():
         fwd = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp]
         lib.ln_fwd.argtypes = fwd
         lib.rms_fwd.argtypes = fwd
-        lib.ln_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, i32, vp, sz, vp]
-        lib.rms_bwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, i32, vp, sz, vp]
+        lib.ln_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz, vp]
+        lib.rms_bwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
+                                vp]
         lib.norm_bwd_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
         lib.norm_status_string.argtypes = [i32]
         lib.norm_status_string.restype = ctypes.c_char_p
@@ -168,8 +170,8 @@ def bwd_workspace_size(M, N, dtype):
     return n.value
 
 
-def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbeta, workspace,
-         stream, out):
+def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbeta, want_dbias,
+         workspace, stream, out):
     lib = library()
     N = x.shape[-1]
     M = x.numel() // N if N else 0
@@ -185,6 +187,9 @@ def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbet
     dbeta = out.get("dbeta")
     if dbeta is None and want_dbeta:
         dbeta = torch.empty(N, dtype=pdt, device=x.device)
+    dbias = out.get("dbias")
+    if dbias is None and want_dbias:
+        dbias = torch.empty(N, dtype=pdt, device=x.device)
     need = bwd_workspace_size(M, N, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
@@ -195,23 +200,26 @@ def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbet
     else:
         args += [_ptr(rstd, "rstd", torch.float32, M), float(eps)]
     args += [M, N, _dtype_code(x), _ptr(dx, "dx", dt, M * N),
-             _ptr(dgamma, "dgamma", pdt, N), _ptr(dbeta, "dbeta", pdt, N), pcode,
+             _ptr(dgamma, "dgamma", pdt, N), _ptr(dbeta, "dbeta", pdt, N),
+             _ptr(dbias, "dbias", pdt, N), pcode,
              _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
              _stream(stream)]
     _check(fn, getattr(lib, fn)(*args))
-    return {"dx": dx, "dgamma": dgamma, "dbeta": dbeta}
+    return {"dx": dx, "dgamma": dgamma, "dbeta": dbeta, "dbias": dbias}
 
 
 def ln_bwd(dy, x, gamma, mean, rstd, *, dparam_dtype=None, want_dgamma=True, want_dbeta=True,
-           workspace=None, stream=None, out=None):
+           want_dbias=False, workspace=None, stream=None, out=None):
     """LayerNorm backward (dx, dgamma, dbeta) from one read of dy and x.
-    ``dparam_dtype`` (default: x's dtype) is the type of dgamma / dbeta."""
+    ``dparam_dtype`` (default: x's dtype) is the type of dgamma / dbeta.
+    ``want_dbias`` also returns the gradient of the forward's bias (the
+    column sums of dx), for a forward that fused (x + bias) + residual."""
     return _bwd("ln_bwd", dy, x, gamma, mean, rstd, 0.0, dparam_dtype, want_dgamma, want_dbeta,
-                workspace, stream, out)
+                want_dbias, workspace, stream, out)
 
 
 def rms_bwd(dy, x, gamma, rstd=None, eps=1e-6, *, dparam_dtype=None, want_dgamma=True,
-            want_dbeta=False, workspace=None, stream=None, out=None):
+            want_dbeta=False, want_dbias=False, workspace=None, stream=None, out=None):
     """RMSNorm backward; ``rstd=None`` recomputes it from ``x`` and ``eps``."""
     return _bwd("rms_bwd", dy, x, gamma, None, rstd, eps, dparam_dtype, want_dgamma, want_dbeta,
-                workspace, stream, out)
+                want_dbias, workspace, stream, out)

@@ -261,15 +261,15 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
 
 // ----------------------------------------------------------------- backward
 // Stage-1 walk of the backward for the shape used on these pointers, and
-// the workspace it needs: the stage-1 partials (two blocks of `grid` rows of
-// N floats), then for many partial rows the second summation level (two
-// blocks of colsum_slices(grid) rows).
+// the workspace it needs: the stage-1 partials (nb blocks of `grid` rows of
+// N floats: dgamma, dbeta, and dbias when asked for), then for many partial
+// rows the second summation level (nb blocks of colsum_slices(grid) rows).
 struct BwdLayout {
     size_t level2_off = 0, bytes = 0; // in bytes
     bool two_level = false;
 };
 
-norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, const Knobs &kn,
+norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, int nb, const Knobs &kn,
                        const BwdEntry **entry, Walk *w, BwdLayout *lay)
 {
     const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
@@ -283,15 +283,17 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, const Knob
     *entry = e;
     const int slices = colsum_slices(w->grid);
     lay->two_level = slices > 1;
-    lay->level2_off = 2 * size_t(w->grid) * size_t(N) * sizeof(float);
-    lay->bytes = lay->level2_off + (lay->two_level ? 2 * size_t(slices) * size_t(N) * sizeof(float) : 0);
+    lay->level2_off = size_t(nb) * size_t(w->grid) * size_t(N) * sizeof(float);
+    lay->bytes =
+        lay->level2_off + (lay->two_level ? size_t(nb) * size_t(slices) * size_t(N) * sizeof(float) : 0);
     return NORM_OK;
 }
 
 norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *gamma,
                          const float *mean, const float *rstd, float eps, int64_t M, int64_t N,
-                         int32_t dtype, void *dx, void *dgamma, void *dbeta, int32_t dparam_dtype,
-                         void *workspace, size_t workspace_bytes, void *stream)
+                         int32_t dtype, void *dx, void *dgamma, void *dbeta, void *dbias,
+                         int32_t dparam_dtype, void *workspace, size_t workspace_bytes,
+                         void *stream)
 {
     if (!dtype_ok(dtype) || !dtype_ok(dparam_dtype))
         return NORM_ERR_DTYPE;
@@ -309,7 +311,7 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         if (p && !aligned(p, 4))
             return NORM_ERR_ALIGN;
     const size_t ps = elem_size(dparam_dtype);
-    for (const void *p : {(const void *)dgamma, (const void *)dbeta})
+    for (const void *p : {(const void *)dgamma, (const void *)dbeta, (const void *)dbias})
         if (p && !aligned(p, ps))
             return NORM_ERR_ALIGN;
 
@@ -320,7 +322,8 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
     const BwdEntry *e = nullptr;
     Walk w;
     BwdLayout lay;
-    if (norm_status_t st = bwd_plan(M, N, dtype, vec, kn, &e, &w, &lay))
+    const int nb = dbias ? 3 : 2;
+    if (norm_status_t st = bwd_plan(M, N, dtype, vec, nb, kn, &e, &w, &lay))
         return st;
     const size_t need = lay.bytes;
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -343,13 +346,15 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         a.K = w.K;
         a.A = w.A;
         a.eps = eps;
-        if (norm_status_t st = launched((rms ? e->rms : e->ln)(a, int(w.grid), s)))
+        const BwdLaunch run = dbias ? (rms ? e->rms_db : e->ln_db) : (rms ? e->rms : e->ln);
+        if (norm_status_t st = launched(run(a, int(w.grid), s)))
             return st;
     }
     float *level2 =
         lay.two_level ? reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.level2_off)
                       : nullptr;
-    return launched(launch_colsum(ws, int(w.grid), int(N), dgamma, dbeta, dparam_dtype, level2, s));
+    return launched(launch_colsum(ws, int(w.grid), nb, int(N), dgamma, dbeta, dbias, dparam_dtype,
+                                  level2, s));
 }
 
 } // namespace
@@ -383,7 +388,7 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
     if (norm_status_t st = check_device())
         return st;
     // Largest need over the kernels a call of this shape may take (the
-    // 16-byte path or the element-wise one).
+    // 16-byte path or the element-wise one, with dbias).
     const Knobs kn = knobs();
     size_t best = 0;
     const int vec = int(16 / elem_size(dtype));
@@ -393,7 +398,7 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
         const BwdEntry *e = nullptr;
         Walk w;
         BwdLayout lay;
-        if (norm_status_t st = bwd_plan(M, N, dtype, v == 1, kn, &e, &w, &lay))
+        if (norm_status_t st = bwd_plan(M, N, dtype, v == 1, 3, kn, &e, &w, &lay))
             return st;
         if (lay.bytes > best)
             best = lay.bytes;
@@ -404,20 +409,20 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
 
 norm_status_t ln_bwd(const void *dy, const void *x, const void *gamma, const float *mean,
                      const float *rstd, int64_t M, int64_t N, int32_t dtype, void *dx,
-                     void *dgamma, void *dbeta, int32_t dparam_dtype, void *workspace,
-                     size_t workspace_bytes, void *stream)
+                     void *dgamma, void *dbeta, void *dbias, int32_t dparam_dtype,
+                     void *workspace, size_t workspace_bytes, void *stream)
 {
     return bwd_common(false, dy, x, gamma, mean, rstd, 0.f, M, N, dtype, dx, dgamma, dbeta,
-                      dparam_dtype, workspace, workspace_bytes, stream);
+                      dbias, dparam_dtype, workspace, workspace_bytes, stream);
 }
 
 norm_status_t rms_bwd(const void *dy, const void *x, const void *gamma, const float *rstd,
                       float eps, int64_t M, int64_t N, int32_t dtype, void *dx, void *dgamma,
-                      void *dbeta, int32_t dparam_dtype, void *workspace,
+                      void *dbeta, void *dbias, int32_t dparam_dtype, void *workspace,
                       size_t workspace_bytes, void *stream)
 {
     return bwd_common(true, dy, x, gamma, nullptr, rstd, eps, M, N, dtype, dx, dgamma, dbeta,
-                      dparam_dtype, workspace, workspace_bytes, stream);
+                      dbias, dparam_dtype, workspace, workspace_bytes, stream);
 }
 
 const char *norm_status_string(norm_status_t st)

@@ -16,10 +16,10 @@ hipError_t launch_zero_u32(unsigned *p, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_colsum(const float *ws, int parts, int N, void *dgamma, void *dbeta,
-                         int out_dtype, float *level2, hipStream_t s)
+hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma, void *dbeta,
+                         void *dbias, int out_dtype, float *level2, hipStream_t s)
 {
-    if (dgamma == nullptr && dbeta == nullptr)
+    if (dgamma == nullptr && dbeta == nullptr && dbias == nullptr)
         return hipSuccess;
     const unsigned tiles = unsigned((N + COLSUM_COLS - 1) / COLSUM_COLS);
     const dim3 block(COLSUM_COLS * COLSUM_SUB);
@@ -27,19 +27,19 @@ hipError_t launch_colsum(const float *ws, int parts, int N, void *dgamma, void *
     int rows = parts;
     const int slices = colsum_slices(parts);
     if (slices > 1) {
-        hipLaunchKernelGGL((colsum_kernel<false, false>), dim3(tiles, slices, 2), block, 0, s, ws,
-                           parts, N, COLSUM_SPAN, level2, nullptr, nullptr);
+        hipLaunchKernelGGL((colsum_kernel<false, false>), dim3(tiles, slices, nb), block, 0, s,
+                           ws, parts, N, COLSUM_SPAN, level2, nullptr, nullptr, nullptr);
         if (hipError_t e = hipGetLastError())
             return e;
         src = level2;
         rows = slices;
     }
     if (out_dtype == 1)
-        hipLaunchKernelGGL((colsum_kernel<true, true>), dim3(tiles, 1, 2), block, 0, s, src, rows,
-                           N, rows, nullptr, dgamma, dbeta);
+        hipLaunchKernelGGL((colsum_kernel<true, true>), dim3(tiles, 1, nb), block, 0, s, src,
+                           rows, N, rows, nullptr, dgamma, dbeta, dbias);
     else
-        hipLaunchKernelGGL((colsum_kernel<true, false>), dim3(tiles, 1, 2), block, 0, s, src,
-                           rows, N, rows, nullptr, dgamma, dbeta);
+        hipLaunchKernelGGL((colsum_kernel<true, false>), dim3(tiles, 1, nb), block, 0, s, src,
+                           rows, N, rows, nullptr, dgamma, dbeta, dbias);
     return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ struct FwdEntry {
 };
 struct BwdEntry {
     RowShape shape;
-    BwdLaunch ln, rms;
+    BwdLaunch ln, rms;       // dgamma, dbeta partials
+    BwdLaunch ln_db, rms_db; // also the dbias partials
 };
 
 // Tables of instantiated shapes, ordered by capacity; vectorised = 16-byte
@@ -72,17 +73,18 @@ constexpr int WIDE_LPR = 128;
 
 // Small kernels.
 hipError_t launch_zero_u32(unsigned *p, hipStream_t s);
-// Column sums of the stage-1 partials (two blocks of `parts` rows of N
-// floats at ws); writes dgamma / dbeta (each optional) in fp32 (out_dtype 0)
-// or bf16 (1).  parts = 0 writes zeros.  More than COLSUM_SPAN parts are
-// summed in two launches: colsum_slices(parts) slice sums go to `level2`
-// (two blocks of that many rows of N floats), then a final launch adds them.
+// Column sums of the stage-1 partials (nb blocks -- dgamma, dbeta and, when
+// nb = 3, dbias -- of `parts` rows of N floats at ws); writes the outputs
+// given (each optional) in fp32 (out_dtype 0) or bf16 (1).  parts = 0
+// writes zeros.  More than COLSUM_SPAN parts are summed in two launches:
+// colsum_slices(parts) slice sums go to `level2` (nb blocks of that many
+// rows of N floats), then a final launch adds them.
 constexpr int COLSUM_SPAN = 512;
 inline int colsum_slices(int64_t parts)
 {
     return parts <= COLSUM_SPAN ? 1 : int((parts + COLSUM_SPAN - 1) / COLSUM_SPAN);
 }
-hipError_t launch_colsum(const float *ws, int parts, int N, void *dgamma, void *dbeta,
-                         int out_dtype, float *level2, hipStream_t s);
+hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma, void *dbeta,
+                         void *dbias, int out_dtype, float *level2, hipStream_t s);
 
 } // namespace nf

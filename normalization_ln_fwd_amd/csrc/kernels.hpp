@@ -499,7 +499,7 @@ constexpr bool bwd_pipelined()
 // the workgroup's rows, folded over the workgroup in a fixed order and
 // written as this workgroup's partial row of the workspace.
 // ---------------------------------------------------------------------------
-template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS>
+template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS, bool DB>
 __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 {
     using IO = VecIO<T, VEC>;
@@ -516,7 +516,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     static_assert(WG % 64 == 0, "workgroup of whole waves");
 
     __shared__ float red_lds[TeamLds<LPR, TEAMS, 2>::size];
-    __shared__ float col_lds[SLOTS > 1 ? 2 * CAP : 1];
+    constexpr int NB = DB ? 3 : 2; // column sums: dgamma, dbeta (, dbias)
+    __shared__ float col_lds[SLOTS > 1 ? NB * CAP : 1];
     __shared__ __attribute__((aligned(16))) float par[PLDS ? CAP : 4];
 
     const int tid = threadIdx.x;
@@ -587,11 +588,13 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
             issue(walk.group(0), A);
     }
 
-    float acc_g[E], acc_b[E];
+    float acc_g[E], acc_b[E], acc_d[DB ? E : 1];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         acc_g[e] = 0.f;
         acc_b[e] = 0.f;
+        if constexpr (DB)
+            acc_d[e] = 0.f;
     }
     int parity = 0;
 
@@ -668,6 +671,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
                 if (rv) { // rows past M read zeros; columns past N too
                     acc_g[i] = fmaf(dv[e], xh, acc_g[i]);
                     acc_b[i] += dv[e];
+                    if constexpr (DB)
+                        acc_d[i] += dxv[e]; // dbias: column sums of dx
                 }
             }
             if (hold)
@@ -734,14 +739,18 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     }
 
     // ---- fold the column partials of this workgroup, in a fixed order ----
+    // Block b of the workspace (dgamma, dbeta, dbias) holds row blockIdx.x.
     float *pg = a.ws + (int64_t)blockIdx.x * N;
     float *pb = a.ws + (int64_t)gridDim.x * N + (int64_t)blockIdx.x * N;
+    float *pd = a.ws + 2 * (int64_t)gridDim.x * N + (int64_t)blockIdx.x * N;
     if constexpr (LPR < 64) {
         // teams of one wave cover the same columns: fold them first
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             acc_g[e] = fold_teams_sum<LPR>(acc_g[e]);
             acc_b[e] = fold_teams_sum<LPR>(acc_b[e]);
+            if constexpr (DB)
+                acc_d[e] = fold_teams_sum<LPR>(acc_d[e]);
         }
     }
     if constexpr (SLOTS == 1) {
@@ -754,6 +763,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
                     if (VEC > 1 || c0 + e < N) {
                         pg[c0 + e] = acc_g[k * VEC + e];
                         pb[c0 + e] = acc_b[k * VEC + e];
+                        if constexpr (DB)
+                            pd[c0 + e] = acc_d[k * VEC + e];
                     }
                 }
             }
@@ -772,6 +783,9 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
                             const int c = c0 + e;
                             col_lds[c] = (sl == 0 ? 0.f : col_lds[c]) + acc_g[k * VEC + e];
                             col_lds[CAP + c] = (sl == 0 ? 0.f : col_lds[CAP + c]) + acc_b[k * VEC + e];
+                            if constexpr (DB)
+                                col_lds[2 * CAP + c] =
+                                    (sl == 0 ? 0.f : col_lds[2 * CAP + c]) + acc_d[k * VEC + e];
                         }
                     }
                 }
@@ -781,19 +795,22 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
         for (int c = tid; c < N; c += WG) {
             pg[c] = col_lds[c];
             pb[c] = col_lds[CAP + c];
+            if constexpr (DB)
+                pd[c] = col_lds[2 * CAP + c];
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Backward stage 2: column sums of the partial rows.  src holds two blocks
-// (dgamma, dbeta) of `rows` rows of N floats.  Workgroup (column tile, slice
-// s, block) adds rows [s*span, min(rows, (s+1)*span)) of its 64 columns:
+// Backward stage 2: column sums of the partial rows.  src holds gridDim.z
+// blocks (dgamma, dbeta, dbias) of `rows` rows of N floats.  Workgroup
+// (column tile, slice s, block) adds rows [s*span, min(rows, (s+1)*span)) of
+// its 64 columns:
 // thread (c, t) takes rows t, t + 16, ... of the slice in ascending order,
 // and the sixteen threads of a column are added in order t = 0..15.  FINAL: one
-// slice; down-cast and store to dgamma / dbeta.  Otherwise slice s stores its
-// sums as row s of dst (two blocks of gridDim.y rows), which a FINAL launch
-// then adds the same way.  Every addition happens in a fixed order.
+// slice; down-cast and store to dgamma / dbeta / dbias.  Otherwise slice s
+// stores its sums as row s of dst (blocks of gridDim.y rows), which a FINAL
+// launch then adds the same way.  Every addition happens in a fixed order.
 // (A one-launch variant that lets the last workgroup finish needs a
 // device-scope release per workgroup, i.e. an L2 write-back each, which
 // costs more than the second launch.)
@@ -804,12 +821,13 @@ constexpr int COLSUM_SUB = 16;
 template <bool FINAL, bool BF16_OUT>
 __global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SUB)
     colsum_kernel(const float *src, int rows, int N, int span, float *dst, void *dgamma,
-                  void *dbeta)
+                  void *dbeta, void *dbias)
 {
     const int tx = threadIdx.x % COLSUM_COLS;
     const int ty = threadIdx.x / COLSUM_COLS;
     const int which = blockIdx.z;
-    if (FINAL && (which == 0 ? dgamma : dbeta) == nullptr)
+    void *out = which == 0 ? dgamma : (which == 1 ? dbeta : dbias);
+    if (FINAL && out == nullptr)
         return; // uniform over the block
     const int j = blockIdx.x * COLSUM_COLS + tx;
     const int s = blockIdx.y;
@@ -833,10 +851,9 @@ __global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SUB)
         if constexpr (!FINAL) {
             dst[((int64_t)which * gridDim.y + s) * N + j] = t;
         } else if constexpr (BF16_OUT) {
-            static_cast<uint16_t *>(which == 0 ? dgamma : dbeta)[j] =
-                uint16_t(pack_bf16x2(t, 0.f) & 0xffffu);
+            static_cast<uint16_t *>(out)[j] = uint16_t(pack_bf16x2(t, 0.f) & 0xffffu);
         } else {
-            static_cast<float *>(which == 0 ? dgamma : dbeta)[j] = t;
+            static_cast<float *>(out)[j] = t;
         }
     }
 }
@@ -849,11 +866,11 @@ hipError_t launch_fwd(const FwdArgs &a, int grid, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS>
+template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS, bool DB>
 hipError_t launch_bwd(const BwdArgs &a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((bwd_kernel<T, VEC, LPR, VPL, TEAMS, RMS>), dim3(grid), dim3(LPR * TEAMS),
-                       0, s, a);
+    hipLaunchKernelGGL((bwd_kernel<T, VEC, LPR, VPL, TEAMS, RMS, DB>), dim3(grid),
+                       dim3(LPR * TEAMS), 0, s, a);
     return hipGetLastError();
 }
 

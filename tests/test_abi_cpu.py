@@ -105,10 +105,11 @@ def test_rms_forward_takes_no_mean(lib):
 
 def bwd_args(fn, **over):
     a = dict(dy=P, x=P, gamma=P, mean=P, rstd=P, eps=1e-6, M=4, N=64, dtype=1, dx=P,
-             dgamma=P, dbeta=P, pdtype=0, ws=P, ws_bytes=1 << 20, stream=None)
+             dgamma=P, dbeta=P, dbias=None, pdtype=0, ws=P, ws_bytes=1 << 20, stream=None)
     a.update(over)
     keys = ["dy", "x", "gamma"] + (["mean", "rstd"] if fn == "ln_bwd" else ["rstd", "eps"]) + [
-        "M", "N", "dtype", "dx", "dgamma", "dbeta", "pdtype", "ws", "ws_bytes", "stream"]
+        "M", "N", "dtype", "dx", "dgamma", "dbeta", "dbias", "pdtype", "ws", "ws_bytes",
+        "stream"]
     return [a[k] for k in keys]
 
 
@@ -119,6 +120,7 @@ def bwd_args(fn, **over):
     (dict(M=-2), 2), (dict(N=0), 2), (dict(N=16385), 2),
     (dict(dy=BAD1), 5), (dict(dx=BAD1), 5), (dict(rstd=BAD2), 5), (dict(ws=BAD2), 5),
     (dict(pdtype=0, dgamma=BAD2), 5), (dict(pdtype=1, dbeta=BAD1), 5),
+    (dict(pdtype=0, dbias=BAD2), 5), (dict(pdtype=1, dbias=BAD1), 5),
 ])
 def test_backward_rejects(lib, fn, over, code):
     assert getattr(lib, fn)(*bwd_args(fn, **over)) == code

@@ -14,7 +14,7 @@ import normalization_ln_fwd_amd as nf
 import oracle
 import synth
 from gpu_util import BF16, F32, f64, from_dev, require_gpu, to_dev
-from tolerance import assert_colsums_close, assert_rows_close, dx_term_scale
+from tolerance import assert_colsums_close, assert_rows_close, dbias_term_l2, dx_term_scale
 
 pytestmark = pytest.mark.gpu
 
@@ -42,25 +42,28 @@ def make_case(M, N, dtype, rms, seed, outlier_p=0.0, eps=None):
 
 
 def run_bwd(rms, inp, dtype, eps, misalign=False, recompute=False, dparam_dtype=None,
-            want_dbeta=True):
+            want_dbeta=True, want_dbias=False):
     dy = to_dev(inp["dy"], dtype, misalign)
     x = to_dev(inp["x"], dtype)
     g = to_dev(inp["gamma"], dtype)
     rstd = None if recompute else torch.from_numpy(inp["rstd"]).cuda()
     if rms:
-        out = nf.rms_bwd(dy, x, g, rstd, eps, dparam_dtype=dparam_dtype, want_dbeta=want_dbeta)
+        out = nf.rms_bwd(dy, x, g, rstd, eps, dparam_dtype=dparam_dtype, want_dbeta=want_dbeta,
+                         want_dbias=want_dbias)
     else:
         mean = torch.from_numpy(inp["mean"]).cuda()
-        out = nf.ln_bwd(dy, x, g, mean, rstd, dparam_dtype=dparam_dtype, want_dbeta=want_dbeta)
+        out = nf.ln_bwd(dy, x, g, mean, rstd, dparam_dtype=dparam_dtype, want_dbeta=want_dbeta,
+                        want_dbias=want_dbias)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_bwd(rms, inp, dtype, eps, recompute=False, rows=None):
+def oracle_bwd(rms, inp, dtype, eps, recompute=False, rows=None, want_dbias=False):
     sl = slice(None) if rows is None else rows
     return oracle.norm_bwd(inp["dy"][sl], inp["x"][sl], inp["gamma"],
                            None if rms else inp["mean"][sl],
-                           None if recompute else inp["rstd"][sl], eps, rms=rms, dtype=dtype)
+                           None if recompute else inp["rstd"][sl], eps, rms=rms, dtype=dtype,
+                           want_dbias=want_dbias)
 
 
 @pytest.mark.parametrize("M,N", SHAPES)
@@ -77,6 +80,36 @@ def test_bwd_matches_oracle(M, N, rms, dtype, misalign):
                          "dgamma")
     assert_colsums_close(f64(out["dbeta"]), ref["dbeta"], ref["dbeta_l2"], COLSUM_REL_SMALL,
                          "dbeta")
+
+
+@pytest.mark.parametrize("M,N", SHAPES)
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("misalign", [False, True], ids=["vec", "elem"])
+def test_bwd_dbias_matches_oracle(M, N, rms, dtype, misalign):
+    """The gradient of the forward's bias (column sums of dx) from the same
+    pass; dx, dgamma and dbeta are bit-identical to a call without it."""
+    inp, eps = make_case(M, N, dtype, rms, seed=M * 37 + N)
+    out = run_bwd(rms, inp, dtype, eps, misalign, dparam_dtype=torch.float32, want_dbias=True)
+    ref = oracle_bwd(rms, inp, dtype, eps, want_dbias=True)
+    l2 = np.maximum(ref["dbias_l2"], dbias_term_l2(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+    assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
+    plain = run_bwd(rms, inp, dtype, eps, misalign, dparam_dtype=torch.float32)
+    for k in ("dx", "dgamma", "dbeta"):
+        assert torch.equal(out[k], plain[k]), k
+
+
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+def test_bwd_dbias_bf16_is_rounded_sum(rms):
+    M, N = 3000, 384
+    inp, eps = make_case(M, N, BF16, rms, seed=77)
+    o32 = run_bwd(rms, inp, BF16, eps, dparam_dtype=torch.float32, want_dbias=True)
+    o16 = run_bwd(rms, inp, BF16, eps, dparam_dtype=torch.bfloat16, want_dbias=True)
+    assert torch.equal(o16["dbias"], o32["dbias"].to(torch.bfloat16))
+    ref = oracle_bwd(rms, inp, BF16, eps, want_dbias=True)
+    l2 = np.maximum(ref["dbias_l2"], dbias_term_l2(inp["dy"], inp["gamma"], ref["rstd"], BF16))
+    assert_colsums_close(f64(o16["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL,
+                         "dbias (bf16)", dtype=BF16)
 
 
 @pytest.mark.parametrize("N", [7, 384, 4096])
@@ -133,10 +166,12 @@ def test_bwd_empty_rows_zero_params():
     st = torch.empty((0,), dtype=torch.float32, device="cuda")
     dg = torch.full((384,), 7.0, device="cuda")
     db = torch.full((384,), 7.0, device="cuda")
+    dbias = torch.full((384,), 7.0, device="cuda")
     out = nf.ln_bwd(x, x, None, st, st, dparam_dtype=torch.float32,
-                    out={"dgamma": dg, "dbeta": db})
+                    out={"dgamma": dg, "dbeta": db, "dbias": dbias})
     torch.cuda.synchronize()
     assert torch.count_nonzero(out["dgamma"]) == 0 and torch.count_nonzero(out["dbeta"]) == 0
+    assert torch.count_nonzero(out["dbias"]) == 0
 
 
 def test_bwd_rejects_small_workspace():

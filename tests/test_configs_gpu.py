@@ -70,15 +70,17 @@ def _big_bwd(rms):
     outs = {}
     for pdt in (torch.float32, torch.bfloat16):
         if rms:
-            outs[pdt] = nf.rms_bwd(dy, x, g, None, eps, dparam_dtype=pdt)
+            outs[pdt] = nf.rms_bwd(dy, x, g, None, eps, dparam_dtype=pdt, want_dbias=True)
         else:
             outs[pdt] = nf.ln_bwd(dy, x, g, torch.from_numpy(mean).cuda(),
-                                  torch.from_numpy(rstd).cuda(), dparam_dtype=pdt)
+                                  torch.from_numpy(rstd).cuda(), dparam_dtype=pdt,
+                                  want_dbias=True)
     torch.cuda.synchronize()
-    # column sums over every row
+    # column sums over every row (dbias: the backward of a fused bias add,
+    # asked for alongside)
     ref = oracle.norm_bwd(inp["dy"], inp["x"], inp["gamma"], mean, rstd if not rms else None,
-                          eps, rms=rms, dtype=BF16, want_dx=False)
-    keys = ("dgamma",) if rms else ("dgamma", "dbeta")
+                          eps, rms=rms, dtype=BF16, want_dx=False, want_dbias=True)
+    keys = ("dgamma", "dbias") if rms else ("dgamma", "dbeta", "dbias")
     for k in keys:
         e32 = assert_colsums_close(f64(outs[torch.float32][k]), ref[k], ref[k + "_l2"],
                                    COLSUM_REL_BIG, k)

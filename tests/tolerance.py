@@ -12,9 +12,11 @@
   * bf16 outputs (y, dx, residual_out): |got - ref| <= max(ulp_bf16(ref),
     1e-5 * s_i), ulp_bf16(v) = 2^(floor(log2 |v|) - 7) -- one bf16 ulp, with
     an absolute floor where cancellation makes an element tiny next to its row;
-  * column sums (dgamma, dbeta): |got - ref| <= rel * max(|ref|, ||terms||_2),
-    ||terms||_2 being the 2-norm of the summed terms (the scale a zero-mean sum
-    is judged against); bf16 outputs additionally may be one bf16 ulp off.
+  * column sums (dgamma, dbeta, dbias): |got - ref| <= rel * max(|ref|,
+    ||terms||_2), ||terms||_2 being the 2-norm of the summed terms (the scale a
+    zero-mean sum is judged against); for dbias, whose terms are dx, at least
+    the 2-norm of dx's own terms rstd * |dy * gamma| (dbias_term_l2); bf16
+    outputs additionally may be one bf16 ulp off.
 The reference ``ref`` is the oracle's exact (double) value.
 """
 import numpy as np
@@ -54,6 +56,17 @@ def dx_term_scale(dy, gamma, rstd, dtype):
     dy = to_f64(dy, dtype)
     g = dy if gamma is None else dy * to_f64(gamma, dtype)[None, :]
     return np.asarray(rstd, np.float64).reshape(-1) * np.max(np.abs(g), axis=1)
+
+
+def dbias_term_l2(dy, gamma, rstd, dtype):
+    """Per-column 2-norm over the rows of rstd_i * |dy_ij * gamma_j|, the
+    scale of the terms each dx_ij is formed from.  dbias_j sums dx_ij; where
+    dx cancels to almost nothing (e.g. N = 1) its rounding error is relative
+    to these terms, not to dx."""
+    dy = to_f64(dy, dtype)
+    g = dy if gamma is None else dy * to_f64(gamma, dtype)[None, :]
+    r = np.asarray(rstd, np.float64).reshape(-1, 1)
+    return np.sqrt(np.sum((r * g) ** 2, axis=0))
 
 
 def to_f64(a, dtype):
