@@ -21,6 +21,10 @@ Parity status of each function (what pins it, in ``tests/test_oracle.py``):
                            form sum_j dbias_j = 0.
   round_to_dtype        -- pinned: exhaustive checks against exactly
                            representable neighbours and ties.
+  quantize_e4m3         -- pinned: torch's float8_e4m3fn cast on every code,
+                           every midpoint and its neighbours and random
+                           in-range values; the format's fixed codes
+                           (1.0, 448, 2^-6, 2^-9); saturation and NaN.
 
 This module is a thin ctypes shim over ``liboracle.so`` (built from
 ``oracle.c`` by ``oracle/build.py``); arrays are numpy.  bf16 tensors are
@@ -59,6 +63,8 @@ def _load():
         lib.oracle_norm_bwd.restype = ci
         lib.oracle_round_to_dtype.argtypes = [vp, i64, ci, vp]
         lib.oracle_round_to_dtype.restype = ci
+        lib.oracle_quantize_e4m3.argtypes = [vp, i64, ctypes.c_float, vp]
+        lib.oracle_quantize_e4m3.restype = ci
         _lib = lib
     return _lib
 
@@ -159,6 +165,18 @@ def round_to_dtype(v, dtype=BF16):
     out = np.empty(v.shape, _io_dtype(dtype))
     if lib.oracle_round_to_dtype(_ptr(v), v.size, dtype, _ptr(out)) != 0:
         raise ValueError("oracle_round_to_dtype rejected its arguments")
+    return out
+
+
+def quantize_e4m3(v, scale):
+    """OCP FP8 E4M3 codes (uint8) of the fp32 products ``v * scale``: round to
+    nearest, ties to even, magnitudes beyond 448 saturate.  ``v`` is taken as
+    float32 values (bf16 patterns must be widened by the caller)."""
+    lib = _load()
+    v = np.ascontiguousarray(v, np.float32)
+    out = np.empty(v.shape, np.uint8)
+    if lib.oracle_quantize_e4m3(_ptr(v), v.size, float(np.float32(scale)), _ptr(out)) != 0:
+        raise ValueError("oracle_quantize_e4m3 rejected its arguments")
     return out
 
 

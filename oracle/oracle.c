@@ -444,3 +444,53 @@ int oracle_round_to_dtype(const double *v, int64_t n, int dtype, void *out)
         store_io(out, dtype, i, round_io(v[i], dtype));
     return 0;
 }
+
+/* ---------------------------------------------------------- FP8 output */
+
+/*
+ * OCP FP8 E4M3 (the "e4m3fn" variant): 1 sign, 4 exponent (bias 7) and 3
+ * mantissa bits; normal magnitudes 2^-6 .. 448 (= 1.75 * 2^8), subnormals
+ * k * 2^-9, no infinity, S.1111.111 is NaN.  Rounds to nearest, ties to
+ * even; magnitudes beyond 448 saturate to 448, since the format has no
+ * infinity to round to.  This is the FP8 output that the nvFuser issue's
+ * layernorm + amax comment computes the scaling amax for.
+ */
+static uint8_t encode_e4m3(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    const uint8_t s = signbit(v) ? 0x80 : 0x00;
+    const double a = fabs(v);
+    if (a == 0.0)
+        return s;
+    int e;
+    (void)frexp(a, &e); /* a in [2^(e-1), 2^e): spacing 2^(e-1-3) */
+    int q = e - 4;
+    if (q < -9)
+        q = -9; /* subnormal spacing */
+    double r = ldexp(nearbyint(ldexp(a, -q)), q); /* nearbyint: ties to even */
+    if (r > 448.0)
+        r = 448.0;
+    if (r == 0.0)
+        return s;
+    if (r < 0x1p-6) /* subnormal: exponent field 0, mantissa r / 2^-9 */
+        return (uint8_t)(s | (uint8_t)(r / 0x1p-9));
+    int er;
+    const double m = frexp(r, &er); /* r = (2m) 2^(er-1), 2m in [1, 2) */
+    const int exp_field = er - 1 + 7;
+    const int mant = (int)((2.0 * m - 1.0) * 8.0);
+    return (uint8_t)(s | (exp_field << 3) | mant);
+}
+
+/* out[i] = E4M3 code of the fp32 product v[i] * scale (the product rounded
+ * to fp32 first, as a kernel computing in fp32 forms it). */
+int oracle_quantize_e4m3(const float *v, int64_t n, float scale, uint8_t *out)
+{
+    if (n < 0 || (n > 0 && (!v || !out)))
+        return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        const float p = v[i] * scale;
+        out[i] = encode_e4m3((double)p);
+    }
+    return 0;
+}

@@ -488,3 +488,60 @@ def test_bad_arguments_are_rejected(oracle_mod):
         oracle_mod.norm_fwd(np.zeros((2, 3), np.uint16), eps=-1.0)
     with pytest.raises(ValueError):
         oracle_mod.norm_bwd(np.zeros((2, 3), np.uint16), np.zeros((2, 3), np.uint16))  # no stats
+
+
+# ------------------------------------------------------------ FP8 output
+
+def _e4m3_values():
+    """Every finite OCP E4M3 value, by code (sign, 4-bit exponent bias 7,
+    3-bit mantissa; exponent field 0 is subnormal k * 2^-9)."""
+    vals = {}
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            continue
+        v = m * 2.0**-9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        vals[c] = -v if s else v
+    return vals
+
+
+def test_e4m3_matches_torch_cast(oracle_mod):
+    vals = _e4m3_values()
+    pos = sorted(v for c, v in vals.items() if c < 128)
+    probe = [v for v in vals.values()]
+    for lo, hi in zip(pos, pos[1:]):
+        mid = np.float32((lo + hi) / 2)
+        probe += [mid, np.nextafter(mid, np.float32(1e30)), np.nextafter(mid, np.float32(-1e30))]
+    rng = np.random.default_rng(13)
+    probe += list(rng.uniform(-448, 448, 20000)) + list(rng.uniform(-0.02, 0.02, 20000))
+    v = f32(probe)
+    v = np.concatenate([v, -v])
+    got = oracle_mod.quantize_e4m3(v, 1.0)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_fixed_codes_saturation_and_nan(oracle_mod):
+    cases = {1.0: 0x38, -1.0: 0xB8, 448.0: 0x7E, -448.0: 0xFE, 2.0**-6: 0x08, 2.0**-9: 0x01,
+             0.0: 0x00, 449.0: 0x7E, 464.0: 0x7E, 1e9: 0x7E, -3e38: 0xFE, 2.0**-11: 0x00,
+             1.5 * 2.0**-10: 0x01, 0.1: 0x1D}
+    v = f32(list(cases))
+    got = oracle_mod.quantize_e4m3(v, 1.0)
+    assert [int(g) for g in got] == list(cases.values())
+    assert int(oracle_mod.quantize_e4m3(f32([np.nan]), 1.0)[0]) & 0x7F == 0x7F
+    assert int(oracle_mod.quantize_e4m3(f32([-0.0]), 1.0)[0]) == 0x80
+
+
+def test_e4m3_scale_applies_in_fp32(oracle_mod):
+    """The code is that of the fp32 product v * scale."""
+    # (1.0625 - 2^-23) * (1 + 2^-23) is 1.0625 + 2^-27 - 2^-46 exactly, which
+    # fp32 rounds to 1.0625, the midpoint of codes 0x38 (1.0) and 0x39
+    # (1.125): the tie goes to the even code; the exact product would round up
+    v = f32([1.0625 - 2.0**-23])
+    assert int(oracle_mod.quantize_e4m3(v, np.float32(1 + 2.0**-23))[0]) == 0x38
+    rng = np.random.default_rng(14)
+    v = f32(rng.standard_normal(5000) * 3)
+    for scale in (1.0, 0.37, 57.5, 3.1e-3):
+        p = v * np.float32(scale)
+        ref = torch.from_numpy(np.clip(p, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8)
+        assert np.array_equal(oracle_mod.quantize_e4m3(v, scale), ref.numpy())

@@ -51,6 +51,13 @@ MUTANTS = [
     ("xhat ignores the mean", "(xv - c->mean[i]) * c->rstd[i]", "xv * c->rstd[i]"),
     ("dbias sums dy instead of dx", "double t = c->dx[i * c->N + j];",
      "double t = elem(c->dy, c->dtype, i * c->N + j);"),
+    ("e4m3 keeps 4 mantissa bits", "int q = e - 4;", "int q = e - 5;"),
+    ("e4m3 subnormal spacing 2^-10", "q = -9; /* subnormal spacing */", "q = -10;"),
+    ("e4m3 without saturation", "if (r > 448.0)\n        r = 448.0;", ""),
+    ("e4m3 truncates", "double r = ldexp(nearbyint(ldexp(a, -q)), q);",
+     "double r = ldexp(floor(ldexp(a, -q)), q);"),
+    ("e4m3 product in double", "const float p = v[i] * scale;",
+     "const double p = (double)v[i] * (double)scale;"),
     ("dbias skips the last row", "for (int64_t i = 0; i < c->M; ++i) {\n            double t = c->dx",
      "for (int64_t i = 0; i + 1 < c->M; ++i) {\n            double t = c->dx"),
 ]
