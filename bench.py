@@ -295,6 +295,17 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
     rec("ln_fwd_576000x384", lambda: nf.ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"],
                                                 d["beta"], 1e-5, want_amax=True, out=fwd_out),
         fwd_bytes(M, N), True)
+    # FP8 output (E4M3 codes, one byte per element) with the scale taken from
+    # the amax of a previous call, as a training step would
+    y8 = torch.empty((M, N), dtype=torch.float8_e4m3fn, device=dev)
+    sc = (448.0 / fwd_out["amax"]).to(torch.float32)
+    fp8_out = {"y": y8, "residual_out": fwd_out["residual_out"], "mean": fwd_out["mean"],
+               "rstd": fwd_out["rstd"], "amax": fwd_out["amax"]}
+    rec("ln_fwd_fp8_576000x384", lambda: nf.ln_fwd_fp8(d["x"], sc, d["bias"], d["residual"],
+                                                        d["gamma"], d["beta"], 1e-5,
+                                                        want_amax=True, out=fp8_out),
+        M * (7 * N + 8), False)
+    del y8
     rms_out = {"y": fwd_out["y"], "residual_out": fwd_out["residual_out"],
                "rstd": fwd_out["rstd"], "amax": fwd_out["amax"]}
     rec("rms_fwd_576000x384", lambda: nf.rms_fwd(d["x"], d["bias"], d["residual"], d["gamma"],

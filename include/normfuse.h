@@ -135,6 +135,36 @@ norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, con
                       void *residual_out, float *mean, float *rstd, float *amax, void *stream);
 
 /*
+ * ln_fwd_fp8 / rms_fwd_fp8 -- the same forward with y emitted as OCP FP8
+ * E4M3 codes for a following FP8 matrix product: the output the nvFuser
+ * issue's layernorm + amax comment obtains the scaling amax for.  Arguments
+ * as ln_fwd / rms_fwd, except:
+ *   y_scale      [1]   fp32    device memory, required when M > 0: each
+ *                              output is y * (*y_scale) (a scale that can
+ *                              come from a previous call's amax, e.g.
+ *                              448 / amax, without a host round trip)
+ *   y_fp8        [M,N] uint8   required when M > 0: E4M3 codes (sign, 4-bit
+ *                              exponent with bias 7, 3-bit mantissa) of
+ *                              round_io(y) * (*y_scale), the product rounded
+ *                              to fp32 and then to nearest E4M3, ties to
+ *                              even; magnitudes beyond 448 saturate to 448.
+ *                              Any alignment; 16 / sizeof(dtype)-byte
+ *                              alignment keeps the vectorised kernels.
+ *   amax         as ln_fwd: max |round_io(y)|, before the scale.
+ * residual_out, mean, rstd and amax are bit-identical to those of ln_fwd /
+ * rms_fwd on the same inputs when both calls take the same kernels (their
+ * pointers fall in the same alignment class).
+ */
+norm_status_t ln_fwd_fp8(const void *x, const void *bias, const void *residual,
+                         const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
+                         int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
+                         float *mean, float *rstd, float *amax, void *stream);
+norm_status_t rms_fwd_fp8(const void *x, const void *bias, const void *residual,
+                          const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
+                          int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
+                          float *mean, float *rstd, float *amax, void *stream);
+
+/*
  * norm_bwd_workspace_size -- bytes of device workspace ln_bwd / rms_bwd need
  * for an [M, N] problem of the given dtype on the current device (the
  * per-workgroup dgamma / dbeta / dbias column partials; the size covers a

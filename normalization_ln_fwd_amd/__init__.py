@@ -28,8 +28,8 @@ N_MAX = 16384
 STATUS = {0: "NORM_OK", 1: "NORM_ERR_NULL", 2: "NORM_ERR_SHAPE", 3: "NORM_ERR_ARG",
           4: "NORM_ERR_DTYPE", 5: "NORM_ERR_ALIGN", 6: "NORM_ERR_WORKSPACE", 7: "NORM_ERR_LAUNCH",
           8: "NORM_ERR_DEVICE"}
-EXPORTS = ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "norm_bwd_workspace_size",
-           "norm_status_string")
+EXPORTS = ("ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd",
+           "norm_bwd_workspace_size", "norm_status_string")
 
 
 class NormLibraryMissing(RuntimeError):
@@ -59,6 +59,9 @@ def library():
         fwd = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp]
         lib.ln_fwd.argtypes = fwd
         lib.rms_fwd.argtypes = fwd
+        fwd8 = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+        lib.ln_fwd_fp8.argtypes = fwd8
+        lib.rms_fwd_fp8.argtypes = fwd8
         lib.ln_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz, vp]
         lib.rms_bwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
                                 vp]
@@ -106,15 +109,19 @@ def _stream(stream):
 
 
 def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, want_rstd,
-         want_amax, stream, out):
+         want_amax, stream, out, y_scale=None):
     lib = library()
     N = x.shape[-1]
     M = x.numel() // N if N else 0
     dt = x.dtype
+    fp8 = fn.endswith("_fp8")
     out = dict(out or {})
     y = out.get("y")
     if y is None:
-        y = torch.empty_like(x)
+        y = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device) if fp8 \
+            else torch.empty_like(x)
+    if fp8 and y.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise TypeError(f"y: expected float8_e4m3fn or uint8, got {y.dtype}")
     res_out = out.get("residual_out")
     if res_out is None and want_residual_out:
         res_out = torch.empty_like(x)
@@ -127,10 +134,15 @@ def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, 
     amax = out.get("amax")
     if amax is None and want_amax:
         amax = torch.empty(1, dtype=torch.float32, device=x.device)
+    head = [_ptr(x, "x"), _ptr(bias, "bias", dt, N), _ptr(residual, "residual", dt, M * N),
+            _ptr(gamma, "gamma", dt, N), _ptr(beta, "beta", dt, N), float(eps), M, N,
+            _dtype_code(x)]
+    if fp8:
+        head += [_ptr(y_scale, "y_scale", torch.float32, 1), _ptr(y, "y", y.dtype, M * N)]
+    else:
+        head += [_ptr(y, "y", dt, M * N)]
     st = getattr(lib, fn)(
-        _ptr(x, "x"), _ptr(bias, "bias", dt, N), _ptr(residual, "residual", dt, M * N),
-        _ptr(gamma, "gamma", dt, N), _ptr(beta, "beta", dt, N), float(eps), M, N,
-        _dtype_code(x), _ptr(y, "y", dt, M * N), _ptr(res_out, "residual_out", dt, M * N),
+        *head, _ptr(res_out, "residual_out", dt, M * N),
         _ptr(mean, "mean", torch.float32, M), _ptr(rstd, "rstd", torch.float32, M),
         _ptr(amax, "amax", torch.float32, 1), _stream(stream))
     _check(fn, st)
@@ -159,6 +171,26 @@ def rms_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-6, *,
         want_residual_out = bias is not None or residual is not None
     return _fwd("rms_fwd", x, bias, residual, gamma, beta, eps, want_residual_out, False,
                 want_stats, want_amax, stream, out)
+
+
+def ln_fwd_fp8(x, y_scale, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, *,
+               want_residual_out=None, want_stats=True, want_amax=False, stream=None, out=None):
+    """:func:`ln_fwd` with ``y`` as OCP FP8 E4M3 codes of y * y_scale
+    (``y_scale``: a 1-element fp32 tensor on the GPU); ``y`` is returned as a
+    ``float8_e4m3fn`` tensor (``out`` may supply one, or a ``uint8`` one)."""
+    if want_residual_out is None:
+        want_residual_out = bias is not None or residual is not None
+    return _fwd("ln_fwd_fp8", x, bias, residual, gamma, beta, eps, want_residual_out,
+                want_stats, want_stats, want_amax, stream, out, y_scale)
+
+
+def rms_fwd_fp8(x, y_scale, bias=None, residual=None, gamma=None, beta=None, eps=1e-6, *,
+                want_residual_out=None, want_stats=True, want_amax=False, stream=None, out=None):
+    """:func:`rms_fwd` with ``y`` as OCP FP8 E4M3 codes of y * y_scale."""
+    if want_residual_out is None:
+        want_residual_out = bias is not None or residual is not None
+    return _fwd("rms_fwd_fp8", x, bias, residual, gamma, beta, eps, want_residual_out, False,
+                want_stats, want_amax, stream, out, y_scale)
 
 
 def bwd_workspace_size(M, N, dtype):

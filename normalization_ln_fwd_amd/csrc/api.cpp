@@ -190,31 +190,39 @@ bool vectorisable(int64_t N, int32_t dtype, std::initializer_list<const void *> 
 norm_status_t launched(hipError_t e) { return e == hipSuccess ? NORM_OK : NORM_ERR_LAUNCH; }
 
 // ------------------------------------------------------------------ forward
+// y_scale == nullptr: y in the I/O dtype; else y holds FP8 E4M3 codes of
+// y * (*y_scale) (one byte per element).
 norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *residual,
                          const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
-                         int32_t dtype, void *y, void *residual_out, float *mean, float *rstd,
-                         float *amax, void *stream)
+                         int32_t dtype, const float *y_scale, void *y, void *residual_out,
+                         float *mean, float *rstd, float *amax, bool f8, void *stream)
 {
     if (!dtype_ok(dtype))
         return NORM_ERR_DTYPE;
     if (norm_status_t st = check_shape(M, N))
         return st;
-    if (M > 0 && (!x || !y)) // with no rows there is nothing to read or write
+    // with no rows there is nothing to read or write
+    if (M > 0 && (!x || !y || (f8 && !y_scale)))
         return NORM_ERR_NULL;
     if (!eps_ok(eps) || (rms && mean))
         return NORM_ERR_ARG;
     const size_t es = elem_size(dtype);
-    for (const void *p : {x, bias, residual, gamma, beta, (const void *)y, (const void *)residual_out})
+    for (const void *p : {x, bias, residual, gamma, beta, (const void *)(f8 ? nullptr : y),
+                          (const void *)residual_out})
         if (p && !aligned(p, es))
             return NORM_ERR_ALIGN;
-    for (const void *p : {(const void *)mean, (const void *)rstd, (const void *)amax})
+    for (const void *p :
+         {(const void *)mean, (const void *)rstd, (const void *)amax, (const void *)y_scale})
         if (p && !aligned(p, 4))
             return NORM_ERR_ALIGN;
 
     if (norm_status_t st = check_device())
         return st;
     const Knobs kn = knobs();
-    const bool vec = vectorisable(N, dtype, {x, bias, residual, gamma, beta, y, residual_out});
+    // FP8 codes of a 16-byte vector of elements take 16 / es bytes
+    const bool vec = vectorisable(N, dtype, {x, bias, residual, gamma, beta,
+                                             f8 ? nullptr : y, residual_out}) &&
+                     (!f8 || !y || aligned(y, 16 / es));
     const FwdEntry *e = fwd_entry(dtype, vec, M, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
@@ -246,6 +254,7 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     a.gamma = gamma;
     a.beta = beta;
     a.y = y;
+    a.y_scale = f8 ? y_scale : nullptr;
     a.res_out = residual_out;
     a.mean = mean;
     a.rstd = rstd;
@@ -256,7 +265,8 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     a.K = w.K;
     a.A = w.A;
     a.eps = eps;
-    return launched((rms ? e->rms : e->ln)(a, int(w.grid), s));
+    const FwdLaunch run = f8 ? (rms ? e->rms_f8 : e->ln_f8) : (rms ? e->rms : e->ln);
+    return launched(run(a, int(w.grid), s));
 }
 
 // ----------------------------------------------------------------- backward
@@ -365,16 +375,34 @@ norm_status_t ln_fwd(const void *x, const void *bias, const void *residual, cons
                      const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
                      void *residual_out, float *mean, float *rstd, float *amax, void *stream)
 {
-    return fwd_common(false, x, bias, residual, gamma, beta, eps, M, N, dtype, y, residual_out,
-                      mean, rstd, amax, stream);
+    return fwd_common(false, x, bias, residual, gamma, beta, eps, M, N, dtype, nullptr, y,
+                      residual_out, mean, rstd, amax, false, stream);
 }
 
 norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                       const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
                       void *residual_out, float *mean, float *rstd, float *amax, void *stream)
 {
-    return fwd_common(true, x, bias, residual, gamma, beta, eps, M, N, dtype, y, residual_out,
-                      mean, rstd, amax, stream);
+    return fwd_common(true, x, bias, residual, gamma, beta, eps, M, N, dtype, nullptr, y,
+                      residual_out, mean, rstd, amax, false, stream);
+}
+
+norm_status_t ln_fwd_fp8(const void *x, const void *bias, const void *residual,
+                         const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
+                         int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
+                         float *mean, float *rstd, float *amax, void *stream)
+{
+    return fwd_common(false, x, bias, residual, gamma, beta, eps, M, N, dtype, y_scale, y_fp8,
+                      residual_out, mean, rstd, amax, true, stream);
+}
+
+norm_status_t rms_fwd_fp8(const void *x, const void *bias, const void *residual,
+                          const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
+                          int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
+                          float *mean, float *rstd, float *amax, void *stream)
+{
+    return fwd_common(true, x, bias, residual, gamma, beta, eps, M, N, dtype, y_scale, y_fp8,
+                      residual_out, mean, rstd, amax, true, stream);
 }
 
 norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_t *bytes)

@@ -236,6 +236,41 @@ struct BufIO<float, 1> {
     }
 };
 
+// ---------------------------------------------------------------------------
+// FP8 output: VEC fp32 values, each already scaled, to OCP FP8 E4M3 codes
+// (round to nearest even by the hardware convert, which turns magnitudes
+// beyond the format into NaN, so they are first clamped to +-448, the
+// largest finite E4M3 value) stored as VEC bytes at byte offset `off`.
+// ---------------------------------------------------------------------------
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float sat_e4m3(float v)
+{
+    return __builtin_amdgcn_fmed3f(v, -448.f, 448.f);
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_e4m3(rsrc_t r, uint32_t off, const float *v)
+{
+    if constexpr (VEC == 8) {
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), sat_e4m3(v[1]), 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[2]), sat_e4m3(v[3]), w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[4]), sat_e4m3(v[5]), 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[6]), sat_e4m3(v[7]), w1, true);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{unsigned(w0), unsigned(w1)}, r, int(off), 0,
+                                              BUF_NT);
+    } else if constexpr (VEC == 4) {
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), sat_e4m3(v[1]), 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[2]), sat_e4m3(v[3]), w, true);
+        __builtin_amdgcn_raw_buffer_store_b32(unsigned(w), r, int(off), 0, BUF_NT);
+    } else {
+        static_assert(VEC == 1, "FP8 store of 1, 4 or 8 values");
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), 0.f, 0, false);
+        __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(w & 0xff), r, int(off),
+                                             0, BUF_NT);
+    }
+}
+
 // VEC floats from LDS (16-byte reads when VEC is a multiple of 4).
 template <int VEC>
 __device__ __forceinline__ void lds_read(const float *p, float *out)

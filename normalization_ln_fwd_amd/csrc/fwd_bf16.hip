@@ -6,8 +6,10 @@ namespace nf {
 
 #define NF_ENTRY(T, VEC, LPR, VPL, TEAMS)                                                          \
     {{LPR, VPL, TEAMS, VEC},                                                                     \
-     &launch_fwd<T, VEC, LPR, VPL, TEAMS, false>,                                                 \
-     &launch_fwd<T, VEC, LPR, VPL, TEAMS, true>},
+     &launch_fwd<T, VEC, LPR, VPL, TEAMS, false, false>,                                          \
+     &launch_fwd<T, VEC, LPR, VPL, TEAMS, true, false>,                                           \
+     &launch_fwd<T, VEC, LPR, VPL, TEAMS, false, true>,                                           \
+     &launch_fwd<T, VEC, LPR, VPL, TEAMS, true, true>},
 
 static const FwdEntry k_vec[] = {NF_SHAPES_BF16_VEC(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, bf16, 8)};
 static const FwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, bf16)};

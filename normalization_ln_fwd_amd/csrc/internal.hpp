@@ -13,7 +13,8 @@ namespace nf {
 // groups, interleaved over blocks of A workgroups (see GroupWalk).
 struct FwdArgs {
     const void *x, *bias, *res, *gamma, *beta;
-    void *y, *res_out;
+    void *y, *res_out;       // y: I/O dtype, or FP8 E4M3 codes (uint8) when y_scale is set
+    const float *y_scale;    // FP8 output: one fp32 scale in device memory
     float *mean, *rstd;
     unsigned *amax; // bit pattern of a non-negative float, combined with atomicMax
     int64_t M;
@@ -51,7 +52,8 @@ struct RowShape {
 
 struct FwdEntry {
     RowShape shape;
-    FwdLaunch ln, rms;
+    FwdLaunch ln, rms;       // y in the I/O dtype
+    FwdLaunch ln_f8, rms_f8; // y as FP8 E4M3 codes
 };
 struct BwdEntry {
     RowShape shape;

@@ -219,7 +219,7 @@ __device__ __forceinline__ void param_vec(const float *lds, const Raw &reg, int 
 // Forward: t = (x + bias) + residual (fp32), u = round(t) -> residual_out,
 // statistics of u, y = normalise(u) * gamma + beta -> y, running max |y|.
 // ---------------------------------------------------------------------------
-template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS>
+template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS, bool F8>
 __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
 {
     using IO = VecIO<T, VEC>;
@@ -253,6 +253,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         off[k] = cvalid[k] ? uint32_t(team * N + (k * LPR + tl) * VEC) * uint32_t(sizeof(T))
                            : BUF_OOB;
     }
+    // FP8 output: one byte per element, and the scale every value takes
+    const float y_scale = F8 ? *a.y_scale : 1.f;
 
     // x and residual of row group g (zeros outside the matrix).  Wide teams
     // walk their row groups with the next group's loads in flight while the
@@ -427,7 +429,11 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
 #pragma unroll
         for (int k = 0; k < VPL; ++k)
             reload_barrier(ur[k]);
-        const rsrc_t ys = make_rsrc(static_cast<char *>(a.y) + gbyte, bytes);
+        // FP8: y rounded to the I/O dtype (the values amax is taken over),
+        // times the scale, to E4M3 codes, one byte per element
+        const rsrc_t ys = F8 ? make_rsrc(static_cast<char *>(a.y) + gbyte / int64_t(sizeof(T)),
+                                         bytes / uint32_t(sizeof(T)))
+                             : make_rsrc(static_cast<char *>(a.y) + gbyte, bytes);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
@@ -438,7 +444,16 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 yv[e] = fmaf(fmaf(u[e] - mean, rstd, lo_r), gv[e], bv[e]);
-            BIO::store(ys, off[k], IO::pack(yv));
+            if constexpr (F8) {
+                float q[VEC];
+                IO::unpack(IO::pack(yv), q);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    q[e] *= y_scale;
+                store_e4m3<VEC>(ys, cvalid[k] ? off[k] / uint32_t(sizeof(T)) : BUF_OOB, q);
+            } else {
+                BIO::store(ys, off[k], IO::pack(yv));
+            }
             if (rv && cvalid[k]) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
@@ -858,11 +873,11 @@ __global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SUB)
     }
 }
 
-template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS>
+template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS, bool F8>
 hipError_t launch_fwd(const FwdArgs &a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((fwd_kernel<T, VEC, LPR, VPL, TEAMS, RMS>), dim3(grid), dim3(LPR * TEAMS),
-                       0, s, a);
+    hipLaunchKernelGGL((fwd_kernel<T, VEC, LPR, VPL, TEAMS, RMS, F8>), dim3(grid),
+                       dim3(LPR * TEAMS), 0, s, a);
     return hipGetLastError();
 }
 

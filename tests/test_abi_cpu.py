@@ -99,6 +99,32 @@ def test_no_rows_allows_null_row_tensors(lib):
                                 rstd=None)) == 8
 
 
+def fwd8_args(**over):
+    a = dict(x=P, bias=None, res=None, gamma=None, beta=None, eps=1e-5, M=4, N=64, dtype=1,
+             scale=P, y=P, res_out=None, mean=None, rstd=None, amax=None, stream=None)
+    a.update(over)
+    return [a[k] for k in ("x", "bias", "res", "gamma", "beta", "eps", "M", "N", "dtype",
+                           "scale", "y", "res_out", "mean", "rstd", "amax", "stream")]
+
+
+@pytest.mark.parametrize("fn", ["ln_fwd_fp8", "rms_fwd_fp8"])
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=2), 4), (dict(scale=None), 1), (dict(y=None), 1), (dict(x=None), 1),
+    (dict(N=0), 2), (dict(eps=-1.0), 3), (dict(scale=BAD2), 5), (dict(x=BAD1), 5),
+    (dict(amax=BAD2), 5),
+])
+def test_fp8_forward_rejects(lib, fn, over, code):
+    assert getattr(lib, fn)(*fwd8_args(**over)) == code
+
+
+def test_fp8_forward_takes_any_output_alignment(lib):
+    """y_fp8 holds bytes: an odd address is not an argument error (it only
+    leaves the vectorised kernels), so the check reaches the device."""
+    if _gpu_visible():
+        pytest.skip("would launch")
+    assert lib.ln_fwd_fp8(*fwd8_args(y=P + 1)) == 8
+
+
 def test_rms_forward_takes_no_mean(lib):
     assert lib.rms_fwd(*fwd_args(mean=P)) == 3
 
