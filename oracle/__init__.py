@@ -21,6 +21,12 @@ Parity status of each function (what pins it, in ``tests/test_oracle.py``):
                            form sum_j dbias_j = 0.
   round_to_dtype        -- pinned: exhaustive checks against exactly
                            representable neighbours and ties.
+  zero_centered_gamma   -- pinned: torch's float64 layer_norm / rms_norm with
+                           the weight `1 + gamma` formed by torch in the I/O
+                           dtype (the expression the nvFuser comment uses), and
+                           float64 autograd of dx / dgamma through w = 1 + gamma.
+  dparam_mean           -- pinned: the closed form of dbeta's row mean with a
+                           row-constant dy, and the sums over M rows / M.
   quantize_e4m3         -- pinned: torch's float8_e4m3fn cast on every code,
                            every midpoint and its neighbours and random
                            in-range values; the format's fixed codes
@@ -56,10 +62,10 @@ def _load():
         lib = ctypes.CDLL(path)
         vp, i64, dbl, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, ctypes.c_int
         lib.oracle_norm_fwd.argtypes = [ci, vp, vp, vp, vp, vp, dbl, i64, i64, ci, ci,
-                                        vp, vp, vp, vp, vp]
+                                        vp, vp, vp, vp, vp, ci]
         lib.oracle_norm_fwd.restype = ci
         lib.oracle_norm_bwd.argtypes = [ci, vp, vp, vp, vp, vp, dbl, i64, i64, ci, ci,
-                                        vp, vp, vp, vp, vp, vp, vp, vp]
+                                        vp, vp, vp, vp, vp, vp, vp, vp, ci, ci]
         lib.oracle_norm_bwd.restype = ci
         lib.oracle_round_to_dtype.argtypes = [vp, i64, ci, vp]
         lib.oracle_round_to_dtype.restype = ci
@@ -93,12 +99,14 @@ def default_threads():
 
 
 def norm_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, *,
-             rms=False, dtype=BF16, nthreads=None, want_u=True, want_y=True):
+             rms=False, dtype=BF16, nthreads=None, want_u=True, want_y=True,
+             zero_centered_gamma=False):
     """Forward of the fused op on an (M, N) matrix.
 
     Returns a dict: ``u`` (residual_out, I/O dtype), ``y`` (float64, exact,
     unrounded), ``mean`` / ``rstd`` (float64 [M]; mean is 0 for RMSNorm) and
     ``amax`` (float64 scalar, max |y| after rounding y to the I/O dtype).
+    ``zero_centered_gamma``: the weight is 1 + gamma, formed in the I/O dtype.
     """
     lib = _load()
     x = _in(x, dtype, name="x")
@@ -115,14 +123,15 @@ def norm_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, *,
     rc = lib.oracle_norm_fwd(int(rms), _ptr(x), _ptr(bias), _ptr(residual), _ptr(gamma),
                              _ptr(beta), float(eps), M, N, dtype,
                              nthreads or default_threads(), _ptr(u), _ptr(y), _ptr(mean),
-                             _ptr(rstd), _ptr(amax))
+                             _ptr(rstd), _ptr(amax), int(bool(zero_centered_gamma)))
     if rc != 0:
         raise ValueError("oracle_norm_fwd rejected its arguments")
     return {"u": u, "y": y, "mean": mean, "rstd": rstd, "amax": float(amax[0])}
 
 
 def norm_bwd(dy, x, gamma=None, mean=None, rstd=None, eps=1e-5, *, rms=False,
-             dtype=BF16, nthreads=None, want_dx=True, want_params=True, want_dbias=False):
+             dtype=BF16, nthreads=None, want_dx=True, want_params=True, want_dbias=False,
+             zero_centered_gamma=False, dparam_mean=False):
     """Backward on an (M, N) matrix.
 
     ``mean`` / ``rstd`` are per-row arrays (any float dtype, widened exactly
@@ -131,6 +140,8 @@ def norm_bwd(dy, x, gamma=None, mean=None, rstd=None, eps=1e-5, *, rms=False,
     ``dgamma_l2``, ``dbeta_l2`` (N,), all unrounded, and ``rstd`` (M,), the
     rstd the gradients used; with ``want_dbias`` also ``dbias`` (N,), the
     gradient of the forward's bias (column sums of dx), and ``dbias_l2``.
+    ``zero_centered_gamma``: the forward's weight was 1 + gamma.
+    ``dparam_mean``: the column results (and their 2-norms) are divided by M.
     """
     lib = _load()
     dy = _in(dy, dtype, name="dy")
@@ -149,7 +160,8 @@ def norm_bwd(dy, x, gamma=None, mean=None, rstd=None, eps=1e-5, *, rms=False,
                              float(eps), M, N, dtype, nthreads or default_threads(), _ptr(dx),
                              _ptr(out["dgamma"]), _ptr(out["dbeta"]), _ptr(out["dgamma_l2"]),
                              _ptr(out["dbeta_l2"]), _ptr(rstd_used), _ptr(out["dbias"]),
-                             _ptr(out["dbias_l2"]))
+                             _ptr(out["dbias_l2"]), int(bool(zero_centered_gamma)),
+                             int(bool(dparam_mean)))
     if rc != 0:
         raise ValueError("oracle_norm_bwd rejected its arguments")
     out["dx"] = dx

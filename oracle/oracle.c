@@ -171,7 +171,18 @@ typedef struct {
     void *u_out;
     double *y, *mean, *rstd;
     double *row_amax; /* per row: max |round_io(y)| */
+    int zero_centered;
 } fwd_ctx;
+
+/* The scale the normalised value is multiplied by: gamma (1 when absent),
+ * or with a zero-centred gamma w = 1 + gamma, formed in the I/O dtype as the
+ * nvFuser issue's layernorm + amax comment forms it (`1 + ln_weight` on the
+ * weight tensor) before it is handed to layer_norm. */
+static double weight_of(const void *gamma, int dtype, int zero_centered, int64_t j)
+{
+    const double g = elem_or(gamma, dtype, j, zero_centered ? 0.0 : 1.0);
+    return zero_centered ? round_io(1.0 + g, dtype) : g;
+}
 
 static void fwd_rows(void *vctx, int64_t r0, int64_t r1)
 {
@@ -210,7 +221,7 @@ static void fwd_rows(void *vctx, int64_t r0, int64_t r1)
         }
         double amax = 0.0;
         for (int64_t j = 0; j < N; ++j) {
-            double g = elem_or(c->gamma, c->dtype, j, 1.0);
+            double g = weight_of(c->gamma, c->dtype, c->zero_centered, j);
             double b = elem_or(c->beta, c->dtype, j, 0.0);
             double yv = (u[j] - mean) * rstd * g + b;
             if (c->y)
@@ -236,12 +247,13 @@ static void fwd_rows(void *vctx, int64_t r0, int64_t r1)
  *   outputs (each optional): u_out [M,N] in the I/O dtype (residual_out),
  *            y [M,N] exact (double, before any output rounding),
  *            mean [M] (LayerNorm; 0 for RMSNorm), rstd [M], *amax.
+ *   zero_centered: the weight is w = round_io(1 + gamma) (weight_of).
  * Returns 0, or -1 on a bad argument.
  */
 int oracle_norm_fwd(int is_rms, const void *x, const void *bias, const void *residual,
                     const void *gamma, const void *beta, double eps, int64_t M, int64_t N,
                     int dtype, int nthreads, void *u_out, double *y, double *mean, double *rstd,
-                    double *amax)
+                    double *amax, int zero_centered)
 {
     if (!x || M < 0 || N <= 0 || (dtype != OR_F32 && dtype != OR_BF16) || !(eps >= 0.0))
         return -1;
@@ -252,7 +264,7 @@ int oracle_norm_fwd(int is_rms, const void *x, const void *bias, const void *res
             return -1;
     }
     fwd_ctx c = {is_rms, dtype, x, bias, residual, gamma, beta, eps, N,
-                 u_out, y, mean, rstd, row_amax};
+                 u_out, y, mean, rstd, row_amax, zero_centered};
     parallel_ranges(nthreads, M, fwd_rows, &c);
     if (amax) {
         double m = 0.0; /* M = 0: nothing to take the max of */
@@ -277,6 +289,7 @@ typedef struct {
     double *dx;
     double *dgamma, *dbeta, *dgamma_l2, *dbeta_l2;
     double *dbias, *dbias_l2;
+    int zero_centered;
 } bwd_ctx;
 
 static double xhat_of(const bwd_ctx *c, int64_t i, int64_t j)
@@ -316,14 +329,16 @@ static void bwd_dx_rows(void *vctx, int64_t r0, int64_t r1)
     for (int64_t i = r0; i < r1; ++i) {
         double s_gx = 0.0, s_g = 0.0;
         for (int64_t j = 0; j < N; ++j) {
-            double g = elem(c->dy, c->dtype, i * N + j) * elem_or(c->gamma, c->dtype, j, 1.0);
+            double g = elem(c->dy, c->dtype, i * N + j) *
+                       weight_of(c->gamma, c->dtype, c->zero_centered, j);
             s_gx += g * xhat_of(c, i, j);
             s_g += g;
         }
         double c1 = s_gx / (double)N;
         double c2 = c->is_rms ? 0.0 : s_g / (double)N;
         for (int64_t j = 0; j < N; ++j) {
-            double g = elem(c->dy, c->dtype, i * N + j) * elem_or(c->gamma, c->dtype, j, 1.0);
+            double g = elem(c->dy, c->dtype, i * N + j) *
+                       weight_of(c->gamma, c->dtype, c->zero_centered, j);
             c->dx[i * N + j] = c->rstd[i] * (g - c2 - xhat_of(c, i, j) * c1);
         }
     }
@@ -390,13 +405,18 @@ static void bwd_dbias_cols(void *vctx, int64_t j0, int64_t j1)
  *            rstd_out [M] = the rstd used (given or recomputed); dbias [N] =
  *            the gradient of the forward's bias (column sums of dx) and
  *            dbias_l2 [N] the 2-norm of its terms.
+ *   zero_centered: the forward's weight was w = round_io(1 + gamma); dx uses
+ *            w, and dgamma (dL/dgamma = dL/dw) keeps its form.
+ *   dparam_mean: the "division for mean" epilogue of PyTorch PR #165370
+ *            (description, step 3): dgamma, dbeta, dbias and their 2-norms
+ *            are divided by M (the mean over the rows instead of the sum).
  * Returns 0, or -1 on a bad argument.
  */
 int oracle_norm_bwd(int is_rms, const void *dy, const void *x, const void *gamma,
                     const double *mean, const double *rstd, double eps, int64_t M, int64_t N,
                     int dtype, int nthreads, double *dx, double *dgamma, double *dbeta,
                     double *dgamma_l2, double *dbeta_l2, double *rstd_out, double *dbias,
-                    double *dbias_l2)
+                    double *dbias_l2, int zero_centered, int dparam_mean)
 {
     if (!dy || !x || M < 0 || N <= 0 || (dtype != OR_F32 && dtype != OR_BF16))
         return -1;
@@ -418,7 +438,8 @@ int oracle_norm_bwd(int is_rms, const void *dy, const void *x, const void *gamma
         }
     }
     bwd_ctx c = {is_rms, dtype, dy, x, gamma, mean, rstd, eps, M, N,
-                 rstd_used, dx_buf, dgamma, dbeta, dgamma_l2, dbeta_l2, dbias, dbias_l2};
+                 rstd_used, dx_buf, dgamma, dbeta, dgamma_l2, dbeta_l2, dbias, dbias_l2,
+                 zero_centered};
     parallel_ranges(nthreads, M, bwd_rstd_rows, &c);
     if (dx_buf)
         parallel_ranges(nthreads, M, bwd_dx_rows, &c);
@@ -426,6 +447,13 @@ int oracle_norm_bwd(int is_rms, const void *dy, const void *x, const void *gamma
         parallel_ranges(nthreads, N, bwd_col_sums, &c);
     if (want_db)
         parallel_ranges(nthreads, N, bwd_dbias_cols, &c);
+    if (dparam_mean && M > 0) {
+        double *outs[6] = {dgamma, dbeta, dgamma_l2, dbeta_l2, dbias, dbias_l2};
+        for (int k = 0; k < 6; ++k)
+            if (outs[k])
+                for (int64_t j = 0; j < N; ++j)
+                    outs[k][j] /= (double)M;
+    }
     if (rstd_out && M > 0)
         memcpy(rstd_out, rstd_used, (size_t)M * sizeof(double));
     if (dx_buf != dx)

@@ -545,3 +545,72 @@ def test_e4m3_scale_applies_in_fp32(oracle_mod):
         p = v * np.float32(scale)
         ref = torch.from_numpy(np.clip(p, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8)
         assert np.array_equal(oracle_mod.quantize_e4m3(v, scale), ref.numpy())
+
+
+# ----------------------------------------------- zero-centred gamma, mean
+
+@pytest.mark.parametrize("rms", [False, True])
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_zero_centered_gamma_matches_torch(oracle_mod, rms, dtype):
+    """w = 1 + gamma formed by torch in the I/O dtype, then the float64
+    normalisation with that weight (the nvFuser comment's expression)."""
+    M, N = 9, 50
+    inp = synth.make_inputs(M, N, dtype=dtype, seed=15, names=("x", "gamma", "beta"))
+    tdt = torch.bfloat16 if dtype == BF16 else torch.float32
+    def t_of(a):
+        return (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dtype == BF16
+                else torch.from_numpy(a))
+    # a zero-centred weight ~ 0.1 * N(0,1), finer than the I/O dtype's
+    # spacing near 1, so that forming 1 + gamma rounds
+    gamma = synth.make_inputs(1, N, dtype=dtype, seed=19, names=("beta",))["beta"]
+    g0 = t_of(gamma)
+    assert dtype == F32 or bool(((1 + g0).double() != 1 + g0.double()).any())
+    w = (1 + g0).to(torch.float64)
+    x, beta = t_of(inp["x"]).to(torch.float64), t_of(inp["beta"]).to(torch.float64)
+    eps = 1e-5
+    ref = (F.rms_norm(x, (N,), w, eps) + beta) if rms else F.layer_norm(x, (N,), w, beta, eps)
+    r = oracle_mod.norm_fwd(inp["x"], gamma=gamma, beta=inp["beta"], eps=eps, rms=rms,
+                            dtype=dtype, zero_centered_gamma=True)
+    np.testing.assert_allclose(r["y"], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("rms", [False, True])
+def test_zero_centered_gamma_backward_autograd(oracle_mod, rms):
+    """dx and dgamma through w = 1 + gamma (gamma chosen so that 1 + gamma
+    is exact in fp32; autograd in float64)."""
+    M, N = 7, 33
+    rng = np.random.default_rng(16)
+    x = f32(rng.standard_normal((M, N)))
+    gamma = dyadic(rng, (N,), -40, 40, 8)
+    dy = f32(rng.standard_normal((M, N)))
+    eps = 1e-5
+    gt = t64(gamma).requires_grad_()
+    xt = t64(x).requires_grad_()
+    w = 1 + gt
+    y = F.rms_norm(xt, (N,), w, eps) if rms else F.layer_norm(xt, (N,), w, None, eps)
+    (y * t64(dy)).sum().backward()
+    f = oracle_mod.norm_fwd(x, gamma=gamma, eps=eps, rms=rms, dtype=F32,
+                            zero_centered_gamma=True)
+    b = oracle_mod.norm_bwd(dy, x, gamma, None if rms else f["mean"], f["rstd"], eps, rms=rms,
+                            dtype=F32, zero_centered_gamma=True)
+    np.testing.assert_allclose(b["dx"], xt.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(b["dgamma"], gt.grad.numpy(), rtol=1e-11, atol=1e-11)
+
+
+def test_dparam_mean_divides_by_rows(oracle_mod):
+    """With dy constant c_j down every column, dbeta's row mean is c_j
+    exactly; every mean is the sum over the M rows divided by M."""
+    M, N = 24, 16
+    rng = np.random.default_rng(17)
+    inp = synth.make_inputs(M, N, dtype=F32, seed=18, names=("x", "gamma"))
+    c = dyadic(rng, (N,))
+    dy = f32(np.broadcast_to(c, (M, N)))
+    f = oracle_mod.norm_fwd(inp["x"], eps=1e-5, dtype=F32)
+    s = oracle_mod.norm_bwd(dy, inp["x"], inp["gamma"], f["mean"], f["rstd"], 1e-5, dtype=F32,
+                            want_dbias=True)
+    m = oracle_mod.norm_bwd(dy, inp["x"], inp["gamma"], f["mean"], f["rstd"], 1e-5, dtype=F32,
+                            want_dbias=True, dparam_mean=True)
+    np.testing.assert_array_equal(m["dbeta"], c.astype(np.float64))
+    for k in ("dgamma", "dbeta", "dbias", "dgamma_l2", "dbeta_l2", "dbias_l2"):
+        np.testing.assert_allclose(m[k], s[k] / M, rtol=1e-15, atol=0)
+    np.testing.assert_array_equal(m["dx"], s["dx"])

@@ -42,7 +42,8 @@ MUTANTS = [
      "c->rstd[i] * (g - c2 + xhat_of(c, i, j) * c1)"),
     ("dx missing rstd", "c->rstd[i] * (g - c2 - xhat_of(c, i, j) * c1)",
      "(g - c2 - xhat_of(c, i, j) * c1)"),
-    ("dx without gamma", "double g = elem(c->dy, c->dtype, i * N + j) * elem_or(c->gamma, c->dtype, j, 1.0);\n            s_gx",
+    ("dx without gamma",
+     "double g = elem(c->dy, c->dtype, i * N + j) *\n                       weight_of(c->gamma, c->dtype, c->zero_centered, j);\n            s_gx",
      "double g = elem(c->dy, c->dtype, i * N + j);\n            s_gx"),
     ("dgamma without xhat", "double tg = d * xhat_of(c, i, j);", "double tg = d;"),
     ("dbeta sums squares", "sb += d;", "sb += d * d;"),
@@ -58,6 +59,12 @@ MUTANTS = [
      "double r = ldexp(floor(ldexp(a, -q)), q);"),
     ("e4m3 product in double", "const float p = v[i] * scale;",
      "const double p = (double)v[i] * (double)scale;"),
+    ("zero-centred weight not rounded", "return zero_centered ? round_io(1.0 + g, dtype) : g;",
+     "return zero_centered ? 1.0 + g : g;"),
+    ("zero-centred weight ignored in dx",
+     "double g = elem(c->dy, c->dtype, i * N + j) *\n                       weight_of(c->gamma, c->dtype, c->zero_centered, j);\n            s_gx",
+     "double g = elem(c->dy, c->dtype, i * N + j) *\n                       elem_or(c->gamma, c->dtype, j, 1.0);\n            s_gx"),
+    ("mean epilogue divides by N", "outs[k][j] /= (double)M;", "outs[k][j] /= (double)N;"),
     ("dbias skips the last row", "for (int64_t i = 0; i < c->M; ++i) {\n            double t = c->dx",
      "for (int64_t i = 0; i + 1 < c->M; ++i) {\n            double t = c->dx"),
 ]
