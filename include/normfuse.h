@@ -108,6 +108,20 @@ typedef int32_t norm_status_t;
 #define NORM_N_MAX 16384
 
 /*
+ * Option bits (`flags` of every compute entry point; others: NORM_ERR_ARG).
+ * NORM_ZERO_CENTERED_GAMMA -- gamma is stored around 0 and the weight is
+ *     w = 1 + gamma, formed in the I/O dtype: the `zero_centered_gamma`
+ *     branch of the nvFuser issue's layernorm + amax comment.  An absent
+ *     gamma is then a weight of 1.  In the backward, dx uses w and dgamma
+ *     (= dL/dw) keeps its form.
+ * NORM_DPARAM_MEAN (backward only) -- dgamma / dbeta / dbias are the mean
+ *     over the M rows instead of the sum: the "division for mean" epilogue of
+ *     the outer reduction in PyTorch PR #165370 (description, step 3).
+ */
+#define NORM_ZERO_CENTERED_GAMMA 1u
+#define NORM_DPARAM_MEAN 2u
+
+/*
  * ln_fwd -- fused (bias +) residual + LayerNorm forward.
  *   x            [M,N] dtype   required
  *   bias         [N]   dtype   optional (NULL: no bias)
@@ -119,11 +133,13 @@ typedef int32_t norm_status_t;
  *   residual_out [M,N] dtype   optional: u, the rounded sum that was normalised
  *   mean, rstd   [M]   fp32    optional
  *   amax         [1]   fp32    optional: overwritten with max |y| (0 when M = 0)
+ *   flags        0 or NORM_ZERO_CENTERED_GAMMA
  *   stream       hipStream_t
  */
 norm_status_t ln_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                      const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
-                     void *residual_out, float *mean, float *rstd, float *amax, void *stream);
+                     void *residual_out, float *mean, float *rstd, float *amax, uint32_t flags,
+                     void *stream);
 
 /*
  * rms_fwd -- fused (bias +) residual + RMSNorm forward.  Arguments as ln_fwd;
@@ -132,7 +148,8 @@ norm_status_t ln_fwd(const void *x, const void *bias, const void *residual, cons
  */
 norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                       const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
-                      void *residual_out, float *mean, float *rstd, float *amax, void *stream);
+                      void *residual_out, float *mean, float *rstd, float *amax, uint32_t flags,
+                      void *stream);
 
 /*
  * ln_fwd_fp8 / rms_fwd_fp8 -- the same forward with y emitted as OCP FP8
@@ -158,11 +175,13 @@ norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, con
 norm_status_t ln_fwd_fp8(const void *x, const void *bias, const void *residual,
                          const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                          int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
-                         float *mean, float *rstd, float *amax, void *stream);
+                         float *mean, float *rstd, float *amax, uint32_t flags,
+                         void *stream);
 norm_status_t rms_fwd_fp8(const void *x, const void *bias, const void *residual,
                           const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                           int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
-                          float *mean, float *rstd, float *amax, void *stream);
+                          float *mean, float *rstd, float *amax, uint32_t flags,
+                          void *stream);
 
 /*
  * norm_bwd_workspace_size -- bytes of device workspace ln_bwd / rms_bwd need
@@ -191,11 +210,12 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
  *                fp32 and rounded (to nearest, ties to even) to this type
  *   workspace    device memory of at least norm_bwd_workspace_size bytes
  *                (may be NULL when that size is 0)
+ *   flags        NORM_ZERO_CENTERED_GAMMA and / or NORM_DPARAM_MEAN
  */
 norm_status_t ln_bwd(const void *dy, const void *x, const void *gamma, const float *mean,
                      const float *rstd, int64_t M, int64_t N, int32_t dtype, void *dx,
                      void *dgamma, void *dbeta, void *dbias, int32_t dparam_dtype,
-                     void *workspace, size_t workspace_bytes, void *stream);
+                     void *workspace, size_t workspace_bytes, uint32_t flags, void *stream);
 
 /*
  * rms_bwd -- RMSNorm backward with the mix-order reduction.  Arguments as
@@ -206,7 +226,7 @@ norm_status_t ln_bwd(const void *dy, const void *x, const void *gamma, const flo
 norm_status_t rms_bwd(const void *dy, const void *x, const void *gamma, const float *rstd,
                       float eps, int64_t M, int64_t N, int32_t dtype, void *dx, void *dgamma,
                       void *dbeta, void *dbias, int32_t dparam_dtype, void *workspace,
-                      size_t workspace_bytes, void *stream);
+                      size_t workspace_bytes, uint32_t flags, void *stream);
 
 /* Static text for a status code. */
 const char *norm_status_string(norm_status_t status);

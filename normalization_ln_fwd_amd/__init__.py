@@ -28,6 +28,9 @@ N_MAX = 16384
 STATUS = {0: "NORM_OK", 1: "NORM_ERR_NULL", 2: "NORM_ERR_SHAPE", 3: "NORM_ERR_ARG",
           4: "NORM_ERR_DTYPE", 5: "NORM_ERR_ALIGN", 6: "NORM_ERR_WORKSPACE", 7: "NORM_ERR_LAUNCH",
           8: "NORM_ERR_DEVICE"}
+ZERO_CENTERED_GAMMA = 1  # option bits of include/normfuse.h
+DPARAM_MEAN = 2
+
 EXPORTS = ("ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd",
            "norm_bwd_workspace_size", "norm_status_string")
 
@@ -56,15 +59,17 @@ def library():
         lib = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                  ctypes.c_float, ctypes.c_size_t)
-        fwd = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp]
+        u32 = ctypes.c_uint32
+        fwd = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, u32, vp]
         lib.ln_fwd.argtypes = fwd
         lib.rms_fwd.argtypes = fwd
-        fwd8 = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp]
+        fwd8 = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp, u32, vp]
         lib.ln_fwd_fp8.argtypes = fwd8
         lib.rms_fwd_fp8.argtypes = fwd8
-        lib.ln_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz, vp]
+        lib.ln_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
+                               u32, vp]
         lib.rms_bwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
-                                vp]
+                                u32, vp]
         lib.norm_bwd_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
         lib.norm_status_string.argtypes = [i32]
         lib.norm_status_string.restype = ctypes.c_char_p
@@ -109,7 +114,7 @@ def _stream(stream):
 
 
 def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, want_rstd,
-         want_amax, stream, out, y_scale=None):
+         want_amax, stream, out, y_scale=None, zero_centered_gamma=False):
     lib = library()
     N = x.shape[-1]
     M = x.numel() // N if N else 0
@@ -144,53 +149,59 @@ def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, 
     st = getattr(lib, fn)(
         *head, _ptr(res_out, "residual_out", dt, M * N),
         _ptr(mean, "mean", torch.float32, M), _ptr(rstd, "rstd", torch.float32, M),
-        _ptr(amax, "amax", torch.float32, 1), _stream(stream))
+        _ptr(amax, "amax", torch.float32, 1), ZERO_CENTERED_GAMMA if zero_centered_gamma else 0,
+        _stream(stream))
     _check(fn, st)
     return {"y": y, "residual_out": res_out, "mean": mean, "rstd": rstd, "amax": amax}
 
 
 def ln_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, *,
-           want_residual_out=None, want_stats=True, want_amax=False, stream=None, out=None):
+           want_residual_out=None, want_stats=True, want_amax=False, zero_centered_gamma=False,
+           stream=None, out=None):
     """Fused (bias +) residual + LayerNorm over the last dimension of ``x``.
 
     Returns a dict with ``y``, ``residual_out`` (when bias or residual is given,
     unless disabled), ``mean`` / ``rstd`` (fp32, when ``want_stats``) and
     ``amax`` (1-element fp32, when ``want_amax``).  ``out`` may supply any of
-    these tensors preallocated.
+    these tensors preallocated.  ``zero_centered_gamma``: the weight is
+    1 + gamma.
     """
     if want_residual_out is None:
         want_residual_out = bias is not None or residual is not None
     return _fwd("ln_fwd", x, bias, residual, gamma, beta, eps, want_residual_out, want_stats,
-                want_stats, want_amax, stream, out)
+                want_stats, want_amax, stream, out, zero_centered_gamma=zero_centered_gamma)
 
 
 def rms_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-6, *,
-            want_residual_out=None, want_stats=True, want_amax=False, stream=None, out=None):
+            want_residual_out=None, want_stats=True, want_amax=False, zero_centered_gamma=False,
+            stream=None, out=None):
     """Fused (bias +) residual + RMSNorm; as :func:`ln_fwd` without ``mean``."""
     if want_residual_out is None:
         want_residual_out = bias is not None or residual is not None
     return _fwd("rms_fwd", x, bias, residual, gamma, beta, eps, want_residual_out, False,
-                want_stats, want_amax, stream, out)
+                want_stats, want_amax, stream, out, zero_centered_gamma=zero_centered_gamma)
 
 
 def ln_fwd_fp8(x, y_scale, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, *,
-               want_residual_out=None, want_stats=True, want_amax=False, stream=None, out=None):
+               want_residual_out=None, want_stats=True, want_amax=False,
+               zero_centered_gamma=False, stream=None, out=None):
     """:func:`ln_fwd` with ``y`` as OCP FP8 E4M3 codes of y * y_scale
     (``y_scale``: a 1-element fp32 tensor on the GPU); ``y`` is returned as a
     ``float8_e4m3fn`` tensor (``out`` may supply one, or a ``uint8`` one)."""
     if want_residual_out is None:
         want_residual_out = bias is not None or residual is not None
     return _fwd("ln_fwd_fp8", x, bias, residual, gamma, beta, eps, want_residual_out,
-                want_stats, want_stats, want_amax, stream, out, y_scale)
+                want_stats, want_stats, want_amax, stream, out, y_scale, zero_centered_gamma)
 
 
 def rms_fwd_fp8(x, y_scale, bias=None, residual=None, gamma=None, beta=None, eps=1e-6, *,
-                want_residual_out=None, want_stats=True, want_amax=False, stream=None, out=None):
+                want_residual_out=None, want_stats=True, want_amax=False,
+                zero_centered_gamma=False, stream=None, out=None):
     """:func:`rms_fwd` with ``y`` as OCP FP8 E4M3 codes of y * y_scale."""
     if want_residual_out is None:
         want_residual_out = bias is not None or residual is not None
     return _fwd("rms_fwd_fp8", x, bias, residual, gamma, beta, eps, want_residual_out, False,
-                want_stats, want_amax, stream, out, y_scale)
+                want_stats, want_amax, stream, out, y_scale, zero_centered_gamma)
 
 
 def bwd_workspace_size(M, N, dtype):
@@ -203,7 +214,7 @@ def bwd_workspace_size(M, N, dtype):
 
 
 def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbeta, want_dbias,
-         workspace, stream, out):
+         workspace, stream, out, flags=0):
     lib = library()
     N = x.shape[-1]
     M = x.numel() // N if N else 0
@@ -235,23 +246,32 @@ def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbet
              _ptr(dgamma, "dgamma", pdt, N), _ptr(dbeta, "dbeta", pdt, N),
              _ptr(dbias, "dbias", pdt, N), pcode,
              _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-             _stream(stream)]
+             flags, _stream(stream)]
     _check(fn, getattr(lib, fn)(*args))
     return {"dx": dx, "dgamma": dgamma, "dbeta": dbeta, "dbias": dbias}
 
 
+def _bwd_flags(zero_centered_gamma, dparam_mean):
+    return (ZERO_CENTERED_GAMMA if zero_centered_gamma else 0) | (DPARAM_MEAN if dparam_mean
+                                                                  else 0)
+
+
 def ln_bwd(dy, x, gamma, mean, rstd, *, dparam_dtype=None, want_dgamma=True, want_dbeta=True,
-           want_dbias=False, workspace=None, stream=None, out=None):
+           want_dbias=False, zero_centered_gamma=False, dparam_mean=False, workspace=None,
+           stream=None, out=None):
     """LayerNorm backward (dx, dgamma, dbeta) from one read of dy and x.
     ``dparam_dtype`` (default: x's dtype) is the type of dgamma / dbeta.
     ``want_dbias`` also returns the gradient of the forward's bias (the
-    column sums of dx), for a forward that fused (x + bias) + residual."""
+    column sums of dx), for a forward that fused (x + bias) + residual.
+    ``zero_centered_gamma``: the forward's weight was 1 + gamma;
+    ``dparam_mean``: the column results are means over the rows."""
     return _bwd("ln_bwd", dy, x, gamma, mean, rstd, 0.0, dparam_dtype, want_dgamma, want_dbeta,
-                want_dbias, workspace, stream, out)
+                want_dbias, workspace, stream, out, _bwd_flags(zero_centered_gamma, dparam_mean))
 
 
 def rms_bwd(dy, x, gamma, rstd=None, eps=1e-6, *, dparam_dtype=None, want_dgamma=True,
-            want_dbeta=False, want_dbias=False, workspace=None, stream=None, out=None):
+            want_dbeta=False, want_dbias=False, zero_centered_gamma=False, dparam_mean=False,
+            workspace=None, stream=None, out=None):
     """RMSNorm backward; ``rstd=None`` recomputes it from ``x`` and ``eps``."""
     return _bwd("rms_bwd", dy, x, gamma, None, rstd, eps, dparam_dtype, want_dgamma, want_dbeta,
-                want_dbias, workspace, stream, out)
+                want_dbias, workspace, stream, out, _bwd_flags(zero_centered_gamma, dparam_mean))

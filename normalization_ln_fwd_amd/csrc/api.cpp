@@ -195,7 +195,8 @@ norm_status_t launched(hipError_t e) { return e == hipSuccess ? NORM_OK : NORM_E
 norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *residual,
                          const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                          int32_t dtype, const float *y_scale, void *y, void *residual_out,
-                         float *mean, float *rstd, float *amax, bool f8, void *stream)
+                         float *mean, float *rstd, float *amax, bool f8, uint32_t flags,
+                         void *stream)
 {
     if (!dtype_ok(dtype))
         return NORM_ERR_DTYPE;
@@ -204,7 +205,7 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     // with no rows there is nothing to read or write
     if (M > 0 && (!x || !y || (f8 && !y_scale)))
         return NORM_ERR_NULL;
-    if (!eps_ok(eps) || (rms && mean))
+    if (!eps_ok(eps) || (rms && mean) || (flags & ~uint32_t(NORM_ZERO_CENTERED_GAMMA)))
         return NORM_ERR_ARG;
     const size_t es = elem_size(dtype);
     for (const void *p : {x, bias, residual, gamma, beta, (const void *)(f8 ? nullptr : y),
@@ -265,6 +266,7 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     a.K = w.K;
     a.A = w.A;
     a.eps = eps;
+    a.zero_centred = (flags & NORM_ZERO_CENTERED_GAMMA) != 0;
     const FwdLaunch run = f8 ? (rms ? e->rms_f8 : e->ln_f8) : (rms ? e->rms : e->ln);
     return launched(run(a, int(w.grid), s));
 }
@@ -303,7 +305,7 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
                          const float *mean, const float *rstd, float eps, int64_t M, int64_t N,
                          int32_t dtype, void *dx, void *dgamma, void *dbeta, void *dbias,
                          int32_t dparam_dtype, void *workspace, size_t workspace_bytes,
-                         void *stream)
+                         uint32_t flags, void *stream)
 {
     if (!dtype_ok(dtype) || !dtype_ok(dparam_dtype))
         return NORM_ERR_DTYPE;
@@ -312,6 +314,8 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
     if (M > 0 && (!dy || !x || !dx || (!rms && (!mean || !rstd))))
         return NORM_ERR_NULL;
     if (rms && !rstd && !eps_ok(eps))
+        return NORM_ERR_ARG;
+    if (flags & ~uint32_t(NORM_ZERO_CENTERED_GAMMA | NORM_DPARAM_MEAN))
         return NORM_ERR_ARG;
     const size_t es = elem_size(dtype);
     for (const void *p : {dy, x, gamma, (const void *)dx})
@@ -356,6 +360,7 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         a.K = w.K;
         a.A = w.A;
         a.eps = eps;
+        a.zero_centred = (flags & NORM_ZERO_CENTERED_GAMMA) != 0;
         const BwdLaunch run = dbias ? (rms ? e->rms_db : e->ln_db) : (rms ? e->rms : e->ln);
         if (norm_status_t st = launched(run(a, int(w.grid), s)))
             return st;
@@ -363,8 +368,10 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
     float *level2 =
         lay.two_level ? reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.level2_off)
                       : nullptr;
+    // the mean over the rows instead of the sum (no rows: zeros either way)
+    const float divisor = (flags & NORM_DPARAM_MEAN) && M > 0 ? float(M) : 1.f;
     return launched(launch_colsum(ws, int(w.grid), nb, int(N), dgamma, dbeta, dbias, dparam_dtype,
-                                  level2, s));
+                                  divisor, level2, s));
 }
 
 } // namespace
@@ -373,36 +380,40 @@ extern "C" {
 
 norm_status_t ln_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                      const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
-                     void *residual_out, float *mean, float *rstd, float *amax, void *stream)
+                     void *residual_out, float *mean, float *rstd, float *amax, uint32_t flags,
+                     void *stream)
 {
     return fwd_common(false, x, bias, residual, gamma, beta, eps, M, N, dtype, nullptr, y,
-                      residual_out, mean, rstd, amax, false, stream);
+                      residual_out, mean, rstd, amax, false, flags, stream);
 }
 
 norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                       const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
-                      void *residual_out, float *mean, float *rstd, float *amax, void *stream)
+                      void *residual_out, float *mean, float *rstd, float *amax, uint32_t flags,
+                      void *stream)
 {
     return fwd_common(true, x, bias, residual, gamma, beta, eps, M, N, dtype, nullptr, y,
-                      residual_out, mean, rstd, amax, false, stream);
+                      residual_out, mean, rstd, amax, false, flags, stream);
 }
 
 norm_status_t ln_fwd_fp8(const void *x, const void *bias, const void *residual,
                          const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                          int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
-                         float *mean, float *rstd, float *amax, void *stream)
+                         float *mean, float *rstd, float *amax, uint32_t flags,
+                         void *stream)
 {
     return fwd_common(false, x, bias, residual, gamma, beta, eps, M, N, dtype, y_scale, y_fp8,
-                      residual_out, mean, rstd, amax, true, stream);
+                      residual_out, mean, rstd, amax, true, flags, stream);
 }
 
 norm_status_t rms_fwd_fp8(const void *x, const void *bias, const void *residual,
                           const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                           int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
-                          float *mean, float *rstd, float *amax, void *stream)
+                          float *mean, float *rstd, float *amax, uint32_t flags,
+                          void *stream)
 {
     return fwd_common(true, x, bias, residual, gamma, beta, eps, M, N, dtype, y_scale, y_fp8,
-                      residual_out, mean, rstd, amax, true, stream);
+                      residual_out, mean, rstd, amax, true, flags, stream);
 }
 
 norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_t *bytes)
@@ -438,19 +449,19 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
 norm_status_t ln_bwd(const void *dy, const void *x, const void *gamma, const float *mean,
                      const float *rstd, int64_t M, int64_t N, int32_t dtype, void *dx,
                      void *dgamma, void *dbeta, void *dbias, int32_t dparam_dtype,
-                     void *workspace, size_t workspace_bytes, void *stream)
+                     void *workspace, size_t workspace_bytes, uint32_t flags, void *stream)
 {
     return bwd_common(false, dy, x, gamma, mean, rstd, 0.f, M, N, dtype, dx, dgamma, dbeta,
-                      dbias, dparam_dtype, workspace, workspace_bytes, stream);
+                      dbias, dparam_dtype, workspace, workspace_bytes, flags, stream);
 }
 
 norm_status_t rms_bwd(const void *dy, const void *x, const void *gamma, const float *rstd,
                       float eps, int64_t M, int64_t N, int32_t dtype, void *dx, void *dgamma,
                       void *dbeta, void *dbias, int32_t dparam_dtype, void *workspace,
-                      size_t workspace_bytes, void *stream)
+                      size_t workspace_bytes, uint32_t flags, void *stream)
 {
     return bwd_common(true, dy, x, gamma, nullptr, rstd, eps, M, N, dtype, dx, dgamma, dbeta,
-                      dbias, dparam_dtype, workspace, workspace_bytes, stream);
+                      dbias, dparam_dtype, workspace, workspace_bytes, flags, stream);
 }
 
 const char *norm_status_string(norm_status_t st)

@@ -17,7 +17,7 @@ hipError_t launch_zero_u32(unsigned *p, hipStream_t s)
 }
 
 hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma, void *dbeta,
-                         void *dbias, int out_dtype, float *level2, hipStream_t s)
+                         void *dbias, int out_dtype, float divisor, float *level2, hipStream_t s)
 {
     if (dgamma == nullptr && dbeta == nullptr && dbias == nullptr)
         return hipSuccess;
@@ -28,7 +28,7 @@ hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma
     const int slices = colsum_slices(parts);
     if (slices > 1) {
         hipLaunchKernelGGL((colsum_kernel<false, false>), dim3(tiles, slices, nb), block, 0, s,
-                           ws, parts, N, COLSUM_SPAN, level2, nullptr, nullptr, nullptr);
+                           ws, parts, N, COLSUM_SPAN, level2, nullptr, nullptr, nullptr, 1.f);
         if (hipError_t e = hipGetLastError())
             return e;
         src = level2;
@@ -36,10 +36,10 @@ hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma
     }
     if (out_dtype == 1)
         hipLaunchKernelGGL((colsum_kernel<true, true>), dim3(tiles, 1, nb), block, 0, s, src,
-                           rows, N, rows, nullptr, dgamma, dbeta, dbias);
+                           rows, N, rows, nullptr, dgamma, dbeta, dbias, divisor);
     else
         hipLaunchKernelGGL((colsum_kernel<true, false>), dim3(tiles, 1, nb), block, 0, s, src,
-                           rows, N, rows, nullptr, dgamma, dbeta, dbias);
+                           rows, N, rows, nullptr, dgamma, dbeta, dbias, divisor);
     return hipGetLastError();
 }
 

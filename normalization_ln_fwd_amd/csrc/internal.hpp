@@ -22,6 +22,7 @@ struct FwdArgs {
     int N;
     int K, A;
     float eps;
+    bool zero_centred; // weight = round_T(1 + gamma)
 };
 
 // Arguments of one backward stage-1 call.  `ws` holds the per-workgroup
@@ -36,6 +37,7 @@ struct BwdArgs {
     int N;
     int K, A;
     float eps;
+    bool zero_centred; // weight = round_T(1 + gamma)
 };
 
 typedef hipError_t (*FwdLaunch)(const FwdArgs &, int grid, hipStream_t);
@@ -77,8 +79,8 @@ constexpr int WIDE_LPR = 128;
 hipError_t launch_zero_u32(unsigned *p, hipStream_t s);
 // Column sums of the stage-1 partials (nb blocks -- dgamma, dbeta and, when
 // nb = 3, dbias -- of `parts` rows of N floats at ws); writes the outputs
-// given (each optional) in fp32 (out_dtype 0) or bf16 (1).  parts = 0
-// writes zeros.  More than COLSUM_SPAN parts are summed in two launches:
+// given (each optional), divided by `divisor`, in fp32 (out_dtype 0) or
+// bf16 (1).  parts = 0 writes zeros.  More than COLSUM_SPAN parts are summed in two launches:
 // colsum_slices(parts) slice sums go to `level2` (nb blocks of that many
 // rows of N floats), then a final launch adds them.
 constexpr int COLSUM_SPAN = 512;
@@ -87,6 +89,6 @@ inline int colsum_slices(int64_t parts)
     return parts <= COLSUM_SPAN ? 1 : int((parts + COLSUM_SPAN - 1) / COLSUM_SPAN);
 }
 hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma, void *dbeta,
-                         void *dbias, int out_dtype, float *level2, hipStream_t s);
+                         void *dbias, int out_dtype, float divisor, float *level2, hipStream_t s);
 
 } // namespace nf

@@ -143,6 +143,18 @@ __device__ __forceinline__ double team_sum_f64(double v, double *lds, int &parit
 // ---------------------------------------------------------------------------
 constexpr int PARAMS_LDS_MAX = 4096;
 
+// The weight of a zero-centred gamma, w = 1 + gamma, formed in fp32 and
+// rounded to the I/O dtype (as a weight tensor holding it would be).
+template <typename T, int VEC>
+__device__ __forceinline__ typename VecIO<T, VEC>::Raw plus_one(const float *g)
+{
+    float w[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+        w[e] = 1.f + g[e];
+    return VecIO<T, VEC>::pack(w);
+}
+
 // Staging of one per-column vector into LDS (fp32, `neutral` beyond N or
 // where absent) in two phases, so that the workgroup's first row loads go out
 // between them: fetch() issues this thread's loads, put() converts and
@@ -163,8 +175,10 @@ struct ParamStage {
                                                           : BUF_OOB);
         }
     }
+    // zero_centred: store round_T(1 + v) (the weight of a zero-centred
+    // gamma; 1 where absent)
     __device__ __forceinline__ void put(float *dst, const void *src, int N, float neutral,
-                                        int tid) const
+                                        int tid, bool zero_centred = false) const
     {
 #pragma unroll
         for (int i = 0; i < SI; ++i) {
@@ -172,6 +186,8 @@ struct ParamStage {
             if (c < CAP) {
                 float v[VEC];
                 VecIO<T, VEC>::unpack(r[i], v);
+                if (zero_centred)
+                    VecIO<T, VEC>::unpack(plus_one<T, VEC>(v), v);
                 const bool ok = src != nullptr && c < N;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
@@ -181,11 +197,12 @@ struct ParamStage {
     }
 };
 
-// This lane's VPL vectors of a per-column vector (registers, packed).
+// This lane's VPL vectors of a per-column vector (registers, packed);
+// zero_centred: the weight round_T(1 + gamma) instead (1 where absent).
 template <typename T, int VEC, int VPL>
 __device__ __forceinline__ void load_param_regs(typename VecIO<T, VEC>::Raw (&dst)[VPL],
                                                 const void *src, int N, const uint32_t (&poff)[VPL],
-                                                bool ones_if_absent)
+                                                bool ones_if_absent, bool zero_centred = false)
 {
     using IO = VecIO<T, VEC>;
     if (src == nullptr && ones_if_absent) {
@@ -200,8 +217,14 @@ __device__ __forceinline__ void load_param_regs(typename VecIO<T, VEC>::Raw (&ds
     }
     const rsrc_t r = make_rsrc(src, src ? uint32_t(N) * uint32_t(sizeof(T)) : 0u);
 #pragma unroll
-    for (int k = 0; k < VPL; ++k)
+    for (int k = 0; k < VPL; ++k) {
         dst[k] = BufIO<T, VEC>::load_cached(r, poff[k]);
+        if (zero_centred) {
+            float v[VEC];
+            IO::unpack(dst[k], v);
+            dst[k] = plus_one<T, VEC>(v); // columns past N are never used
+        }
+    }
 }
 
 // VEC values of a per-column vector at column c0: from LDS when staged, else
@@ -285,7 +308,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         if (PREFETCH)
             issue(walk.group(0));
         sb.put(par, a.bias, N, 0.f, tid);
-        sg.put(par + CAP, a.gamma, N, 1.f, tid);
+        sg.put(par + CAP, a.gamma, N, 1.f, tid, a.zero_centred);
         se.put(par + 2 * CAP, a.beta, N, 0.f, tid);
         __syncthreads();
     } else {
@@ -294,7 +317,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         for (int k = 0; k < VPL; ++k)
             poff[k] = cvalid[k] ? uint32_t((k * LPR + tl) * VEC) * uint32_t(sizeof(T)) : BUF_OOB;
         load_param_regs<T, VEC, VPL>(pbias, a.bias, N, poff, false);
-        load_param_regs<T, VEC, VPL>(pgam, a.gamma, N, poff, true);
+        load_param_regs<T, VEC, VPL>(pgam, a.gamma, N, poff, true, a.zero_centred);
         load_param_regs<T, VEC, VPL>(pbeta, a.beta, N, poff, false);
         if (PREFETCH)
             issue(walk.group(0));
@@ -591,14 +614,14 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
         sg.fetch(a.gamma, N, tid);
         if (PIPE)
             issue(walk.group(0), A);
-        sg.put(par, a.gamma, N, 1.f, tid);
+        sg.put(par, a.gamma, N, 1.f, tid, a.zero_centred);
         __syncthreads();
     } else {
         uint32_t poff[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k)
             poff[k] = cvalid[k] ? uint32_t((k * LPR + tl) * VEC) * uint32_t(sizeof(T)) : BUF_OOB;
-        load_param_regs<T, VEC, VPL>(pgam, a.gamma, N, poff, true);
+        load_param_regs<T, VEC, VPL>(pgam, a.gamma, N, poff, true, a.zero_centred);
         if (PIPE)
             issue(walk.group(0), A);
     }
@@ -823,7 +846,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 // its 64 columns:
 // thread (c, t) takes rows t, t + 16, ... of the slice in ascending order,
 // and the sixteen threads of a column are added in order t = 0..15.  FINAL: one
-// slice; down-cast and store to dgamma / dbeta / dbias.  Otherwise slice s
+// slice; divide by `divisor` (1, or M for the mean over the rows), down-cast
+// and store to dgamma / dbeta / dbias.  Otherwise slice s
 // stores its sums as row s of dst (blocks of gridDim.y rows), which a FINAL
 // launch then adds the same way.  Every addition happens in a fixed order.
 // (A one-launch variant that lets the last workgroup finish needs a
@@ -836,7 +860,7 @@ constexpr int COLSUM_SUB = 16;
 template <bool FINAL, bool BF16_OUT>
 __global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SUB)
     colsum_kernel(const float *src, int rows, int N, int span, float *dst, void *dgamma,
-                  void *dbeta, void *dbias)
+                  void *dbeta, void *dbias, float divisor)
 {
     const int tx = threadIdx.x % COLSUM_COLS;
     const int ty = threadIdx.x / COLSUM_COLS;
@@ -863,6 +887,8 @@ __global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SUB)
 #pragma unroll
         for (int q = 1; q < COLSUM_SUB; ++q)
             t += sl[q][tx];
+        if constexpr (FINAL)
+            t = t / divisor; // 1, or M for the row mean
         if constexpr (!FINAL) {
             dst[((int64_t)which * gridDim.y + s) * N + j] = t;
         } else if constexpr (BF16_OUT) {

@@ -66,10 +66,10 @@ def test_status_strings(lib):
 
 def fwd_args(**over):
     a = dict(x=P, bias=None, residual=None, gamma=P, beta=P, eps=1e-5, M=4, N=64, dtype=1,
-             y=P, residual_out=None, mean=P, rstd=P, amax=None, stream=None)
+             y=P, residual_out=None, mean=P, rstd=P, amax=None, flags=0, stream=None)
     a.update(over)
     return [a[k] for k in ("x", "bias", "residual", "gamma", "beta", "eps", "M", "N", "dtype",
-                           "y", "residual_out", "mean", "rstd", "amax", "stream")]
+                           "y", "residual_out", "mean", "rstd", "amax", "flags", "stream")]
 
 
 @pytest.mark.parametrize("fn", ["ln_fwd", "rms_fwd"])
@@ -101,17 +101,17 @@ def test_no_rows_allows_null_row_tensors(lib):
 
 def fwd8_args(**over):
     a = dict(x=P, bias=None, res=None, gamma=None, beta=None, eps=1e-5, M=4, N=64, dtype=1,
-             scale=P, y=P, res_out=None, mean=None, rstd=None, amax=None, stream=None)
+             scale=P, y=P, res_out=None, mean=None, rstd=None, amax=None, flags=0, stream=None)
     a.update(over)
     return [a[k] for k in ("x", "bias", "res", "gamma", "beta", "eps", "M", "N", "dtype",
-                           "scale", "y", "res_out", "mean", "rstd", "amax", "stream")]
+                           "scale", "y", "res_out", "mean", "rstd", "amax", "flags", "stream")]
 
 
 @pytest.mark.parametrize("fn", ["ln_fwd_fp8", "rms_fwd_fp8"])
 @pytest.mark.parametrize("over,code", [
     (dict(dtype=2), 4), (dict(scale=None), 1), (dict(y=None), 1), (dict(x=None), 1),
     (dict(N=0), 2), (dict(eps=-1.0), 3), (dict(scale=BAD2), 5), (dict(x=BAD1), 5),
-    (dict(amax=BAD2), 5),
+    (dict(amax=BAD2), 5), (dict(flags=2), 3), (dict(flags=8), 3),
 ])
 def test_fp8_forward_rejects(lib, fn, over, code):
     assert getattr(lib, fn)(*fwd8_args(**over)) == code
@@ -125,17 +125,32 @@ def test_fp8_forward_takes_any_output_alignment(lib):
     assert lib.ln_fwd_fp8(*fwd8_args(y=P + 1)) == 8
 
 
+@pytest.mark.parametrize("fn", ["ln_fwd", "rms_fwd"])
+def test_forward_rejects_unknown_or_backward_flags(lib, fn):
+    extra = dict(mean=None) if fn == "rms_fwd" else {}
+    assert getattr(lib, fn)(*fwd_args(flags=2, **extra)) == 3   # a backward-only option
+    assert getattr(lib, fn)(*fwd_args(flags=16, **extra)) == 3
+
+
+def test_binding_option_bits_match_header():
+    text = open(HEADER).read()
+    assert int(re.search(r"#define NORM_ZERO_CENTERED_GAMMA (\d+)u", text).group(1)) == \
+        nf.ZERO_CENTERED_GAMMA
+    assert int(re.search(r"#define NORM_DPARAM_MEAN (\d+)u", text).group(1)) == nf.DPARAM_MEAN
+
+
 def test_rms_forward_takes_no_mean(lib):
     assert lib.rms_fwd(*fwd_args(mean=P)) == 3
 
 
 def bwd_args(fn, **over):
     a = dict(dy=P, x=P, gamma=P, mean=P, rstd=P, eps=1e-6, M=4, N=64, dtype=1, dx=P,
-             dgamma=P, dbeta=P, dbias=None, pdtype=0, ws=P, ws_bytes=1 << 20, stream=None)
+             dgamma=P, dbeta=P, dbias=None, pdtype=0, ws=P, ws_bytes=1 << 20, flags=0,
+             stream=None)
     a.update(over)
     keys = ["dy", "x", "gamma"] + (["mean", "rstd"] if fn == "ln_bwd" else ["rstd", "eps"]) + [
         "M", "N", "dtype", "dx", "dgamma", "dbeta", "dbias", "pdtype", "ws", "ws_bytes",
-        "stream"]
+        "flags", "stream"]
     return [a[k] for k in keys]
 
 
@@ -147,6 +162,7 @@ def bwd_args(fn, **over):
     (dict(dy=BAD1), 5), (dict(dx=BAD1), 5), (dict(rstd=BAD2), 5), (dict(ws=BAD2), 5),
     (dict(pdtype=0, dgamma=BAD2), 5), (dict(pdtype=1, dbeta=BAD1), 5),
     (dict(pdtype=0, dbias=BAD2), 5), (dict(pdtype=1, dbias=BAD1), 5),
+    (dict(flags=4), 3), (dict(flags=0x80000000), 3),
 ])
 def test_backward_rejects(lib, fn, over, code):
     assert getattr(lib, fn)(*bwd_args(fn, **over)) == code
