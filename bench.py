@@ -306,6 +306,9 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
                                                         want_amax=True, out=fp8_out),
         M * (7 * N + 8), False)
     del y8
+    rec("ln_fwd_576000x384_zero_centered", lambda: nf.ln_fwd(
+        d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 1e-5, want_amax=True,
+        zero_centered_gamma=True, out=fwd_out), fwd_bytes(M, N), False)
     rms_out = {"y": fwd_out["y"], "residual_out": fwd_out["residual_out"],
                "rstd": fwd_out["rstd"], "amax": fwd_out["amax"]}
     rec("rms_fwd_576000x384", lambda: nf.rms_fwd(d["x"], d["bias"], d["residual"], d["gamma"],
@@ -328,6 +331,10 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
         d["dy"], d["x"], d["gamma"], fwd_out["mean"], fwd_out["rstd"],
         dparam_dtype=torch.bfloat16, workspace=ws,
         out={"dx": dx, "dgamma": dg, "dbeta": db, "dbias": dbias}), bwd_bytes(M, N), False)
+    rec("ln_bwd_576000x384_mean", lambda: nf.ln_bwd(
+        d["dy"], d["x"], d["gamma"], fwd_out["mean"], fwd_out["rstd"],
+        dparam_dtype=torch.bfloat16, dparam_mean=True, workspace=ws,
+        out={"dx": dx, "dgamma": dg, "dbeta": db}), bwd_bytes(M, N), False)
     del dx
     # config 2 (launch-bound size): consecutive calls take consecutive
     # 4096-row slices of the large tensors
