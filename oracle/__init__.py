@@ -27,6 +27,9 @@ Parity status of each function (what pins it, in ``tests/test_oracle.py``):
                            float64 autograd of dx / dgamma through w = 1 + gamma.
   dparam_mean           -- pinned: the closed form of dbeta's row mean with a
                            row-constant dy, and the sums over M rows / M.
+  softmax_fwd           -- pinned: torch's float64 softmax, rows summing to 1,
+                           shift invariance, the two-element closed form, a
+                           constant row (1/N) and a large row offset.
   quantize_e4m3         -- pinned: torch's float8_e4m3fn cast on every code,
                            every midpoint and its neighbours and random
                            in-range values; the format's fixed codes
@@ -71,6 +74,8 @@ def _load():
         lib.oracle_round_to_dtype.restype = ci
         lib.oracle_quantize_e4m3.argtypes = [vp, i64, ctypes.c_float, vp]
         lib.oracle_quantize_e4m3.restype = ci
+        lib.oracle_softmax_fwd.argtypes = [vp, i64, i64, ci, ci, vp]
+        lib.oracle_softmax_fwd.restype = ci
         _lib = lib
     return _lib
 
@@ -190,6 +195,18 @@ def quantize_e4m3(v, scale):
     if lib.oracle_quantize_e4m3(_ptr(v), v.size, float(np.float32(scale)), _ptr(out)) != 0:
         raise ValueError("oracle_quantize_e4m3 rejected its arguments")
     return out
+
+
+def softmax_fwd(x, *, dtype=BF16, nthreads=None):
+    """Row softmax of an (M, N) matrix in the I/O dtype: float64 (M, N),
+    unrounded."""
+    lib = _load()
+    x = _in(x, dtype, name="x")
+    M, N = x.shape
+    y = np.empty((M, N), np.float64)
+    if lib.oracle_softmax_fwd(_ptr(x), M, N, dtype, nthreads or default_threads(), _ptr(y)) != 0:
+        raise ValueError("oracle_softmax_fwd rejected its arguments")
+    return y
 
 
 def bf16_bits_to_f64(a):

@@ -522,3 +522,49 @@ int oracle_quantize_e4m3(const float *v, int64_t n, float scale, uint8_t *out)
     }
     return 0;
 }
+
+/* ------------------------------------------------------------- softmax */
+
+/*
+ * Row softmax, the other normalisation IREE issue #9139 ("Investigate a
+ * fusion opportunity on Layer Normalization") fuses into one dispatch in its
+ * softmax walk-through: per row, the max, the sum of exp(x - max), and the
+ * division:
+ *   y_ij = exp(x_ij - max_k x_ik) / sum_k exp(x_ik - max_k x_ik)
+ * Subtracting the row max leaves y unchanged and keeps exp in range.
+ */
+typedef struct {
+    const void *x;
+    int dtype;
+    int64_t N;
+    double *y;
+} smx_ctx;
+
+static void smx_rows(void *vctx, int64_t r0, int64_t r1)
+{
+    smx_ctx *c = (smx_ctx *)vctx;
+    const int64_t N = c->N;
+    for (int64_t i = r0; i < r1; ++i) {
+        double m = -INFINITY;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = elem(c->x, c->dtype, i * N + j);
+            if (v > m)
+                m = v;
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < N; ++j)
+            s += exp(elem(c->x, c->dtype, i * N + j) - m);
+        for (int64_t j = 0; j < N; ++j)
+            c->y[i * N + j] = exp(elem(c->x, c->dtype, i * N + j) - m) / s;
+    }
+}
+
+/* y [M,N] (double, unrounded) = row softmax of x [M,N] (finite values). */
+int oracle_softmax_fwd(const void *x, int64_t M, int64_t N, int dtype, int nthreads, double *y)
+{
+    if (!x || !y || M < 0 || N <= 0 || (dtype != OR_F32 && dtype != OR_BF16))
+        return -1;
+    smx_ctx c = {x, dtype, N, y};
+    parallel_ranges(nthreads, M, smx_rows, &c);
+    return 0;
+}

@@ -614,3 +614,36 @@ def test_dparam_mean_divides_by_rows(oracle_mod):
     for k in ("dgamma", "dbeta", "dbias", "dgamma_l2", "dbeta_l2", "dbias_l2"):
         np.testing.assert_allclose(m[k], s[k] / M, rtol=1e-15, atol=0)
     np.testing.assert_array_equal(m["dx"], s["dx"])
+
+
+# ------------------------------------------------------------- softmax
+
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_softmax_matches_torch_and_sums_to_one(oracle_mod, dtype):
+    M, N = 21, 67
+    inp = synth.make_inputs(M, N, dtype=dtype, seed=20, names=("x",))
+    y = oracle_mod.softmax_fwd(inp["x"], dtype=dtype)
+    xd = synth.to_f64(inp["x"], dtype)
+    ref = torch.softmax(t64(xd), dim=1).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(y.sum(1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_softmax_closed_forms(oracle_mod):
+    # two elements: y0 = 1 / (1 + e^(b - a))
+    x = f32([[1.5, -0.25], [0.0, 0.0], [3.0, 3.0]])
+    y = oracle_mod.softmax_fwd(x, dtype=F32)
+    np.testing.assert_allclose(y[0, 0], 1.0 / (1.0 + math.exp(-1.75)), rtol=1e-15)
+    np.testing.assert_array_equal(y[1], [0.5, 0.5])
+    # a constant row is uniform: 1 / N
+    c = f32(np.full((2, 10), -7.25))
+    np.testing.assert_allclose(oracle_mod.softmax_fwd(c, dtype=F32), 0.1, rtol=1e-15)
+
+
+def test_softmax_shift_invariance_and_large_offsets(oracle_mod):
+    rng = np.random.default_rng(21)
+    x = dyadic(rng, (6, 40))
+    y0 = oracle_mod.softmax_fwd(x, dtype=F32)
+    for c in (1000.0, -1000.0, 60000.0):
+        y = oracle_mod.softmax_fwd(f32(x + np.float32(c)), dtype=F32)
+        np.testing.assert_allclose(y, y0, rtol=1e-12, atol=1e-300)

@@ -65,6 +65,11 @@ MUTANTS = [
      "double g = elem(c->dy, c->dtype, i * N + j) *\n                       weight_of(c->gamma, c->dtype, c->zero_centered, j);\n            s_gx",
      "double g = elem(c->dy, c->dtype, i * N + j) *\n                       elem_or(c->gamma, c->dtype, j, 1.0);\n            s_gx"),
     ("mean epilogue divides by N", "outs[k][j] /= (double)M;", "outs[k][j] /= (double)N;"),
+    ("softmax sum skips the first column", "for (int64_t j = 0; j < N; ++j)\n            s += exp(",
+     "for (int64_t j = 1; j < N; ++j)\n            s += exp("),
+    ("softmax numerator without the max",
+     "c->y[i * N + j] = exp(elem(c->x, c->dtype, i * N + j) - m) / s;",
+     "c->y[i * N + j] = exp(elem(c->x, c->dtype, i * N + j)) / s;"),
     ("dbias skips the last row", "for (int64_t i = 0; i < c->M; ++i) {\n            double t = c->dx",
      "for (int64_t i = 0; i + 1 < c->M; ++i) {\n            double t = c->dx"),
 ]
