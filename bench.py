@@ -336,6 +336,10 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
         dparam_dtype=torch.bfloat16, dparam_mean=True, workspace=ws,
         out={"dx": dx, "dgamma": dg, "dbeta": db}), bwd_bytes(M, N), False)
     del dx
+    # row softmax on the same rows (x in, y out, bf16)
+    smx = torch.empty_like(d["x"])
+    rec("softmax_fwd_576000x384", lambda: nf.softmax_fwd(d["x"], out=smx), M * 4 * N, False)
+    del smx
     # config 2 (launch-bound size): consecutive calls take consecutive
     # 4096-row slices of the large tensors
     M2 = 4096

@@ -184,6 +184,20 @@ norm_status_t rms_fwd_fp8(const void *x, const void *bias, const void *residual,
                           void *stream);
 
 /*
+ * softmax_fwd -- row softmax in one read of x: per row, the max, the sum of
+ * exp(x - max), and y = exp(x - max) / sum.  The other normalisation IREE
+ * issue #9139 ("Investigate a fusion opportunity on Layer Normalization")
+ * walks through fusing into a single dispatch; here it runs on the same
+ * row kernels as the LayerNorm forward.
+ *   x            [M,N] dtype   required (finite values)
+ *   y            [M,N] dtype   required
+ *   flags        0 (reserved)
+ * Conventions as above (M = 0: nothing to do).
+ */
+norm_status_t softmax_fwd(const void *x, int64_t M, int64_t N, int32_t dtype, void *y,
+                          uint32_t flags, void *stream);
+
+/*
  * norm_bwd_workspace_size -- bytes of device workspace ln_bwd / rms_bwd need
  * for an [M, N] problem of the given dtype on the current device (the
  * per-workgroup dgamma / dbeta / dbias column partials; the size covers a

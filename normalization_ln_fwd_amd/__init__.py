@@ -9,8 +9,13 @@ library, importing works but every call raises ``NormLibraryMissing``.
 Operations (definitions in ``include/normfuse.h``):
   ln_fwd / rms_fwd   fused (bias +) residual + LayerNorm / RMSNorm forward
                      with optional residual_out, mean / rstd and amax
+  ln_fwd_fp8 / rms_fwd_fp8
+                     the same forward with y as FP8 E4M3 codes of y * scale
   ln_bwd / rms_bwd   backward: dx plus dgamma / dbeta (and optionally dbias)
                      from one read of dy, x
+  softmax_fwd        row softmax in one read of x
+Option keywords: ``zero_centered_gamma`` (forward and backward) and
+``dparam_mean`` (backward).
 """
 import ctypes
 import os
@@ -19,8 +24,9 @@ import torch
 
 from .build import LIB as _LIB_PATH
 
-__all__ = ["ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "bwd_workspace_size", "NormError",
-           "NormLibraryMissing", "library", "F32", "BF16", "N_MAX"]
+__all__ = ["ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd", "softmax_fwd",
+           "bwd_workspace_size", "NormError", "NormLibraryMissing", "library", "F32", "BF16",
+           "N_MAX", "ZERO_CENTERED_GAMMA", "DPARAM_MEAN"]
 
 F32 = 0
 BF16 = 1
@@ -32,7 +38,7 @@ ZERO_CENTERED_GAMMA = 1  # option bits of include/normfuse.h
 DPARAM_MEAN = 2
 
 EXPORTS = ("ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd",
-           "norm_bwd_workspace_size", "norm_status_string")
+           "softmax_fwd", "norm_bwd_workspace_size", "norm_status_string")
 
 
 class NormLibraryMissing(RuntimeError):
@@ -70,6 +76,7 @@ def library():
                                u32, vp]
         lib.rms_bwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
                                 u32, vp]
+        lib.softmax_fwd.argtypes = [vp, i64, i64, i32, vp, u32, vp]
         lib.norm_bwd_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
         lib.norm_status_string.argtypes = [i32]
         lib.norm_status_string.restype = ctypes.c_char_p
@@ -202,6 +209,18 @@ def rms_fwd_fp8(x, y_scale, bias=None, residual=None, gamma=None, beta=None, eps
         want_residual_out = bias is not None or residual is not None
     return _fwd("rms_fwd_fp8", x, bias, residual, gamma, beta, eps, want_residual_out, False,
                 want_stats, want_amax, stream, out, y_scale, zero_centered_gamma)
+
+
+def softmax_fwd(x, *, stream=None, out=None):
+    """Row softmax over the last dimension of ``x`` (bf16 or fp32), one read
+    of x: returns y of x's shape and dtype (``out`` may supply it)."""
+    lib = library()
+    N = x.shape[-1]
+    M = x.numel() // N if N else 0
+    y = out if out is not None else torch.empty_like(x)
+    _check("softmax_fwd", lib.softmax_fwd(_ptr(x, "x"), M, N, _dtype_code(x),
+                                          _ptr(y, "y", x.dtype, M * N), 0, _stream(stream)))
+    return y
 
 
 def bwd_workspace_size(M, N, dtype):

@@ -271,6 +271,58 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     return launched(run(a, int(w.grid), s));
 }
 
+// ------------------------------------------------------------------ softmax
+norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype, void *y,
+                             uint32_t flags, void *stream)
+{
+    if (!dtype_ok(dtype))
+        return NORM_ERR_DTYPE;
+    if (norm_status_t st = check_shape(M, N))
+        return st;
+    if (M > 0 && (!x || !y))
+        return NORM_ERR_NULL;
+    if (flags != 0)
+        return NORM_ERR_ARG;
+    const size_t es = elem_size(dtype);
+    for (const void *p : {x, (const void *)y})
+        if (p && !aligned(p, es))
+            return NORM_ERR_ALIGN;
+    if (norm_status_t st = check_device())
+        return st;
+    if (M == 0)
+        return NORM_OK;
+    const Knobs kn = knobs();
+    const bool vec = vectorisable(N, dtype, {x, y});
+    int n = 0;
+    const SoftmaxEntry *tab =
+        dtype == NORM_F32 ? softmax_table_f32(vec, &n) : softmax_table_bf16(vec, &n);
+    const SoftmaxEntry *e = pick_shape(tab, n, int(N), 0, 0, 0);
+    if (!e)
+        return NORM_ERR_SHAPE;
+    // the 512-thread variant of a narrow shape when rows are plentiful
+    for (int i = 0; i < n; ++i) {
+        const RowShape &w = tab[i].shape;
+        if (w.lpr == e->shape.lpr && w.vpl == e->shape.vpl && w.teams == 2 * e->shape.teams &&
+            (M + w.teams - 1) / w.teams >= kMinWideGroups) {
+            e = &tab[i];
+            break;
+        }
+    }
+    Walk w;
+    const int K = e->shape.lpr >= WIDE_LPR ? kFwdGroupsWide : 1;
+    if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
+        return st;
+    SoftmaxArgs a;
+    a.x = x;
+    a.y = y;
+    a.M = M;
+    a.n_groups = w.n_groups;
+    a.N = int(N);
+    a.K = w.K;
+    a.A = w.A;
+    return launched(e->run(a, int(w.grid), static_cast<hipStream_t>(stream)));
+}
+
 // ----------------------------------------------------------------- backward
 // Stage-1 walk of the backward for the shape used on these pointers, and
 // the workspace it needs: the stage-1 partials (nb blocks of `grid` rows of
@@ -414,6 +466,12 @@ norm_status_t rms_fwd_fp8(const void *x, const void *bias, const void *residual,
 {
     return fwd_common(true, x, bias, residual, gamma, beta, eps, M, N, dtype, y_scale, y_fp8,
                       residual_out, mean, rstd, amax, true, flags, stream);
+}
+
+norm_status_t softmax_fwd(const void *x, int64_t M, int64_t N, int32_t dtype, void *y,
+                          uint32_t flags, void *stream)
+{
+    return softmax_common(x, M, N, dtype, y, flags, stream);
 }
 
 norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_t *bytes)

@@ -63,6 +63,23 @@ struct BwdEntry {
     BwdLaunch ln_db, rms_db; // also the dbias partials
 };
 
+// Arguments of one row-softmax call.
+struct SoftmaxArgs {
+    const void *x;
+    void *y;
+    int64_t M;
+    int64_t n_groups;
+    int N;
+    int K, A;
+};
+typedef hipError_t (*SoftmaxLaunch)(const SoftmaxArgs &, int grid, hipStream_t);
+struct SoftmaxEntry {
+    RowShape shape;
+    SoftmaxLaunch run;
+};
+const SoftmaxEntry *softmax_table_f32(bool vectorised, int *count);
+const SoftmaxEntry *softmax_table_bf16(bool vectorised, int *count);
+
 // Tables of instantiated shapes, ordered by capacity; vectorised = 16-byte
 // accesses (else element-wise).  One translation unit per dtype/direction.
 const FwdEntry *fwd_table_f32(bool vectorised, int *count);

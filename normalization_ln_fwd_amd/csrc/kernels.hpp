@@ -69,22 +69,23 @@ __device__ __forceinline__ float row_stat(const float *v, const RowGroup &rg, in
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, team * 4, 0, 0));
 }
 
-// Sum over a team.  LPR <= 64: inside the wave.  LPR > 64: wave partials
-// meet in LDS (double-buffered by `parity`, so one barrier per reduction
-// suffices) and are added in wave order.  NV values are reduced together.
-template <int LPR, int TEAMS, int NV>
-__device__ __forceinline__ void team_sum(float (&v)[NV], float *lds, int &parity, int team,
-                                         int wave_in_team, int lane)
+// Reduction (Op: sum or max) over a team.  LPR <= 64: inside the wave.
+// LPR > 64: wave partials meet in LDS (double-buffered by `parity`, so one
+// barrier per reduction suffices) and are combined in wave order.  NV values
+// are reduced together.
+template <int LPR, int TEAMS, int NV, class Op>
+__device__ __forceinline__ void team_reduce(float (&v)[NV], float *lds, int &parity, int team,
+                                            int wave_in_team, int lane)
 {
     if constexpr (LPR <= 64) {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            v[i] = group_reduce<LPR, OpSum>(v[i]);
+            v[i] = group_reduce<LPR, Op>(v[i]);
     } else {
         constexpr int WPT = LPR / 64;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-            v[i] = group_reduce<64, OpSum>(v[i]);
+            v[i] = group_reduce<64, Op>(v[i]);
         float *b = lds + parity * (TEAMS * WPT * NV);
         if (lane == 0) {
 #pragma unroll
@@ -97,11 +98,18 @@ __device__ __forceinline__ void team_sum(float (&v)[NV], float *lds, int &parity
             float s = b[(team * WPT) * NV + i];
 #pragma unroll
             for (int w = 1; w < WPT; ++w)
-                s += b[(team * WPT + w) * NV + i];
+                s = Op::apply(s, b[(team * WPT + w) * NV + i]);
             v[i] = s;
         }
         parity ^= 1;
     }
+}
+
+template <int LPR, int TEAMS, int NV>
+__device__ __forceinline__ void team_sum(float (&v)[NV], float *lds, int &parity, int team,
+                                         int wave_in_team, int lane)
+{
+    team_reduce<LPR, TEAMS, NV, OpSum>(v, lds, parity, team, wave_in_team, lane);
 }
 
 template <int LPR, int TEAMS, int NV>
@@ -837,6 +845,101 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
                 pd[c] = col_lds[2 * CAP + c];
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Row softmax in one pass over HBM: per row group the rows are loaded once,
+// the team takes the row max, then sum_j exp(x_j - max) with the exponentials
+// kept in registers, and stores exp(x_j - max) / sum.
+// ---------------------------------------------------------------------------
+template <typename T, int VEC, int LPR, int VPL, int TEAMS>
+__global__ void __launch_bounds__(LPR *TEAMS) softmax_kernel(const SoftmaxArgs a)
+{
+    using IO = VecIO<T, VEC>;
+    using BIO = BufIO<T, VEC>;
+    using Raw = typename IO::Raw;
+    constexpr int WG = LPR * TEAMS;
+    static_assert(WG % 64 == 0, "workgroup of whole waves");
+
+    __shared__ float red_lds[TeamLds<LPR, TEAMS, 1>::size];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int team = tid / LPR;
+    const int tl = tid % LPR;
+    const int wave_in_team = LPR > 64 ? tl / 64 : 0;
+    const int N = a.N;
+
+    bool cvalid[VPL];
+    uint32_t off[VPL];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+        cvalid[k] = (k * LPR + tl) * VEC < N;
+        off[k] = cvalid[k] ? uint32_t(team * N + (k * LPR + tl) * VEC) * uint32_t(sizeof(T))
+                           : BUF_OOB;
+    }
+
+    int parity = 0;
+    const GroupWalk walk(a.K, a.A);
+    for (int kk = 0; kk < a.K; ++kk) {
+        const int64_t grp = walk.group(kk);
+        if (grp >= a.n_groups)
+            break; // uniform over the workgroup; later groups are larger
+        const RowGroup rg(grp, TEAMS, a.M, N, sizeof(T));
+        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + rg.byte0, rg.bytes);
+        Raw xr[VPL];
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+            xr[k] = BIO::load(xs, off[k]);
+
+        // row max (columns past N do not take part)
+        float m[1] = {-INFINITY};
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            if (cvalid[k]) {
+                float v[VEC];
+                IO::unpack(xr[k], v);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    m[0] = fmaxf(m[0], v[e]);
+            }
+        }
+        team_reduce<LPR, TEAMS, 1, OpMax>(m, red_lds, parity, team, wave_in_team, lane);
+
+        // exponentials and their sum
+        float ev[VPL][VEC];
+        float sum[1] = {0.f};
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float v[VEC];
+            IO::unpack(xr[k], v);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                ev[k][e] = cvalid[k] ? __expf(v[e] - m[0]) : 0.f;
+                sum[0] += ev[k][e];
+            }
+        }
+        team_sum<LPR, TEAMS, 1>(sum, red_lds, parity, team, wave_in_team, lane);
+        const float inv = 1.f / sum[0];
+
+        const rsrc_t ys = make_rsrc(static_cast<char *>(a.y) + rg.byte0, rg.bytes);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            float yv[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                yv[e] = ev[k][e] * inv;
+            BIO::store(ys, off[k], IO::pack(yv));
+        }
+    }
+}
+
+template <typename T, int VEC, int LPR, int VPL, int TEAMS>
+hipError_t launch_softmax(const SoftmaxArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((softmax_kernel<T, VEC, LPR, VPL, TEAMS>), dim3(grid), dim3(LPR * TEAMS),
+                       0, s, a);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -139,6 +139,16 @@ def test_binding_option_bits_match_header():
     assert int(re.search(r"#define NORM_DPARAM_MEAN (\d+)u", text).group(1)) == nf.DPARAM_MEAN
 
 
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=5), 4), (dict(x=None), 1), (dict(y=None), 1), (dict(N=0), 2),
+    (dict(M=-1), 2), (dict(flags=1), 3), (dict(x=BAD1), 5), (dict(dtype=0, y=BAD2), 5),
+])
+def test_softmax_rejects(lib, over, code):
+    a = dict(x=P, M=4, N=64, dtype=1, y=P, flags=0, stream=None)
+    a.update(over)
+    assert lib.softmax_fwd(*[a[k] for k in ("x", "M", "N", "dtype", "y", "flags", "stream")]) == code
+
+
 def test_rms_forward_takes_no_mean(lib):
     assert lib.rms_fwd(*fwd_args(mean=P)) == 3
 
