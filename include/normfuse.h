@@ -222,8 +222,8 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
  *                              receive dx itself
  *   dparam_dtype NORM_F32 or NORM_BF16: dgamma / dbeta / dbias are summed in
  *                fp32 and rounded (to nearest, ties to even) to this type
- *   workspace    device memory of at least norm_bwd_workspace_size bytes
- *                (may be NULL when that size is 0)
+ *   workspace    device memory of at least norm_bwd_workspace_size bytes,
+ *                16-byte aligned (may be NULL when that size is 0)
  *   flags        NORM_ZERO_CENTERED_GAMMA and / or NORM_DPARAM_MEAN
  */
 norm_status_t ln_bwd(const void *dy, const void *x, const void *gamma, const float *mean,

@@ -326,7 +326,7 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
 // ----------------------------------------------------------------- backward
 // Stage-1 walk of the backward for the shape used on these pointers, and
 // the workspace it needs: the stage-1 partials (nb blocks of `grid` rows of
-// N floats: dgamma, dbeta, and dbias when asked for), then for many partial
+// colsum_ld(N) floats: dgamma, dbeta, and dbias when asked for), then for many partial
 // rows the second summation level (nb blocks of colsum_slices(grid) rows).
 struct BwdLayout {
     size_t level2_off = 0, bytes = 0; // in bytes
@@ -347,9 +347,9 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, int nb, co
     *entry = e;
     const int slices = colsum_slices(w->grid);
     lay->two_level = slices > 1;
-    lay->level2_off = size_t(nb) * size_t(w->grid) * size_t(N) * sizeof(float);
-    lay->bytes =
-        lay->level2_off + (lay->two_level ? size_t(nb) * size_t(slices) * size_t(N) * sizeof(float) : 0);
+    const size_t ld = size_t(colsum_ld(N));
+    lay->level2_off = size_t(nb) * size_t(w->grid) * ld * sizeof(float);
+    lay->bytes = lay->level2_off + (lay->two_level ? size_t(nb) * size_t(slices) * ld * sizeof(float) : 0);
     return NORM_OK;
 }
 
@@ -373,9 +373,11 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
     for (const void *p : {dy, x, gamma, (const void *)dx})
         if (p && !aligned(p, es))
             return NORM_ERR_ALIGN;
-    for (const void *p : {(const void *)mean, (const void *)rstd, (const void *)workspace})
+    for (const void *p : {(const void *)mean, (const void *)rstd})
         if (p && !aligned(p, 4))
             return NORM_ERR_ALIGN;
+    if (workspace && !aligned(workspace, 16)) // the column sums read 16-byte vectors
+        return NORM_ERR_ALIGN;
     const size_t ps = elem_size(dparam_dtype);
     for (const void *p : {(const void *)dgamma, (const void *)dbeta, (const void *)dbias})
         if (p && !aligned(p, ps))

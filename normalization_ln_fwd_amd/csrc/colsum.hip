@@ -22,7 +22,7 @@ hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma
     if (dgamma == nullptr && dbeta == nullptr && dbias == nullptr)
         return hipSuccess;
     const unsigned tiles = unsigned((N + COLSUM_COLS - 1) / COLSUM_COLS);
-    const dim3 block(COLSUM_COLS * COLSUM_SUB);
+    const dim3 block(COLSUM_QUADS * COLSUM_SUB);
     const float *src = ws;
     int rows = parts;
     const int slices = colsum_slices(parts);

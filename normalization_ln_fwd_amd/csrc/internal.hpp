@@ -95,15 +95,21 @@ constexpr int WIDE_LPR = 128;
 // Small kernels.
 hipError_t launch_zero_u32(unsigned *p, hipStream_t s);
 // Column sums of the stage-1 partials (nb blocks -- dgamma, dbeta and, when
-// nb = 3, dbias -- of `parts` rows of N floats at ws); writes the outputs
+// nb = 3, dbias -- of `parts` rows of colsum_ld(N) floats at ws); writes the outputs
 // given (each optional), divided by `divisor`, in fp32 (out_dtype 0) or
-// bf16 (1).  parts = 0 writes zeros.  More than COLSUM_SPAN parts are summed in two launches:
-// colsum_slices(parts) slice sums go to `level2` (nb blocks of that many
-// rows of N floats), then a final launch adds them.
-constexpr int COLSUM_SPAN = 512;
+// bf16 (1).  parts = 0 writes zeros.  Up to COLSUM_ONE_LAUNCH parts are
+// summed in one launch; more in two: colsum_slices(parts) sums of
+// COLSUM_SPAN rows each go to `level2` (nb blocks of that many rows of
+// colsum_ld(N) floats), then a final launch adds them.  The short slices give the first
+// launch enough workgroups to spread evenly over the CUs.
+// Row stride, in floats, of the partial rows in the workspace: N rounded up
+// to a multiple of 4, so that the column sums read 16-byte vectors.
+__host__ __device__ inline int64_t colsum_ld(int64_t N) { return (N + 3) & ~int64_t(3); }
+constexpr int COLSUM_ONE_LAUNCH = 512;
+constexpr int COLSUM_SPAN = 128;
 inline int colsum_slices(int64_t parts)
 {
-    return parts <= COLSUM_SPAN ? 1 : int((parts + COLSUM_SPAN - 1) / COLSUM_SPAN);
+    return parts <= COLSUM_ONE_LAUNCH ? 1 : int((parts + COLSUM_SPAN - 1) / COLSUM_SPAN);
 }
 hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma, void *dbeta,
                          void *dbias, int out_dtype, float divisor, float *level2, hipStream_t s);

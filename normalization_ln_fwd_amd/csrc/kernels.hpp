@@ -786,9 +786,10 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 
     // ---- fold the column partials of this workgroup, in a fixed order ----
     // Block b of the workspace (dgamma, dbeta, dbias) holds row blockIdx.x.
-    float *pg = a.ws + (int64_t)blockIdx.x * N;
-    float *pb = a.ws + (int64_t)gridDim.x * N + (int64_t)blockIdx.x * N;
-    float *pd = a.ws + 2 * (int64_t)gridDim.x * N + (int64_t)blockIdx.x * N;
+    const int64_t ld = colsum_ld(N);
+    float *pg = a.ws + (int64_t)blockIdx.x * ld;
+    float *pb = a.ws + (int64_t)gridDim.x * ld + (int64_t)blockIdx.x * ld;
+    float *pd = a.ws + 2 * (int64_t)gridDim.x * ld + (int64_t)blockIdx.x * ld;
     if constexpr (LPR < 64) {
         // teams of one wave cover the same columns: fold them first
 #pragma unroll
@@ -946,9 +947,10 @@ hipError_t launch_softmax(const SoftmaxArgs &a, int grid, hipStream_t s)
 // Backward stage 2: column sums of the partial rows.  src holds gridDim.z
 // blocks (dgamma, dbeta, dbias) of `rows` rows of N floats.  Workgroup
 // (column tile, slice s, block) adds rows [s*span, min(rows, (s+1)*span)) of
-// its 64 columns:
-// thread (c, t) takes rows t, t + 16, ... of the slice in ascending order,
-// and the sixteen threads of a column are added in order t = 0..15.  FINAL: one
+// its 64 columns (rows are padded to colsum_ld(N) floats, so each thread
+// reads 16-byte vectors of 4 columns): thread (q, t) takes rows t, t + 16,
+// ... of the slice in ascending order, and the sixteen threads of a column
+// are added in order t = 0..15.  FINAL: one
 // slice; divide by `divisor` (1, or M for the mean over the rows), down-cast
 // and store to dgamma / dbeta / dbias.  Otherwise slice s
 // stores its sums as row s of dst (blocks of gridDim.y rows), which a FINAL
@@ -957,47 +959,67 @@ hipError_t launch_softmax(const SoftmaxArgs &a, int grid, hipStream_t s)
 // device-scope release per workgroup, i.e. an L2 write-back each, which
 // costs more than the second launch.)
 // ---------------------------------------------------------------------------
-constexpr int COLSUM_COLS = 64;
-constexpr int COLSUM_SUB = 16;
+constexpr int COLSUM_COLS = 64; // columns per workgroup, 4 per thread
+constexpr int COLSUM_QUADS = COLSUM_COLS / 4;
+constexpr int COLSUM_SUB = 16;  // row subsets per workgroup
 
 template <bool FINAL, bool BF16_OUT>
-__global__ void __launch_bounds__(COLSUM_COLS *COLSUM_SUB)
+__global__ void __launch_bounds__(COLSUM_QUADS *COLSUM_SUB)
     colsum_kernel(const float *src, int rows, int N, int span, float *dst, void *dgamma,
                   void *dbeta, void *dbias, float divisor)
 {
-    const int tx = threadIdx.x % COLSUM_COLS;
-    const int ty = threadIdx.x / COLSUM_COLS;
+    const int tq = threadIdx.x % COLSUM_QUADS;
+    const int ty = threadIdx.x / COLSUM_QUADS;
     const int which = blockIdx.z;
     void *out = which == 0 ? dgamma : (which == 1 ? dbeta : dbias);
     if (FINAL && out == nullptr)
         return; // uniform over the block
-    const int j = blockIdx.x * COLSUM_COLS + tx;
+    const int64_t ld = colsum_ld(N);
+    const int j0 = blockIdx.x * COLSUM_COLS + tq * 4;
     const int s = blockIdx.y;
     const int r0 = s * span;
     const int r1 = min(rows, r0 + span);
-    const float *part = src + (int64_t)which * rows * N;
-    float acc = 0.f;
-    if (j < N) {
-#pragma unroll 16
-        for (int r = r0 + ty; r < r1; r += COLSUM_SUB)
-            acc += part[(int64_t)r * N + j];
+    const float *part = src + (int64_t)which * rows * ld;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (j0 < N) { // columns j0 .. j0+3 lie within the padded row of ld floats
+#pragma unroll 8
+        for (int r = r0 + ty; r < r1; r += COLSUM_SUB) {
+            const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)r * ld + j0);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
     }
-    __shared__ float sl[COLSUM_SUB][COLSUM_COLS];
-    sl[ty][tx] = acc;
+    __shared__ float4 sl[COLSUM_SUB][COLSUM_QUADS];
+    sl[ty][tq] = acc;
     __syncthreads();
-    if (ty == 0 && j < N) {
-        float t = sl[0][tx];
+    if (ty == 0 && j0 < N) {
+        float4 t = sl[0][tq];
 #pragma unroll
-        for (int q = 1; q < COLSUM_SUB; ++q)
-            t += sl[q][tx];
-        if constexpr (FINAL)
-            t = t / divisor; // 1, or M for the row mean
-        if constexpr (!FINAL) {
-            dst[((int64_t)which * gridDim.y + s) * N + j] = t;
-        } else if constexpr (BF16_OUT) {
-            static_cast<uint16_t *>(out)[j] = uint16_t(pack_bf16x2(t, 0.f) & 0xffffu);
-        } else {
-            static_cast<float *>(out)[j] = t;
+        for (int q = 1; q < COLSUM_SUB; ++q) {
+            const float4 u = sl[q][tq];
+            t.x += u.x;
+            t.y += u.y;
+            t.z += u.z;
+            t.w += u.w;
+        }
+        const float tv[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = j0 + e;
+            if (j >= N)
+                break;
+            float v = tv[e];
+            if constexpr (FINAL)
+                v = v / divisor; // 1, or M for the row mean
+            if constexpr (!FINAL) {
+                dst[((int64_t)which * gridDim.y + s) * ld + j] = v;
+            } else if constexpr (BF16_OUT) {
+                static_cast<uint16_t *>(out)[j] = uint16_t(pack_bf16x2(v, 0.f) & 0xffffu);
+            } else {
+                static_cast<float *>(out)[j] = v;
+            }
         }
     }
 }

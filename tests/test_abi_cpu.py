@@ -169,7 +169,7 @@ def bwd_args(fn, **over):
     (dict(dtype=3), 4), (dict(pdtype=7), 4),
     (dict(dy=None), 1), (dict(x=None), 1), (dict(dx=None), 1),
     (dict(M=-2), 2), (dict(N=0), 2), (dict(N=16385), 2),
-    (dict(dy=BAD1), 5), (dict(dx=BAD1), 5), (dict(rstd=BAD2), 5), (dict(ws=BAD2), 5),
+    (dict(dy=BAD1), 5), (dict(dx=BAD1), 5), (dict(rstd=BAD2), 5), (dict(ws=BAD2), 5), (dict(ws=P + 4), 5),
     (dict(pdtype=0, dgamma=BAD2), 5), (dict(pdtype=1, dbeta=BAD1), 5),
     (dict(pdtype=0, dbias=BAD2), 5), (dict(pdtype=1, dbias=BAD1), 5),
     (dict(flags=4), 3), (dict(flags=0x80000000), 3),
