@@ -121,7 +121,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--breakdown-iters", type=int, default=50)
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=M_BIG,
@@ -254,15 +254,23 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+WARM_S = 0.02  # untimed calls before each breakdown case, in seconds of GPU work
+
+
 def time_calls(fns, iters, torch):
-    """Microseconds per call in steady state: after 3 untimed calls, `iters`
-    calls run back to back between two events, cycling through fns (the same
-    operation on different buffers, so that small cases do not run out of
-    the 256 MB last-level cache).  Returns (per call over the whole run, best
-    of 5 equal slices, per call of the run)."""
+    """Microseconds per call in steady state: after untimed calls that keep
+    the GPU busy for WARM_S (after host-side work the GPU runs slower for a
+    few milliseconds), `iters` calls run back to back between two events,
+    cycling through fns (the same operation on different buffers, so that
+    small cases do not run out of the 256 MB last-level cache).  Returns (per
+    call over the whole run, best of 5 equal slices, per call of the run)."""
     stream = torch.cuda.current_stream().cuda_stream
-    for i in range(3):
-        fns[i % len(fns)]()
+    t0, n = time.perf_counter(), 0
+    while n < 10 or time.perf_counter() - t0 < WARM_S:
+        for _ in range(5):
+            fns[n % len(fns)]()
+            n += 1
+        torch.cuda.synchronize()
     slices = 5
     per = max(1, iters // slices)
     ev = HipEvents(slices + 1)

@@ -70,6 +70,9 @@
  *              _BWD_INTERLEAVE, read at every call, override those choices
  *              among the compiled shapes (for tuning; results stay within
  *              the same tolerances, but column sums may round differently).
+ *              NORMFUSE_WT_BYTES sets how many output bytes, counted from
+ *              the end of a call, are stored write-through instead of
+ *              nontemporal (a cache policy: values do not change).
  *   Alignment: pointers must be aligned to their element size.  16-byte
  *              aligned [M, N] / [N] pointers with N a multiple of 16 bytes'
  *              worth of elements take the vectorised kernels; anything else

@@ -16,30 +16,39 @@ hipError_t launch_zero_u32(unsigned *p, hipStream_t s)
     return hipGetLastError();
 }
 
+// Thread layouts of the column sums: the slices of many partial rows take
+// 64-column tiles of 16 row subsets; the final sums take 32-column tiles of
+// 128 subsets, so that a few hundred rows of a wide N spread over all CUs
+// with every thread's loads issued at once.
+constexpr int SLICE_QUADS = 16, SLICE_SUB = 16;
+constexpr int FINAL_QUADS = 8, FINAL_SUB = 128;
+
 hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma, void *dbeta,
                          void *dbias, int out_dtype, float divisor, float *level2, hipStream_t s)
 {
     if (dgamma == nullptr && dbeta == nullptr && dbias == nullptr)
         return hipSuccess;
-    const unsigned tiles = unsigned((N + COLSUM_COLS - 1) / COLSUM_COLS);
-    const dim3 block(COLSUM_QUADS * COLSUM_SUB);
     const float *src = ws;
     int rows = parts;
     const int slices = colsum_slices(parts);
     if (slices > 1) {
-        hipLaunchKernelGGL((colsum_kernel<false, false>), dim3(tiles, slices, nb), block, 0, s,
-                           ws, parts, N, COLSUM_SPAN, level2, nullptr, nullptr, nullptr, 1.f);
+        const unsigned tiles = unsigned((N + 4 * SLICE_QUADS - 1) / (4 * SLICE_QUADS));
+        hipLaunchKernelGGL((colsum_kernel<false, false, SLICE_QUADS, SLICE_SUB>),
+                           dim3(tiles, slices, nb), dim3(SLICE_QUADS * SLICE_SUB), 0, s, ws,
+                           parts, N, COLSUM_SPAN, level2, nullptr, nullptr, nullptr, 1.f);
         if (hipError_t e = hipGetLastError())
             return e;
         src = level2;
         rows = slices;
     }
+    const dim3 grid(unsigned((N + 4 * FINAL_QUADS - 1) / (4 * FINAL_QUADS)), 1, nb);
+    const dim3 block(FINAL_QUADS * FINAL_SUB);
     if (out_dtype == 1)
-        hipLaunchKernelGGL((colsum_kernel<true, true>), dim3(tiles, 1, nb), block, 0, s, src,
-                           rows, N, rows, nullptr, dgamma, dbeta, dbias, divisor);
+        hipLaunchKernelGGL((colsum_kernel<true, true, FINAL_QUADS, FINAL_SUB>), grid, block, 0, s,
+                           src, rows, N, rows, nullptr, dgamma, dbeta, dbias, divisor);
     else
-        hipLaunchKernelGGL((colsum_kernel<true, false>), dim3(tiles, 1, nb), block, 0, s, src,
-                           rows, N, rows, nullptr, dgamma, dbeta, dbias, divisor);
+        hipLaunchKernelGGL((colsum_kernel<true, false, FINAL_QUADS, FINAL_SUB>), grid, block, 0, s,
+                           src, rows, N, rows, nullptr, dgamma, dbeta, dbias, divisor);
     return hipGetLastError();
 }
 

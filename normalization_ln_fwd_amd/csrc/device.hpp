@@ -155,12 +155,19 @@ struct VecIO<float, 1> {
 // valid bytes of one row group (uniform, scalar registers); each lane adds a
 // 32-bit byte offset.  Accesses beyond the descriptor's range read 0 and
 // write nothing, so rows past M and columns past N need no predication: such
-// lanes use an offset past the range (BUF_OOB).  Loads and stores carry the
-// nontemporal hint.
+// lanes use an offset past the range (BUF_OOB).  Loads carry the
+// nontemporal hint; stores too, or the write-through policy (BUF_WT).
 // ---------------------------------------------------------------------------
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t BUF_OOB = 0x80000000u; // above any row group's byte range
 constexpr int BUF_NT = 2;                 // cache policy: nontemporal
+// Stores marked with system-scope coherence (sc0 sc1) are written through
+// the L2 instead of being held there dirty.  Streams store this way from
+// their last row groups on: what the L2 still holds dirty when a kernel ends
+// is written back before the kernel counts as complete, a few microseconds
+// that short kernels feel.  Earlier row groups keep the nontemporal policy,
+// which streams slightly faster.
+constexpr int BUF_WT = 17;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -182,9 +189,12 @@ struct BufIO<bf16, 8> {
     {
         return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
     }
-    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v, bool wt)
     {
-        __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, BUF_NT);
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, int(off), 0, BUF_NT);
     }
 };
 template <>
@@ -198,9 +208,12 @@ struct BufIO<float, 4> {
     {
         return __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
     }
-    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v, bool wt)
     {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, int(off), 0, BUF_NT);
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, int(off), 0, BUF_NT);
     }
 };
 template <>
@@ -214,9 +227,12 @@ struct BufIO<bf16, 1> {
     {
         return __builtin_amdgcn_raw_buffer_load_b16(r, int(off), 0, 0);
     }
-    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v, bool wt)
     {
-        __builtin_amdgcn_raw_buffer_store_b16(v, r, int(off), 0, BUF_NT);
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b16(v, r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b16(v, r, int(off), 0, BUF_NT);
     }
 };
 template <>
@@ -230,9 +246,12 @@ struct BufIO<float, 1> {
     {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0));
     }
-    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v)
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v, bool wt)
     {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, int(off), 0, BUF_NT);
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, int(off), 0, BUF_NT);
     }
 };
 
@@ -250,24 +269,33 @@ __device__ __forceinline__ float sat_e4m3(float v)
 }
 
 template <int VEC>
-__device__ __forceinline__ void store_e4m3(rsrc_t r, uint32_t off, const float *v)
+__device__ __forceinline__ void store_e4m3(rsrc_t r, uint32_t off, const float *v, bool wt)
 {
     if constexpr (VEC == 8) {
         int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), sat_e4m3(v[1]), 0, false);
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[2]), sat_e4m3(v[3]), w0, true);
         int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[4]), sat_e4m3(v[5]), 0, false);
         w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[6]), sat_e4m3(v[7]), w1, true);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{unsigned(w0), unsigned(w1)}, r, int(off), 0,
-                                              BUF_NT);
+        const u32x2_t w{unsigned(w0), unsigned(w1)};
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b64(w, r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b64(w, r, int(off), 0, BUF_NT);
     } else if constexpr (VEC == 4) {
         int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), sat_e4m3(v[1]), 0, false);
         w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[2]), sat_e4m3(v[3]), w, true);
-        __builtin_amdgcn_raw_buffer_store_b32(unsigned(w), r, int(off), 0, BUF_NT);
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b32(unsigned(w), r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(unsigned(w), r, int(off), 0, BUF_NT);
     } else {
         static_assert(VEC == 1, "FP8 store of 1, 4 or 8 values");
         const int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), 0.f, 0, false);
-        __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(w & 0xff), r, int(off),
-                                             0, BUF_NT);
+        const unsigned char b = static_cast<unsigned char>(w & 0xff);
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b8(b, r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b8(b, r, int(off), 0, BUF_NT);
     }
 }
 

@@ -21,6 +21,7 @@ struct FwdArgs {
     int64_t n_groups;
     int N;
     int K, A;
+    int64_t wt_group; // row groups from this one on store write-through
     float eps;
     bool zero_centred; // weight = round_T(1 + gamma)
 };
@@ -36,6 +37,7 @@ struct BwdArgs {
     int64_t n_groups;
     int N;
     int K, A;
+    int64_t wt_group; // row groups from this one on store write-through
     float eps;
     bool zero_centred; // weight = round_T(1 + gamma)
 };
@@ -71,6 +73,7 @@ struct SoftmaxArgs {
     int64_t n_groups;
     int N;
     int K, A;
+    int64_t wt_group; // row groups from this one on store write-through
 };
 typedef hipError_t (*SoftmaxLaunch)(const SoftmaxArgs &, int grid, hipStream_t);
 struct SoftmaxEntry {

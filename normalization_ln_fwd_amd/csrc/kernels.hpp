@@ -343,6 +343,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         const RowGroup rgp(grp, TEAMS, a.M, N, sizeof(T));
         const uint32_t bytes = rgp.bytes;
         const int64_t gbyte = rgp.byte0;
+        const bool wt = grp >= a.wt_group; // store policy (see BUF_WT)
         if (!PREFETCH)
             issue(grp);
         if constexpr (!PLDS) {
@@ -399,7 +400,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
             const rsrc_t os = make_rsrc(static_cast<char *>(a.res_out) + gbyte, bytes);
 #pragma unroll
             for (int k = 0; k < VPL; ++k)
-                BIO::store(os, off[k], ur[k]);
+                BIO::store(os, off[k], ur[k], wt);
         }
 
         // Statistics.  LayerNorm keeps its mean as an fp32 pair mean + lo
@@ -481,9 +482,9 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     q[e] *= y_scale;
-                store_e4m3<VEC>(ys, cvalid[k] ? off[k] / uint32_t(sizeof(T)) : BUF_OOB, q);
+                store_e4m3<VEC>(ys, cvalid[k] ? off[k] / uint32_t(sizeof(T)) : BUF_OOB, q, wt);
             } else {
-                BIO::store(ys, off[k], IO::pack(yv));
+                BIO::store(ys, off[k], IO::pack(yv), wt);
             }
             if (rv && cvalid[k]) {
 #pragma unroll
@@ -545,6 +546,37 @@ constexpr bool bwd_pipelined()
 // the workgroup's rows, folded over the workgroup in a fixed order and
 // written as this workgroup's partial row of the workspace.
 // ---------------------------------------------------------------------------
+// One lane's VEC consecutive columns, from c0, of the partial rows pg / pb
+// (/ pd): 16-byte stores when VEC is a multiple of 4 (the rows start on
+// 16-byte boundaries and vectorised kernels have N a multiple of VEC).  The
+// partials keep the default write-back policy: the column sums read them
+// next, and measured, write-through or nontemporal partials were slower.
+template <int VEC, bool DB>
+__device__ __forceinline__ void store_partial(float *pg, float *pb, float *pd, int c0, int N,
+                                              const float *vg, const float *vb, const float *vd)
+{
+    if constexpr (VEC % 4 == 0) {
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4) {
+            *reinterpret_cast<float4 *>(pg + c0 + e) = float4{vg[e], vg[e + 1], vg[e + 2], vg[e + 3]};
+            *reinterpret_cast<float4 *>(pb + c0 + e) = float4{vb[e], vb[e + 1], vb[e + 2], vb[e + 3]};
+            if constexpr (DB)
+                *reinterpret_cast<float4 *>(pd + c0 + e) =
+                    float4{vd[e], vd[e + 1], vd[e + 2], vd[e + 3]};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if (c0 + e < N) {
+                pg[c0 + e] = vg[e];
+                pb[c0 + e] = vb[e];
+                if constexpr (DB)
+                    pd[c0 + e] = vd[e];
+            }
+        }
+    }
+}
+
 template <typename T, int VEC, int LPR, int VPL, int TEAMS, bool RMS, bool DB>
 __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 {
@@ -647,7 +679,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     // dx of the last group worked on, held back by pipelined walks
     Raw dxh[VPL];
     RowGroup hrg;
-    bool held = false;
+    bool held = false, hwt = false; // hwt: store policy of the held dx (see BUF_WT)
 
     // The work on row group grp, whose rows and statistics are in sl; dx is
     // stored, or held in dxh when `hold`.
@@ -724,10 +756,11 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
             if (hold)
                 dxh[k] = IO::pack(dxv);
             else
-                BIO::store(dxs, off[k], IO::pack(dxv));
+                BIO::store(dxs, off[k], IO::pack(dxv), grp >= a.wt_group);
         }
         if (hold) {
             hrg = rgp;
+            hwt = grp >= a.wt_group;
             held = true;
         }
     };
@@ -754,7 +787,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
                 const rsrc_t dxs = make_rsrc(static_cast<char *>(a.dx) + hrg.byte0, hrg.bytes);
 #pragma unroll
                 for (int k = 0; k < VPL; ++k)
-                    BIO::store(dxs, off[k], dxh[k]);
+                    BIO::store(dxs, off[k], dxh[k], hwt);
             }
         };
         for (int kk = 0; kk < a.K; kk += 2) {
@@ -804,22 +837,16 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
-            if (cvalid[k] && (LPR >= 64 || lane < LPR)) {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    if (VEC > 1 || c0 + e < N) {
-                        pg[c0 + e] = acc_g[k * VEC + e];
-                        pb[c0 + e] = acc_b[k * VEC + e];
-                        if constexpr (DB)
-                            pd[c0 + e] = acc_d[k * VEC + e];
-                    }
-                }
-            }
+            if (cvalid[k] && (LPR >= 64 || lane < LPR))
+                store_partial<VEC, DB>(pg, pb, pd, c0, N, acc_g + k * VEC, acc_b + k * VEC,
+                                       acc_d + (DB ? k * VEC : 0));
         }
     } else {
+        // slots 0 .. SLOTS-2 add their sums into LDS in slot order; the last
+        // slot adds its own and stores the row from registers
         const int slot = LPR <= 64 ? (tid >> 6) : team;
         const bool holder = LPR < 64 ? lane < LPR : true;
-        for (int sl = 0; sl < SLOTS; ++sl) {
+        for (int sl = 0; sl < SLOTS - 1; ++sl) {
             if (slot == sl && holder) {
 #pragma unroll
                 for (int k = 0; k < VPL; ++k) {
@@ -828,22 +855,37 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 #pragma unroll
                         for (int e = 0; e < VEC; ++e) {
                             const int c = c0 + e;
-                            col_lds[c] = (sl == 0 ? 0.f : col_lds[c]) + acc_g[k * VEC + e];
-                            col_lds[CAP + c] = (sl == 0 ? 0.f : col_lds[CAP + c]) + acc_b[k * VEC + e];
+                            const int i = k * VEC + e;
+                            col_lds[c] = sl == 0 ? acc_g[i] : col_lds[c] + acc_g[i];
+                            col_lds[CAP + c] = sl == 0 ? acc_b[i] : col_lds[CAP + c] + acc_b[i];
                             if constexpr (DB)
                                 col_lds[2 * CAP + c] =
-                                    (sl == 0 ? 0.f : col_lds[2 * CAP + c]) + acc_d[k * VEC + e];
+                                    sl == 0 ? acc_d[i] : col_lds[2 * CAP + c] + acc_d[i];
                         }
                     }
                 }
             }
             __syncthreads();
         }
-        for (int c = tid; c < N; c += WG) {
-            pg[c] = col_lds[c];
-            pb[c] = col_lds[CAP + c];
-            if constexpr (DB)
-                pd[c] = col_lds[2 * CAP + c];
+        if (slot == SLOTS - 1 && holder) {
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const int c0 = (k * LPR + tl) * VEC;
+                if (!cvalid[k])
+                    continue;
+                float vg[VEC], vb[VEC], vd[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int i = k * VEC + e;
+                    vg[e] = col_lds[c0 + e] + acc_g[i];
+                    vb[e] = col_lds[CAP + c0 + e] + acc_b[i];
+                    if constexpr (DB)
+                        vd[e] = col_lds[2 * CAP + c0 + e] + acc_d[i];
+                    else
+                        vd[e] = 0.f;
+                }
+                store_partial<VEC, DB>(pg, pb, pd, c0, N, vg, vb, vd);
+            }
         }
     }
 }
@@ -930,7 +972,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) softmax_kernel(const SoftmaxArgs a
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 yv[e] = ev[k][e] * inv;
-            BIO::store(ys, off[k], IO::pack(yv));
+            BIO::store(ys, off[k], IO::pack(yv), grp >= a.wt_group);
         }
     }
 }
@@ -945,45 +987,46 @@ hipError_t launch_softmax(const SoftmaxArgs &a, int grid, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Backward stage 2: column sums of the partial rows.  src holds gridDim.z
-// blocks (dgamma, dbeta, dbias) of `rows` rows of N floats.  Workgroup
-// (column tile, slice s, block) adds rows [s*span, min(rows, (s+1)*span)) of
-// its 64 columns (rows are padded to colsum_ld(N) floats, so each thread
-// reads 16-byte vectors of 4 columns): thread (q, t) takes rows t, t + 16,
-// ... of the slice in ascending order, and the sixteen threads of a column
-// are added in order t = 0..15.  FINAL: one
-// slice; divide by `divisor` (1, or M for the mean over the rows), down-cast
-// and store to dgamma / dbeta / dbias.  Otherwise slice s
-// stores its sums as row s of dst (blocks of gridDim.y rows), which a FINAL
-// launch then adds the same way.  Every addition happens in a fixed order.
+// blocks (dgamma, dbeta, dbias) of `rows` rows of N floats, each row padded
+// to colsum_ld(N) floats so that a thread reads 16-byte vectors of 4 columns.
+// Workgroup (column tile, slice s, block) adds rows [s*span, min(rows,
+// (s+1)*span)) of its 4*QUADS columns with QUADS x SUB threads: thread
+// (q, t) takes rows t, t + SUB, ... of the slice in ascending order.  The SUB
+// row subsets of a column are then added in a fixed tree: within a wave by
+// xor-shuffles over the subsets it holds (64 / QUADS of them), then the
+// waves' sums in wave order.  FINAL: one slice; divide by `divisor` (1, or M
+// for the mean over the rows), down-cast and store to dgamma / dbeta /
+// dbias.  Otherwise slice s stores its sums as row s of dst (blocks of
+// gridDim.y rows), which a FINAL launch then adds.  Every addition happens
+// in a fixed order.
 // (A one-launch variant that lets the last workgroup finish needs a
 // device-scope release per workgroup, i.e. an L2 write-back each, which
 // costs more than the second launch.)
 // ---------------------------------------------------------------------------
-constexpr int COLSUM_COLS = 64; // columns per workgroup, 4 per thread
-constexpr int COLSUM_QUADS = COLSUM_COLS / 4;
-constexpr int COLSUM_SUB = 16;  // row subsets per workgroup
-
-template <bool FINAL, bool BF16_OUT>
-__global__ void __launch_bounds__(COLSUM_QUADS *COLSUM_SUB)
+template <bool FINAL, bool BF16_OUT, int QUADS, int SUB>
+__global__ void __launch_bounds__(QUADS *SUB)
     colsum_kernel(const float *src, int rows, int N, int span, float *dst, void *dgamma,
                   void *dbeta, void *dbias, float divisor)
 {
-    const int tq = threadIdx.x % COLSUM_QUADS;
-    const int ty = threadIdx.x / COLSUM_QUADS;
+    static_assert(QUADS <= 64 && 64 % QUADS == 0 && (QUADS * SUB) % 64 == 0, "layout");
+    constexpr int NWAVE = QUADS * SUB / 64;
+    const int tq = threadIdx.x % QUADS;
+    const int ty = threadIdx.x / QUADS;
+    const int wave = threadIdx.x / 64;
     const int which = blockIdx.z;
     void *out = which == 0 ? dgamma : (which == 1 ? dbeta : dbias);
     if (FINAL && out == nullptr)
         return; // uniform over the block
     const int64_t ld = colsum_ld(N);
-    const int j0 = blockIdx.x * COLSUM_COLS + tq * 4;
+    const int j0 = blockIdx.x * (4 * QUADS) + tq * 4;
     const int s = blockIdx.y;
     const int r0 = s * span;
     const int r1 = min(rows, r0 + span);
     const float *part = src + (int64_t)which * rows * ld;
     float4 acc = {0.f, 0.f, 0.f, 0.f};
     if (j0 < N) { // columns j0 .. j0+3 lie within the padded row of ld floats
-#pragma unroll 8
-        for (int r = r0 + ty; r < r1; r += COLSUM_SUB) {
+#pragma unroll 4
+        for (int r = r0 + ty; r < r1; r += SUB) {
             const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)r * ld + j0);
             acc.x += v.x;
             acc.y += v.y;
@@ -991,14 +1034,22 @@ __global__ void __launch_bounds__(COLSUM_QUADS *COLSUM_SUB)
             acc.w += v.w;
         }
     }
-    __shared__ float4 sl[COLSUM_SUB][COLSUM_QUADS];
-    sl[ty][tq] = acc;
+#pragma unroll
+    for (int m = QUADS; m < 64; m <<= 1) {
+        acc.x += __shfl_xor(acc.x, m);
+        acc.y += __shfl_xor(acc.y, m);
+        acc.z += __shfl_xor(acc.z, m);
+        acc.w += __shfl_xor(acc.w, m);
+    }
+    __shared__ float4 sl[NWAVE][QUADS];
+    if ((threadIdx.x & 63) < QUADS)
+        sl[wave][tq] = acc;
     __syncthreads();
-    if (ty == 0 && j0 < N) {
+    if (threadIdx.x < QUADS && j0 < N) {
         float4 t = sl[0][tq];
 #pragma unroll
-        for (int q = 1; q < COLSUM_SUB; ++q) {
-            const float4 u = sl[q][tq];
+        for (int w = 1; w < NWAVE; ++w) {
+            const float4 u = sl[w][tq];
             t.x += u.x;
             t.y += u.y;
             t.z += u.z;
