@@ -43,11 +43,16 @@ constexpr int kBwdGroupsPerWg = 0; // 0: chosen per shape (see bwd_plan)
 // Row groups per workgroup.  Teams of several waves (wide rows) have few
 // rows in flight per CU; walking several groups per workgroup, with the next
 // group's loads in flight, keeps the loads going.  The backward's count also
-// sets how many rows one column partial covers: for wide rows a workgroup
-// walks kBwdRowsWide rows.
+// sets how many rows one column partial covers, i.e. how finely the column
+// reduction is split over the rows (see bwd_groups_per_wg).
 constexpr int kFwdGroupsWide = 4;
 constexpr int kBwdGroupsNarrow = 3;
 constexpr int kBwdRowsWide = 32;
+constexpr int kBwdNarrowMaxK = 16;
+// Compute units of the gfx950 parts.  A constant rather than a device query,
+// so that the grid (and with it every summation order, and the workspace
+// size) follows from the call's arguments alone.
+constexpr int64_t kCUs = 256;
 constexpr int kFwdInterleave = 1024;
 constexpr int kBwdInterleave = 256;
 // Output bytes, counted from the end of a call, that its kernel stores
@@ -367,15 +372,40 @@ struct BwdLayout {
     bool two_level = false;
 };
 
+// Row groups per backward workgroup: the split of the column reduction over
+// the rows.  Each workgroup's partial row costs N floats per column sum,
+// written and read once more, so fewer, longer walks save traffic, but the
+// walks must still spread over the CUs.  Measured on MI355X:
+//  - wide rows (one to two rows per group, 1024-thread workgroups, one per
+//    CU): one workgroup per CU, each walking up to kBwdRowsWide rows and at
+//    least two rows (below that the partials outweigh the rows themselves);
+//    small M thus gets as many workgroups as the CUs can take, where a fixed
+//    walk of kBwdRowsWide rows left most CUs idle (2 workgroups for 64 rows
+//    of 16384 columns: 102 us; now 18 us);
+//  - narrow rows (256-thread workgroups of many rows): about two workgroups
+//    per CU while that takes at most kBwdNarrowMaxK groups each (10-20%
+//    faster than the fixed walk between 16384 and 131072 rows); for more rows
+//    short walks of kBwdGroupsNarrow groups, many workgroups deep, which
+//    balance best.
+int bwd_groups_per_wg(int64_t M, const RowShape &sh)
+{
+    const int64_t groups = (M + sh.teams - 1) / sh.teams;
+    if (sh.lpr >= WIDE_LPR) {
+        const int64_t kmax = std::max(1, kBwdRowsWide / sh.teams);
+        const int64_t kmin = std::min<int64_t>(kmax, (2 + sh.teams - 1) / sh.teams);
+        return int(std::min(kmax, std::max(kmin, (groups + kCUs - 1) / kCUs)));
+    }
+    const int64_t k = (groups + 2 * kCUs - 1) / (2 * kCUs);
+    return k <= kBwdNarrowMaxK ? int(std::max<int64_t>(1, k)) : kBwdGroupsNarrow;
+}
+
 norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, int nb, const Knobs &kn,
                        const BwdEntry **entry, Walk *w, BwdLayout *lay)
 {
     const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    int K = kn.bwd_k;
-    if (K == 0)
-        K = e->shape.lpr >= WIDE_LPR ? std::max(1, kBwdRowsWide / e->shape.teams) : kBwdGroupsNarrow;
+    const int K = kn.bwd_k > 0 ? kn.bwd_k : bwd_groups_per_wg(M, e->shape);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.bwd_a, w))
         return st;
     *entry = e;

@@ -186,6 +186,26 @@ def test_bwd_rejects_small_workspace():
     assert e.value.status == 6
 
 
+# Shapes whose split of the column reduction over the rows (row groups per
+# workgroup) lands between its bounds, with ragged last workgroups: wide rows
+# at one workgroup per CU, narrow rows at about two per CU.
+SPLIT_SHAPES = [(1024, 16384), (601, 8192), (4097, 4096), (65537, 384), (16385, 2048)]
+
+
+@pytest.mark.parametrize("M,N", SPLIT_SHAPES)
+@pytest.mark.parametrize("rms,dtype", [(False, BF16), (True, F32)], ids=["ln-bf16", "rms-f32"])
+def test_bwd_row_splits_match_oracle(M, N, rms, dtype):
+    inp, eps = make_case(M, N, dtype, rms, seed=M + 7 * N)
+    out = run_bwd(rms, inp, dtype, eps, dparam_dtype=torch.float32, want_dbias=True)
+    ref = oracle_bwd(rms, inp, dtype, eps, want_dbias=True)
+    assert_rows_close(f64(out["dx"]), ref["dx"], dtype, "dx",
+                      scale=dx_term_scale(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+    for k in ("dgamma", "dbeta"):
+        assert_colsums_close(f64(out[k]), ref[k], ref[k + "_l2"], COLSUM_REL_SMALL, k)
+    l2 = np.maximum(ref["dbias_l2"], dbias_term_l2(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+    assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
+
+
 def test_bwd_is_deterministic():
     inp, eps = make_case(20000, 384, BF16, False, seed=8)
     a = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32)
