@@ -137,6 +137,26 @@ const Entry *pick_shape(const Entry *tab, int n, int N, int force_lpr, int force
 // walking, and are used when they still leave kMinWideGroups workgroups.
 constexpr int64_t kMaxAmaxWgs = 20000;
 constexpr int64_t kMinWideGroups = 2048;
+// Up to this many row groups the forward walks several groups per workgroup
+// (about one workgroup per CU, at most kFwdGroupsWide groups each); beyond
+// it, one group per workgroup (many workgroups deep) balances best.
+constexpr int64_t kFwdFewGroups = 4096;
+
+// Row groups per forward workgroup.  Measured on MI355X: one workgroup per
+// CU walking up to kFwdGroupsWide groups suits wide rows and, up to
+// kFwdFewGroups groups, narrow ones too (16384 x 1024: 35 -> 25 us);
+// narrow rows in larger numbers run one group per workgroup.  With amax, at
+// most kMaxAmaxWgs workgroups.
+int fwd_groups_per_wg(int64_t M, const RowShape &sh, bool amax)
+{
+    const int64_t groups = (M + sh.teams - 1) / sh.teams;
+    int64_t k = 1;
+    if (sh.lpr >= WIDE_LPR || groups <= kFwdFewGroups)
+        k = std::min<int64_t>(kFwdGroupsWide, std::max<int64_t>(1, (groups + kCUs - 1) / kCUs));
+    if (amax)
+        k = std::max(k, (groups + kMaxAmaxWgs - 1) / kMaxAmaxWgs);
+    return int(std::max<int64_t>(1, k));
+}
 
 const FwdEntry *fwd_entry(int dtype, bool vec, int64_t M, int N, const Knobs &k)
 {
@@ -263,15 +283,7 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     const FwdEntry *e = fwd_entry(dtype, vec, M, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    int K = kn.fwd_k;
-    if (K == 0) {
-        const int64_t groups = (M + e->shape.teams - 1) / e->shape.teams;
-        K = amax ? int((groups + kMaxAmaxWgs - 1) / kMaxAmaxWgs) : 1;
-        if (e->shape.lpr >= WIDE_LPR && K < kFwdGroupsWide)
-            K = kFwdGroupsWide;
-        if (K < 1)
-            K = 1;
-    }
+    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, e->shape, amax != nullptr);
     Walk w;
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
         return st;
@@ -347,7 +359,7 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
         }
     }
     Walk w;
-    const int K = e->shape.lpr >= WIDE_LPR ? kFwdGroupsWide : 1;
+    const int K = fwd_groups_per_wg(M, e->shape, false);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
         return st;
     SoftmaxArgs a;
