@@ -287,6 +287,39 @@ def time_calls(fns, iters, torch):
     return total, min(sl), total
 
 
+def time_graph(fns, torch, replays=20):
+    """Microseconds per call of fns (a list of calls, each run once) captured
+    into one HIP graph and replayed: the GPU time of a launch-bound case
+    without the host's per-call cost (Python binding, launch API)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:  # warm-up on the capture stream
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for f in fns:
+            f()
+    stream = torch.cuda.current_stream().cuda_stream
+    t0, n = time.perf_counter(), 0
+    while n < 3 or time.perf_counter() - t0 < WARM_S:
+        g.replay()
+        n += 1
+        torch.cuda.synchronize()
+    ev = HipEvents(2)
+    ev.record(0, stream)
+    for _ in range(replays):
+        g.replay()
+    ev.record(1, stream)
+    torch.cuda.synchronize()
+    us = ev.elapsed_ms(0, 1) * 1e3 / (replays * len(fns))
+    ev.close()
+    del g
+    return us
+
+
 def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
     out = {}
 
@@ -298,6 +331,14 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
                      "GB_s": round(gbs, 1), "frac_peak": round(gbs / PEAK_GBS, 4),
                      "gated_70pct": gated}
         log(f"  {name}: {med:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_GBS:.1f}% of peak)")
+
+    def graph_rec(name, fns, nbytes):
+        us = time_graph(fns, torch)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us_per_call": round(us, 2), "bytes": nbytes, "GB_s": round(gbs, 1),
+                     "frac_peak": round(gbs / PEAK_GBS, 4), "gated_70pct": False,
+                     "timing": f"HIP graph of {len(fns)} calls, replayed"}
+        log(f"  {name}: {us:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_GBS:.1f}% of peak)")
 
     M, N = M_BIG, N_BIG
     rec("ln_fwd_576000x384", lambda: nf.ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"],
@@ -356,6 +397,30 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
     rec("ln_fwd_4096x384_amax", [
         (lambda s=s: nf.ln_fwd(s["x"], s["bias"], s["residual"], s["gamma"], s["beta"], 1e-5,
                                want_amax=True)) for s in subs], fwd_bytes(M2, N), False)
+    # the same calls replayed from a captured graph (outputs preallocated):
+    # the GPU time of the launch-bound size, amax reset included
+    outs2 = [{"y": torch.empty_like(s["x"]), "residual_out": torch.empty_like(s["x"]),
+              "mean": torch.empty(M2, device=dev), "rstd": torch.empty(M2, device=dev),
+              "amax": torch.empty(1, device=dev)} for s in subs[:64]]
+    graph_rec("ln_fwd_4096x384_amax_graph", [
+        (lambda s=s, o=o: nf.ln_fwd(s["x"], s["bias"], s["residual"], s["gamma"], s["beta"],
+                                    1e-5, want_amax=True, out=o))
+        for s, o in zip(subs[:64], outs2)], fwd_bytes(M2, N))
+    del outs2
+    # config 1: LayerNorm forward, fp32, 64 x 384, bias + residual; y, mean, rstd
+    M1 = 64
+    g1 = synth.make_inputs(M1 * 64, N, dtype=synth.F32, seed=0,
+                           names=("x", "residual", "bias", "gamma", "beta"))
+    d1 = {k: torch.from_numpy(v).to(dev) for k, v in g1.items()}
+    calls1 = []
+    for i in range(64):
+        o1 = {"y": torch.empty(M1, N, device=dev), "mean": torch.empty(M1, device=dev),
+              "rstd": torch.empty(M1, device=dev)}
+        xs, rs = d1["x"][i * M1:(i + 1) * M1], d1["residual"][i * M1:(i + 1) * M1]
+        calls1.append(lambda xs=xs, rs=rs, o1=o1: nf.ln_fwd(
+            xs, d1["bias"], rs, d1["gamma"], d1["beta"], 1e-5, want_residual_out=False, out=o1))
+    graph_rec("ln_fwd_64x384_f32_graph", calls1, M1 * (3 * 4 * N + 8))
+    del d1, calls1
     # config 5: 8192 x 4096, residual + LayerNorm, 1% outliers; two buffer
     # sets alternate (512 MB working set)
     M5, N5 = 8192, 4096
