@@ -47,7 +47,7 @@ constexpr int kBwdGroupsPerWg = 0; // 0: chosen per shape (see bwd_plan)
 // reduction is split over the rows (see bwd_groups_per_wg).
 constexpr int kFwdGroupsWide = 4;
 constexpr int kBwdGroupsNarrow = 3;
-constexpr int kBwdRowsWide = 32;
+constexpr int kBwdRowsWide = 128;
 constexpr int kBwdNarrowMaxK = 16;
 // Compute units of the gfx950 parts.  A constant rather than a device query,
 // so that the grid (and with it every summation order, and the workspace
@@ -388,24 +388,28 @@ struct BwdLayout {
 // the rows.  Each workgroup's partial row costs N floats per column sum,
 // written and read once more, so fewer, longer walks save traffic, but the
 // walks must still spread over the CUs.  Measured on MI355X:
-//  - wide rows (one to two rows per group, 1024-thread workgroups, one per
-//    CU): one workgroup per CU, each walking up to kBwdRowsWide rows and at
-//    least two rows (below that the partials outweigh the rows themselves);
-//    small M thus gets as many workgroups as the CUs can take, where a fixed
-//    walk of kBwdRowsWide rows left most CUs idle (2 workgroups for 64 rows
-//    of 16384 columns: 102 us; now 18 us);
+//  - wide rows (teams of 256 to 1024 lanes): as many workgroups as the CUs
+//    hold at once -- one per CU, two for the fp32 shapes up to 8192
+//    columns, whose registers leave room for a second -- each walking at
+//    least 2 and at most kBwdRowsWide rows (below 2 rows the partials
+//    outweigh the rows themselves).  A fixed 32-row walk left most CUs idle
+//    at small M (64 x 16384 bf16: 102 us, now 18 us) and cut large M into
+//    more partials than needed (32768 x 4096 bf16: 141 us, now 129 us;
+//    8192 x 4096 fp32: 92 us, now 68 us);
 //  - narrow rows (256-thread workgroups of many rows): about two workgroups
 //    per CU while that takes at most kBwdNarrowMaxK groups each (10-20%
 //    faster than the fixed walk between 16384 and 131072 rows); for more rows
 //    short walks of kBwdGroupsNarrow groups, many workgroups deep, which
 //    balance best.
-int bwd_groups_per_wg(int64_t M, const RowShape &sh)
+int bwd_groups_per_wg(int64_t M, const RowShape &sh, int32_t dtype)
 {
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
     if (sh.lpr >= WIDE_LPR) {
+        const int64_t per_cu = dtype == NORM_F32 && sh.capacity() <= 8192 ? 2 : 1;
         const int64_t kmax = std::max(1, kBwdRowsWide / sh.teams);
         const int64_t kmin = std::min<int64_t>(kmax, (2 + sh.teams - 1) / sh.teams);
-        return int(std::min(kmax, std::max(kmin, (groups + kCUs - 1) / kCUs)));
+        const int64_t slots = kCUs * per_cu;
+        return int(std::min(kmax, std::max(kmin, (groups + slots - 1) / slots)));
     }
     const int64_t k = (groups + 2 * kCUs - 1) / (2 * kCUs);
     return k <= kBwdNarrowMaxK ? int(std::max<int64_t>(1, k)) : kBwdGroupsNarrow;
@@ -417,7 +421,7 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, int nb, co
     const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    const int K = kn.bwd_k > 0 ? kn.bwd_k : bwd_groups_per_wg(M, e->shape);
+    const int K = kn.bwd_k > 0 ? kn.bwd_k : bwd_groups_per_wg(M, e->shape, dtype);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.bwd_a, w))
         return st;
     *entry = e;
