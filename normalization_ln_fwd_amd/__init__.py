@@ -115,9 +115,17 @@ def _ptr(t, name, dtype=None, numel=None):
     return t.data_ptr()
 
 
+# The raw handle of the current stream without building a Stream object
+# (a few microseconds per call otherwise).
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _current_raw_stream is not None:
+        return _current_raw_stream(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, want_rstd,

@@ -19,11 +19,8 @@ using namespace nf;
 // ---------------------------------------------------------------- device
 norm_status_t check_device()
 {
-    int dev = -1, cus = 0;
+    int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0)
-        return NORM_ERR_DEVICE;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
         return NORM_ERR_DEVICE;
     return NORM_OK;
 }
