@@ -27,13 +27,11 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ---------------------------------------------------------------------------
-// Vector I/O.  VecIO<T, VEC> moves VEC consecutive elements of type T between
-// memory and float registers.  VEC = 16 / sizeof(T) is one 16-byte access per
-// lane (the caller guarantees 16-byte alignment); VEC = 1 is element-wise.
-// `Raw` is the packed register form.  load/store are ordinary cached accesses
-// (for the per-column vectors, reused by every row); load_stream /
-// store_stream carry the nontemporal hint, for [M, N] tensors that cross HBM
-// once.  pack() rounds to T (nearest, ties to even); unpack() widens exactly.
+// Register forms.  VecIO<T, VEC> converts VEC consecutive elements of type T
+// between their packed register form `Raw` (what one 16-byte access per lane,
+// VEC = 16 / sizeof(T), or one element, VEC = 1, brings in; see BufIO below)
+// and floats.  pack() rounds to T (nearest, ties to even); unpack() widens
+// exactly.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -44,23 +42,6 @@ struct VecIO;
 template <>
 struct VecIO<bf16, 8> {
     using Raw = u32x4_t;
-    static __device__ __forceinline__ const Raw *at(const void *b, int64_t i)
-    {
-        return reinterpret_cast<const Raw *>(static_cast<const uint16_t *>(b) + i);
-    }
-    static __device__ __forceinline__ Raw *at(void *b, int64_t i)
-    {
-        return reinterpret_cast<Raw *>(static_cast<uint16_t *>(b) + i);
-    }
-    static __device__ __forceinline__ Raw load(const void *b, int64_t i) { return *at(b, i); }
-    static __device__ __forceinline__ Raw load_stream(const void *b, int64_t i)
-    {
-        return __builtin_nontemporal_load(at(b, i));
-    }
-    static __device__ __forceinline__ void store_stream(void *b, int64_t i, Raw r)
-    {
-        __builtin_nontemporal_store(r, at(b, i));
-    }
     static __device__ __forceinline__ void unpack(const Raw &r, float *f)
     {
         f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
@@ -79,18 +60,6 @@ struct VecIO<bf16, 8> {
 template <>
 struct VecIO<bf16, 1> {
     using Raw = uint16_t;
-    static __device__ __forceinline__ Raw load(const void *b, int64_t i)
-    {
-        return static_cast<const uint16_t *>(b)[i];
-    }
-    static __device__ __forceinline__ Raw load_stream(const void *b, int64_t i)
-    {
-        return __builtin_nontemporal_load(static_cast<const uint16_t *>(b) + i);
-    }
-    static __device__ __forceinline__ void store_stream(void *b, int64_t i, Raw r)
-    {
-        __builtin_nontemporal_store(r, static_cast<uint16_t *>(b) + i);
-    }
     static __device__ __forceinline__ void unpack(const Raw &r, float *f)
     {
         f[0] = __uint_as_float(uint32_t(r) << 16);
@@ -105,23 +74,6 @@ struct VecIO<bf16, 1> {
 template <>
 struct VecIO<float, 4> {
     using Raw = f32x4_t;
-    static __device__ __forceinline__ const Raw *at(const void *b, int64_t i)
-    {
-        return reinterpret_cast<const Raw *>(static_cast<const float *>(b) + i);
-    }
-    static __device__ __forceinline__ Raw *at(void *b, int64_t i)
-    {
-        return reinterpret_cast<Raw *>(static_cast<float *>(b) + i);
-    }
-    static __device__ __forceinline__ Raw load(const void *b, int64_t i) { return *at(b, i); }
-    static __device__ __forceinline__ Raw load_stream(const void *b, int64_t i)
-    {
-        return __builtin_nontemporal_load(at(b, i));
-    }
-    static __device__ __forceinline__ void store_stream(void *b, int64_t i, Raw r)
-    {
-        __builtin_nontemporal_store(r, at(b, i));
-    }
     static __device__ __forceinline__ void unpack(const Raw &r, float *f)
     {
         f[0] = r.x; f[1] = r.y; f[2] = r.z; f[3] = r.w;
@@ -133,18 +85,6 @@ struct VecIO<float, 4> {
 template <>
 struct VecIO<float, 1> {
     using Raw = float;
-    static __device__ __forceinline__ Raw load(const void *b, int64_t i)
-    {
-        return static_cast<const float *>(b)[i];
-    }
-    static __device__ __forceinline__ Raw load_stream(const void *b, int64_t i)
-    {
-        return __builtin_nontemporal_load(static_cast<const float *>(b) + i);
-    }
-    static __device__ __forceinline__ void store_stream(void *b, int64_t i, Raw r)
-    {
-        __builtin_nontemporal_store(r, static_cast<float *>(b) + i);
-    }
     static __device__ __forceinline__ void unpack(const Raw &r, float *f) { f[0] = r; }
     static __device__ __forceinline__ Raw pack(const float *f) { return f[0]; }
     static __device__ __forceinline__ Raw zero() { return 0.f; }
