@@ -239,6 +239,36 @@ __device__ __forceinline__ void store_e4m3(rsrc_t r, uint32_t off, const float *
     }
 }
 
+// FP8 codes of the 8 values of this lane and of its partner lane (lane ^ 1),
+// whose 8 columns directly follow (even lane) or precede (odd lane) this
+// lane's: the even lane stores both as one 16-byte vector when the partner's
+// columns are valid, else its own 8 bytes; odd lanes store nothing.  Every
+// lane of the wave must call it (the codes move across lanes).
+__device__ __forceinline__ void store_e4m3_pair(rsrc_t r, uint32_t off, const float *v,
+                                                bool even, bool partner_valid, bool wt)
+{
+    int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), sat_e4m3(v[1]), 0, false);
+    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[2]), sat_e4m3(v[3]), w0, true);
+    int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[4]), sat_e4m3(v[5]), 0, false);
+    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[6]), sat_e4m3(v[7]), w1, true);
+    const int p0 = __shfl_xor(w0, 1), p1 = __shfl_xor(w1, 1);
+    if (!even)
+        return;
+    if (partner_valid) {
+        const u32x4_t w{unsigned(w0), unsigned(w1), unsigned(p0), unsigned(p1)};
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b128(w, r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b128(w, r, int(off), 0, BUF_NT);
+    } else {
+        const u32x2_t w{unsigned(w0), unsigned(w1)};
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b64(w, r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b64(w, r, int(off), 0, BUF_NT);
+    }
+}
+
 // VEC floats from LDS (16-byte reads when VEC is a multiple of 4).
 template <int VEC>
 __device__ __forceinline__ void lds_read(const float *p, float *out)

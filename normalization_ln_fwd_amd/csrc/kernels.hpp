@@ -482,7 +482,14 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     q[e] *= y_scale;
-                store_e4m3<VEC>(ys, cvalid[k] ? off[k] / uint32_t(sizeof(T)) : BUF_OOB, q, wt);
+                const uint32_t off8 = cvalid[k] ? off[k] / uint32_t(sizeof(T)) : BUF_OOB;
+                if constexpr (VEC == 8 && LPR >= 2) {
+                    // lane pairs store 16 codes at once
+                    const bool pvalid = ((k * LPR + (tl ^ 1)) * VEC) < N;
+                    store_e4m3_pair(ys, off8, q, (tl & 1) == 0, pvalid, wt);
+                } else {
+                    store_e4m3<VEC>(ys, off8, q, wt);
+                }
             } else {
                 BIO::store(ys, off[k], IO::pack(yv), wt);
             }
