@@ -73,6 +73,9 @@
  *              NORMFUSE_WT_BYTES sets how many output bytes, counted from
  *              the end of a call, are stored write-through instead of
  *              nontemporal (a cache policy: values do not change).
+ *              NORMFUSE_BWD_SPLIT=0 / 1 turns off / forces the backward's
+ *              split of rows along N (otherwise chosen for few bf16 rows of
+ *              many columns; sums may round differently).
  *   Alignment: pointers must be aligned to their element size.  16-byte
  *              aligned [M, N] / [N] pointers with N a multiple of 16 bytes'
  *              worth of elements take the vectorised kernels; anything else
@@ -203,8 +206,10 @@ norm_status_t softmax_fwd(const void *x, int64_t M, int64_t N, int32_t dtype, vo
 /*
  * norm_bwd_workspace_size -- bytes of device workspace ln_bwd / rms_bwd need
  * for an [M, N] problem of the given dtype on the current device (the
- * per-workgroup dgamma / dbeta / dbias column partials; the size covers a
- * call that asks for dbias).  Writes 0 when none is needed.  The workspace
+ * per-workgroup dgamma / dbeta / dbias column partials, and for rows split
+ * along N their per-chunk row sums; the size covers a call that asks for
+ * dbias).  Writes 0 when none is needed.  Query it under the same tuning
+ * environment as the call.  The workspace
  * needs no initialisation and may be reused by calls ordered on one stream.
  */
 norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_t *bytes);

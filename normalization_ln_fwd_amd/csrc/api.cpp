@@ -32,6 +32,9 @@ norm_status_t check_device()
 // NORMFUSE_{FWD,BWD}_INTERLEAVE     : workgroups per interleave block (A)
 // NORMFUSE_WT_BYTES                 : output bytes, counted from the end,
 //                                     stored write-through (see wt_group)
+// NORMFUSE_BWD_SPLIT                : 0 never splits backward rows along N,
+//                                     1 splits them wherever the kernel can
+//                                     (see bwd_plan)
 // Read on every call (a few getenv lookups, far below launch cost), so a
 // process can change them between calls; tests use them to cross-check
 // shapes and groupings against each other.
@@ -46,6 +49,7 @@ constexpr int kFwdGroupsWide = 4;
 constexpr int kBwdGroupsNarrow = 3;
 constexpr int kBwdRowsWide = 128;
 constexpr int kBwdNarrowMaxK = 16;
+constexpr int64_t kBwdFewGroups = 64;
 // Compute units of the gfx950 parts.  A constant rather than a device query,
 // so that the grid (and with it every summation order, and the workspace
 // size) follows from the call's arguments alone.
@@ -66,6 +70,7 @@ struct Knobs {
     int fwd_k = kFwdGroupsPerWg, bwd_k = kBwdGroupsPerWg;
     int fwd_a = kFwdInterleave, bwd_a = kBwdInterleave;
     double wt_bytes = kWtBytes;
+    int bwd_split = -1; // -1: chosen per shape
 };
 
 // "LPRxVPL" or "LPRxVPLxTEAMS"
@@ -102,6 +107,8 @@ Knobs knobs()
     parse_positive(std::getenv("NORMFUSE_BWD_GROUPS_PER_WG"), &r.bwd_k);
     parse_positive(std::getenv("NORMFUSE_FWD_INTERLEAVE"), &r.fwd_a);
     parse_positive(std::getenv("NORMFUSE_BWD_INTERLEAVE"), &r.bwd_a);
+    if (const char *v = std::getenv("NORMFUSE_BWD_SPLIT"))
+        r.bwd_split = std::atoi(v) != 0 ? 1 : 0;
     if (const char *v = std::getenv("NORMFUSE_WT_BYTES")) {
         const double b = std::atof(v);
         if (b >= 0.0)
@@ -379,7 +386,24 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
 struct BwdLayout {
     size_t level2_off = 0, bytes = 0; // in bytes
     bool two_level = false;
+    // rows split along N: `chunks` column chunks, `blocks` row blocks of
+    // split_k groups of SPLIT_ROWS_PER_GROUP rows; the row sums follow the
+    // column partials at rowsums_off
+    bool split = false;
+    int chunks = 0, blocks = 0, split_k = 0;
+    size_t rowsums_off = 0;
 };
+
+// Backward workgroups with the rows split along N, for few rows of many
+// columns: about two per CU over the grid of (chunk, row block).  Chosen
+// where it measured faster on MI355X (graph replays): bf16 rows of
+// kSplitMinChunks chunks or more, kSplitMinGroups row groups or more, and a
+// whole-row walk that still leaves CUs idle (64 to 384 rows of 16384
+// columns: 6-12% less time).  With fewer chunks or rows, and for fp32
+// beyond 128 rows, the third launch costs more than the split gains.
+constexpr int64_t kSplitTarget = 2 * kCUs;
+constexpr int64_t kSplitMinChunks = 8;
+constexpr int64_t kSplitMinGroups = 64;
 
 // Row groups per backward workgroup: the split of the column reduction over
 // the rows.  Each workgroup's partial row costs N floats per column sum,
@@ -392,7 +416,11 @@ struct BwdLayout {
 //    outweigh the rows themselves).  A fixed 32-row walk left most CUs idle
 //    at small M (64 x 16384 bf16: 102 us, now 18 us) and cut large M into
 //    more partials than needed (32768 x 4096 bf16: 141 us, now 129 us;
-//    8192 x 4096 fp32: 92 us, now 68 us);
+//    8192 x 4096 fp32: 92 us, now 68 us).  Up to kBwdFewGroups row groups
+//    take one workgroup each: their partials are a few MiB at most, the
+//    call is latency-bound, and a second row per workgroup adds its memory
+//    round trip (4 x 16384 bf16: 11.7 us with two rows per workgroup, 9.0 us
+//    with one);
 //  - narrow rows (256-thread workgroups of many rows): about two workgroups
 //    per CU while that takes at most kBwdNarrowMaxK groups each (10-20%
 //    faster than the fixed walk between 16384 and 131072 rows); for more rows
@@ -404,7 +432,9 @@ int bwd_groups_per_wg(int64_t M, const RowShape &sh, int32_t dtype)
     if (sh.lpr >= WIDE_LPR) {
         const int64_t per_cu = dtype == NORM_F32 && sh.capacity() <= 8192 ? 2 : 1;
         const int64_t kmax = std::max(1, kBwdRowsWide / sh.teams);
-        const int64_t kmin = std::min<int64_t>(kmax, (2 + sh.teams - 1) / sh.teams);
+        const int64_t kmin = groups <= kBwdFewGroups
+                                 ? 1
+                                 : std::min<int64_t>(kmax, (2 + sh.teams - 1) / sh.teams);
         const int64_t slots = kCUs * per_cu;
         return int(std::min(kmax, std::max(kmin, (groups + slots - 1) / slots)));
     }
@@ -422,11 +452,36 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, int nb, co
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.bwd_a, w))
         return st;
     *entry = e;
-    const int slices = colsum_slices(w->grid);
+    // Split the rows along N where whole-row workgroups of wide rows leave
+    // CUs idle (fewer workgroups than CUs) and a row spans two chunks or more.
+    const int chunk = split_chunk_cols(dtype);
+    const int64_t chunks = (N + chunk - 1) / chunk;
+    lay->split = vec && M > 0 && e->shape.lpr >= WIDE_LPR && chunks >= 2 &&
+                 (kn.bwd_split == 1 ||
+                  (kn.bwd_split < 0 && dtype == NORM_BF16 && chunks >= kSplitMinChunks &&
+                   w->n_groups >= kSplitMinGroups && w->grid < kCUs));
+    int64_t parts = w->grid;
+    if (lay->split) {
+        constexpr int64_t R = SPLIT_ROWS_PER_GROUP;
+        const int64_t want = std::max<int64_t>(1, kSplitTarget / chunks);
+        const int64_t K = kn.bwd_k > 0 ? kn.bwd_k : std::max<int64_t>(1, (M + R * want - 1) / (R * want));
+        const int64_t blocks = (M + R * K - 1) / (R * K);
+        if (blocks > 65535 || K > INT32_MAX)
+            return NORM_ERR_SHAPE;
+        lay->chunks = int(chunks);
+        lay->blocks = int(blocks);
+        lay->split_k = int(K);
+        parts = blocks;
+    }
+    const int slices = colsum_slices(parts);
     lay->two_level = slices > 1;
     const size_t ld = size_t(colsum_ld(N));
-    lay->level2_off = size_t(nb) * size_t(w->grid) * ld * sizeof(float);
+    lay->level2_off = size_t(nb) * size_t(parts) * ld * sizeof(float);
     lay->bytes = lay->level2_off + (lay->two_level ? size_t(nb) * size_t(slices) * ld * sizeof(float) : 0);
+    if (lay->split) {
+        lay->rowsums_off = lay->bytes;
+        lay->bytes += size_t(M) * size_t(lay->chunks) * 2 * sizeof(float);
+    }
     return NORM_OK;
 }
 
@@ -493,16 +548,31 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         a.wt_group = wt_group(w, e->shape.teams, N, double(es), kn);
         a.eps = eps;
         a.zero_centred = (flags & NORM_ZERO_CENTERED_GAMMA) != 0;
-        const BwdLaunch run = dbias ? (rms ? e->rms_db : e->ln_db) : (rms ? e->rms : e->ln);
-        if (norm_status_t st = launched(run(a, int(w.grid), s)))
-            return st;
+        a.rowsums = nullptr;
+        a.chunks = 0;
+        if (lay.split) {
+            // rows, not row groups, from which dx is stored write-through
+            const double rows_wt = std::ceil(kn.wt_bytes / (double(N) * double(es)));
+            a.wt_group = rows_wt >= double(M) ? 0 : M - int64_t(rows_wt);
+            a.K = lay.split_k;
+            a.rowsums = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.rowsums_off);
+            a.chunks = lay.chunks;
+            if (norm_status_t st =
+                    launched(launch_bwd_split(a, dtype, rms, dbias != nullptr, lay.blocks, s)))
+                return st;
+        } else {
+            const BwdLaunch run = dbias ? (rms ? e->rms_db : e->ln_db) : (rms ? e->rms : e->ln);
+            if (norm_status_t st = launched(run(a, int(w.grid), s)))
+                return st;
+        }
     }
     float *level2 =
         lay.two_level ? reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.level2_off)
                       : nullptr;
     // the mean over the rows instead of the sum (no rows: zeros either way)
     const float divisor = (flags & NORM_DPARAM_MEAN) && M > 0 ? float(M) : 1.f;
-    return launched(launch_colsum(ws, int(w.grid), nb, int(N), dgamma, dbeta, dbias, dparam_dtype,
+    const int parts = lay.split ? lay.blocks : int(w.grid);
+    return launched(launch_colsum(ws, parts, nb, int(N), dgamma, dbeta, dbias, dparam_dtype,
                                   divisor, level2, s));
 }
 

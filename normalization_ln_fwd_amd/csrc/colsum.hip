@@ -19,9 +19,29 @@ hipError_t launch_zero_u32(unsigned *p, hipStream_t s)
 // Thread layouts of the column sums: the slices of many partial rows take
 // 64-column tiles of 16 row subsets; the final sums take 32-column tiles of
 // 128 subsets, so that a few hundred rows of a wide N spread over all CUs
-// with every thread's loads issued at once.
+// with every thread's loads issued at once.  Final sums of at most
+// FEW_ROWS rows take 64-column tiles of 16 subsets instead: an eighth of
+// the waves, which at these counts would mostly idle and still cost their
+// launch (measured on MI355X, whole backward calls: 1 x 16384 bf16 11.7 ->
+// 8.8 us, 1024 x 16384 38.5 -> 35.7 us).
 constexpr int SLICE_QUADS = 16, SLICE_SUB = 16;
 constexpr int FINAL_QUADS = 8, FINAL_SUB = 128;
+constexpr int FEW_QUADS = 16, FEW_SUB = 16, FEW_ROWS = 256;
+
+template <int QUADS, int SUB>
+hipError_t launch_final(const float *src, int rows, int nb, int N, void *dgamma, void *dbeta,
+                        void *dbias, int out_dtype, float divisor, hipStream_t s)
+{
+    const dim3 grid(unsigned((N + 4 * QUADS - 1) / (4 * QUADS)), 1, nb);
+    const dim3 block(QUADS * SUB);
+    if (out_dtype == 1)
+        hipLaunchKernelGGL((colsum_kernel<true, true, QUADS, SUB>), grid, block, 0, s, src, rows, N,
+                           rows, nullptr, dgamma, dbeta, dbias, divisor);
+    else
+        hipLaunchKernelGGL((colsum_kernel<true, false, QUADS, SUB>), grid, block, 0, s, src, rows,
+                           N, rows, nullptr, dgamma, dbeta, dbias, divisor);
+    return hipGetLastError();
+}
 
 hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma, void *dbeta,
                          void *dbias, int out_dtype, float divisor, float *level2, hipStream_t s)
@@ -41,15 +61,11 @@ hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma
         src = level2;
         rows = slices;
     }
-    const dim3 grid(unsigned((N + 4 * FINAL_QUADS - 1) / (4 * FINAL_QUADS)), 1, nb);
-    const dim3 block(FINAL_QUADS * FINAL_SUB);
-    if (out_dtype == 1)
-        hipLaunchKernelGGL((colsum_kernel<true, true, FINAL_QUADS, FINAL_SUB>), grid, block, 0, s,
-                           src, rows, N, rows, nullptr, dgamma, dbeta, dbias, divisor);
-    else
-        hipLaunchKernelGGL((colsum_kernel<true, false, FINAL_QUADS, FINAL_SUB>), grid, block, 0, s,
-                           src, rows, N, rows, nullptr, dgamma, dbeta, dbias, divisor);
-    return hipGetLastError();
+    if (rows <= FEW_ROWS)
+        return launch_final<FEW_QUADS, FEW_SUB>(src, rows, nb, N, dgamma, dbeta, dbias, out_dtype,
+                                                divisor, s);
+    return launch_final<FINAL_QUADS, FINAL_SUB>(src, rows, nb, N, dgamma, dbeta, dbias, out_dtype,
+                                                divisor, s);
 }
 
 } // namespace nf

@@ -40,6 +40,10 @@ struct BwdArgs {
     int64_t wt_group; // row groups from this one on store write-through
     float eps;
     bool zero_centred; // weight = round_T(1 + gamma)
+    // rows split along N (bwd_split_kernel): `chunks` column chunks per row;
+    // rowsums holds the two row sums of every (row, chunk), [M][chunks][2]
+    float *rowsums;
+    int chunks;
 };
 
 typedef hipError_t (*FwdLaunch)(const FwdArgs &, int grid, hipStream_t);
@@ -114,6 +118,14 @@ inline int colsum_slices(int64_t parts)
 {
     return parts <= COLSUM_ONE_LAUNCH ? 1 : int((parts + COLSUM_SPAN - 1) / COLSUM_SPAN);
 }
+// Backward with the rows split along N (few rows of many columns): the
+// columns of one chunk, and the launch of both passes over a grid of
+// (chunks, row blocks) workgroups.
+int split_chunk_cols(int32_t dtype);
+constexpr int SPLIT_ROWS_PER_GROUP = 4; // one row per wave, four waves
+hipError_t launch_bwd_split(const BwdArgs &a, int32_t dtype, bool rms, bool dbias, int blocks,
+                            hipStream_t s);
+
 hipError_t launch_colsum(const float *ws, int parts, int nb, int N, void *dgamma, void *dbeta,
                          void *dbias, int out_dtype, float divisor, float *level2, hipStream_t s);
 

@@ -898,6 +898,185 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Backward with the rows split along N, for few rows of many columns, where
+// whole-row workgroups cannot fill the GPU.  Row sums need the whole row, so
+// the work takes two passes over a grid of (chunk s, row block b)
+// workgroups: chunk s is SPLIT_VPL * 64 * VEC columns, and a row block is K
+// groups of SPLIT_ROWS_PER_GROUP rows (one row per wave).
+//  pass 0: each wave's two row sums over its chunk go to rowsums[row][s];
+//          with mean and rstd given, the chunk's dgamma / dbeta column
+//          partials are added as well;
+//  pass 1: the row sums of all chunks are added in chunk order, giving the
+//          row's c1, c2 (and rstd when it is recomputed); dx of the chunk is
+//          stored, and the dbias partials (and dgamma / dbeta when rstd is
+//          recomputed) are added.
+// Each pass folds its partials over the four waves in wave order into row b
+// of the workspace blocks, at the chunk's columns, for the usual column sums.
+// The second pass reads x and dy again; at these sizes they come from the
+// last-level cache.
+// ---------------------------------------------------------------------------
+constexpr int SPLIT_VPL = 4;
+template <typename T, int VEC>
+constexpr int split_cols()
+{
+    return 64 * SPLIT_VPL * VEC;
+}
+
+template <typename T, int VEC, bool RMS, bool DB, int PASS>
+__global__ void __launch_bounds__(64 * SPLIT_ROWS_PER_GROUP) bwd_split_kernel(const BwdArgs a)
+{
+    using IO = VecIO<T, VEC>;
+    using BIO = BufIO<T, VEC>;
+    using Raw = typename IO::Raw;
+    constexpr int E = SPLIT_VPL * VEC;
+    constexpr int C = split_cols<T, VEC>();
+    constexpr int W = SPLIT_ROWS_PER_GROUP;
+    __shared__ float fold[W][C];
+
+    const int s = blockIdx.x, b = blockIdx.y;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x & 63;
+    const int N = a.N, S = a.chunks;
+    const bool recompute = RMS && a.rstd == nullptr;
+    // which column partials this pass adds
+    const bool add_gb = PASS == 0 ? !recompute : recompute;
+    const bool add_d = PASS == 1 && DB;
+
+    bool cvalid[SPLIT_VPL];
+    uint32_t off[SPLIT_VPL];
+#pragma unroll
+    for (int k = 0; k < SPLIT_VPL; ++k) {
+        const int col = s * C + (k * 64 + lane) * VEC;
+        cvalid[k] = col < N;
+        off[k] = cvalid[k] ? uint32_t(col) * uint32_t(sizeof(T)) : BUF_OOB;
+    }
+    Raw pg[SPLIT_VPL];
+    load_param_regs<T, VEC, SPLIT_VPL>(pg, a.gamma, N, off, true, a.zero_centred);
+
+    float acc_g[E], acc_b[E], acc_d[DB ? E : 1];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        acc_g[e] = 0.f;
+        acc_b[e] = 0.f;
+        if constexpr (DB)
+            acc_d[e] = 0.f;
+    }
+    const uint32_t row_bytes = uint32_t(N) * uint32_t(sizeof(T));
+    for (int kk = 0; kk < a.K; ++kk) {
+        const int64_t row = (int64_t(b) * a.K + kk) * W + wave;
+        if (row >= a.M)
+            break; // uniform over the wave; no barrier in this loop
+        const int64_t byte0 = row * int64_t(row_bytes);
+        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + byte0, row_bytes);
+        const rsrc_t ds = make_rsrc(static_cast<const char *>(a.dy) + byte0, row_bytes);
+        Raw xr[SPLIT_VPL], dr[SPLIT_VPL];
+#pragma unroll
+        for (int k = 0; k < SPLIT_VPL; ++k) {
+            xr[k] = BIO::load(xs, off[k]);
+            dr[k] = BIO::load(ds, off[k]);
+        }
+        const float mean = RMS ? 0.f : a.mean[row];
+        float rstd = recompute ? 0.f : a.rstd[row];
+        float c1 = 0.f, c2 = 0.f;
+        if constexpr (PASS == 0) {
+            // row sums over the chunk, g = dy * gamma (invalid columns hold 0):
+            //   LN: sum g (x - mean), sum g;  RMS: sum g x (, sum x^2)
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int k = 0; k < SPLIT_VPL; ++k) {
+                float xv[VEC], dv[VEC], gv[VEC];
+                IO::unpack(xr[k], xv);
+                IO::unpack(dr[k], dv);
+                IO::unpack(pg[k], gv);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const float g = dv[e] * gv[e];
+                    if constexpr (!RMS) {
+                        s0 = fmaf(g, xv[e] - mean, s0);
+                        s1 += g;
+                    } else {
+                        s0 = fmaf(g, xv[e], s0);
+                        if (recompute)
+                            s1 = fmaf(xv[e], xv[e], s1);
+                    }
+                }
+            }
+            s0 = group_reduce<64, OpSum>(s0);
+            s1 = group_reduce<64, OpSum>(s1);
+            if (lane == 0) {
+                a.rowsums[(row * S + s) * 2] = s0;
+                a.rowsums[(row * S + s) * 2 + 1] = s1;
+            }
+        } else {
+            // the row's sums: the chunks' sums added in chunk order
+            float s0 = 0.f, s1 = 0.f;
+            for (int q = 0; q < S; ++q) {
+                s0 += a.rowsums[(row * S + q) * 2];
+                s1 += a.rowsums[(row * S + q) * 2 + 1];
+            }
+            if (recompute)
+                rstd = rsqrtf(s1 / float(N) + a.eps);
+            c1 = rstd * (s0 / float(N));
+            c2 = RMS ? 0.f : s1 / float(N);
+        }
+        const float k1 = -rstd * c1, k2 = -rstd * c2;
+        const rsrc_t dxs = make_rsrc(static_cast<char *>(a.dx) + byte0, row_bytes);
+#pragma unroll
+        for (int k = 0; k < SPLIT_VPL; ++k) {
+            float xv[VEC], dv[VEC], gv[VEC], dxv[VEC];
+            IO::unpack(xr[k], xv);
+            IO::unpack(dr[k], dv);
+            IO::unpack(pg[k], gv);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int i = k * VEC + e;
+                const float xh = RMS ? xv[e] * rstd : (xv[e] - mean) * rstd;
+                if (add_gb && cvalid[k]) {
+                    acc_g[i] = fmaf(dv[e], xh, acc_g[i]);
+                    acc_b[i] += dv[e];
+                }
+                if constexpr (PASS == 1) {
+                    dxv[e] = fmaf(xh, k1, fmaf(dv[e] * gv[e], rstd, k2));
+                    if constexpr (DB)
+                        if (cvalid[k])
+                            acc_d[i] += dxv[e];
+                }
+            }
+            if constexpr (PASS == 1)
+                BIO::store(dxs, off[k], IO::pack(dxv), row >= a.wt_group);
+        }
+    }
+
+    // ---- fold the four waves' partials (wave order) into row b ----
+    const int64_t ld = colsum_ld(N);
+    auto fold_store = [&](const float *acc, float *dst) {
+#pragma unroll
+        for (int k = 0; k < SPLIT_VPL; ++k) {
+            const int c = (k * 64 + lane) * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                fold[wave][c + e] = acc[k * VEC + e];
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < C; c += 64 * W) {
+            const int col = s * C + c;
+            float v = fold[0][c];
+#pragma unroll
+            for (int w = 1; w < W; ++w)
+                v += fold[w][c];
+            if (col < N)
+                dst[col] = v;
+        }
+        __syncthreads();
+    };
+    if (add_gb) { // uniform
+        fold_store(acc_g, a.ws + (int64_t)b * ld);
+        fold_store(acc_b, a.ws + (int64_t)gridDim.y * ld + (int64_t)b * ld);
+    }
+    if (add_d)
+        fold_store(acc_d, a.ws + 2 * (int64_t)gridDim.y * ld + (int64_t)b * ld);
+}
+
+// ---------------------------------------------------------------------------
 // Row softmax in one pass over HBM: per row group the rows are loaded once,
 // the team takes the row max, then sum_j exp(x_j - max) with the exponentials
 // kept in registers, and stores exp(x_j - max) / sum.

@@ -206,6 +206,44 @@ def test_bwd_row_splits_match_oracle(M, N, rms, dtype):
     assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
 
 
+# Few rows of many columns: the rows are split along N into column chunks
+# (two passes: chunk row sums, then dx).  Each shape runs with the split
+# forced on and off; ragged M (not a multiple of the four rows of a group),
+# a ragged last chunk, one row, and a forced split at larger M (several
+# groups per row block).
+SPLIT_N_SHAPES = [(1, 4096), (3, 16384), (16, 16384), (64, 16384), (255, 8192), (7, 3000),
+                  (130, 2056), (1030, 4096)]
+
+
+@pytest.mark.parametrize("M,N", SPLIT_N_SHAPES)
+@pytest.mark.parametrize("case", ["ln-bf16", "rms-f32", "rms-bf16-recompute", "ln-f32"])
+@pytest.mark.parametrize("split", ["1", "0"], ids=["split", "whole"])
+def test_bwd_split_along_n_matches_oracle(M, N, case, split, monkeypatch):
+    rms = case.startswith("rms")
+    dtype = F32 if "f32" in case else BF16
+    recompute = case.endswith("recompute")
+    monkeypatch.setenv("NORMFUSE_BWD_SPLIT", split)
+    inp, eps = make_case(M, N, dtype, rms, seed=M * 5 + N)
+    out = run_bwd(rms, inp, dtype, eps, recompute=recompute, dparam_dtype=torch.float32,
+                  want_dbias=True)
+    ref = oracle_bwd(rms, inp, dtype, eps, recompute=recompute, want_dbias=True)
+    assert_rows_close(f64(out["dx"]), ref["dx"], dtype, "dx",
+                      scale=dx_term_scale(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+    for k in ("dgamma",) + (() if rms else ("dbeta",)):
+        assert_colsums_close(f64(out[k]), ref[k], ref[k + "_l2"], COLSUM_REL_SMALL, k)
+    l2 = np.maximum(ref["dbias_l2"], dbias_term_l2(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+    assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
+
+
+def test_bwd_split_along_n_is_deterministic(monkeypatch):
+    monkeypatch.setenv("NORMFUSE_BWD_SPLIT", "1")
+    inp, eps = make_case(200, 16384, BF16, False, seed=3)
+    a = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32, want_dbias=True)
+    b = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32, want_dbias=True)
+    for k in ("dx", "dgamma", "dbeta", "dbias"):
+        assert torch.equal(a[k], b[k]), k
+
+
 def test_bwd_is_deterministic():
     inp, eps = make_case(20000, 384, BF16, False, seed=8)
     a = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32)
