@@ -46,9 +46,7 @@ constexpr int kBwdGroupsPerWg = 0; // 0: chosen per shape (see bwd_plan)
 // sets how many rows one column partial covers, i.e. how finely the column
 // reduction is split over the rows (see bwd_groups_per_wg).
 constexpr int kFwdGroupsWide = 4;
-constexpr int kBwdGroupsNarrow = 3;
 constexpr int kBwdRowsWide = 128;
-constexpr int kBwdNarrowMaxK = 16;
 constexpr int64_t kBwdFewGroups = 64;
 // Compute units of the gfx950 parts.  A constant rather than a device query,
 // so that the grid (and with it every summation order, and the workspace
@@ -114,6 +112,7 @@ Knobs knobs()
         if (b >= 0.0)
             r.wt_bytes = b;
     }
+
     return r;
 }
 
@@ -208,12 +207,12 @@ norm_status_t plan_walk(int64_t M, int teams, int K, int A, Walk *w)
 // about ascending order (the walk's blocks of workgroups are dispatched in
 // order and step through their groups together), so these are the last
 // stores of the kernel.
-int64_t wt_group(const Walk &w, int teams, int64_t N, double out_bytes, const Knobs &kn)
+int64_t wt_group(const Walk &w, int teams, int64_t N, double out_bytes, double wt_bytes)
 {
     const double per_group = double(teams) * double(N) * out_bytes;
     if (per_group <= 0.0)
         return w.n_groups;
-    const double g = std::ceil(kn.wt_bytes / per_group);
+    const double g = std::ceil(wt_bytes / per_group);
     return g >= double(w.n_groups) ? 0 : w.n_groups - int64_t(g);
 }
 
@@ -318,7 +317,7 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     a.K = w.K;
     a.A = w.A;
     a.wt_group = wt_group(w, e->shape.teams, N,
-                          double(y ? (f8 ? 1 : es) : 0) + double(residual_out ? es : 0), kn);
+                          double(y ? (f8 ? 1 : es) : 0) + double(residual_out ? es : 0), kn.wt_bytes);
     a.eps = eps;
     a.zero_centred = (flags & NORM_ZERO_CENTERED_GAMMA) != 0;
     const FwdLaunch run = f8 ? (rms ? e->rms_f8 : e->ln_f8) : (rms ? e->rms : e->ln);
@@ -374,7 +373,7 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
     a.N = int(N);
     a.K = w.K;
     a.A = w.A;
-    a.wt_group = wt_group(w, e->shape.teams, N, double(es), kn);
+    a.wt_group = wt_group(w, e->shape.teams, N, double(es), kn.wt_bytes);
     return launched(e->run(a, int(w.grid), static_cast<hipStream_t>(stream)));
 }
 
@@ -421,11 +420,15 @@ constexpr int64_t kSplitMinGroups = 64;
 //    call is latency-bound, and a second row per workgroup adds its memory
 //    round trip (4 x 16384 bf16: 11.7 us with two rows per workgroup, 9.0 us
 //    with one);
-//  - narrow rows (256-thread workgroups of many rows): about two workgroups
-//    per CU while that takes at most kBwdNarrowMaxK groups each (10-20%
-//    faster than the fixed walk between 16384 and 131072 rows); for more rows
-//    short walks of kBwdGroupsNarrow groups, many workgroups deep, which
-//    balance best.
+//  - narrow rows (256-thread workgroups of many rows): two workgroups per
+//    CU, each walking its share of the groups, at every M.  Exactly two per
+//    CU matters: grids of three or four per CU, of one, or many workgroups
+//    deep with short walks are all slower.  Against walks of 3 groups many
+//    workgroups deep, bf16: 576000 x 384 222.5 -> 218.6 us (with dbias
+//    228.7 -> 220.4 us), 262144 x 768 209 -> 194.5 us, 131072 x 1024 143 ->
+//    126 us, 65536 x 2048 154 -> 127 us, 1048576 x 256 270 -> 263 us; fp32
+//    576000 x 384 460 -> 447 us, 262144 x 1024 571 -> 536 us.  (4 per CU
+//    at 524288 x 384: 210 us, 2 per CU: 196 us, 1 per CU: 276 us.)
 int bwd_groups_per_wg(int64_t M, const RowShape &sh, int32_t dtype)
 {
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
@@ -438,8 +441,7 @@ int bwd_groups_per_wg(int64_t M, const RowShape &sh, int32_t dtype)
         const int64_t slots = kCUs * per_cu;
         return int(std::min(kmax, std::max(kmin, (groups + slots - 1) / slots)));
     }
-    const int64_t k = (groups + 2 * kCUs - 1) / (2 * kCUs);
-    return k <= kBwdNarrowMaxK ? int(std::max<int64_t>(1, k)) : kBwdGroupsNarrow;
+    return int(std::max<int64_t>(1, (groups + 2 * kCUs - 1) / (2 * kCUs)));
 }
 
 norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, int nb, const Knobs &kn,
@@ -545,7 +547,7 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         a.N = int(N);
         a.K = w.K;
         a.A = w.A;
-        a.wt_group = wt_group(w, e->shape.teams, N, double(es), kn);
+        a.wt_group = wt_group(w, e->shape.teams, N, double(es), kn.wt_bytes);
         a.eps = eps;
         a.zero_centred = (flags & NORM_ZERO_CENTERED_GAMMA) != 0;
         a.rowsums = nullptr;
