@@ -235,6 +235,35 @@ def test_bwd_split_along_n_matches_oracle(M, N, case, split, monkeypatch):
     assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
 
 
+@pytest.mark.parametrize("M,N", [(64, 16384), (13, 4096)])
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+def test_bwd_split_along_n_options(M, N, rms, monkeypatch):
+    """Zero-centred gamma and the mean epilogue on the split path: against
+    the oracle run with the same options."""
+    monkeypatch.setenv("NORMFUSE_BWD_SPLIT", "1")
+    inp, eps = make_case(M, N, BF16, rms, seed=M + 3 * N)
+    dy, x, g = (to_dev(inp[k], BF16) for k in ("dy", "x", "gamma"))
+    rstd = torch.from_numpy(inp["rstd"]).cuda()
+    kw = dict(dparam_dtype=torch.float32, want_dbias=True, zero_centered_gamma=True,
+              dparam_mean=True)
+    if rms:
+        out = nf.rms_bwd(dy, x, g, rstd, eps, **kw)
+    else:
+        out = nf.ln_bwd(dy, x, g, torch.from_numpy(inp["mean"]).cuda(), rstd, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.norm_bwd(inp["dy"], inp["x"], inp["gamma"], None if rms else inp["mean"],
+                          inp["rstd"], eps, rms=rms, dtype=BF16, want_dbias=True,
+                          zero_centered_gamma=True, dparam_mean=True)
+    w = (to_dev(inp["gamma"], BF16).float() + 1.0).to(torch.bfloat16)
+    wh = from_dev(w, BF16)
+    assert_rows_close(f64(out["dx"]), ref["dx"], BF16, "dx",
+                      scale=dx_term_scale(inp["dy"], wh, ref["rstd"], BF16))
+    for k in ("dgamma",) + (() if rms else ("dbeta",)):
+        assert_colsums_close(f64(out[k]), ref[k], ref[k + "_l2"], COLSUM_REL_SMALL, k)
+    l2 = np.maximum(ref["dbias_l2"], dbias_term_l2(inp["dy"], wh, ref["rstd"], BF16) / M)
+    assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
+
+
 def test_bwd_split_along_n_is_deterministic(monkeypatch):
     monkeypatch.setenv("NORMFUSE_BWD_SPLIT", "1")
     inp, eps = make_case(200, 16384, BF16, False, seed=3)
