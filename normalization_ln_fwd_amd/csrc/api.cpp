@@ -148,12 +148,14 @@ constexpr int64_t kFwdFewGroups = 4096;
 // Row groups per forward workgroup.  Measured on MI355X: one workgroup per
 // CU walking up to kFwdGroupsWide groups suits wide rows and, up to
 // kFwdFewGroups groups, narrow ones too (16384 x 1024: 35 -> 25 us);
-// narrow rows in larger numbers run one group per workgroup.  With amax, at
+// narrow rows in larger numbers run one group per workgroup, or two with
+// an FP8 y (576000 x 384: 268 -> 259 us, 262144 x 768: 238 -> 233 us,
+// 65536 x 2048: 162 -> 151 us; 131072 x 1024 is 3% slower).  With amax, at
 // most kMaxAmaxWgs workgroups.
-int fwd_groups_per_wg(int64_t M, const RowShape &sh, bool amax)
+int fwd_groups_per_wg(int64_t M, const RowShape &sh, bool amax, bool f8)
 {
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
-    int64_t k = 1;
+    int64_t k = f8 ? 2 : 1;
     if (sh.lpr >= WIDE_LPR || groups <= kFwdFewGroups)
         k = std::min<int64_t>(kFwdGroupsWide, std::max<int64_t>(1, (groups + kCUs - 1) / kCUs));
     if (amax)
@@ -286,7 +288,7 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     const FwdEntry *e = fwd_entry(dtype, vec, M, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, e->shape, amax != nullptr);
+    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, e->shape, amax != nullptr, f8);
     Walk w;
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
         return st;
@@ -362,7 +364,7 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
         }
     }
     Walk w;
-    const int K = fwd_groups_per_wg(M, e->shape, false);
+    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, e->shape, false, false);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
         return st;
     SoftmaxArgs a;
