@@ -273,6 +273,22 @@ def test_bwd_split_along_n_is_deterministic(monkeypatch):
         assert torch.equal(a[k], b[k]), k
 
 
+@pytest.mark.parametrize("M,N,dtype", [(20000, 384, BF16), (9000, 1000, F32), (3000, 4096, BF16)])
+def test_bwd_many_partial_rows_two_level_sums(M, N, dtype, monkeypatch):
+    """One row group per workgroup (forced) leaves more than 512 partial
+    rows, which the column sums add in two launches."""
+    monkeypatch.setenv("NORMFUSE_BWD_GROUPS_PER_WG", "1")
+    inp, eps = make_case(M, N, dtype, False, seed=M + N)
+    out = run_bwd(False, inp, dtype, eps, dparam_dtype=torch.float32, want_dbias=True)
+    ref = oracle_bwd(False, inp, dtype, eps, want_dbias=True)
+    assert_rows_close(f64(out["dx"]), ref["dx"], dtype, "dx",
+                      scale=dx_term_scale(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+    for k in ("dgamma", "dbeta"):
+        assert_colsums_close(f64(out[k]), ref[k], ref[k + "_l2"], COLSUM_REL_SMALL, k)
+    l2 = np.maximum(ref["dbias_l2"], dbias_term_l2(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+    assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
+
+
 def test_bwd_is_deterministic():
     inp, eps = make_case(20000, 384, BF16, False, seed=8)
     a = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32)
