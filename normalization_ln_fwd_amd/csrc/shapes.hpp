@@ -4,9 +4,11 @@
 //
 // 16-byte path (VEC = 16 / sizeof(T)); narrow rows in workgroups of 256
 // threads (the forward adds 512-thread variants), wide rows in teams of
-// 512 threads:
-//   bf16 capacities: 64 128 256 384 512 768 1024 1536 2048 4096 8192 16384
-//   fp32 capacities: 32 64 128 192 256 384 512 768 1024 2048 4096 8192 16384
+// 320 to 512 threads:
+//   bf16 capacities: 64 128 256 384 512 768 1024 1536 2048 2560 3072 4096
+//                    8192 16384
+//   fp32 capacities: 32 64 128 192 256 384 512 768 1024 1280 1536 2048 4096
+//                    8192 16384
 // Element-wise path (VEC = 1), for rows that are not whole 16-byte vectors
 // or pointers that are not 16-byte aligned: 256 512 1024 4096 16384.
 #pragma once
@@ -23,14 +25,19 @@
     X(T, VEC, 64, 3, 4)                                                                          \
     X(T, VEC, 64, 4, 4)
 
-// Wide rows, several waves per row: teams of 512 lanes holding one vector
-// each, two rows per workgroup, at twice the narrow capacity; beyond that one
-// team per workgroup, holding 2 or 4 vectors per lane.  (Teams of 256 lanes
+// Wide rows, several waves per row: teams of 320, 384 or 512 lanes holding
+// one vector each, two rows per workgroup, up to twice the narrow capacity;
+// beyond that one team of 512 lanes per workgroup, holding 2 or 4 vectors
+// per lane.  (Rows of 2304-3072 bf16 columns on teams of 320 or 384 lanes
+// instead of 512 with idle lanes, measured on MI355X at 32768 rows: forward
+// 61-73% -> 70-75% of peak, backward 56-71% -> 68-79%.)  (Teams of 256 lanes
 // holding 4 vectors, measured on MI355X for the 8192-column bf16 rows: the
 // backward at 32768 x 8192 took 299 us against 252 us, the forward at
 // 8192 x 8192 90 us against 87 us; their 212 registers leave 2 waves per
 // SIMD.)
 #define NF_SHAPES_WIDE(X, T, VEC)                                                                \
+    X(T, VEC, 320, 1, 2)                                                                         \
+    X(T, VEC, 384, 1, 2)                                                                         \
     X(T, VEC, 512, 1, 2)                                                                         \
     X(T, VEC, 512, 2, 1)                                                                         \
     X(T, VEC, 512, 4, 1)

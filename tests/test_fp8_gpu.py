@@ -21,7 +21,8 @@ from tolerance import assert_rows_close
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520), (33, 1024),
-          (17, 1536), (40, 4096), (43, 4096), (5, 5000), (3, 16384), (2, 16383)]
+          (17, 1536), (40, 4096), (43, 4096), (5, 5000), (3, 16384), (2, 16383), (21, 2560),
+          (13, 1200)]
 
 
 @pytest.fixture(autouse=True)
