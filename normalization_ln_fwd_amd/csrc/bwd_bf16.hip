@@ -11,7 +11,7 @@ namespace nf {
      &launch_bwd<T, VEC, LPR, VPL, TEAMS, false, true>,                                           \
      &launch_bwd<T, VEC, LPR, VPL, TEAMS, true, true>},
 
-static const BwdEntry k_vec[] = {NF_SHAPES_BF16_VEC(NF_ENTRY)};
+static const BwdEntry k_vec[] = {NF_SHAPES_BF16_BWD_VEC(NF_ENTRY)};
 static const BwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, bf16)};
 
 const BwdEntry *bwd_table_bf16(bool vectorised, int *count)

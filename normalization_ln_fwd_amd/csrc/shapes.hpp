@@ -6,7 +6,7 @@
 // threads (the forward adds 512-thread variants), wide rows in teams of
 // 320 to 512 threads:
 //   bf16 capacities: 64 128 256 384 512 768 1024 1536 2048 2560 3072 4096
-//                    8192 16384
+//                    (backward: 5120 6144) 8192 16384
 //   fp32 capacities: 32 64 128 192 256 384 512 768 1024 1280 1536 2048 4096
 //                    8192 16384
 // Element-wise path (VEC = 1), for rows that are not whole 16-byte vectors
@@ -35,14 +35,27 @@
 // backward at 32768 x 8192 took 299 us against 252 us, the forward at
 // 8192 x 8192 90 us against 87 us; their 212 registers leave 2 waves per
 // SIMD.)
-#define NF_SHAPES_WIDE(X, T, VEC)                                                                \
+#define NF_SHAPES_WIDE_ONE_VEC(X, T, VEC)                                                        \
     X(T, VEC, 320, 1, 2)                                                                         \
     X(T, VEC, 384, 1, 2)                                                                         \
-    X(T, VEC, 512, 1, 2)                                                                         \
+    X(T, VEC, 512, 1, 2)
+#define NF_SHAPES_WIDE_MULTI_VEC(X, T, VEC)                                                      \
     X(T, VEC, 512, 2, 1)                                                                         \
     X(T, VEC, 512, 4, 1)
+#define NF_SHAPES_WIDE(X, T, VEC) NF_SHAPES_WIDE_ONE_VEC(X, T, VEC) NF_SHAPES_WIDE_MULTI_VEC(X, T, VEC)
 
 #define NF_SHAPES_BF16_VEC(X) NF_SHAPES_NARROW(X, bf16, 8) NF_SHAPES_WIDE(X, bf16, 8)
+// The bf16 backward also runs rows of 4097-6144 columns on one team of 640
+// or 768 lanes holding one vector each, instead of 512 lanes holding two
+// with idle lanes.  Measured on MI355X: 32768 x 5120 219 -> 180 us,
+// 32768 x 6144 230 -> 198 us, 8192 x 5120 62 -> 51 us.  The forward gains
+// nothing there (-7% to +2%), nor does either direction in fp32.
+#define NF_SHAPES_BF16_BWD_VEC(X)                                                                \
+    NF_SHAPES_NARROW(X, bf16, 8)                                                                 \
+    NF_SHAPES_WIDE_ONE_VEC(X, bf16, 8)                                                           \
+    X(bf16, 8, 640, 1, 1)                                                                        \
+    X(bf16, 8, 768, 1, 1)                                                                        \
+    NF_SHAPES_WIDE_MULTI_VEC(X, bf16, 8)
 #define NF_SHAPES_F32_VEC(X)                                                                     \
     NF_SHAPES_NARROW(X, float, 4) NF_SHAPES_WIDE(X, float, 4) X(float, 4, 1024, 4, 1)
 
