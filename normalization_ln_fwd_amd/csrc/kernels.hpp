@@ -246,6 +246,24 @@ __device__ __forceinline__ void param_vec(const float *lds, const Raw &reg, int 
         VecIO<T, VEC>::unpack(reg, out);
 }
 
+// Whether the forward walk keeps the next row group's loads in flight (wide
+// teams): the rows of two groups, packed, and the parameters held in
+// registers when they are not staged in LDS (3 VPL vectors) must fit the
+// wave's share of the 512 VGPRs of a SIMD with about 24 to spare.  The
+// widest fp32 rows (1024 lanes x 4 vectors) and the element-wise rows of
+// 1024 lanes x 16 do not fit: with the prefetch they spilled about 200
+// registers to scratch and ran at 16% of the HBM peak.
+template <typename T, int VEC, int LPR, int VPL, int TEAMS>
+constexpr bool fwd_prefetch()
+{
+    constexpr int raw = VEC * int(sizeof(T)) >= 4 ? VEC * int(sizeof(T)) / 4 : 1;
+    constexpr int waves_per_simd = (LPR * TEAMS / 64 + 3) / 4;
+    constexpr int share = 512 / waves_per_simd;
+    constexpr bool plds = LPR * VPL * VEC <= PARAMS_LDS_MAX;
+    constexpr int need = 4 * VPL * raw + (plds ? 0 : 3 * VPL * raw) + 24;
+    return LPR >= WIDE_LPR && need <= share;
+}
+
 // ---------------------------------------------------------------------------
 // Forward: t = (x + bias) + residual (fp32), u = round(t) -> residual_out,
 // statistics of u, y = normalise(u) * gamma + beta -> y, running max |y|.
@@ -259,7 +277,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     constexpr int WG = LPR * TEAMS;
     constexpr int CAP = LPR * VPL * VEC;
     constexpr bool PLDS = CAP <= PARAMS_LDS_MAX;
-    constexpr bool PREFETCH = LPR >= WIDE_LPR;
+    constexpr bool PREFETCH = fwd_prefetch<T, VEC, LPR, VPL, TEAMS>();
     static_assert(WG % 64 == 0, "workgroup of whole waves");
 
     __shared__ float red_lds[TeamLds<LPR, TEAMS, 1>::size];
