@@ -133,6 +133,8 @@ const Entry *pick_shape(const Entry *tab, int n, int N, int force_lpr, int force
     return nullptr;
 }
 
+size_t elem_size(int32_t dtype) { return dtype == NORM_F32 ? 4 : 2; }
+
 // Forward workgroups.  The forward's amax combines one atomicMax per
 // workgroup on a single address; such atomics serialise, and past about
 // kMaxAmaxWgs workgroups per launch they start to cost more than the kernel
@@ -150,12 +152,18 @@ constexpr int64_t kFwdFewGroups = 4096;
 // kFwdFewGroups groups, narrow ones too (16384 x 1024: 35 -> 25 us);
 // narrow rows in larger numbers run one group per workgroup, or two with
 // an FP8 y (576000 x 384: 268 -> 259 us, 262144 x 768: 238 -> 233 us,
-// 65536 x 2048: 162 -> 151 us; 131072 x 1024 is 3% slower).  With amax, at
-// most kMaxAmaxWgs workgroups.
-int fwd_groups_per_wg(int64_t M, const RowShape &sh, bool amax, bool f8)
+// 65536 x 2048: 162 -> 151 us; 131072 x 1024 is 3% slower) -- or as many
+// as make kFwdMinGroupBytes of each tensor per workgroup: small groups pay
+// their workgroup's set-up (staging the parameters, the final amax) too
+// often (524288 x 256 bf16, 16 KiB per group: 225 -> 174 us with two;
+// 4-byte vectors at 65536 x 386, 3 KiB: 195 -> 54 us with eight).  With
+// amax, at most kMaxAmaxWgs workgroups.
+constexpr double kFwdMinGroupBytes = 24.0 * 1024;
+int fwd_groups_per_wg(int64_t M, int64_t N, int32_t dtype, const RowShape &sh, bool amax, bool f8)
 {
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
-    int64_t k = f8 ? 2 : 1;
+    const double group_bytes = double(sh.teams) * double(N) * double(elem_size(dtype));
+    int64_t k = std::max<int64_t>(f8 ? 2 : 1, int64_t(std::ceil(kFwdMinGroupBytes / group_bytes)));
     if (sh.lpr >= WIDE_LPR || groups <= kFwdFewGroups)
         k = std::min<int64_t>(kFwdGroupsWide, std::max<int64_t>(1, (groups + kCUs - 1) / kCUs));
     if (amax)
@@ -163,7 +171,7 @@ int fwd_groups_per_wg(int64_t M, const RowShape &sh, bool amax, bool f8)
     return int(std::max<int64_t>(1, k));
 }
 
-const FwdEntry *fwd_entry(int dtype, bool vec, int64_t M, int N, const Knobs &k)
+const FwdEntry *fwd_entry(int dtype, int vec, int64_t M, int N, const Knobs &k)
 {
     int n = 0;
     const FwdEntry *tab = dtype == NORM_F32 ? fwd_table_f32(vec, &n) : fwd_table_bf16(vec, &n);
@@ -179,7 +187,7 @@ const FwdEntry *fwd_entry(int dtype, bool vec, int64_t M, int N, const Knobs &k)
     return e;
 }
 
-const BwdEntry *bwd_entry(int dtype, bool vec, int N, const Knobs &k)
+const BwdEntry *bwd_entry(int dtype, int vec, int N, const Knobs &k)
 {
     int n = 0;
     const BwdEntry *tab = dtype == NORM_F32 ? bwd_table_f32(vec, &n) : bwd_table_bf16(vec, &n);
@@ -219,7 +227,6 @@ int64_t wt_group(const Walk &w, int teams, int64_t N, double out_bytes, double w
 }
 
 // ------------------------------------------------------------- validation
-size_t elem_size(int32_t dtype) { return dtype == NORM_F32 ? 4 : 2; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -236,17 +243,29 @@ norm_status_t check_shape(int64_t M, int64_t N)
 
 bool eps_ok(float eps) { return std::isfinite(eps) && eps >= 0.f; }
 
-// 16-byte path: whole 16-byte vectors per row and 16-byte aligned tensors.
-bool vectorisable(int64_t N, int32_t dtype, std::initializer_list<const void *> ptrs)
+// Elements per vector access of a call: the widest access of 16, 8 or 4
+// bytes (fp32: 16 or 8) that holds whole elements of every row (N a
+// multiple of it) and that every pointer is aligned to; else 1.  `f8_y`: an
+// FP8 output of one byte per element, aligned to the element count.
+int vec_width(int64_t N, int32_t dtype, std::initializer_list<const void *> ptrs,
+              const void *f8_y = nullptr)
 {
-    const int vec = int(16 / elem_size(dtype));
-    if (N % vec != 0)
-        return false;
-    for (const void *p : ptrs)
-        if (p && !aligned(p, 16))
-            return false;
-    return true;
+    const int es = int(elem_size(dtype));
+    const int min_bytes = dtype == NORM_F32 ? 8 : 4;
+    for (int bytes = 16; bytes >= min_bytes; bytes /= 2) {
+        const int v = bytes / es;
+        if (N % v != 0)
+            continue;
+        bool ok = f8_y == nullptr || aligned(f8_y, size_t(v));
+        for (const void *p : ptrs)
+            ok = ok && (p == nullptr || aligned(p, size_t(bytes)));
+        if (ok)
+            return v;
+    }
+    return 1;
 }
+
+int full_width(int32_t dtype) { return int(16 / elem_size(dtype)); }
 
 norm_status_t launched(hipError_t e) { return e == hipSuccess ? NORM_OK : NORM_ERR_LAUNCH; }
 
@@ -281,14 +300,14 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     if (norm_status_t st = check_device())
         return st;
     const Knobs kn = knobs();
-    // FP8 codes of a 16-byte vector of elements take 16 / es bytes
-    const bool vec = vectorisable(N, dtype, {x, bias, residual, gamma, beta,
-                                             f8 ? nullptr : y, residual_out}) &&
-                     (!f8 || !y || aligned(y, 16 / es));
+    // FP8 codes of a vector of v elements take v bytes
+    const int vec = vec_width(N, dtype, {x, bias, residual, gamma, beta, f8 ? nullptr : y,
+                                         residual_out},
+                              f8 ? y : nullptr);
     const FwdEntry *e = fwd_entry(dtype, vec, M, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, e->shape, amax != nullptr, f8);
+    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, amax != nullptr, f8);
     Walk w;
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
         return st;
@@ -347,7 +366,7 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
     if (M == 0)
         return NORM_OK;
     const Knobs kn = knobs();
-    const bool vec = vectorisable(N, dtype, {x, y});
+    const int vec = vec_width(N, dtype, {x, y});
     int n = 0;
     const SoftmaxEntry *tab =
         dtype == NORM_F32 ? softmax_table_f32(vec, &n) : softmax_table_bf16(vec, &n);
@@ -364,7 +383,7 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
         }
     }
     Walk w;
-    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, e->shape, false, false);
+    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, false, false);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
         return st;
     SoftmaxArgs a;
@@ -446,7 +465,7 @@ int bwd_groups_per_wg(int64_t M, const RowShape &sh, int32_t dtype)
     return int(std::max<int64_t>(1, (groups + 2 * kCUs - 1) / (2 * kCUs)));
 }
 
-norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, int nb, const Knobs &kn,
+norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, int nb, const Knobs &kn,
                        const BwdEntry **entry, Walk *w, BwdLayout *lay)
 {
     const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
@@ -460,7 +479,7 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, bool vec, int nb, co
     // CUs idle (fewer workgroups than CUs) and a row spans two chunks or more.
     const int chunk = split_chunk_cols(dtype);
     const int64_t chunks = (N + chunk - 1) / chunk;
-    lay->split = vec && M > 0 && e->shape.lpr >= WIDE_LPR && chunks >= 2 &&
+    lay->split = vec == full_width(dtype) && M > 0 && e->shape.lpr >= WIDE_LPR && chunks >= 2 &&
                  (kn.bwd_split == 1 ||
                   (kn.bwd_split < 0 && dtype == NORM_BF16 && chunks >= kSplitMinChunks &&
                    w->n_groups >= kSplitMinGroups && w->grid < kCUs));
@@ -522,7 +541,7 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
     if (norm_status_t st = check_device())
         return st;
     const Knobs kn = knobs();
-    const bool vec = vectorisable(N, dtype, {dy, x, gamma, dx});
+    const int vec = vec_width(N, dtype, {dy, x, gamma, dx});
     const BwdEntry *e = nullptr;
     Walk w;
     BwdLayout lay;
@@ -638,18 +657,17 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
         return st;
     if (norm_status_t st = check_device())
         return st;
-    // Largest need over the kernels a call of this shape may take (the
-    // 16-byte path or the element-wise one, with dbias).
+    // Largest need over the kernels a call of this shape may take (any
+    // vector width N allows, with dbias).
     const Knobs kn = knobs();
     size_t best = 0;
-    const int vec = int(16 / elem_size(dtype));
-    for (int v = 0; v < 2; ++v) {
-        if (v == 1 && N % vec != 0)
+    for (int v = full_width(dtype); v >= 1; v /= 2) {
+        if (N % v != 0)
             continue;
         const BwdEntry *e = nullptr;
         Walk w;
         BwdLayout lay;
-        if (norm_status_t st = bwd_plan(M, N, dtype, v == 1, 3, kn, &e, &w, &lay))
+        if (norm_status_t st = bwd_plan(M, N, dtype, v, 3, kn, &e, &w, &lay))
             return st;
         if (lay.bytes > best)
             best = lay.bytes;

@@ -28,12 +28,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // ---------------------------------------------------------------------------
 // Register forms.  VecIO<T, VEC> converts VEC consecutive elements of type T
-// between their packed register form `Raw` (what one 16-byte access per lane,
-// VEC = 16 / sizeof(T), or one element, VEC = 1, brings in; see BufIO below)
-// and floats.  pack() rounds to T (nearest, ties to even); unpack() widens
+// between their packed register form `Raw` (what one 16-, 8- or 4-byte
+// access per lane, or one element, VEC = 1, brings in; see BufIO below) and
+// floats.  pack() rounds to T (nearest, ties to even); unpack() widens
 // exactly.
 // ---------------------------------------------------------------------------
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T, int VEC>
@@ -55,6 +56,32 @@ struct VecIO<bf16, 8> {
                    pack_bf16x2(f[6], f[7])};
     }
     static __device__ __forceinline__ Raw zero() { return Raw{0u, 0u, 0u, 0u}; }
+};
+
+template <>
+struct VecIO<bf16, 4> {
+    using Raw = u32x2_t;
+    static __device__ __forceinline__ void unpack(const Raw &r, float *f)
+    {
+        f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
+        f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+    }
+    static __device__ __forceinline__ Raw pack(const float *f)
+    {
+        return Raw{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+    }
+    static __device__ __forceinline__ Raw zero() { return Raw{0u, 0u}; }
+};
+
+template <>
+struct VecIO<bf16, 2> {
+    using Raw = uint32_t;
+    static __device__ __forceinline__ void unpack(const Raw &r, float *f)
+    {
+        f[0] = bf16_lo(r); f[1] = bf16_hi(r);
+    }
+    static __device__ __forceinline__ Raw pack(const float *f) { return pack_bf16x2(f[0], f[1]); }
+    static __device__ __forceinline__ Raw zero() { return 0u; }
 };
 
 template <>
@@ -80,6 +107,17 @@ struct VecIO<float, 4> {
     }
     static __device__ __forceinline__ Raw pack(const float *f) { return Raw{f[0], f[1], f[2], f[3]}; }
     static __device__ __forceinline__ Raw zero() { return Raw{0.f, 0.f, 0.f, 0.f}; }
+};
+
+template <>
+struct VecIO<float, 2> {
+    using Raw = f32x2_t;
+    static __device__ __forceinline__ void unpack(const Raw &r, float *f)
+    {
+        f[0] = r.x; f[1] = r.y;
+    }
+    static __device__ __forceinline__ Raw pack(const float *f) { return Raw{f[0], f[1]}; }
+    static __device__ __forceinline__ Raw zero() { return Raw{0.f, 0.f}; }
 };
 
 template <>
@@ -157,6 +195,63 @@ struct BufIO<float, 4> {
     }
 };
 template <>
+struct BufIO<bf16, 4> {
+    using Raw = u32x2_t;
+    static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, BUF_NT);
+    }
+    static __device__ __forceinline__ Raw load_cached(rsrc_t r, uint32_t off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, 0);
+    }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v, bool wt)
+    {
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b64(v, r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b64(v, r, int(off), 0, BUF_NT);
+    }
+};
+template <>
+struct BufIO<bf16, 2> {
+    using Raw = uint32_t;
+    static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, BUF_NT);
+    }
+    static __device__ __forceinline__ Raw load_cached(rsrc_t r, uint32_t off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0);
+    }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v, bool wt)
+    {
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b32(v, r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(v, r, int(off), 0, BUF_NT);
+    }
+};
+template <>
+struct BufIO<float, 2> {
+    using Raw = f32x2_t;
+    static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, BUF_NT));
+    }
+    static __device__ __forceinline__ Raw load_cached(rsrc_t r, uint32_t off)
+    {
+        return __builtin_bit_cast(Raw, __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, 0));
+    }
+    static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, Raw v, bool wt)
+    {
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, int(off), 0, BUF_NT);
+    }
+};
+template <>
 struct BufIO<bf16, 1> {
     using Raw = uint16_t;
     static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off)
@@ -201,8 +296,6 @@ struct BufIO<float, 1> {
 // beyond the format into NaN, so they are first clamped to +-448, the
 // largest finite E4M3 value) stored as VEC bytes at byte offset `off`.
 // ---------------------------------------------------------------------------
-typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ float sat_e4m3(float v)
 {
     return __builtin_amdgcn_fmed3f(v, -448.f, 448.f);
@@ -228,8 +321,15 @@ __device__ __forceinline__ void store_e4m3(rsrc_t r, uint32_t off, const float *
             __builtin_amdgcn_raw_buffer_store_b32(unsigned(w), r, int(off), 0, BUF_WT);
         else
             __builtin_amdgcn_raw_buffer_store_b32(unsigned(w), r, int(off), 0, BUF_NT);
+    } else if constexpr (VEC == 2) {
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), sat_e4m3(v[1]), 0, false);
+        const unsigned short h = static_cast<unsigned short>(w & 0xffff);
+        if (wt)
+            __builtin_amdgcn_raw_buffer_store_b16(h, r, int(off), 0, BUF_WT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b16(h, r, int(off), 0, BUF_NT);
     } else {
-        static_assert(VEC == 1, "FP8 store of 1, 4 or 8 values");
+        static_assert(VEC == 1, "FP8 store of 1, 2, 4 or 8 values");
         const int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(v[0]), 0.f, 0, false);
         const unsigned char b = static_cast<unsigned char>(w & 0xff);
         if (wt)

@@ -12,12 +12,18 @@ namespace nf {
      &launch_fwd<T, VEC, LPR, VPL, TEAMS, true, true>},
 
 static const FwdEntry k_vec[] = {NF_SHAPES_F32_VEC(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, float, 4)};
+static const FwdEntry k_vec2[] = {NF_SHAPES_SHORT_VEC(NF_ENTRY, float, 2)};
 static const FwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, float)};
 
-const FwdEntry *fwd_table_f32(bool vectorised, int *count)
+const FwdEntry *fwd_table_f32(int vec, int *count)
 {
-    *count = vectorised ? int(sizeof k_vec / sizeof k_vec[0]) : int(sizeof k_elem / sizeof k_elem[0]);
-    return vectorised ? k_vec : k_elem;
+    *count = 0;
+    switch (vec) {
+    case 4: return table_of(k_vec, count);
+    case 2: return table_of(k_vec2, count);
+    case 1: return table_of(k_elem, count);
+    default: return nullptr;
+    }
 }
 
 } // namespace nf

@@ -84,15 +84,24 @@ struct SoftmaxEntry {
     RowShape shape;
     SoftmaxLaunch run;
 };
-const SoftmaxEntry *softmax_table_f32(bool vectorised, int *count);
-const SoftmaxEntry *softmax_table_bf16(bool vectorised, int *count);
+const SoftmaxEntry *softmax_table_f32(int vec, int *count);
+const SoftmaxEntry *softmax_table_bf16(int vec, int *count);
 
-// Tables of instantiated shapes, ordered by capacity; vectorised = 16-byte
-// accesses (else element-wise).  One translation unit per dtype/direction.
-const FwdEntry *fwd_table_f32(bool vectorised, int *count);
-const FwdEntry *fwd_table_bf16(bool vectorised, int *count);
-const BwdEntry *bwd_table_f32(bool vectorised, int *count);
-const BwdEntry *bwd_table_bf16(bool vectorised, int *count);
+// Tables of instantiated shapes, ordered by capacity, for elements per
+// vector access `vec`: 16 / sizeof(T) (16-byte accesses), 4 (bf16, 8-byte),
+// 2 (4-byte bf16 pairs, 8-byte fp32 pairs) or 1; an empty table (count 0)
+// for other values.  One translation unit per dtype/direction.
+const FwdEntry *fwd_table_f32(int vec, int *count);
+const FwdEntry *fwd_table_bf16(int vec, int *count);
+const BwdEntry *bwd_table_f32(int vec, int *count);
+const BwdEntry *bwd_table_bf16(int vec, int *count);
+
+template <class E, size_t n>
+const E *table_of(const E (&t)[n], int *count)
+{
+    *count = int(n);
+    return t;
+}
 
 // Teams of at least WIDE_LPR lanes (several waves per row) hold few rows per
 // CU: their kernels prefetch the next row group, and the host gives their

@@ -547,12 +547,14 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     }
 }
 
-// Whether the backward pipelines its row walk (wide teams, see bwd_kernel):
-// two groups' packed rows, one group's packed dx, the column accumulators and
-// the unpacked working values (about 4E + 24 registers) must fit the wave's
-// share of the 512 VGPRs of a SIMD.  Narrow teams hold several rows per
-// wave and keep enough loads in flight without it; fp32 rows (twice the
-// registers per element) do not pipeline.
+// Whether the backward pipelines its row walk (wide teams of 16-byte
+// vectors, see bwd_kernel): two groups' packed rows, one group's packed dx,
+// the column accumulators and the unpacked working values (about 4E + 24
+// registers) must fit the wave's share of the 512 VGPRs of a SIMD, less 16.
+// Narrow teams hold several rows per wave and keep enough loads in flight
+// without it; fp32 rows (twice the registers per element) and the shorter
+// vectors of unaligned rows do not pipeline (in 1024-thread workgroups,
+// capped at 128 registers, they spilled).
 template <typename T, int VEC, int LPR, int VPL, int TEAMS>
 constexpr bool bwd_pipelined()
 {
@@ -561,8 +563,9 @@ constexpr bool bwd_pipelined()
     constexpr int E = VPL * VEC;
     constexpr int waves_per_simd = (LPR * TEAMS / 64 + 3) / 4;
     constexpr int share = 512 / waves_per_simd;
-    constexpr int budget = share >= 256 ? share - 16 : share;
-    return sizeof(T) == 2 && LPR >= WIDE_LPR && 2 * slot + VPL * raw + 4 * E + 24 <= budget;
+    constexpr int budget = share - 16;
+    return sizeof(T) == 2 && VEC * int(sizeof(T)) == 16 && LPR >= WIDE_LPR &&
+           2 * slot + VPL * raw + 4 * E + 24 <= budget;
 }
 
 // ---------------------------------------------------------------------------

@@ -9,9 +9,11 @@
 //                    (backward: 5120 6144) 8192 16384
 //   fp32 capacities: 32 64 128 192 256 384 512 768 1024 1280 1536 2048 4096
 //                    8192 16384
-// Element-wise path (VEC = 1), for rows that are not whole 16-byte vectors
-// or pointers that are not 16-byte aligned: 256 512 1024 2048 4096 8192
-// 16384.  (Steps of 2x capacity and 8 elements per lane beyond 1024 columns:
+// Rows that are not whole 16-byte vectors, or pointers that are not 16-byte
+// aligned, take the widest of 8-byte vectors (bf16, N % 4 == 0, the fp32
+// layouts), 4-byte vectors of 2 elements (N even) or single elements that
+// N and the alignment allow.  Element-wise capacities: 256 512 1024 2048
+// 4096 8192 16384.  (Steps of 2x capacity and 8 elements per lane beyond 1024 columns:
 // with steps of 4x and 16 per lane, 32768 x 1500 bf16 took 205 / 254 us
 // forward / backward, now 117 / 164 us.)
 #pragma once
@@ -76,10 +78,19 @@
     X(T, VEC, 64, 4, 8)
 
 #define NF_SHAPES_ELEM(X, T)                                                                     \
-    X(T, 1, 64, 4, 4)                                                                            \
-    X(T, 1, 64, 8, 4)                                                                            \
-    X(T, 1, 64, 16, 4)                                                                           \
-    X(T, 1, 256, 8, 1)                                                                           \
-    X(T, 1, 512, 8, 1)                                                                           \
-    X(T, 1, 1024, 8, 1)                                                                          \
+    NF_SHAPES_SHORT_VEC(X, T, 1)                                                                 \
     X(T, 1, 1024, 16, 1)
+// Element-wise-like layouts for 4-byte vectors of 2 elements (bf16 rows of
+// an even N, fp32 rows of an even N on 8-byte alignment): capacities 512 to
+// 16384.
+#define NF_SHAPES_SHORT_VEC(X, T, VEC)                                                            \
+    X(T, VEC, 64, 4, 4)                                                                          \
+    X(T, VEC, 64, 8, 4)                                                                          \
+    X(T, VEC, 64, 16, 4)                                                                         \
+    X(T, VEC, 256, 8, 1)                                                                         \
+    X(T, VEC, 512, 8, 1)                                                                         \
+    X(T, VEC, 1024, 8, 1)
+// bf16 rows of a multiple of 4 elements on 8-byte alignment: the fp32
+// layouts (4 elements per vector).
+#define NF_SHAPES_BF16_VEC4(X)                                                                   \
+    NF_SHAPES_NARROW(X, bf16, 4) NF_SHAPES_WIDE(X, bf16, 4) X(bf16, 4, 1024, 4, 1)
