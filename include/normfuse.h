@@ -76,10 +76,13 @@
  *              NORMFUSE_BWD_SPLIT=0 / 1 turns off / forces the backward's
  *              split of rows along N (otherwise chosen for few bf16 rows of
  *              many columns; sums may round differently).
- *   Alignment: pointers must be aligned to their element size.  16-byte
- *              aligned [M, N] / [N] pointers with N a multiple of 16 bytes'
- *              worth of elements take the vectorised kernels; anything else
- *              takes a correct element-wise path.
+ *   Alignment: pointers must be aligned to their element size.  Each call
+ *              takes the widest vector access of 16, 8 or 4 bytes (fp32: 16
+ *              or 8) that N is a multiple of (in elements) and that every
+ *              [M, N] / [N] pointer is aligned to, else single elements;
+ *              all give results within the same tolerances, fastest with
+ *              16-byte aligned tensors and N a multiple of 8 (bf16) or 4
+ *              (fp32).
  *   Sizes    : 0 <= M; 1 <= N <= NORM_N_MAX.  M = 0 enqueues only what
  *              defines the outputs (amax = 0, dgamma = dbeta = dbias = 0), and then
  *              the [M, N] and [M] pointers may be NULL.
