@@ -449,8 +449,13 @@ constexpr int64_t kSplitMinGroups = 64;
 //    228.7 -> 220.4 us), 262144 x 768 209 -> 194.5 us, 131072 x 1024 143 ->
 //    126 us, 65536 x 2048 154 -> 127 us, 1048576 x 256 270 -> 263 us; fp32
 //    576000 x 384 460 -> 447 us, 262144 x 1024 571 -> 536 us.  (4 per CU
-//    at 524288 x 384: 210 us, 2 per CU: 196 us, 1 per CU: 276 us.)
-int bwd_groups_per_wg(int64_t M, const RowShape &sh, int32_t dtype)
+//    at 524288 x 384: 210 us, 2 per CU: 196 us, 1 per CU: 276 us.)  Row
+//    groups under kBwdSmallGroupBytes per tensor take four workgroups per CU
+//    instead: two leave too few bytes in flight (262144 x 128 bf16: 47.6 ->
+//    40.7 us; 1048576 x 64: 88 -> 73 us; 4-byte vectors at 65536 x 386:
+//    53.8 -> 39.8 us).
+constexpr double kBwdSmallGroupBytes = 6.0 * 1024;
+int bwd_groups_per_wg(int64_t M, int64_t N, const RowShape &sh, int32_t dtype)
 {
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
     if (sh.lpr >= WIDE_LPR) {
@@ -462,7 +467,9 @@ int bwd_groups_per_wg(int64_t M, const RowShape &sh, int32_t dtype)
         const int64_t slots = kCUs * per_cu;
         return int(std::min(kmax, std::max(kmin, (groups + slots - 1) / slots)));
     }
-    return int(std::max<int64_t>(1, (groups + 2 * kCUs - 1) / (2 * kCUs)));
+    const double group_bytes = double(sh.teams) * double(N) * double(elem_size(dtype));
+    const int64_t slots = (group_bytes < kBwdSmallGroupBytes ? 4 : 2) * kCUs;
+    return int(std::max<int64_t>(1, (groups + slots - 1) / slots));
 }
 
 norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, int nb, const Knobs &kn,
@@ -471,7 +478,7 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, int nb, con
     const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    const int K = kn.bwd_k > 0 ? kn.bwd_k : bwd_groups_per_wg(M, e->shape, dtype);
+    const int K = kn.bwd_k > 0 ? kn.bwd_k : bwd_groups_per_wg(M, N, e->shape, dtype);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.bwd_a, w))
         return st;
     *entry = e;
