@@ -429,7 +429,7 @@ constexpr int64_t kSplitMinGroups = 64;
 // the rows.  Each workgroup's partial row costs N floats per column sum,
 // written and read once more, so fewer, longer walks save traffic, but the
 // walks must still spread over the CUs.  Measured on MI355X:
-//  - wide rows (teams of 256 to 1024 lanes): as many workgroups as the CUs
+//  - wide rows (teams of 320 to 1024 lanes): as many workgroups as the CUs
 //    hold at once -- one per CU, two for the fp32 shapes up to 8192
 //    columns, whose registers leave room for a second -- each walking at
 //    least 2 and at most kBwdRowsWide rows (below 2 rows the partials
