@@ -21,7 +21,7 @@ from tolerance import (assert_colsums_close, assert_fused_add_close, assert_rows
 pytestmark = pytest.mark.gpu
 
 SHAPES = [(3, 7), (130, 64), (300, 384), (77, 520), (33, 1024), (17, 1536), (43, 4096),
-          (5, 5000), (3, 16384)]
+          (5, 5000), (3, 16384), (45, 1002), (19, 4100), (21, 2560)]
 
 
 @pytest.fixture(autouse=True)
