@@ -136,11 +136,13 @@ const Entry *pick_shape(const Entry *tab, int n, int N, int force_lpr, int force
 size_t elem_size(int32_t dtype) { return dtype == NORM_F32 ? 4 : 2; }
 
 // Forward workgroups.  The forward's amax combines one atomicMax per
-// workgroup on a single address; such atomics serialise, and past about
-// kMaxAmaxWgs workgroups per launch they start to cost more than the kernel
-// hides.  Bigger workgroups (twice the teams) reach that bound with less
-// walking, and are used when they still leave kMinWideGroups workgroups.
-constexpr int64_t kMaxAmaxWgs = 20000;
+// workgroup on a single address; such atomics serialise, so the launch is
+// kept to at most kMaxAmaxWgs workgroups.  Measured on MI355X, 125000 of
+// them (4000000 x 384 bf16) still hide behind the rows: an earlier bound of
+// 20000 forced longer walks there and cost 3-5% (4000000 x 384: 2320 ->
+// 2253 us; 16000000 x 64: 1527 -> 1447 us).  Bigger workgroups (twice the
+// teams) are used when they still leave kMinWideGroups workgroups.
+constexpr int64_t kMaxAmaxWgs = 131072;
 constexpr int64_t kMinWideGroups = 2048;
 // Up to this many row groups the forward walks several groups per workgroup
 // (about one workgroup per CU, at most kFwdGroupsWide groups each); beyond
