@@ -468,10 +468,21 @@ def cpu_baseline(h, rows):
     sec = time.perf_counter() - t0
     nbytes = fwd_bytes(R, N_BIG) + bwd_bytes(R, N_BIG)
     log(f"cpu oracle: {R} rows in {sec:.2f}s on {threads} threads")
+    # one thread on a sixteenth of those rows
+    R1 = max(1, R // 16)
+    t0 = time.perf_counter()
+    f1 = oracle.norm_fwd(sub["x"][:R1], sub["bias"], sub["residual"][:R1], sub["gamma"],
+                         sub["beta"], 1e-5, nthreads=1)
+    oracle.norm_bwd(sub["dy"][:R1], f1["u"], sub["gamma"], f1["mean"], f1["rstd"], 1e-5,
+                    nthreads=1)
+    sec1 = time.perf_counter() - t0
+    log(f"cpu oracle: {R1} rows in {sec1:.2f}s on 1 thread")
     return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"first {R} of {M_BIG} rows of the same workload (fwd + bwd), "
-                      f"{sec:.2f} s wall, same algorithmic-byte accounting"}
+                      f"{sec:.2f} s wall, same algorithmic-byte accounting",
+            "single_thread_value": round((fwd_bytes(R1, N_BIG) + bwd_bytes(R1, N_BIG)) / sec1 / 1e9, 3),
+            "single_thread_sample": f"first {R1} rows on 1 thread, {sec1:.2f} s wall"}
 
 
 if __name__ == "__main__":
