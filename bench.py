@@ -133,8 +133,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (the path has no multi-GPU "
-              "component); run with --gpus 1", file=sys.stderr)
+        print("bench.py: measures one GPU only (the path has no multi-GPU component); "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -26,8 +26,8 @@ from tolerance import (assert_colsums_close, assert_fused_add_close, assert_rows
 pytestmark = pytest.mark.gpu
 
 BIG_M = 1152 * 500
-# spec bound for the column sums at M = 576000, relative to
-# max(|sum|, ||terms||_2); the observed error is printed
+# bound for the column sums at M = 576000 (relative error 1e-3), relative
+# to max(|sum|, ||terms||_2); the observed error is printed
 COLSUM_REL_BIG = 1e-3
 
 
