@@ -363,7 +363,8 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
     rec("rms_fwd_576000x384", lambda: nf.rms_fwd(d["x"], d["bias"], d["residual"], d["gamma"],
                                                   None, 1e-6, want_amax=True, out=rms_out),
         fwd_bytes(M, N, stats=1), False)
-    # configs 3 and 4: backward on x = N(0,1) (the generator's x), dy
+    # the 576000 x 384 backwards (RMSNorm with rstd recomputed, LayerNorm from
+    # saved statistics): on x = N(0,1) (the generator's x), dy
     dx = torch.empty_like(d["x"])
     dg = torch.empty(N, dtype=torch.bfloat16, device=dev)
     db = torch.empty(N, dtype=torch.bfloat16, device=dev)
@@ -389,7 +390,7 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
     smx = torch.empty_like(d["x"])
     rec("softmax_fwd_576000x384", lambda: nf.softmax_fwd(d["x"], out=smx), M * 4 * N, False)
     del smx
-    # config 2 (launch-bound size): consecutive calls take consecutive
+    # 4096 x 384 bf16 forward with amax (launch-bound size): consecutive calls take consecutive
     # 4096-row slices of the large tensors
     M2 = 4096
     subs = [{k: (v[i * M2:(i + 1) * M2] if v.dim() == 2 else v) for k, v in d.items()}
@@ -407,7 +408,7 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
                                     1e-5, want_amax=True, out=o))
         for s, o in zip(subs[:64], outs2)], fwd_bytes(M2, N))
     del outs2
-    # config 1: LayerNorm forward, fp32, 64 x 384, bias + residual; y, mean, rstd
+    # LayerNorm forward, fp32, 64 x 384, bias + residual; y, mean, rstd
     M1 = 64
     g1 = synth.make_inputs(M1 * 64, N, dtype=synth.F32, seed=0,
                            names=("x", "residual", "bias", "gamma", "beta"))
@@ -421,7 +422,7 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
             xs, d1["bias"], rs, d1["gamma"], d1["beta"], 1e-5, want_residual_out=False, out=o1))
     graph_rec("ln_fwd_64x384_f32_graph", calls1, M1 * (3 * 4 * N + 8))
     del d1, calls1
-    # config 5: 8192 x 4096, residual + LayerNorm, 1% outliers; two buffer
+    # 8192 x 4096 bf16, residual + LayerNorm, 1% outliers; two buffer
     # sets alternate (512 MB working set)
     M5, N5 = 8192, 4096
     sets = []

@@ -1,11 +1,11 @@
-"""The five workload configurations at their full sizes, plus the fused
-forward at the (576000, 384) benchmark shape, on the GPU against the oracle.
+"""Five workloads at their full sizes, plus the fused forward at the
+(576000, 384) benchmark shape, on the GPU against the oracle:
 
-  1. LayerNorm fwd, fp32, 64 x 384, bias + residual + gamma + beta, eps 1e-5
-  2. fused bias + residual + LayerNorm fwd, bf16, 4096 x 384, residual_out, amax
-  3. RMSNorm bwd, bf16, 576000 x 384, rstd recomputed (eps 1e-6), dgamma cast to bf16
-  4. LayerNorm bwd, bf16, 576000 x 384, fp32 saved mean / rstd, dgamma, dbeta
-  5. residual + LayerNorm fwd then bwd, bf16, 8192 x 4096, 1% of x / residual /
+  - LayerNorm fwd, fp32, 64 x 384, bias + residual + gamma + beta, eps 1e-5
+  - fused bias + residual + LayerNorm fwd, bf16, 4096 x 384, residual_out, amax
+  - RMSNorm bwd, bf16, 576000 x 384, rstd recomputed (eps 1e-6), dgamma cast to bf16
+  - LayerNorm bwd, bf16, 576000 x 384, fp32 saved mean / rstd, dgamma, dbeta
+  - residual + LayerNorm fwd then bwd, bf16, 8192 x 4096, 1% of x / residual /
      dy elements scaled by 100
 At 576000 rows dx is compared on sampled rows (the oracle computes those
 rows one by one); the column sums and amax are compared in full.  The kernel
@@ -43,14 +43,14 @@ def sample_rows(M, seed=0, n_random=4096, edge=2048):
     return np.unique(rows)
 
 
-def test_config1_ln_fwd_fp32():
+def test_ln_fwd_fp32_64x384():
     M, N = 64, 384
     inp = synth.make_inputs(M, N, dtype=F32, seed=0)
     out = run_fwd(False, inp, F32, 1e-5, want_amax=False)
     check_fwd(False, inp, F32, 1e-5, out)
 
 
-def test_config2_fused_ln_fwd_bf16_amax():
+def test_fused_ln_fwd_bf16_amax_4096x384():
     M, N = 4096, 384
     inp = synth.make_inputs(M, N, dtype=BF16, seed=0)
     out = run_fwd(False, inp, BF16, 1e-5, want_amax=True)
@@ -104,11 +104,11 @@ def _big_bwd(rms):
         assert float((rowsum / rowscale).max()) < 384 * 2.0 ** -8
 
 
-def test_config3_rms_bwd_576k():
+def test_rms_bwd_recompute_576000x384():
     _big_bwd(rms=True)
 
 
-def test_config4_ln_bwd_576k():
+def test_ln_bwd_576000x384():
     _big_bwd(rms=False)
 
 
@@ -133,7 +133,7 @@ def test_fused_ln_fwd_576k_amax():
     assert rel.max() <= 1e-5
 
 
-def test_config5_wide_fwd_then_bwd():
+def test_ln_fwd_then_bwd_outliers_8192x4096():
     M, N = 8192, 4096
     inp = synth.make_inputs(M, N, dtype=BF16, seed=0, outlier_p=0.01,
                             names=("x", "residual", "gamma", "beta", "dy"))
