@@ -23,7 +23,8 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520), (64, 1000),
           (33, 1024), (17, 1536), (9, 2000), (40, 4096), (43, 4096), (30, 3000), (5, 5000),
           (3, 16384), (2, 16383), (21, 2560), (11, 2304), (13, 1200),
-          (45, 1002), (19, 4100), (7, 6002), (6, 12004)]
+          (45, 1002), (19, 4100), (7, 6002), (6, 12004),
+          (5, 2), (6, 4), (7, 6), (9, 12)]
 
 
 def run_fwd(rms, inp, dtype, eps, misalign=False, want_amax=True, parts=None):
