@@ -423,6 +423,42 @@ def test_column_sums_brute_force_and_additivity(oracle_mod):
     np.testing.assert_allclose(p1["dgamma"] + p2["dgamma"], b["dgamma"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(p1["dbeta"] + p2["dbeta"], b["dbeta"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(b["dbeta_l2"], np.sqrt((dy ** 2).sum(0)), rtol=1e-12)
+    # dgamma_l2 (the scale every dgamma comparison divides by) is the 2-norm
+    # of the terms dy_ij xhat_ij that dgamma_j adds, by explicit loops
+    for j in range(N):
+        q = 0.0
+        for i in range(M):
+            t = dy[i, j] * (x[i, j] - fwd["mean"][i]) * fwd["rstd"][i]
+            q += t * t
+        assert abs(b["dgamma_l2"][j] - math.sqrt(q)) <= 1e-12 * math.sqrt(q)
+    # and it bounds the sum it scales: |dgamma_j| <= sqrt(M) * dgamma_l2_j
+    assert np.all(np.abs(b["dgamma"]) <= math.sqrt(M) * b["dgamma_l2"] * (1 + 1e-12))
+
+
+def test_column_l2_scales_of_rank_one_terms(oracle_mod):
+    """Closed forms of the 2-norm scales: with dy_ij = a_i (the same value
+    across a row) the terms of dbeta_j are a_i, so dbeta_l2_j = ||a||_2 for
+    every j; and with gamma = 1 and dy = xhat (LayerNorm, eps = 0 on rows of
+    nonzero variance) the terms of dgamma_j are xhat_ij^2, so dgamma_l2_j^2 =
+    sum_i xhat_ij^4."""
+    M, N = 12, 8
+    rng = np.random.default_rng(23)
+    x = dyadic(rng, (M, N))
+    a = dyadic(rng, (M,), -64, 64, 4)
+    dy = f32(np.broadcast_to(a[:, None], (M, N)))
+    fwd = oracle_mod.norm_fwd(x, eps=0.0, dtype=F32)
+    b = oracle_mod.norm_bwd(dy, x, None, fwd["mean"], fwd["rstd"], 0.0, dtype=F32)
+    np.testing.assert_allclose(b["dbeta_l2"], np.linalg.norm(a.astype(np.float64)), rtol=1e-14)
+    xh = (x.astype(np.float64) - fwd["mean"][:, None]) * fwd["rstd"][:, None]
+    dy2 = f32(xh)
+    b2 = oracle_mod.norm_bwd(dy2, x, None, fwd["mean"], fwd["rstd"], 0.0, dtype=F32)
+    t = dy2.astype(np.float64) * xh
+    np.testing.assert_allclose(b2["dgamma_l2"], np.sqrt((t ** 2).sum(0)), rtol=1e-13)
+    # every term dy * xhat is within fp32 rounding of xhat^2 >= 0, so the sum
+    # and the 2-norm scale of dgamma meet the norm inequalities of
+    # nonnegative terms: l2 <= sum <= sqrt(M) l2
+    assert np.all(b2["dgamma_l2"] <= b2["dgamma"] * (1 + 1e-6))
+    assert np.all(b2["dgamma"] <= math.sqrt(M) * b2["dgamma_l2"] * (1 + 1e-12))
 
 
 def test_distributive_identity_on_column_sums(oracle_mod):

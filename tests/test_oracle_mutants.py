@@ -70,6 +70,11 @@ MUTANTS = [
     ("softmax numerator without the max",
      "c->y[i * N + j] = exp(elem(c->x, c->dtype, i * N + j) - m) / s;",
      "c->y[i * N + j] = exp(elem(c->x, c->dtype, i * N + j)) / s;"),
+    ("dgamma_l2 scaled up", "qg += tg * tg;", "qg += 1e6 * tg * tg;"),
+    ("dgamma_l2 sums |terms|", "qg += tg * tg;", "qg += fabs(tg);"),
+    ("dgamma_l2 from dbeta's terms", "qg += tg * tg;", "qg += d * d;"),
+    ("dbeta_l2 scaled up", "qb += d * d;", "qb += 4.0 * d * d;"),
+    ("dbias_l2 scaled up", "q += t * t;", "q += 1e6 * t * t;"),
     ("dbias skips the last row", "for (int64_t i = 0; i < c->M; ++i) {\n            double t = c->dx",
      "for (int64_t i = 0; i + 1 < c->M; ++i) {\n            double t = c->dx"),
 ]
