@@ -64,18 +64,18 @@
  *   Results  : deterministic: the same inputs give bit-identical outputs.
  *              The kernel shape, the grid and every summation order follow
  *              from M, N, the dtypes and the pointers' alignment alone.
- *   Tuning   : the environment variables NORMFUSE_FWD_SHAPE / _BWD_SHAPE
+ *   Tuning   : this library reads no environment variables.  Its test
+ *              build, libnormfuse_tuning.so (same kernels and entry points),
+ *              also honours tuning overrides read at every call, for tests
+ *              that cross-check kernel shapes against each other and for
+ *              measurements: NORMFUSE_FWD_SHAPE / _BWD_SHAPE
  *              ("LPRxVPL[xTEAMS]"), NORMFUSE_FWD_GROUPS_PER_WG /
- *              _BWD_GROUPS_PER_WG and NORMFUSE_FWD_INTERLEAVE /
- *              _BWD_INTERLEAVE, read at every call, override those choices
- *              among the compiled shapes (for tuning; results stay within
- *              the same tolerances, but column sums may round differently).
- *              NORMFUSE_WT_BYTES sets how many output bytes, counted from
- *              the end of a call, are stored write-through instead of
- *              nontemporal (a cache policy: values do not change).
- *              NORMFUSE_BWD_SPLIT=0 / 1 turns off / forces the backward's
- *              split of rows along N (otherwise chosen for few bf16 rows of
- *              many columns; sums may round differently).
+ *              _BWD_GROUPS_PER_WG, NORMFUSE_FWD_INTERLEAVE / _BWD_INTERLEAVE
+ *              (results stay within the same tolerances, but column sums
+ *              may round differently), NORMFUSE_WT_BYTES (output bytes,
+ *              counted from the end of a call, stored write-through: a cache
+ *              policy, values do not change) and NORMFUSE_BWD_SPLIT=0 / 1
+ *              (turns off / forces the backward's split of rows along N).
  *   Alignment: pointers must be aligned to their element size.  Each call
  *              takes the widest vector access of 16, 8 or 4 bytes (fp32: 16
  *              or 8) that N is a multiple of (in elements) and that every
@@ -211,8 +211,8 @@ norm_status_t softmax_fwd(const void *x, int64_t M, int64_t N, int32_t dtype, vo
  * for an [M, N] problem of the given dtype on the current device (the
  * per-workgroup dgamma / dbeta / dbias column partials, and for rows split
  * along N their per-chunk row sums; the size covers a call that asks for
- * dbias).  Writes 0 when none is needed.  Query it under the same tuning
- * environment as the call.  The workspace
+ * dbias).  Writes 0 when none is needed.  (In the test build, query it
+ * under the same tuning overrides as the call.)  The workspace
  * needs no initialisation and may be reused by calls ordered on one stream.
  */
 norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_t *bytes);

@@ -23,9 +23,11 @@ import os
 import torch
 
 from .build import LIB as _LIB_PATH
+from .build import TUNING_LIB as _TUNING_LIB_PATH
 
 __all__ = ["ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd", "softmax_fwd",
-           "bwd_workspace_size", "NormError", "NormLibraryMissing", "library", "F32", "BF16",
+           "bwd_workspace_size", "NormError", "NormLibraryMissing", "library", "load", "TUNING_LIB",
+           "F32", "BF16",
            "N_MAX", "ZERO_CENTERED_GAMMA", "DPARAM_MEAN"]
 
 F32 = 0
@@ -58,32 +60,43 @@ def library():
     """The loaded ``libnormfuse.so`` (ctypes), with argument types set."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            raise NormLibraryMissing(
-                f"{_LIB_PATH} is not built; run normalization_ln_fwd_amd/build.py "
-                "(or __graft_entry__.build()) first")
-        lib = ctypes.CDLL(_LIB_PATH)
-        vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                                 ctypes.c_float, ctypes.c_size_t)
-        u32 = ctypes.c_uint32
-        fwd = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, u32, vp]
-        lib.ln_fwd.argtypes = fwd
-        lib.rms_fwd.argtypes = fwd
-        fwd8 = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp, u32, vp]
-        lib.ln_fwd_fp8.argtypes = fwd8
-        lib.rms_fwd_fp8.argtypes = fwd8
-        lib.ln_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
-                               u32, vp]
-        lib.rms_bwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
-                                u32, vp]
-        lib.softmax_fwd.argtypes = [vp, i64, i64, i32, vp, u32, vp]
-        lib.norm_bwd_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
-        lib.norm_status_string.argtypes = [i32]
-        lib.norm_status_string.restype = ctypes.c_char_p
-        for name in ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "norm_bwd_workspace_size"):
-            getattr(lib, name).restype = i32
-        _lib = lib
+        _lib = load(_LIB_PATH)
     return _lib
+
+
+def load(path):
+    """Load a build of the library at ``path`` (ctypes) and set its argument
+    types.  The package's functions use :func:`library`; the test build
+    ``libnormfuse_tuning.so`` (same kernels, host code that also reads the
+    ``NORMFUSE_*`` tuning overrides) is loaded with ``load(TUNING_LIB)``."""
+    if not os.path.exists(path):
+        raise NormLibraryMissing(
+            f"{path} is not built; run normalization_ln_fwd_amd/build.py "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                             ctypes.c_float, ctypes.c_size_t)
+    u32 = ctypes.c_uint32
+    fwd = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, u32, vp]
+    lib.ln_fwd.argtypes = fwd
+    lib.rms_fwd.argtypes = fwd
+    fwd8 = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp, u32, vp]
+    lib.ln_fwd_fp8.argtypes = fwd8
+    lib.rms_fwd_fp8.argtypes = fwd8
+    lib.ln_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
+                           u32, vp]
+    lib.rms_bwd.argtypes = [vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
+                            u32, vp]
+    lib.softmax_fwd.argtypes = [vp, i64, i64, i32, vp, u32, vp]
+    lib.norm_bwd_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
+    lib.norm_status_string.argtypes = [i32]
+    lib.norm_status_string.restype = ctypes.c_char_p
+    for name in ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "norm_bwd_workspace_size"):
+        getattr(lib, name).restype = i32
+    return lib
+
+
+TUNING_LIB = _TUNING_LIB_PATH
 
 
 def _check(fn, st):
@@ -242,15 +255,17 @@ def bwd_workspace_size(M, N, dtype):
 
 def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbeta, want_dbias,
          workspace, stream, out, flags=0):
+    dt = x.dtype
+    pdt = dt if dparam_dtype is None else dparam_dtype
+    if pdt not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"dparam_dtype {pdt} unsupported; use torch.float32 or torch.bfloat16")
     lib = library()
     N = x.shape[-1]
     M = x.numel() // N if N else 0
-    dt = x.dtype
     out = dict(out or {})
     dx = out.get("dx")
     if dx is None:
         dx = torch.empty_like(x)
-    pdt = dt if dparam_dtype is None else dparam_dtype
     dgamma = out.get("dgamma")
     if dgamma is None and want_dgamma:
         dgamma = torch.empty(N, dtype=pdt, device=x.device)

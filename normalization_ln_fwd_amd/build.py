@@ -2,7 +2,11 @@
 
 Every translation unit under ``csrc/`` is compiled by hipcc in parallel into
 ``_build/`` and linked into ``normalization_ln_fwd_amd/libnormfuse.so``.
-Cross-compiles without a GPU.
+The C-ABI layer ``api.cpp`` is compiled a second time with ``NORMFUSE_TUNING``
+defined and linked with the same kernel objects into
+``libnormfuse_tuning.so``: the test build, whose host code also reads the
+``NORMFUSE_*`` tuning overrides from the environment.  Cross-compiles without
+a GPU.
 """
 import glob
 import os
@@ -15,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libnormfuse.so")
+TUNING_LIB = os.path.join(PKG, "libnormfuse_tuning.so")
+TUNING_DEFINE = "-DNORMFUSE_TUNING"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -28,9 +34,10 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
+def _compile(src, verbose, defines=()):
+    tag = "".join("." + d.lstrip("-D").lower() for d in defines)
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
+    cmd = [HIPCC] + CFLAGS + list(defines) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -46,17 +53,26 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    api = os.path.join(CSRC, "api.cpp")
+    jobs_list = [(s, ()) for s in srcs] + [(api, (TUNING_DEFINE,))]
+    with ThreadPoolExecutor(max_workers=min(jobs, len(jobs_list))) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs_list))
+    product = objs[:len(srcs)]
+    tuning = [o for s, o in zip(srcs, product) if s != api] + [objs[-1]]
+    _link(product, LIB, verbose)
+    _link(tuning, TUNING_LIB, verbose)
     return LIB
 
 

@@ -25,7 +25,13 @@ norm_status_t check_device()
     return NORM_OK;
 }
 
-// ------------------------------------------------------ optional tuning knobs
+// ------------------------------------------------ tuning overrides (test build)
+// The product library takes every choice below from the call's arguments
+// alone.  A separate build of this file with NORMFUSE_TUNING defined
+// (libnormfuse_tuning.so, same kernels) also reads these environment
+// variables on every call, so that tests can force shapes, walks and the
+// split along N and cross-check them against each other, and measurements
+// can sweep them:
 // NORMFUSE_{FWD,BWD}_SHAPE          : "LPRxVPL" or "LPRxVPLxTEAMS" -- use that
 //                                     instantiated shape when it covers the row
 // NORMFUSE_{FWD,BWD}_GROUPS_PER_WG  : row groups per workgroup (K)
@@ -35,9 +41,6 @@ norm_status_t check_device()
 // NORMFUSE_BWD_SPLIT                : 0 never splits backward rows along N,
 //                                     1 splits them wherever the kernel can
 //                                     (see bwd_plan)
-// Read on every call (a few getenv lookups, far below launch cost), so a
-// process can change them between calls; tests use them to cross-check
-// shapes and groupings against each other.
 constexpr int kFwdGroupsPerWg = 0; // 0: chosen per call (see fwd_common)
 constexpr int kBwdGroupsPerWg = 0; // 0: chosen per shape (see bwd_plan)
 // Row groups per workgroup.  Teams of several waves (wide rows) have few
@@ -71,6 +74,7 @@ struct Knobs {
     int bwd_split = -1; // -1: chosen per shape
 };
 
+#ifdef NORMFUSE_TUNING
 // "LPRxVPL" or "LPRxVPLxTEAMS"
 void parse_shape(const char *s, int *lpr, int *vpl, int *teams)
 {
@@ -115,6 +119,9 @@ Knobs knobs()
 
     return r;
 }
+#else
+Knobs knobs() { return Knobs(); }
+#endif
 
 template <class Entry>
 const Entry *pick_shape(const Entry *tab, int n, int N, int force_lpr, int force_vpl,

@@ -17,3 +17,13 @@ def oracle_mod():
     import oracle
     oracle._load()
     return oracle
+
+
+@pytest.fixture
+def tuning(monkeypatch):
+    """Run this test on the test build of the library (libnormfuse_tuning.so:
+    the same kernels, with host code that also reads the NORMFUSE_* tuning
+    overrides); returns the monkeypatch fixture, whose setenv sets them."""
+    import normalization_ln_fwd_amd as nf
+    monkeypatch.setattr(nf, "_lib", nf.load(nf.TUNING_LIB))
+    return monkeypatch

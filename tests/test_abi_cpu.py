@@ -225,3 +225,31 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_product_library_reads_no_tuning_variables(lib):
+    """Only the test build's host code reads the NORMFUSE_* overrides: the
+    names are in libnormfuse_tuning.so and absent from the product library,
+    whose results and workspace sizes follow from a call's arguments."""
+    from normalization_ln_fwd_amd import build as b
+    prod = open(b.LIB, "rb").read()
+    test_build = open(b.TUNING_LIB, "rb").read()
+    for name in (b"NORMFUSE_BWD_SPLIT", b"NORMFUSE_WT_BYTES", b"NORMFUSE_FWD_SHAPE",
+                 b"NORMFUSE_BWD_GROUPS_PER_WG"):
+        assert name not in prod, name
+        assert name in test_build, name
+
+
+def test_binding_rejects_unsupported_dparam_dtype():
+    """dgamma / dbeta are fp32 or bf16; any other dparam_dtype is refused
+    before anything reaches the library (no silent bf16 bit patterns in an
+    fp16 tensor)."""
+    import torch
+    x = torch.zeros(2, 8, dtype=torch.bfloat16)
+    for bad in (torch.float16, torch.float64, torch.int32):
+        with pytest.raises(TypeError, match="dparam_dtype"):
+            nf.ln_bwd(x, x, None, None, None, dparam_dtype=bad)
+        with pytest.raises(TypeError, match="dparam_dtype"):
+            nf.rms_bwd(x, x, None, dparam_dtype=bad)
+    with pytest.raises(TypeError, match="dparam_dtype"):
+        nf.ln_bwd(x.half(), x.half(), None, None, None)  # defaults to x's dtype

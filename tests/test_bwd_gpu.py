@@ -6,6 +6,8 @@ comparison isolates the backward.  dx is checked row by row (one bf16 ulp or
 1e-5 of the row scale), dgamma / dbeta against the oracle's exact column
 sums relative to max(|sum|, ||terms||_2).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -221,11 +223,11 @@ SPLIT_N_SHAPES = [(1, 4096), (3, 16384), (16, 16384), (64, 16384), (255, 8192), 
 @pytest.mark.parametrize("M,N", SPLIT_N_SHAPES)
 @pytest.mark.parametrize("case", ["ln-bf16", "rms-f32", "rms-bf16-recompute", "ln-f32"])
 @pytest.mark.parametrize("split", ["1", "0"], ids=["split", "whole"])
-def test_bwd_split_along_n_matches_oracle(M, N, case, split, monkeypatch):
+def test_bwd_split_along_n_matches_oracle(M, N, case, split, tuning):
     rms = case.startswith("rms")
     dtype = F32 if "f32" in case else BF16
     recompute = case.endswith("recompute")
-    monkeypatch.setenv("NORMFUSE_BWD_SPLIT", split)
+    tuning.setenv("NORMFUSE_BWD_SPLIT", split)
     inp, eps = make_case(M, N, dtype, rms, seed=M * 5 + N)
     out = run_bwd(rms, inp, dtype, eps, recompute=recompute, dparam_dtype=torch.float32,
                   want_dbias=True)
@@ -240,10 +242,10 @@ def test_bwd_split_along_n_matches_oracle(M, N, case, split, monkeypatch):
 
 @pytest.mark.parametrize("M,N", [(64, 16384), (13, 4096)])
 @pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
-def test_bwd_split_along_n_options(M, N, rms, monkeypatch):
+def test_bwd_split_along_n_options(M, N, rms, tuning):
     """Zero-centred gamma and the mean epilogue on the split path: against
     the oracle run with the same options."""
-    monkeypatch.setenv("NORMFUSE_BWD_SPLIT", "1")
+    tuning.setenv("NORMFUSE_BWD_SPLIT", "1")
     inp, eps = make_case(M, N, BF16, rms, seed=M + 3 * N)
     dy, x, g = (to_dev(inp[k], BF16) for k in ("dy", "x", "gamma"))
     rstd = torch.from_numpy(inp["rstd"]).cuda()
@@ -267,8 +269,8 @@ def test_bwd_split_along_n_options(M, N, rms, monkeypatch):
     assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
 
 
-def test_bwd_split_along_n_is_deterministic(monkeypatch):
-    monkeypatch.setenv("NORMFUSE_BWD_SPLIT", "1")
+def test_bwd_split_along_n_is_deterministic(tuning):
+    tuning.setenv("NORMFUSE_BWD_SPLIT", "1")
     inp, eps = make_case(200, 16384, BF16, False, seed=3)
     a = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32, want_dbias=True)
     b = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32, want_dbias=True)
@@ -277,10 +279,10 @@ def test_bwd_split_along_n_is_deterministic(monkeypatch):
 
 
 @pytest.mark.parametrize("M,N,dtype", [(20000, 384, BF16), (9000, 1000, F32), (3000, 4096, BF16)])
-def test_bwd_many_partial_rows_two_level_sums(M, N, dtype, monkeypatch):
+def test_bwd_many_partial_rows_two_level_sums(M, N, dtype, tuning):
     """One row group per workgroup (forced) leaves more than 512 partial
     rows, which the column sums add in two launches."""
-    monkeypatch.setenv("NORMFUSE_BWD_GROUPS_PER_WG", "1")
+    tuning.setenv("NORMFUSE_BWD_GROUPS_PER_WG", "1")
     inp, eps = make_case(M, N, dtype, False, seed=M + N)
     out = run_bwd(False, inp, dtype, eps, dparam_dtype=torch.float32, want_dbias=True)
     ref = oracle_bwd(False, inp, dtype, eps, want_dbias=True)
@@ -298,3 +300,18 @@ def test_bwd_is_deterministic():
     b = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32)
     for k in ("dx", "dgamma", "dbeta"):
         assert torch.equal(a[k], b[k]), k
+
+
+def test_product_library_ignores_tuning_environment(tuning):
+    """The product build takes its choices from the call's arguments alone:
+    a tuning override changes the test build's workspace size, not the
+    product's."""
+    M, N = 20000, 384
+    base = nf.bwd_workspace_size(M, N, torch.bfloat16)  # the test build, no overrides
+    tuning.setenv("NORMFUSE_BWD_GROUPS_PER_WG", "1")
+    forced = nf.bwd_workspace_size(M, N, torch.bfloat16)
+    assert forced > base
+    product = nf.load(nf.build.LIB)
+    n = ctypes.c_size_t(0)
+    assert product.norm_bwd_workspace_size(M, N, nf.BF16, ctypes.byref(n)) == 0
+    assert n.value == base
