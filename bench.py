@@ -33,8 +33,9 @@ sys.path.insert(0, ROOT)
 PEAK_GBS = 8000.0  # MI355X HBM3E
 M_BIG, N_BIG = 1152 * 500, 384
 CALIB_BYTES = 512 << 20
-KERNEL_SOURCES = ("normalization_ln_fwd_amd/csrc/kernels.hpp",
-                  "normalization_ln_fwd_amd/csrc/device.hpp")
+# every source that decides what the measured kernels do (the kernels, the
+# host code that picks their shapes, grids and cache policies, the header)
+KERNEL_SOURCE_DIRS = ("normalization_ln_fwd_amd/csrc", "include")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_ln_bf16_576000x384_traffic.md")
 
 
@@ -52,9 +53,12 @@ def bwd_bytes(M, N, es=2, stats=2):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as fh:
-            h.update(fh.read())
+    for d in KERNEL_SOURCE_DIRS:
+        for name in sorted(os.listdir(os.path.join(ROOT, d))):
+            if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+                h.update(name.encode())
+                with open(os.path.join(ROOT, d, name), "rb") as fh:
+                    h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -129,6 +133,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--cases", default="",
+                    help="comma-separated breakdown cases to run (name prefixes; default all)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -215,7 +221,7 @@ def main():
     traffic = recorded_traffic()
     roofline = {"bound": "hbm", "achieved": round(fwd_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(fwd_gbs / PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "fwd_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 32, LayerNorm>",
+                "kernel": nf.describe("ln_fwd", M, N, torch.bfloat16, amax=True),
                 "bytes_per_launch": fwd_bytes(M, N), "avg_launch_us": round(fwd_avg, 2),
                 "kernel_source_hash": kernel_source_hash()}
 
@@ -243,8 +249,9 @@ def main():
         log("calibration copies done")
 
     if not args.no_breakdown:
+        cases = [c for c in args.cases.split(",") if c]
         result["breakdown"] = breakdown(args.breakdown_iters, nf, torch, np, synth, d, h, dev,
-                                        fwd_out, ws)
+                                        fwd_out, ws, cases)
 
     # free the device copies before the CPU leg
     del d
@@ -255,6 +262,31 @@ def main():
 
 
 WARM_S = 0.02  # untimed calls before each breakdown case, in seconds of GPU work
+PREQUEUE = 4   # untimed calls queued right before a timed interval starts
+FLUSH_BYTES = 512 << 20  # scratch written before each call of a flushed timing
+
+
+def time_flushed(fns, iters, torch, scratch):
+    """Microseconds of single calls that each follow a write of FLUSH_BYTES
+    to a scratch buffer (larger than the 256 MB last-level cache plus the L2s,
+    so no input of the call is cached when it starts): events bracket each
+    call, the write runs outside them.  Returns the median over `iters`
+    calls, cycling through fns."""
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(3):
+        scratch.fill_(i)
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    ev = HipEvents(2 * iters)
+    for i in range(iters):
+        scratch.fill_(i & 0x7F)
+        ev.record(2 * i, stream)
+        fns[i % len(fns)]()
+        ev.record(2 * i + 1, stream)
+    torch.cuda.synchronize()
+    us = sorted(ev.elapsed_ms(2 * i, 2 * i + 1) * 1e3 for i in range(iters))
+    ev.close()
+    return us[len(us) // 2]
 
 
 def time_calls(fns, iters, torch):
@@ -262,8 +294,12 @@ def time_calls(fns, iters, torch):
     the GPU busy for WARM_S (after host-side work the GPU runs slower for a
     few milliseconds), `iters` calls run back to back between two events,
     cycling through fns (the same operation on different buffers, so that
-    small cases do not run out of the 256 MB last-level cache).  Returns (per
-    call over the whole run, best of 5 equal slices, per call of the run)."""
+    small cases do not run out of the 256 MB last-level cache).  A few
+    untimed calls are queued right before the first event, so that the GPU
+    is still busy with them while the host issues the timed ones (otherwise
+    the first timed call waits for the host, a gap of tens of microseconds
+    inside the timed interval).  Returns (per call over the whole run, best
+    of 5 equal slices, per call of the run)."""
     stream = torch.cuda.current_stream().cuda_stream
     t0, n = time.perf_counter(), 0
     while n < 10 or time.perf_counter() - t0 < WARM_S:
@@ -275,6 +311,8 @@ def time_calls(fns, iters, torch):
     per = max(1, iters // slices)
     ev = HipEvents(slices + 1)
     torch.cuda.synchronize()
+    for i in range(PREQUEUE):
+        fns[(n + i) % len(fns)]()
     ev.record(0, stream)
     for j in range(slices):
         for i in range(per):
@@ -320,10 +358,15 @@ def time_graph(fns, torch, replays=20):
     return us
 
 
-def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
+def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws, cases=()):
     out = {}
 
+    def want(*names):
+        return not cases or any(n.startswith(c) for n in names for c in cases)
+
     def rec(name, fn, nbytes, gated):
+        if not want(name):
+            return
         fns = fn if isinstance(fn, list) else [fn]
         med, mn, _ = time_calls(fns, iters, torch)
         gbs = nbytes / (med * 1e-6) / 1e9
@@ -333,6 +376,8 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
         log(f"  {name}: {med:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_GBS:.1f}% of peak)")
 
     def graph_rec(name, fns, nbytes):
+        if not want(name):
+            return
         us = time_graph(fns, torch)
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us_per_call": round(us, 2), "bytes": nbytes, "GB_s": round(gbs, 1),
@@ -422,11 +467,19 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
             xs, d1["bias"], rs, d1["gamma"], d1["beta"], 1e-5, want_residual_out=False, out=o1))
     graph_rec("ln_fwd_64x384_f32_graph", calls1, M1 * (3 * 4 * N + 8))
     del d1, calls1
-    # 8192 x 4096 bf16, residual + LayerNorm, 1% outliers; two buffer
-    # sets alternate (512 MB working set)
+    # 8192 x 4096 bf16, residual + LayerNorm, 1% outliers.  Four buffer sets
+    # rotate: between two uses of a set the other three move 600 MB
+    # (backward) to 800 MB (forward), more than twice the 256 MB last-level
+    # cache, so no call finds its inputs cached from its previous use.  The
+    # same calls are also timed one at a time, each after a 512 MB scratch
+    # write ("_flushed"), and on two alternating sets ("_2sets"), whose
+    # working set of 400-540 MB lets part of a set survive in the last-level
+    # cache until its next use (for comparison only).
+    if not want("ln_fwd_8192x4096", "ln_bwd_8192x4096"):
+        return out
     M5, N5 = 8192, 4096
     sets = []
-    for seed in (0, 1):
+    for seed in range(4):
         g5 = synth.make_inputs(M5, N5, dtype=synth.BF16, seed=seed, outlier_p=0.01,
                                names=("x", "residual", "gamma", "beta", "dy"))
         d5 = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -438,16 +491,28 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws):
         sets.append((d5, o5, b5))
     ws5 = torch.empty(max(4, nf.bwd_workspace_size(M5, N5, torch.bfloat16)), dtype=torch.uint8,
                       device=dev)
-    rec("ln_fwd_8192x4096", [
-        (lambda d5=d5, o5=o5: nf.ln_fwd(d5["x"], None, d5["residual"], d5["gamma"], d5["beta"],
-                                        1e-5, out=o5)) for d5, o5, _ in sets],
-        fwd_bytes(M5, N5), True)
-    rec("ln_bwd_8192x4096", [
-        (lambda d5=d5, o5=o5, b5=b5: nf.ln_bwd(d5["dy"], o5["residual_out"], d5["gamma"],
-                                               o5["mean"], o5["rstd"],
-                                               dparam_dtype=torch.bfloat16, workspace=ws5,
-                                               out=b5)) for d5, o5, b5 in sets],
-        bwd_bytes(M5, N5), True)
+    fwd5 = [(lambda d5=d5, o5=o5: nf.ln_fwd(d5["x"], None, d5["residual"], d5["gamma"],
+                                            d5["beta"], 1e-5, out=o5)) for d5, o5, _ in sets]
+    bwd5 = [(lambda d5=d5, o5=o5, b5=b5: nf.ln_bwd(d5["dy"], o5["residual_out"], d5["gamma"],
+                                                   o5["mean"], o5["rstd"],
+                                                   dparam_dtype=torch.bfloat16, workspace=ws5,
+                                                   out=b5)) for d5, o5, b5 in sets]
+    rec("ln_fwd_8192x4096", fwd5, fwd_bytes(M5, N5), True)
+    rec("ln_bwd_8192x4096", bwd5, bwd_bytes(M5, N5), True)
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    for name, fns, nbytes in (("ln_fwd_8192x4096_flushed", fwd5, fwd_bytes(M5, N5)),
+                              ("ln_bwd_8192x4096_flushed", bwd5, bwd_bytes(M5, N5))):
+        if not want(name):
+            continue
+        us = time_flushed(fns, iters, torch, scratch)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us_per_call": round(us, 2), "bytes": nbytes, "GB_s": round(gbs, 1),
+                     "frac_peak": round(gbs / PEAK_GBS, 4), "gated_70pct": False,
+                     "timing": "median of single calls, each after a 512 MB scratch write"}
+        log(f"  {name}: {us:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_GBS:.1f}% of peak)")
+    del scratch
+    rec("ln_fwd_8192x4096_2sets", fwd5[:2], fwd_bytes(M5, N5), False)
+    rec("ln_bwd_8192x4096_2sets", bwd5[:2], bwd_bytes(M5, N5), False)
     torch.cuda.synchronize()
     return out
 

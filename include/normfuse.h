@@ -256,6 +256,32 @@ norm_status_t rms_bwd(const void *dy, const void *x, const void *gamma, const fl
 /* Static text for a status code. */
 const char *norm_status_string(norm_status_t status);
 
+/*
+ * norm_describe -- the launches a call of operation `op` on an [M, N]
+ * problem of `dtype` would make, as text in buf (at most len - 1 characters
+ * and a terminating NUL): kernel template arguments, grid, row groups per
+ * workgroup, and for the backward the column-sum launches.  Enqueues
+ * nothing and touches no device; for profilers and benchmarks that label
+ * what they timed.  It runs the same planning code as the calls and assumes
+ * their pointers are 16-byte aligned.
+ *   op    NORM_OP_LN_FWD, NORM_OP_RMS_FWD (ln_fwd / rms_fwd and their _fp8
+ *         forms), NORM_OP_LN_BWD, NORM_OP_RMS_BWD, NORM_OP_SOFTMAX
+ *   opts  NORM_DESCRIBE_AMAX (forward asked for amax), NORM_DESCRIBE_FP8
+ *         (the _fp8 forward), NORM_DESCRIBE_DBIAS (backward asked for dbias)
+ * Errors: buf NULL or len 0 -> NORM_ERR_NULL; dtype / shape as the calls;
+ * unknown op or opts -> NORM_ERR_ARG.
+ */
+#define NORM_OP_LN_FWD 0
+#define NORM_OP_RMS_FWD 1
+#define NORM_OP_LN_BWD 2
+#define NORM_OP_RMS_BWD 3
+#define NORM_OP_SOFTMAX 4
+#define NORM_DESCRIBE_AMAX 1u
+#define NORM_DESCRIBE_FP8 2u
+#define NORM_DESCRIBE_DBIAS 4u
+norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uint32_t opts,
+                            char *buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

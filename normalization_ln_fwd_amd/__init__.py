@@ -26,7 +26,7 @@ from .build import LIB as _LIB_PATH
 from .build import TUNING_LIB as _TUNING_LIB_PATH
 
 __all__ = ["ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd", "softmax_fwd",
-           "bwd_workspace_size", "NormError", "NormLibraryMissing", "library", "load", "TUNING_LIB",
+           "bwd_workspace_size", "describe", "NormError", "NormLibraryMissing", "library", "load", "TUNING_LIB",
            "F32", "BF16",
            "N_MAX", "ZERO_CENTERED_GAMMA", "DPARAM_MEAN"]
 
@@ -40,7 +40,10 @@ ZERO_CENTERED_GAMMA = 1  # option bits of include/normfuse.h
 DPARAM_MEAN = 2
 
 EXPORTS = ("ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd",
-           "softmax_fwd", "norm_bwd_workspace_size", "norm_status_string")
+           "softmax_fwd", "norm_bwd_workspace_size", "norm_status_string", "norm_describe")
+# operation codes and option bits of norm_describe
+OPS = {"ln_fwd": 0, "rms_fwd": 1, "ln_bwd": 2, "rms_bwd": 3, "softmax_fwd": 4}
+DESCRIBE_AMAX, DESCRIBE_FP8, DESCRIBE_DBIAS = 1, 2, 4
 
 
 class NormLibraryMissing(RuntimeError):
@@ -91,7 +94,9 @@ def load(path):
     lib.norm_bwd_workspace_size.argtypes = [i64, i64, i32, ctypes.POINTER(sz)]
     lib.norm_status_string.argtypes = [i32]
     lib.norm_status_string.restype = ctypes.c_char_p
-    for name in ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "norm_bwd_workspace_size"):
+    lib.norm_describe.argtypes = [i32, i64, i64, i32, u32, ctypes.c_char_p, sz]
+    for name in ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "norm_bwd_workspace_size",
+                 "norm_describe"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -242,6 +247,20 @@ def softmax_fwd(x, *, stream=None, out=None):
     _check("softmax_fwd", lib.softmax_fwd(_ptr(x, "x"), M, N, _dtype_code(x),
                                           _ptr(y, "y", x.dtype, M * N), 0, _stream(stream)))
     return y
+
+
+def describe(op, M, N, dtype, *, amax=False, fp8=False, dbias=False):
+    """Text naming the kernels, grid and walk a call of ``op`` ("ln_fwd",
+    "rms_fwd", "ln_bwd", "rms_bwd", "softmax_fwd"; the _fp8 forwards with
+    ``fp8=True``) on an [M, N] problem would launch, for 16-byte aligned
+    tensors.  Touches no device."""
+    lib = library()
+    code = dtype if isinstance(dtype, int) else (F32 if dtype == torch.float32 else BF16)
+    opts = (DESCRIBE_AMAX if amax else 0) | (DESCRIBE_FP8 if fp8 else 0) | \
+        (DESCRIBE_DBIAS if dbias else 0)
+    buf = ctypes.create_string_buffer(512)
+    _check("norm_describe", lib.norm_describe(OPS[op], M, N, code, opts, buf, len(buf)))
+    return buf.value.decode()
 
 
 def bwd_workspace_size(M, N, dtype):

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -279,6 +280,21 @@ int full_width(int32_t dtype) { return int(16 / elem_size(dtype)); }
 norm_status_t launched(hipError_t e) { return e == hipSuccess ? NORM_OK : NORM_ERR_LAUNCH; }
 
 // ------------------------------------------------------------------ forward
+// Kernel shape and walk of a forward call (shared by the call and by
+// norm_describe, so that a description names what a call launches).
+norm_status_t fwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool amax, bool f8,
+                       const Knobs &kn, const FwdEntry **entry, Walk *w)
+{
+    const FwdEntry *e = fwd_entry(dtype, vec, M, int(N), kn);
+    if (!e)
+        return NORM_ERR_SHAPE;
+    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, amax, f8);
+    if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
+        return st;
+    *entry = e;
+    return NORM_OK;
+}
+
 // y_scale == nullptr: y in the I/O dtype; else y holds FP8 E4M3 codes of
 // y * (*y_scale) (one byte per element).
 norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *residual,
@@ -313,12 +329,9 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     const int vec = vec_width(N, dtype, {x, bias, residual, gamma, beta, f8 ? nullptr : y,
                                          residual_out},
                               f8 ? y : nullptr);
-    const FwdEntry *e = fwd_entry(dtype, vec, M, int(N), kn);
-    if (!e)
-        return NORM_ERR_SHAPE;
-    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, amax != nullptr, f8);
+    const FwdEntry *e = nullptr;
     Walk w;
-    if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
+    if (norm_status_t st = fwd_plan(M, N, dtype, vec, amax != nullptr, f8, kn, &e, &w))
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -355,6 +368,31 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
 }
 
 // ------------------------------------------------------------------ softmax
+norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, const Knobs &kn,
+                           const SoftmaxEntry **entry, Walk *w)
+{
+    int n = 0;
+    const SoftmaxEntry *tab =
+        dtype == NORM_F32 ? softmax_table_f32(vec, &n) : softmax_table_bf16(vec, &n);
+    const SoftmaxEntry *e = pick_shape(tab, n, int(N), 0, 0, 0);
+    if (!e)
+        return NORM_ERR_SHAPE;
+    // the 512-thread variant of a narrow shape when rows are plentiful
+    for (int i = 0; i < n; ++i) {
+        const RowShape &ws = tab[i].shape;
+        if (ws.lpr == e->shape.lpr && ws.vpl == e->shape.vpl && ws.teams == 2 * e->shape.teams &&
+            (M + ws.teams - 1) / ws.teams >= kMinWideGroups) {
+            e = &tab[i];
+            break;
+        }
+    }
+    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, false, false);
+    if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
+        return st;
+    *entry = e;
+    return NORM_OK;
+}
+
 norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype, void *y,
                              uint32_t flags, void *stream)
 {
@@ -376,24 +414,9 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
         return NORM_OK;
     const Knobs kn = knobs();
     const int vec = vec_width(N, dtype, {x, y});
-    int n = 0;
-    const SoftmaxEntry *tab =
-        dtype == NORM_F32 ? softmax_table_f32(vec, &n) : softmax_table_bf16(vec, &n);
-    const SoftmaxEntry *e = pick_shape(tab, n, int(N), 0, 0, 0);
-    if (!e)
-        return NORM_ERR_SHAPE;
-    // the 512-thread variant of a narrow shape when rows are plentiful
-    for (int i = 0; i < n; ++i) {
-        const RowShape &w = tab[i].shape;
-        if (w.lpr == e->shape.lpr && w.vpl == e->shape.vpl && w.teams == 2 * e->shape.teams &&
-            (M + w.teams - 1) / w.teams >= kMinWideGroups) {
-            e = &tab[i];
-            break;
-        }
-    }
+    const SoftmaxEntry *e = nullptr;
     Walk w;
-    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, false, false);
-    if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, &w))
+    if (norm_status_t st = softmax_plan(M, N, dtype, vec, kn, &e, &w))
         return st;
     SoftmaxArgs a;
     a.x = x;
@@ -615,9 +638,107 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
                                   divisor, level2, s));
 }
 
+// Elements per vector access of a call whose pointers are all 16-byte
+// aligned: the widest access N is a multiple of.
+int vec_of_aligned(int64_t N, int32_t dtype)
+{
+    const int es = int(elem_size(dtype));
+    const int min_bytes = dtype == NORM_F32 ? 8 : 4;
+    for (int bytes = 16; bytes >= min_bytes; bytes /= 2)
+        if (N % (bytes / es) == 0)
+            return bytes / es;
+    return 1;
+}
+
+const char *dtype_name(int32_t dtype) { return dtype == NORM_F32 ? "fp32" : "bf16"; }
+
+// Appends to buf (the text is truncated to len - 1 characters).
+struct Text {
+    char *buf;
+    size_t len, used = 0;
+    void add(const char *fmt, ...) __attribute__((format(printf, 2, 3)))
+    {
+        if (!buf || len == 0 || used + 1 >= len)
+            return;
+        va_list ap;
+        va_start(ap, fmt);
+        const int n = std::vsnprintf(buf + used, len - used, fmt, ap);
+        va_end(ap);
+        if (n > 0)
+            used = std::min(len - 1, used + size_t(n));
+    }
+};
+
+void describe_shape(Text &t, const char *kernel, int32_t dtype, const RowShape &sh)
+{
+    t.add("%s<%s, VEC %d, LPR %d, VPL %d, TEAMS %d", kernel, dtype_name(dtype), sh.vec, sh.lpr,
+          sh.vpl, sh.teams);
+}
+
 } // namespace
 
 extern "C" {
+
+norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uint32_t opts,
+                            char *buf, size_t len)
+{
+    if (!buf || len == 0)
+        return NORM_ERR_NULL;
+    buf[0] = '\0';
+    if (!dtype_ok(dtype))
+        return NORM_ERR_DTYPE;
+    if (norm_status_t st = check_shape(M, N))
+        return st;
+    if (op < NORM_OP_LN_FWD || op > NORM_OP_SOFTMAX ||
+        (opts & ~uint32_t(NORM_DESCRIBE_AMAX | NORM_DESCRIBE_FP8 | NORM_DESCRIBE_DBIAS)))
+        return NORM_ERR_ARG;
+    const Knobs kn = knobs();
+    const int vec = vec_of_aligned(N, dtype);
+    Text t{buf, len};
+    Walk w;
+    if (op == NORM_OP_LN_FWD || op == NORM_OP_RMS_FWD) {
+        const bool amax = opts & NORM_DESCRIBE_AMAX, f8 = opts & NORM_DESCRIBE_FP8;
+        const FwdEntry *e = nullptr;
+        if (norm_status_t st = fwd_plan(M, N, dtype, vec, amax, f8, kn, &e, &w))
+            return st;
+        describe_shape(t, "fwd_kernel", dtype, e->shape);
+        t.add(", %s%s>; grid %lld x %d threads, %d row group(s) of %d rows per workgroup",
+              op == NORM_OP_RMS_FWD ? "RMSNorm" : "LayerNorm", f8 ? ", FP8 y" : "",
+              (long long)w.grid, e->shape.threads(), w.K, e->shape.teams);
+        if (amax)
+            t.add("; amax: one-thread reset kernel first");
+        return NORM_OK;
+    }
+    if (op == NORM_OP_SOFTMAX) {
+        const SoftmaxEntry *e = nullptr;
+        if (norm_status_t st = softmax_plan(M, N, dtype, vec, kn, &e, &w))
+            return st;
+        describe_shape(t, "softmax_kernel", dtype, e->shape);
+        t.add(">; grid %lld x %d threads, %d row group(s) of %d rows per workgroup",
+              (long long)w.grid, e->shape.threads(), w.K, e->shape.teams);
+        return NORM_OK;
+    }
+    const bool dbias = opts & NORM_DESCRIBE_DBIAS;
+    const BwdEntry *e = nullptr;
+    BwdLayout lay;
+    if (norm_status_t st = bwd_plan(M, N, dtype, vec, dbias ? 3 : 2, kn, &e, &w, &lay))
+        return st;
+    const char *norm = op == NORM_OP_RMS_BWD ? "RMSNorm" : "LayerNorm";
+    if (lay.split) {
+        t.add("bwd_split_kernel<%s, VEC %d, %s%s>, two passes; grid %d chunks x %d row blocks "
+              "x %d threads", dtype_name(dtype), vec, norm, dbias ? ", dbias" : "", lay.chunks,
+              lay.blocks, 64 * SPLIT_ROWS_PER_GROUP);
+    } else {
+        describe_shape(t, "bwd_kernel", dtype, e->shape);
+        t.add(", %s%s>; grid %lld x %d threads, %d row group(s) of %d rows per workgroup", norm,
+              dbias ? ", dbias" : "", (long long)w.grid, e->shape.threads(), w.K,
+              e->shape.teams);
+    }
+    const int64_t parts = lay.split ? lay.blocks : w.grid;
+    t.add("; then column sums of %lld partial rows in %d launch(es)", (long long)parts,
+          lay.two_level ? 2 : 1);
+    return NORM_OK;
+}
 
 norm_status_t ln_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                      const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,

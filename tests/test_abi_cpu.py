@@ -51,6 +51,11 @@ def test_exports_every_declared_function(lib):
 
 def test_binding_constants_match_header():
     d = header_defines()
+    for op, code in nf.OPS.items():
+        assert d["NORM_OP_" + op.replace("_fwd", "_FWD").replace("_bwd", "_BWD")
+                 .replace("softmax_FWD", "SOFTMAX").upper()] == code
+    assert (d["NORM_DESCRIBE_AMAX"], d["NORM_DESCRIBE_FP8"], d["NORM_DESCRIBE_DBIAS"]) == \
+        (nf.DESCRIBE_AMAX, nf.DESCRIBE_FP8, nf.DESCRIBE_DBIAS)
     assert d["NORM_F32"] == nf.F32 and d["NORM_BF16"] == nf.BF16
     assert d["NORM_N_MAX"] == nf.N_MAX
     for code, name in nf.STATUS.items():
@@ -253,3 +258,37 @@ def test_binding_rejects_unsupported_dparam_dtype():
             nf.rms_bwd(x, x, None, dparam_dtype=bad)
     with pytest.raises(TypeError, match="dparam_dtype"):
         nf.ln_bwd(x.half(), x.half(), None, None, None)  # defaults to x's dtype
+
+
+def test_describe_names_the_planned_kernels(lib):
+    """norm_describe runs the calls' planning code without a device: the
+    benchmark's shapes take the kernels its roofline names."""
+    d = nf.describe("ln_fwd", 576000, 384, nf.BF16, amax=True)
+    assert d.startswith("fwd_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 32, LayerNorm>"), d
+    assert "grid 18000 x 512 threads" in d, d
+    d = nf.describe("rms_fwd", 576000, 384, nf.BF16, amax=True)
+    assert "TEAMS 32, RMSNorm>" in d, d
+    d = nf.describe("ln_bwd", 576000, 384, nf.BF16)
+    assert d.startswith("bwd_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 16, LayerNorm>"), d
+    assert "grid 508 x 256 threads, 71 row group(s)" in d, d
+    assert "column sums of 508 partial rows in 1" in d, d
+    d = nf.describe("ln_bwd", 8192, 4096, nf.BF16, dbias=True)
+    assert d.startswith("bwd_kernel<bf16, VEC 8, LPR 512, VPL 1, TEAMS 2, LayerNorm, dbias>"), d
+    assert "grid 256 x 1024 threads, 16 row group(s)" in d, d
+    assert nf.describe("softmax_fwd", 576000, 384, nf.BF16).startswith(
+        "softmax_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 32>")
+    assert "bwd_split_kernel" in nf.describe("ln_bwd", 64, 16384, nf.BF16)
+
+
+def test_describe_rejects(lib):
+    buf = ctypes.create_string_buffer(64)
+    assert lib.norm_describe(0, 4, 64, 1, 0, None, 64) == 1
+    assert lib.norm_describe(0, 4, 64, 1, 0, buf, 0) == 1
+    assert lib.norm_describe(0, 4, 64, 7, 0, buf, 64) == 4
+    assert lib.norm_describe(0, 4, 0, 1, 0, buf, 64) == 2
+    assert lib.norm_describe(9, 4, 64, 1, 0, buf, 64) == 3
+    assert lib.norm_describe(0, 4, 64, 1, 8, buf, 64) == 3
+    # a short buffer holds a truncated, terminated text
+    small = ctypes.create_string_buffer(8)
+    assert lib.norm_describe(0, 4, 64, 1, 0, small, 8) == 0
+    assert small.value == b"fwd_ker"

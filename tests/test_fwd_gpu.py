@@ -79,6 +79,24 @@ def test_fwd_matches_oracle(M, N, rms, dtype, misalign):
     check_fwd(rms, inp, dtype, eps, out)
 
 
+# Row counts that take the 512-thread variants of the narrow shapes (twice
+# the teams per workgroup, chosen from 2048 row groups of the doubled team
+# count on), with ragged tails: the instantiations the benchmark's 576000-row
+# forwards and softmax run (bf16, 384 columns: teams of 16 lanes, 32 rows per
+# workgroup) and their fp32 counterparts (teams of 32 or 64 lanes).
+WIDE_WG_SHAPES = [(100003, 384, BF16), (40001, 384, F32), (40001, 1024, BF16),
+                  (20001, 1024, F32)]
+
+
+@pytest.mark.parametrize("M,N,dtype", WIDE_WG_SHAPES)
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+def test_fwd_512_thread_workgroups_match_oracle(M, N, dtype, rms):
+    inp = synth.make_inputs(M, N, dtype=dtype, seed=M + N)
+    eps = 1e-6 if rms else 1e-5
+    out = run_fwd(rms, inp, dtype, eps)
+    check_fwd(rms, inp, dtype, eps, out)
+
+
 @pytest.mark.parametrize("parts", [("x",), ("x", "residual"), ("x", "bias"), ("x", "gamma"),
                                    ("x", "residual", "gamma", "beta")],
                          ids=["x", "x+res", "x+bias", "x+gamma", "x+res+affine"])

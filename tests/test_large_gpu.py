@@ -1,8 +1,10 @@
 """The largest sizes: tensors past 4 GiB (64-bit addressing of row groups)
-and the longest rows (N = NORM_N_MAX), on sampled rows against the oracle.
+and the longest rows (N = NORM_N_MAX), against the oracle.
 
 M = 6,000,000 rows of 384 bf16 elements is 4.6 GB per tensor; the forward
-runs on it end to end and the backward's column sums cover every row."""
+runs on it end to end (y and residual_out on sampled rows, amax over all of
+y) and the backward's column sums over every row are compared with the
+oracle's, at the 1e-3 bar of the 576000-row workloads."""
 import numpy as np
 import pytest
 import torch
@@ -60,17 +62,17 @@ def test_forward_and_backward_past_4gib():
                       scale=ref_b["rstd"] * np.max(np.abs(synth.to_f64(bits(dy[ridx]), BF16)
                                                           * synth.to_f64(sub["gamma"], BF16)),
                                                    axis=1))
-    # column sums over every row, against fp64 sums of the same terms on the GPU
-    xhat = (out["residual_out"].float() - out["mean"][:, None]) * out["rstd"][:, None]
-    dbeta64 = dy.double().sum(0)
-    dgamma64 = (dy.float() * xhat).double().sum(0)
-    dbeta_l2 = dy.double().pow(2).sum(0).sqrt()
-    dgamma_l2 = (dy.float() * xhat).double().pow(2).sum(0).sqrt()
-    del xhat
-    assert_colsums_close(f64(b["dbeta"]), dbeta64.cpu().numpy(), dbeta_l2.cpu().numpy(), 1e-3,
-                         "dbeta (all rows)")
-    assert_colsums_close(f64(b["dgamma"]), dgamma64.cpu().numpy(), dgamma_l2.cpu().numpy(),
-                         2e-3, "dgamma (all rows)")
+    # column sums over every row against the oracle (its column sums only),
+    # on the same dy, residual_out, gamma and the GPU forward's fp32 mean / rstd
+    dy_h = bits(dy)
+    del dy
+    u_h = bits(out["residual_out"])
+    mean_h, rstd_h = out["mean"].cpu().numpy(), out["rstd"].cpu().numpy()
+    ref_c = oracle.norm_bwd(dy_h, u_h, sub["gamma"], mean_h, rstd_h, 1e-5, want_dx=False)
+    del dy_h, u_h
+    for k in ("dgamma", "dbeta"):
+        e = assert_colsums_close(f64(b[k]), ref_c[k], ref_c[k + "_l2"], 1e-3, k + " (all rows)")
+        print(f"{k} over {M} rows: max |err| / max(|ref|, l2) = {e:.3e}")
 
 
 @pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])

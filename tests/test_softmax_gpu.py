@@ -39,6 +39,16 @@ def test_softmax_matches_oracle(M, N, dtype, misalign):
         assert np.all(np.abs(rs - 1.0) <= N * (2.0**-8 if dtype == BF16 else 2.0**-22))
 
 
+@pytest.mark.parametrize("M,N,dtype", [(100003, 384, BF16), (40001, 384, F32)])
+def test_softmax_512_thread_workgroups_match_oracle(M, N, dtype):
+    """Row counts that take the 512-thread variant of the narrow shape (the
+    instantiation the benchmark's 576000-row softmax runs), ragged tail."""
+    x = synth.make_inputs(M, N, dtype=dtype, seed=M + 1, names=("x",))["x"]
+    y = nf.softmax_fwd(to_dev(x, dtype))
+    torch.cuda.synchronize()
+    assert_rows_close(f64(y), oracle.softmax_fwd(x, dtype=dtype), dtype, "softmax")
+
+
 def test_softmax_special_rows():
     N = 384
     x = np.zeros((4, N), np.float32)
