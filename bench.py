@@ -175,10 +175,13 @@ def main():
                      device=dev)
     fwd_out = {"y": y, "residual_out": res_out, "mean": mean, "rstd": rstd, "amax": amax}
     bwd_out = {"dx": dx, "dgamma": dgamma, "dbeta": dbeta}
+    # amax in one kernel launch: the forward's workspace (zero-filled once,
+    # left zero-filled by every call)
+    amax_ws = nf.amax_workspace(dev)
 
     def fwd():
         nf.ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 1e-5,
-                  want_amax=True, out=fwd_out)
+                  want_amax=True, amax_workspace=amax_ws, out=fwd_out)
 
     def bwd():
         nf.ln_bwd(d["dy"], res_out, d["gamma"], mean, rstd, dparam_dtype=torch.bfloat16,
@@ -214,14 +217,14 @@ def main():
 
     # Per-launch durations of the two halves of the step: K forward calls back
     # to back between two events, then K backward calls.  A forward call is
-    # the amax reset (one tiny kernel) and the forward kernel.
+    # one kernel (amax through the workspace).
     fwd_avg = time_calls([fwd], K, torch)[2]
     bwd_avg = time_calls([bwd], K, torch)[2]
     fwd_gbs = fwd_bytes(M, N) / (fwd_avg * 1e-6) / 1e9
     traffic = recorded_traffic()
     roofline = {"bound": "hbm", "achieved": round(fwd_gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(fwd_gbs / PEAK_GBS, 4), "traffic": traffic,
-                "kernel": nf.describe("ln_fwd", M, N, torch.bfloat16, amax=True),
+                "kernel": nf.describe("ln_fwd", M, N, torch.bfloat16, amax=True, amax_ws=True),
                 "bytes_per_launch": fwd_bytes(M, N), "avg_launch_us": round(fwd_avg, 2),
                 "kernel_source_hash": kernel_source_hash()}
 
@@ -251,7 +254,7 @@ def main():
     if not args.no_breakdown:
         cases = [c for c in args.cases.split(",") if c]
         result["breakdown"] = breakdown(args.breakdown_iters, nf, torch, np, synth, d, h, dev,
-                                        fwd_out, ws, cases)
+                                        fwd_out, ws, cases, amax_ws)
 
     # free the device copies before the CPU leg
     del d
@@ -358,7 +361,7 @@ def time_graph(fns, torch, replays=20):
     return us
 
 
-def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws, cases=()):
+def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws, cases=(), amax_ws=None):
     out = {}
 
     def want(*names):
@@ -387,8 +390,13 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws, cases=()):
 
     M, N = M_BIG, N_BIG
     rec("ln_fwd_576000x384", lambda: nf.ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"],
-                                                d["beta"], 1e-5, want_amax=True, out=fwd_out),
+                                                d["beta"], 1e-5, want_amax=True,
+                                                amax_workspace=amax_ws, out=fwd_out),
         fwd_bytes(M, N), True)
+    # the same without the amax workspace: a one-thread kernel zeroes amax first
+    rec("ln_fwd_576000x384_amax_reset", lambda: nf.ln_fwd(
+        d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 1e-5, want_amax=True,
+        out=fwd_out), fwd_bytes(M, N), False)
     # FP8 output (E4M3 codes, one byte per element) with the scale taken from
     # the amax of a previous call, as a training step would
     y8 = torch.empty((M, N), dtype=torch.float8_e4m3fn, device=dev)
@@ -397,16 +405,18 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws, cases=()):
                "rstd": fwd_out["rstd"], "amax": fwd_out["amax"]}
     rec("ln_fwd_fp8_576000x384", lambda: nf.ln_fwd_fp8(d["x"], sc, d["bias"], d["residual"],
                                                         d["gamma"], d["beta"], 1e-5,
-                                                        want_amax=True, out=fp8_out),
+                                                        want_amax=True, amax_workspace=amax_ws,
+                                                        out=fp8_out),
         M * (7 * N + 8), False)
     del y8
     rec("ln_fwd_576000x384_zero_centered", lambda: nf.ln_fwd(
         d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 1e-5, want_amax=True,
-        zero_centered_gamma=True, out=fwd_out), fwd_bytes(M, N), False)
+        zero_centered_gamma=True, amax_workspace=amax_ws, out=fwd_out), fwd_bytes(M, N), False)
     rms_out = {"y": fwd_out["y"], "residual_out": fwd_out["residual_out"],
                "rstd": fwd_out["rstd"], "amax": fwd_out["amax"]}
     rec("rms_fwd_576000x384", lambda: nf.rms_fwd(d["x"], d["bias"], d["residual"], d["gamma"],
-                                                  None, 1e-6, want_amax=True, out=rms_out),
+                                                  None, 1e-6, want_amax=True,
+                                                  amax_workspace=amax_ws, out=rms_out),
         fwd_bytes(M, N, stats=1), False)
     # the 576000 x 384 backwards (RMSNorm with rstd recomputed, LayerNorm from
     # saved statistics): on x = N(0,1) (the generator's x), dy
@@ -442,13 +452,19 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws, cases=()):
             for i in range(M // M2)]
     rec("ln_fwd_4096x384_amax", [
         (lambda s=s: nf.ln_fwd(s["x"], s["bias"], s["residual"], s["gamma"], s["beta"], 1e-5,
-                               want_amax=True)) for s in subs], fwd_bytes(M2, N), False)
+                               want_amax=True, amax_workspace=amax_ws)) for s in subs],
+        fwd_bytes(M2, N), False)
     # the same calls replayed from a captured graph (outputs preallocated):
-    # the GPU time of the launch-bound size, amax reset included
+    # the GPU time of the launch-bound size, with the amax workspace (one
+    # kernel per call) and with the reset kernel (two)
     outs2 = [{"y": torch.empty_like(s["x"]), "residual_out": torch.empty_like(s["x"]),
               "mean": torch.empty(M2, device=dev), "rstd": torch.empty(M2, device=dev),
               "amax": torch.empty(1, device=dev)} for s in subs[:64]]
     graph_rec("ln_fwd_4096x384_amax_graph", [
+        (lambda s=s, o=o: nf.ln_fwd(s["x"], s["bias"], s["residual"], s["gamma"], s["beta"],
+                                    1e-5, want_amax=True, amax_workspace=amax_ws, out=o))
+        for s, o in zip(subs[:64], outs2)], fwd_bytes(M2, N))
+    graph_rec("ln_fwd_4096x384_amax_reset_graph", [
         (lambda s=s, o=o: nf.ln_fwd(s["x"], s["bias"], s["residual"], s["gamma"], s["beta"],
                                     1e-5, want_amax=True, out=o))
         for s, o in zip(subs[:64], outs2)], fwd_bytes(M2, N))

@@ -142,13 +142,26 @@ typedef int32_t norm_status_t;
  *   residual_out [M,N] dtype   optional: u, the rounded sum that was normalised
  *   mean, rstd   [M]   fp32    optional
  *   amax         [1]   fp32    optional: overwritten with max |y| (0 when M = 0)
+ *   amax_ws      NORM_AMAX_WS_BYTES of device memory, 4-byte aligned, optional
+ *                (ignored without amax).  Without it the call zeroes amax with
+ *                a one-thread kernel before the forward kernel, whose
+ *                workgroups then combine their maxima into it; with it the
+ *                forward kernel alone produces amax: the workgroups combine
+ *                their maxima in the workspace and the last one to finish
+ *                writes amax.  The workspace must hold zeros before its first
+ *                use (e.g. hipMemset once after allocation); every call leaves
+ *                it zero-filled again when it completes, so it can be reused
+ *                by calls ordered on one stream.  Calls that may run at the
+ *                same time must not share one.  A call that did not complete
+ *                (a fault) can leave it non-zero.
  *   flags        0 or NORM_ZERO_CENTERED_GAMMA
  *   stream       hipStream_t
  */
+#define NORM_AMAX_WS_BYTES 4160
 norm_status_t ln_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                      const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
-                     void *residual_out, float *mean, float *rstd, float *amax, uint32_t flags,
-                     void *stream);
+                     void *residual_out, float *mean, float *rstd, float *amax, void *amax_ws,
+                     uint32_t flags, void *stream);
 
 /*
  * rms_fwd -- fused (bias +) residual + RMSNorm forward.  Arguments as ln_fwd;
@@ -157,8 +170,8 @@ norm_status_t ln_fwd(const void *x, const void *bias, const void *residual, cons
  */
 norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                       const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
-                      void *residual_out, float *mean, float *rstd, float *amax, uint32_t flags,
-                      void *stream);
+                      void *residual_out, float *mean, float *rstd, float *amax, void *amax_ws,
+                      uint32_t flags, void *stream);
 
 /*
  * ln_fwd_fp8 / rms_fwd_fp8 -- the same forward with y emitted as OCP FP8
@@ -184,12 +197,12 @@ norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, con
 norm_status_t ln_fwd_fp8(const void *x, const void *bias, const void *residual,
                          const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                          int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
-                         float *mean, float *rstd, float *amax, uint32_t flags,
+                         float *mean, float *rstd, float *amax, void *amax_ws, uint32_t flags,
                          void *stream);
 norm_status_t rms_fwd_fp8(const void *x, const void *bias, const void *residual,
                           const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                           int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
-                          float *mean, float *rstd, float *amax, uint32_t flags,
+                          float *mean, float *rstd, float *amax, void *amax_ws, uint32_t flags,
                           void *stream);
 
 /*
@@ -266,8 +279,9 @@ const char *norm_status_string(norm_status_t status);
  * their pointers are 16-byte aligned.
  *   op    NORM_OP_LN_FWD, NORM_OP_RMS_FWD (ln_fwd / rms_fwd and their _fp8
  *         forms), NORM_OP_LN_BWD, NORM_OP_RMS_BWD, NORM_OP_SOFTMAX
- *   opts  NORM_DESCRIBE_AMAX (forward asked for amax), NORM_DESCRIBE_FP8
- *         (the _fp8 forward), NORM_DESCRIBE_DBIAS (backward asked for dbias)
+ *   opts  NORM_DESCRIBE_AMAX (forward asked for amax), NORM_DESCRIBE_AMAX_WS
+ *         (and passed an amax_ws), NORM_DESCRIBE_FP8 (the _fp8 forward),
+ *         NORM_DESCRIBE_DBIAS (backward asked for dbias)
  * Errors: buf NULL or len 0 -> NORM_ERR_NULL; dtype / shape as the calls;
  * unknown op or opts -> NORM_ERR_ARG.
  */
@@ -279,6 +293,7 @@ const char *norm_status_string(norm_status_t status);
 #define NORM_DESCRIBE_AMAX 1u
 #define NORM_DESCRIBE_FP8 2u
 #define NORM_DESCRIBE_DBIAS 4u
+#define NORM_DESCRIBE_AMAX_WS 8u
 norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uint32_t opts,
                             char *buf, size_t len);
 

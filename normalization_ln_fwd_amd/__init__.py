@@ -26,7 +26,7 @@ from .build import LIB as _LIB_PATH
 from .build import TUNING_LIB as _TUNING_LIB_PATH
 
 __all__ = ["ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd", "softmax_fwd",
-           "bwd_workspace_size", "describe", "NormError", "NormLibraryMissing", "library", "load", "TUNING_LIB",
+           "bwd_workspace_size", "describe", "amax_workspace", "NormError", "NormLibraryMissing", "library", "load", "TUNING_LIB",
            "F32", "BF16",
            "N_MAX", "ZERO_CENTERED_GAMMA", "DPARAM_MEAN"]
 
@@ -43,7 +43,8 @@ EXPORTS = ("ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd"
            "softmax_fwd", "norm_bwd_workspace_size", "norm_status_string", "norm_describe")
 # operation codes and option bits of norm_describe
 OPS = {"ln_fwd": 0, "rms_fwd": 1, "ln_bwd": 2, "rms_bwd": 3, "softmax_fwd": 4}
-DESCRIBE_AMAX, DESCRIBE_FP8, DESCRIBE_DBIAS = 1, 2, 4
+DESCRIBE_AMAX, DESCRIBE_FP8, DESCRIBE_DBIAS, DESCRIBE_AMAX_WS = 1, 2, 4, 8
+AMAX_WS_BYTES = 4160  # NORM_AMAX_WS_BYTES
 
 
 class NormLibraryMissing(RuntimeError):
@@ -80,10 +81,10 @@ def load(path):
     vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                              ctypes.c_float, ctypes.c_size_t)
     u32 = ctypes.c_uint32
-    fwd = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, u32, vp]
+    fwd = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp, u32, vp]
     lib.ln_fwd.argtypes = fwd
     lib.rms_fwd.argtypes = fwd
-    fwd8 = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp, u32, vp]
+    fwd8 = [vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp, u32, vp]
     lib.ln_fwd_fp8.argtypes = fwd8
     lib.rms_fwd_fp8.argtypes = fwd8
     lib.ln_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, i32, vp, sz,
@@ -146,8 +147,16 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+def amax_workspace(device=None):
+    """A zero-filled amax workspace (NORM_AMAX_WS_BYTES) for the forwards'
+    ``amax_workspace``: allocate once and pass it to every call on one
+    stream; each call leaves it zero-filled again."""
+    return torch.zeros(AMAX_WS_BYTES, dtype=torch.uint8,
+                       device=device if device is not None else "cuda")
+
+
 def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, want_rstd,
-         want_amax, stream, out, y_scale=None, zero_centered_gamma=False):
+         want_amax, stream, out, y_scale=None, zero_centered_gamma=False, amax_workspace=None):
     lib = library()
     N = x.shape[-1]
     M = x.numel() // N if N else 0
@@ -182,59 +191,73 @@ def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, 
     st = getattr(lib, fn)(
         *head, _ptr(res_out, "residual_out", dt, M * N),
         _ptr(mean, "mean", torch.float32, M), _ptr(rstd, "rstd", torch.float32, M),
-        _ptr(amax, "amax", torch.float32, 1), ZERO_CENTERED_GAMMA if zero_centered_gamma else 0,
-        _stream(stream))
+        _ptr(amax, "amax", torch.float32, 1), _ws_ptr(amax_workspace),
+        ZERO_CENTERED_GAMMA if zero_centered_gamma else 0, _stream(stream))
     _check(fn, st)
     return {"y": y, "residual_out": res_out, "mean": mean, "rstd": rstd, "amax": amax}
 
 
+def _ws_ptr(ws):
+    if ws is None:
+        return None
+    if not isinstance(ws, torch.Tensor) or ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("amax_workspace must be a contiguous GPU tensor")
+    if ws.numel() * ws.element_size() < AMAX_WS_BYTES:
+        raise ValueError(f"amax_workspace must hold at least {AMAX_WS_BYTES} bytes")
+    return ws.data_ptr()
+
+
 def ln_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, *,
            want_residual_out=None, want_stats=True, want_amax=False, zero_centered_gamma=False,
-           stream=None, out=None):
+           amax_workspace=None, stream=None, out=None):
     """Fused (bias +) residual + LayerNorm over the last dimension of ``x``.
 
     Returns a dict with ``y``, ``residual_out`` (when bias or residual is given,
     unless disabled), ``mean`` / ``rstd`` (fp32, when ``want_stats``) and
     ``amax`` (1-element fp32, when ``want_amax``).  ``out`` may supply any of
     these tensors preallocated.  ``zero_centered_gamma``: the weight is
-    1 + gamma.
+    1 + gamma.  ``amax_workspace`` (see :func:`amax_workspace`): amax in one
+    kernel launch instead of a reset kernel and the forward.
     """
     if want_residual_out is None:
         want_residual_out = bias is not None or residual is not None
     return _fwd("ln_fwd", x, bias, residual, gamma, beta, eps, want_residual_out, want_stats,
-                want_stats, want_amax, stream, out, zero_centered_gamma=zero_centered_gamma)
+                want_stats, want_amax, stream, out, zero_centered_gamma=zero_centered_gamma,
+                amax_workspace=amax_workspace)
 
 
 def rms_fwd(x, bias=None, residual=None, gamma=None, beta=None, eps=1e-6, *,
             want_residual_out=None, want_stats=True, want_amax=False, zero_centered_gamma=False,
-            stream=None, out=None):
+            amax_workspace=None, stream=None, out=None):
     """Fused (bias +) residual + RMSNorm; as :func:`ln_fwd` without ``mean``."""
     if want_residual_out is None:
         want_residual_out = bias is not None or residual is not None
     return _fwd("rms_fwd", x, bias, residual, gamma, beta, eps, want_residual_out, False,
-                want_stats, want_amax, stream, out, zero_centered_gamma=zero_centered_gamma)
+                want_stats, want_amax, stream, out, zero_centered_gamma=zero_centered_gamma,
+                amax_workspace=amax_workspace)
 
 
 def ln_fwd_fp8(x, y_scale, bias=None, residual=None, gamma=None, beta=None, eps=1e-5, *,
                want_residual_out=None, want_stats=True, want_amax=False,
-               zero_centered_gamma=False, stream=None, out=None):
+               zero_centered_gamma=False, amax_workspace=None, stream=None, out=None):
     """:func:`ln_fwd` with ``y`` as OCP FP8 E4M3 codes of y * y_scale
     (``y_scale``: a 1-element fp32 tensor on the GPU); ``y`` is returned as a
     ``float8_e4m3fn`` tensor (``out`` may supply one, or a ``uint8`` one)."""
     if want_residual_out is None:
         want_residual_out = bias is not None or residual is not None
     return _fwd("ln_fwd_fp8", x, bias, residual, gamma, beta, eps, want_residual_out,
-                want_stats, want_stats, want_amax, stream, out, y_scale, zero_centered_gamma)
+                want_stats, want_stats, want_amax, stream, out, y_scale, zero_centered_gamma,
+                amax_workspace)
 
 
 def rms_fwd_fp8(x, y_scale, bias=None, residual=None, gamma=None, beta=None, eps=1e-6, *,
                 want_residual_out=None, want_stats=True, want_amax=False,
-                zero_centered_gamma=False, stream=None, out=None):
+                zero_centered_gamma=False, amax_workspace=None, stream=None, out=None):
     """:func:`rms_fwd` with ``y`` as OCP FP8 E4M3 codes of y * y_scale."""
     if want_residual_out is None:
         want_residual_out = bias is not None or residual is not None
     return _fwd("rms_fwd_fp8", x, bias, residual, gamma, beta, eps, want_residual_out, False,
-                want_stats, want_amax, stream, out, y_scale, zero_centered_gamma)
+                want_stats, want_amax, stream, out, y_scale, zero_centered_gamma, amax_workspace)
 
 
 def softmax_fwd(x, *, stream=None, out=None):
@@ -249,7 +272,7 @@ def softmax_fwd(x, *, stream=None, out=None):
     return y
 
 
-def describe(op, M, N, dtype, *, amax=False, fp8=False, dbias=False):
+def describe(op, M, N, dtype, *, amax=False, fp8=False, dbias=False, amax_ws=False):
     """Text naming the kernels, grid and walk a call of ``op`` ("ln_fwd",
     "rms_fwd", "ln_bwd", "rms_bwd", "softmax_fwd"; the _fp8 forwards with
     ``fp8=True``) on an [M, N] problem would launch, for 16-byte aligned
@@ -257,7 +280,7 @@ def describe(op, M, N, dtype, *, amax=False, fp8=False, dbias=False):
     lib = library()
     code = dtype if isinstance(dtype, int) else (F32 if dtype == torch.float32 else BF16)
     opts = (DESCRIBE_AMAX if amax else 0) | (DESCRIBE_FP8 if fp8 else 0) | \
-        (DESCRIBE_DBIAS if dbias else 0)
+        (DESCRIBE_DBIAS if dbias else 0) | (DESCRIBE_AMAX_WS if amax_ws else 0)
     buf = ctypes.create_string_buffer(512)
     _check("norm_describe", lib.norm_describe(OPS[op], M, N, code, opts, buf, len(buf)))
     return buf.value.decode()

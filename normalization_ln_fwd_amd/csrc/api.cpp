@@ -300,8 +300,8 @@ norm_status_t fwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool amax, 
 norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *residual,
                          const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                          int32_t dtype, const float *y_scale, void *y, void *residual_out,
-                         float *mean, float *rstd, float *amax, bool f8, uint32_t flags,
-                         void *stream)
+                         float *mean, float *rstd, float *amax, void *amax_ws, bool f8,
+                         uint32_t flags, void *stream)
 {
     if (!dtype_ok(dtype))
         return NORM_ERR_DTYPE;
@@ -317,8 +317,8 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
                           (const void *)residual_out})
         if (p && !aligned(p, es))
             return NORM_ERR_ALIGN;
-    for (const void *p :
-         {(const void *)mean, (const void *)rstd, (const void *)amax, (const void *)y_scale})
+    for (const void *p : {(const void *)mean, (const void *)rstd, (const void *)amax,
+                          (const void *)y_scale, (const void *)amax_ws})
         if (p && !aligned(p, 4))
             return NORM_ERR_ALIGN;
 
@@ -336,7 +336,10 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     unsigned *amax_bits = reinterpret_cast<unsigned *>(amax);
-    if (amax_bits)
+    // with a workspace the kernel combines and writes amax itself; without
+    // one (or with no rows to launch for) a one-thread kernel zeroes it first
+    unsigned *ws = amax_bits && M > 0 ? static_cast<unsigned *>(amax_ws) : nullptr;
+    if (amax_bits && !ws)
         if (norm_status_t st = launched(launch_zero_u32(amax_bits, s)))
             return st;
     if (M == 0)
@@ -354,6 +357,7 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     a.mean = mean;
     a.rstd = rstd;
     a.amax = amax_bits;
+    a.amax_ws = ws;
     a.M = M;
     a.n_groups = w.n_groups;
     a.N = int(N);
@@ -690,7 +694,8 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
     if (norm_status_t st = check_shape(M, N))
         return st;
     if (op < NORM_OP_LN_FWD || op > NORM_OP_SOFTMAX ||
-        (opts & ~uint32_t(NORM_DESCRIBE_AMAX | NORM_DESCRIBE_FP8 | NORM_DESCRIBE_DBIAS)))
+        (opts & ~uint32_t(NORM_DESCRIBE_AMAX | NORM_DESCRIBE_FP8 | NORM_DESCRIBE_DBIAS |
+                          NORM_DESCRIBE_AMAX_WS)))
         return NORM_ERR_ARG;
     const Knobs kn = knobs();
     const int vec = vec_of_aligned(N, dtype);
@@ -705,7 +710,9 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
         t.add(", %s%s>; grid %lld x %d threads, %d row group(s) of %d rows per workgroup",
               op == NORM_OP_RMS_FWD ? "RMSNorm" : "LayerNorm", f8 ? ", FP8 y" : "",
               (long long)w.grid, e->shape.threads(), w.K, e->shape.teams);
-        if (amax)
+        if (amax && (opts & NORM_DESCRIBE_AMAX_WS) && M > 0)
+            t.add("; amax: combined in the caller's workspace, written by the last workgroup");
+        else if (amax)
             t.add("; amax: one-thread reset kernel first");
         return NORM_OK;
     }
@@ -742,40 +749,40 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
 
 norm_status_t ln_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                      const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
-                     void *residual_out, float *mean, float *rstd, float *amax, uint32_t flags,
-                     void *stream)
+                     void *residual_out, float *mean, float *rstd, float *amax, void *amax_ws,
+                     uint32_t flags, void *stream)
 {
     return fwd_common(false, x, bias, residual, gamma, beta, eps, M, N, dtype, nullptr, y,
-                      residual_out, mean, rstd, amax, false, flags, stream);
+                      residual_out, mean, rstd, amax, amax_ws, false, flags, stream);
 }
 
 norm_status_t rms_fwd(const void *x, const void *bias, const void *residual, const void *gamma,
                       const void *beta, float eps, int64_t M, int64_t N, int32_t dtype, void *y,
-                      void *residual_out, float *mean, float *rstd, float *amax, uint32_t flags,
-                      void *stream)
+                      void *residual_out, float *mean, float *rstd, float *amax, void *amax_ws,
+                      uint32_t flags, void *stream)
 {
     return fwd_common(true, x, bias, residual, gamma, beta, eps, M, N, dtype, nullptr, y,
-                      residual_out, mean, rstd, amax, false, flags, stream);
+                      residual_out, mean, rstd, amax, amax_ws, false, flags, stream);
 }
 
 norm_status_t ln_fwd_fp8(const void *x, const void *bias, const void *residual,
                          const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                          int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
-                         float *mean, float *rstd, float *amax, uint32_t flags,
+                         float *mean, float *rstd, float *amax, void *amax_ws, uint32_t flags,
                          void *stream)
 {
     return fwd_common(false, x, bias, residual, gamma, beta, eps, M, N, dtype, y_scale, y_fp8,
-                      residual_out, mean, rstd, amax, true, flags, stream);
+                      residual_out, mean, rstd, amax, amax_ws, true, flags, stream);
 }
 
 norm_status_t rms_fwd_fp8(const void *x, const void *bias, const void *residual,
                           const void *gamma, const void *beta, float eps, int64_t M, int64_t N,
                           int32_t dtype, const float *y_scale, void *y_fp8, void *residual_out,
-                          float *mean, float *rstd, float *amax, uint32_t flags,
+                          float *mean, float *rstd, float *amax, void *amax_ws, uint32_t flags,
                           void *stream)
 {
     return fwd_common(true, x, bias, residual, gamma, beta, eps, M, N, dtype, y_scale, y_fp8,
-                      residual_out, mean, rstd, amax, true, flags, stream);
+                      residual_out, mean, rstd, amax, amax_ws, true, flags, stream);
 }
 
 norm_status_t softmax_fwd(const void *x, int64_t M, int64_t N, int32_t dtype, void *y,

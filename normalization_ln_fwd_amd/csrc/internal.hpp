@@ -17,6 +17,9 @@ struct FwdArgs {
     const float *y_scale;    // FP8 output: one fp32 scale in device memory
     float *mean, *rstd;
     unsigned *amax; // bit pattern of a non-negative float, combined with atomicMax
+    // optional: zero before the launch, left zero after it; the cells that
+    // combine the workgroups' maxima (amax_arrive)
+    unsigned *amax_ws;
     int64_t M;
     int64_t n_groups;
     int N;

@@ -265,6 +265,60 @@ constexpr bool fwd_prefetch()
 }
 
 // ---------------------------------------------------------------------------
+// The second stage of amax in one launch, through a caller workspace that is
+// zero when the launch starts.  A cell of two words -- [0] the maxima
+// combined so far (atomicMax on the bit pattern), [1] how many of its
+// members have added theirs -- counts the arrivals of a set of members.
+// Workgroup b is a member of subgroup cell b % AMAX_SUBGROUPS; the last
+// member to arrive at a subgroup cell takes its maximum (swapping in 0),
+// zeroes its count and arrives with it at the top cell, whose last arrival
+// writes amax.  (With one cell for all workgroups, their returning atomics
+// on one address serialise: 18000 workgroups took 150 us longer.)
+// Every atomic here is a device-scope read-modify-write whose result returns
+// from the memory-side point where all atomics on that address are
+// performed, so a returned value means the operation has been applied
+// there.  An arrival's count addend depends on the value its max returned,
+// so the count is issued only after the max has been applied; the arrival
+// that raises a cell's count to its number of members therefore finds every
+// member's maximum in the cell when it takes it.  Every cell is left zero
+// for the next call on the same stream.
+// ---------------------------------------------------------------------------
+constexpr unsigned AMAX_SUBGROUPS = 64;
+constexpr unsigned AMAX_CELL_WORDS = 16; // one 64-byte line per cell
+
+// Arrive at `cell` with `bits`; true for the last of `members` arrivals,
+// which receives the combined maximum in `all`.
+__device__ __forceinline__ bool amax_cell_arrive(unsigned *cell, unsigned bits, unsigned members,
+                                                 unsigned &all)
+{
+    const unsigned prev =
+        __hip_atomic_fetch_max(cell, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // prev is the bit pattern of a non-negative float: bit 31 is clear, so the
+    // addend is 1, but only known once prev has returned
+    const unsigned one = 1u + (prev >> 31);
+    const unsigned arrived =
+        __hip_atomic_fetch_add(cell + 1, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrived != members - 1)
+        return false;
+    all = __hip_atomic_exchange(cell, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(cell + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+__device__ __forceinline__ void amax_arrive(unsigned *amax, unsigned *ws, unsigned bits)
+{
+    const unsigned G = gridDim.x, b = blockIdx.x;
+    const unsigned sg = b % AMAX_SUBGROUPS;
+    const unsigned members = (G - 1 - sg) / AMAX_SUBGROUPS + 1; // b' < G with b' % 64 == sg
+    const unsigned cells = G < AMAX_SUBGROUPS ? G : AMAX_SUBGROUPS;
+    unsigned all = 0;
+    if (!amax_cell_arrive(ws + sg * AMAX_CELL_WORDS, bits, members, all))
+        return;
+    if (amax_cell_arrive(ws + AMAX_SUBGROUPS * AMAX_CELL_WORDS, all, cells, all))
+        *amax = all;
+}
+
+// ---------------------------------------------------------------------------
 // Forward: t = (x + bias) + residual (fp32), u = round(t) -> residual_out,
 // statistics of u, y = normalise(u) * gamma + beta -> y, running max |y|.
 // ---------------------------------------------------------------------------
@@ -542,7 +596,12 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
                 mm = fmaxf(mm, max_lds[w]);
             float r[1] = {mm};
             VecIO<T, 1>::unpack(VecIO<T, 1>::pack(r), r); // max of the stored y
-            atomicMax(a.amax, __float_as_uint(r[0]));
+            const unsigned bits = __float_as_uint(r[0]);
+            if (a.amax_ws == nullptr) {
+                atomicMax(a.amax, bits); // *amax was zeroed by a kernel before this one
+            } else {
+                amax_arrive(a.amax, a.amax_ws, bits);
+            }
         }
     }
 }
@@ -1198,19 +1257,18 @@ hipError_t launch_softmax(const SoftmaxArgs &a, int grid, hipStream_t s)
 // to colsum_ld(N) floats so that a thread reads 16-byte vectors of 4 columns.
 // Workgroup (column tile, slice s, block) adds rows [s*span, min(rows,
 // (s+1)*span)) of its 4*QUADS columns with QUADS x SUB threads: thread
-// (q, t) takes rows t, t + SUB, ... of the slice in ascending order.  The SUB
-// row subsets of a column are then added in a fixed tree: within a wave by
-// xor-shuffles over the subsets it holds (64 / QUADS of them), then the
-// waves' sums in wave order.  FINAL: one slice; divide by `divisor` (1, or M
-// for the mean over the rows), down-cast and store to dgamma / dbeta /
-// dbias.  Otherwise slice s stores its sums as row s of dst (blocks of
-// gridDim.y rows), which a FINAL launch then adds.  Every addition happens
-// in a fixed order.
-// (A one-launch variant that lets the last workgroup finish needs a
-// device-scope release per workgroup, i.e. an L2 write-back each, which
-// costs more than the second launch.)
+// (q, t) takes rows t, t + SUB, t + 2 SUB, ... of the slice in ascending
+// order, RPT of them per pass with all RPT loads in flight at once (one
+// memory round trip per pass; the launches size SUB * RPT to cover a slice
+// in one pass).  The SUB row subsets of a column are then added in a fixed
+// tree: within a wave by xor-shuffles over the subsets it holds (64 / QUADS
+// of them), then the waves' sums in wave order.  FINAL: one slice; divide
+// by `divisor` (1, or M for the mean over the rows), down-cast and store to
+// dgamma / dbeta / dbias.  Otherwise slice s stores its sums as row s of dst
+// (blocks of gridDim.y rows), which a FINAL launch then adds.  Every
+// addition happens in a fixed order.
 // ---------------------------------------------------------------------------
-template <bool FINAL, bool BF16_OUT, int QUADS, int SUB>
+template <bool FINAL, bool BF16_OUT, int QUADS, int SUB, int RPT>
 __global__ void __launch_bounds__(QUADS *SUB)
     colsum_kernel(const float *src, int rows, int N, int span, float *dst, void *dgamma,
                   void *dbeta, void *dbias, float divisor)
@@ -1228,17 +1286,27 @@ __global__ void __launch_bounds__(QUADS *SUB)
     const int j0 = blockIdx.x * (4 * QUADS) + tq * 4;
     const int s = blockIdx.y;
     const int r0 = s * span;
-    const int r1 = min(rows, r0 + span);
-    const float *part = src + (int64_t)which * rows * ld;
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (j0 < N) { // columns j0 .. j0+3 lie within the padded row of ld floats
-#pragma unroll 4
-        for (int r = r0 + ty; r < r1; r += SUB) {
-            const float4 v = *reinterpret_cast<const float4 *>(part + (int64_t)r * ld + j0);
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
+    const int nr = max(0, min(rows, r0 + span) - r0); // rows of this slice
+    // the slice's rows, and nothing else, in range of the descriptor: loads
+    // of rows past the slice (and of columns past N) return zeros
+    const float *part = src + ((int64_t)which * rows + r0) * ld;
+    const rsrc_t rs = make_rsrc(part, uint32_t(nr) * uint32_t(ld) * 4u);
+    const bool cv = j0 < N; // columns j0 .. j0+3 lie within the padded row
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < nr; rb += SUB * RPT) { // uniform
+        f32x4_t v[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const uint32_t r = uint32_t(rb + ty + i * SUB);
+            const uint32_t off = cv ? (r * uint32_t(ld) + uint32_t(j0)) * 4u : BUF_OOB;
+            v[i] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, int(off), 0, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            acc.x += v[i].x;
+            acc.y += v[i].y;
+            acc.z += v[i].z;
+            acc.w += v[i].w;
         }
     }
 #pragma unroll
@@ -1248,15 +1316,15 @@ __global__ void __launch_bounds__(QUADS *SUB)
         acc.z += __shfl_xor(acc.z, m);
         acc.w += __shfl_xor(acc.w, m);
     }
-    __shared__ float4 sl[NWAVE][QUADS];
+    __shared__ f32x4_t sl[NWAVE][QUADS];
     if ((threadIdx.x & 63) < QUADS)
         sl[wave][tq] = acc;
     __syncthreads();
-    if (threadIdx.x < QUADS && j0 < N) {
-        float4 t = sl[0][tq];
+    if (threadIdx.x < QUADS && cv) {
+        f32x4_t t = sl[0][tq];
 #pragma unroll
         for (int w = 1; w < NWAVE; ++w) {
-            const float4 u = sl[w][tq];
+            const f32x4_t u = sl[w][tq];
             t.x += u.x;
             t.y += u.y;
             t.z += u.z;

@@ -54,8 +54,10 @@ def test_binding_constants_match_header():
     for op, code in nf.OPS.items():
         assert d["NORM_OP_" + op.replace("_fwd", "_FWD").replace("_bwd", "_BWD")
                  .replace("softmax_FWD", "SOFTMAX").upper()] == code
-    assert (d["NORM_DESCRIBE_AMAX"], d["NORM_DESCRIBE_FP8"], d["NORM_DESCRIBE_DBIAS"]) == \
-        (nf.DESCRIBE_AMAX, nf.DESCRIBE_FP8, nf.DESCRIBE_DBIAS)
+    assert (d["NORM_DESCRIBE_AMAX"], d["NORM_DESCRIBE_FP8"], d["NORM_DESCRIBE_DBIAS"],
+            d["NORM_DESCRIBE_AMAX_WS"]) == \
+        (nf.DESCRIBE_AMAX, nf.DESCRIBE_FP8, nf.DESCRIBE_DBIAS, nf.DESCRIBE_AMAX_WS)
+    assert d["NORM_AMAX_WS_BYTES"] == nf.AMAX_WS_BYTES
     assert d["NORM_F32"] == nf.F32 and d["NORM_BF16"] == nf.BF16
     assert d["NORM_N_MAX"] == nf.N_MAX
     for code, name in nf.STATUS.items():
@@ -71,10 +73,12 @@ def test_status_strings(lib):
 
 def fwd_args(**over):
     a = dict(x=P, bias=None, residual=None, gamma=P, beta=P, eps=1e-5, M=4, N=64, dtype=1,
-             y=P, residual_out=None, mean=P, rstd=P, amax=None, flags=0, stream=None)
+             y=P, residual_out=None, mean=P, rstd=P, amax=None, amax_ws=None, flags=0,
+             stream=None)
     a.update(over)
     return [a[k] for k in ("x", "bias", "residual", "gamma", "beta", "eps", "M", "N", "dtype",
-                           "y", "residual_out", "mean", "rstd", "amax", "flags", "stream")]
+                           "y", "residual_out", "mean", "rstd", "amax", "amax_ws", "flags",
+                           "stream")]
 
 
 @pytest.mark.parametrize("fn", ["ln_fwd", "rms_fwd"])
@@ -86,7 +90,7 @@ def fwd_args(**over):
     (dict(eps=-1e-3), 3), (dict(eps=math.nan), 3), (dict(eps=math.inf), 3),
     (dict(x=BAD1), 5), (dict(gamma=BAD1), 5), (dict(y=BAD1), 5),
     (dict(dtype=0, x=BAD2), 5), (dict(dtype=0, residual=BAD2), 5),
-    (dict(rstd=BAD2), 5), (dict(amax=BAD2), 5),
+    (dict(rstd=BAD2), 5), (dict(amax=BAD2), 5), (dict(amax=P, amax_ws=BAD2), 5),
 ])
 def test_forward_rejects(lib, fn, over, code):
     if fn == "rms_fwd":
@@ -106,17 +110,20 @@ def test_no_rows_allows_null_row_tensors(lib):
 
 def fwd8_args(**over):
     a = dict(x=P, bias=None, res=None, gamma=None, beta=None, eps=1e-5, M=4, N=64, dtype=1,
-             scale=P, y=P, res_out=None, mean=None, rstd=None, amax=None, flags=0, stream=None)
+             scale=P, y=P, res_out=None, mean=None, rstd=None, amax=None, amax_ws=None, flags=0,
+             stream=None)
     a.update(over)
     return [a[k] for k in ("x", "bias", "res", "gamma", "beta", "eps", "M", "N", "dtype",
-                           "scale", "y", "res_out", "mean", "rstd", "amax", "flags", "stream")]
+                           "scale", "y", "res_out", "mean", "rstd", "amax", "amax_ws", "flags",
+                           "stream")]
 
 
 @pytest.mark.parametrize("fn", ["ln_fwd_fp8", "rms_fwd_fp8"])
 @pytest.mark.parametrize("over,code", [
     (dict(dtype=2), 4), (dict(scale=None), 1), (dict(y=None), 1), (dict(x=None), 1),
     (dict(N=0), 2), (dict(eps=-1.0), 3), (dict(scale=BAD2), 5), (dict(x=BAD1), 5),
-    (dict(amax=BAD2), 5), (dict(flags=2), 3), (dict(flags=8), 3),
+    (dict(amax=BAD2), 5), (dict(amax=P, amax_ws=BAD2), 5), (dict(flags=2), 3),
+    (dict(flags=8), 3),
 ])
 def test_fp8_forward_rejects(lib, fn, over, code):
     assert getattr(lib, fn)(*fwd8_args(**over)) == code
@@ -266,6 +273,9 @@ def test_describe_names_the_planned_kernels(lib):
     d = nf.describe("ln_fwd", 576000, 384, nf.BF16, amax=True)
     assert d.startswith("fwd_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 32, LayerNorm>"), d
     assert "grid 18000 x 512 threads" in d, d
+    assert "reset kernel" in d, d
+    d = nf.describe("ln_fwd", 576000, 384, nf.BF16, amax=True, amax_ws=True)
+    assert "written by the last workgroup" in d, d
     d = nf.describe("rms_fwd", 576000, 384, nf.BF16, amax=True)
     assert "TEAMS 32, RMSNorm>" in d, d
     d = nf.describe("ln_bwd", 576000, 384, nf.BF16)
@@ -287,7 +297,7 @@ def test_describe_rejects(lib):
     assert lib.norm_describe(0, 4, 64, 7, 0, buf, 64) == 4
     assert lib.norm_describe(0, 4, 0, 1, 0, buf, 64) == 2
     assert lib.norm_describe(9, 4, 64, 1, 0, buf, 64) == 3
-    assert lib.norm_describe(0, 4, 64, 1, 8, buf, 64) == 3
+    assert lib.norm_describe(0, 4, 64, 1, 16, buf, 64) == 3
     # a short buffer holds a truncated, terminated text
     small = ctypes.create_string_buffer(8)
     assert lib.norm_describe(0, 4, 64, 1, 0, small, 8) == 0

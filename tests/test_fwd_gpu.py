@@ -158,6 +158,69 @@ def test_fwd_amax_overwrites_previous_value():
     assert out["amax"].item() == float(np.max(np.abs(f64(out["y"]))))
 
 
+# One-launch amax through a caller workspace: sizes from one workgroup to
+# many thousands (the 512-thread workgroups at 100003 rows, 3125 of them),
+# both dtypes and the element-wise kernels, LayerNorm and RMSNorm.
+AMAX_WS_CASES = [(1, 64, BF16, False), (37, 384, BF16, False), (300, 4096, BF16, False),
+                 (100003, 384, BF16, False), (20001, 1024, F32, False), (5, 5000, BF16, True),
+                 (3, 16384, F32, False), (130, 64, F32, True)]
+
+
+@pytest.mark.parametrize("M,N,dtype,misalign", AMAX_WS_CASES)
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+def test_fwd_amax_workspace_matches_reset_path(M, N, dtype, misalign, rms):
+    """amax from the workspace path equals the reset-kernel path's and the
+    brute-force max |y| bit for bit; every other output is identical; the
+    workspace is zero again after each call, so a second call (fewer rows)
+    reuses it."""
+    inp = synth.make_inputs(M, N, dtype=dtype, seed=M * 3 + N)
+    dev = {k: to_dev(inp[k], dtype, misalign and k == "x")
+           for k in ("x", "bias", "residual", "gamma", "beta")}
+    fn = nf.rms_fwd if rms else nf.ln_fwd
+    ws = nf.amax_workspace()
+    plain = fn(dev["x"], dev["bias"], dev["residual"], dev["gamma"], dev["beta"], 1e-5,
+               want_amax=True)
+    for rows in (M, max(1, M // 3)):
+        sub = {k: (v[:rows] if v is not None and v.dim() == 2 else v) for k, v in dev.items()}
+        amax = torch.full((1,), -5.0, device="cuda")  # overwritten, not combined with
+        out = fn(sub["x"], sub["bias"], sub["residual"], sub["gamma"], sub["beta"], 1e-5,
+                 want_amax=True, amax_workspace=ws, out={"amax": amax})
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws).item() == 0, "workspace not left zero-filled"
+        brute = float(out["y"].float().abs().max().item())
+        assert float(out["amax"].item()) == brute, (rows, out["amax"].item(), brute)
+        if rows == M:
+            assert float(out["amax"].item()) == float(plain["amax"].item())
+            for k in ("y", "residual_out", "rstd") + (() if rms else ("mean",)):
+                assert torch.equal(out[k], plain[k]), k
+
+
+def test_fwd_amax_workspace_with_no_rows():
+    ws = nf.amax_workspace()
+    amax = torch.full((1,), 9.0, device="cuda")
+    x = torch.empty((0, 384), dtype=torch.bfloat16, device="cuda")
+    nf.ln_fwd(x, want_amax=True, amax_workspace=ws, out={"amax": amax})
+    torch.cuda.synchronize()
+    assert amax.item() == 0.0 and torch.count_nonzero(ws).item() == 0
+
+
+def test_fwd_amax_workspace_fp8():
+    M, N = 4096, 384
+    inp = synth.make_inputs(M, N, dtype=BF16, seed=4)
+    dev = {k: to_dev(inp[k], BF16) for k in ("x", "bias", "residual", "gamma", "beta")}
+    sc = torch.full((1,), 2.0, device="cuda")
+    ws = nf.amax_workspace()
+    a = nf.ln_fwd_fp8(dev["x"], sc, dev["bias"], dev["residual"], dev["gamma"], dev["beta"],
+                      want_amax=True)
+    b = nf.ln_fwd_fp8(dev["x"], sc, dev["bias"], dev["residual"], dev["gamma"], dev["beta"],
+                      want_amax=True, amax_workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws).item() == 0
+    for k in ("amax", "residual_out", "mean", "rstd"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["y"].view(torch.uint8), b["y"].view(torch.uint8))
+
+
 def test_fwd_is_deterministic():
     M, N = 5000, 384
     inp = synth.make_inputs(M, N, dtype=BF16, seed=9)

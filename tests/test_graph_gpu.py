@@ -1,8 +1,9 @@
-"""The path under HIP graph capture: a forward + backward step (amax reset,
-forward, backward stage 1, column sums) captured once with torch.cuda.graph
-on a side stream and replayed several times, with eager work and
-synchronisations between the replays; every replay must equal the eager
-result bit for bit."""
+"""The path under HIP graph capture: a forward + backward step (amax reset
+kernel or the amax workspace, forward, backward stage 1, column sums)
+captured once with torch.cuda.graph on a side stream and replayed several
+times, with eager work and synchronisations between the replays; every
+replay must equal the eager result bit for bit, and the amax workspace must
+be zero-filled after each."""
 import numpy as np
 import pytest
 import torch
@@ -19,8 +20,10 @@ def _gpu():
     require_gpu()
 
 
-@pytest.mark.parametrize("M,N", [(20000, 384), (512, 4096)])
-def test_captured_step_replays_match_eager(M, N):
+@pytest.mark.parametrize("M,N,amax_ws", [(20000, 384, False), (512, 4096, False),
+                                         (20000, 384, True), (512, 4096, True)],
+                         ids=["20000x384", "512x4096", "20000x384-amax-ws", "512x4096-amax-ws"])
+def test_captured_step_replays_match_eager(M, N, amax_ws):
     inp = synth.make_inputs(M, N, dtype=BF16, seed=31,
                             names=("x", "residual", "bias", "gamma", "beta", "dy"))
     d = {k: to_dev(v, BF16) for k, v in inp.items()}
@@ -34,9 +37,11 @@ def test_captured_step_replays_match_eager(M, N):
           "dbeta": torch.empty(N, dtype=torch.bfloat16, device="cuda"),
           "dbias": torch.empty(N, dtype=torch.bfloat16, device="cuda")}
 
+    aws = nf.amax_workspace() if amax_ws else None
+
     def step():
         nf.ln_fwd(d["x"], d["bias"], d["residual"], d["gamma"], d["beta"], 1e-5, want_amax=True,
-                  out=fo)
+                  amax_workspace=aws, out=fo)
         nf.ln_bwd(d["dy"], fo["residual_out"], d["gamma"], fo["mean"], fo["rstd"],
                   dparam_dtype=torch.bfloat16, want_dbias=True, workspace=ws, out=bo)
 
@@ -61,3 +66,5 @@ def test_captured_step_replays_match_eager(M, N):
         torch.cuda.synchronize()
         for k, v in {**fo, **bo}.items():
             assert torch.equal(v, eager[k]), (rep, k)
+        if aws is not None:
+            assert torch.count_nonzero(aws).item() == 0, rep
