@@ -266,6 +266,30 @@ norm_status_t rms_bwd(const void *dy, const void *x, const void *gamma, const fl
                       void *dbeta, void *dbias, int32_t dparam_dtype, void *workspace,
                       size_t workspace_bytes, uint32_t flags, void *stream);
 
+/*
+ * ln_bwd_noalloc -- ln_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with the column partials in
+ * the library's own static device scratch instead of a caller workspace.
+ * Arguments as ln_bwd without workspace / workspace_bytes.
+ *   - The scratch is NORM_STATIC_SCRATCH_BYTES per device, part of the
+ *     library's code object; each device that runs the call holds it until
+ *     the process ends.  A problem whose workspace (norm_bwd_workspace_size)
+ *     exceeds it returns NORM_ERR_WORKSPACE and enqueues nothing.
+ *   - The call allocates nothing; on its first call on a device it looks up
+ *     that device's scratch address (hipGetSymbolAddress; NORM_ERR_DEVICE if
+ *     that fails).
+ *   - Every call on a device shares that device's scratch: calls that may
+ *     run at the same time on one device (different streams, or different
+ *     threads' streams) race and give wrong results; order them on one
+ *     stream.  The scratch needs no initialisation.
+ */
+#define NORM_STATIC_SCRATCH_BYTES (32u << 20)
+norm_status_t ln_bwd_noalloc(const void *dy, const void *x, const void *gamma, const float *mean,
+                             const float *rstd, int64_t M, int64_t N, int32_t dtype, void *dx,
+                             void *dgamma, void *dbeta, void *dbias, int32_t dparam_dtype,
+                             uint32_t flags, void *stream);
+
 /* Static text for a status code. */
 const char *norm_status_string(norm_status_t status);
 

@@ -26,9 +26,9 @@ from .build import LIB as _LIB_PATH
 from .build import TUNING_LIB as _TUNING_LIB_PATH
 
 __all__ = ["ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd", "softmax_fwd",
-           "bwd_workspace_size", "describe", "amax_workspace", "NormError", "NormLibraryMissing", "library", "load", "TUNING_LIB",
-           "F32", "BF16",
-           "N_MAX", "ZERO_CENTERED_GAMMA", "DPARAM_MEAN"]
+           "ln_bwd_noalloc", "bwd_workspace_size", "describe", "amax_workspace", "NormError",
+           "NormLibraryMissing", "library", "load", "TUNING_LIB", "F32", "BF16", "N_MAX",
+           "ZERO_CENTERED_GAMMA", "DPARAM_MEAN", "STATIC_SCRATCH_BYTES", "AMAX_WS_BYTES"]
 
 F32 = 0
 BF16 = 1
@@ -40,7 +40,9 @@ ZERO_CENTERED_GAMMA = 1  # option bits of include/normfuse.h
 DPARAM_MEAN = 2
 
 EXPORTS = ("ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd",
-           "softmax_fwd", "norm_bwd_workspace_size", "norm_status_string", "norm_describe")
+           "softmax_fwd", "norm_bwd_workspace_size", "norm_status_string", "norm_describe",
+           "ln_bwd_noalloc")
+STATIC_SCRATCH_BYTES = 32 << 20  # NORM_STATIC_SCRATCH_BYTES
 # operation codes and option bits of norm_describe
 OPS = {"ln_fwd": 0, "rms_fwd": 1, "ln_bwd": 2, "rms_bwd": 3, "softmax_fwd": 4}
 DESCRIBE_AMAX, DESCRIBE_FP8, DESCRIBE_DBIAS, DESCRIBE_AMAX_WS = 1, 2, 4, 8
@@ -96,8 +98,10 @@ def load(path):
     lib.norm_status_string.argtypes = [i32]
     lib.norm_status_string.restype = ctypes.c_char_p
     lib.norm_describe.argtypes = [i32, i64, i64, i32, u32, ctypes.c_char_p, sz]
+    lib.ln_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, i32, u32,
+                                   vp]
     for name in ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "norm_bwd_workspace_size",
-                 "norm_describe"):
+                 "norm_describe", "ln_bwd_noalloc"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -317,20 +321,22 @@ def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbet
     dbias = out.get("dbias")
     if dbias is None and want_dbias:
         dbias = torch.empty(N, dtype=pdt, device=x.device)
-    need = bwd_workspace_size(M, N, dt)
-    if workspace is None:
+    noalloc = fn == "ln_bwd_noalloc"
+    if workspace is None and not noalloc:
+        need = bwd_workspace_size(M, N, dt)
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
     pcode = F32 if pdt == torch.float32 else BF16
     args = [_ptr(dy, "dy", dt, M * N), _ptr(x, "x"), _ptr(gamma, "gamma", dt, N)]
-    if fn == "ln_bwd":
+    if fn != "rms_bwd":
         args += [_ptr(mean, "mean", torch.float32, M), _ptr(rstd, "rstd", torch.float32, M)]
     else:
         args += [_ptr(rstd, "rstd", torch.float32, M), float(eps)]
     args += [M, N, _dtype_code(x), _ptr(dx, "dx", dt, M * N),
              _ptr(dgamma, "dgamma", pdt, N), _ptr(dbeta, "dbeta", pdt, N),
-             _ptr(dbias, "dbias", pdt, N), pcode,
-             _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-             flags, _stream(stream)]
+             _ptr(dbias, "dbias", pdt, N), pcode]
+    if not noalloc:
+        args += [_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()]
+    args += [flags, _stream(stream)]
     _check(fn, getattr(lib, fn)(*args))
     return {"dx": dx, "dgamma": dgamma, "dbeta": dbeta, "dbias": dbias}
 
@@ -351,6 +357,18 @@ def ln_bwd(dy, x, gamma, mean, rstd, *, dparam_dtype=None, want_dgamma=True, wan
     ``dparam_mean``: the column results are means over the rows."""
     return _bwd("ln_bwd", dy, x, gamma, mean, rstd, 0.0, dparam_dtype, want_dgamma, want_dbeta,
                 want_dbias, workspace, stream, out, _bwd_flags(zero_centered_gamma, dparam_mean))
+
+
+def ln_bwd_noalloc(dy, x, gamma, mean, rstd, *, dparam_dtype=None, want_dgamma=True,
+                   want_dbeta=True, want_dbias=False, zero_centered_gamma=False,
+                   dparam_mean=False, stream=None, out=None):
+    """:func:`ln_bwd` on the library's static device scratch instead of a
+    workspace (for callers that cannot allocate; pass every output in
+    ``out`` to allocate nothing here either).  Calls that overlap on one GPU
+    race; problems needing more than STATIC_SCRATCH_BYTES are refused."""
+    return _bwd("ln_bwd_noalloc", dy, x, gamma, mean, rstd, 0.0, dparam_dtype, want_dgamma,
+                want_dbeta, want_dbias, None, stream, out,
+                _bwd_flags(zero_centered_gamma, dparam_mean))
 
 
 def rms_bwd(dy, x, gamma, rstd=None, eps=1e-6, *, dparam_dtype=None, want_dgamma=True,

@@ -4,14 +4,25 @@
 #include "normfuse.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <mutex>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
 #include "internal.hpp"
+
+// ------------------------------------------- the library's static scratch
+// The workspace of ln_bwd_noalloc, for callers that cannot allocate: one
+// array per device in the code object's device memory, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (in
+// host code the name is a stand-in, not a device address): each device's
+// address is taken once, with that device current, by hipGetSymbolAddress
+// (static_scratch below), and kept.
+static __device__ __align__(256) unsigned char scratch[NORM_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -551,11 +562,37 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, int nb, con
     return NORM_OK;
 }
 
+constexpr int kMaxDevices = 64;
+
+// The address of the current device's scratch.
+norm_status_t static_scratch(void **ptr)
+{
+    static std::atomic<void *> addr[kMaxDevices];
+    static std::mutex mu;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return NORM_ERR_DEVICE;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return NORM_ERR_DEVICE;
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return NORM_OK;
+}
+
+// use_static: the workspace is the current device's static scratch (the
+// workspace arguments are ignored)
 norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *gamma,
                          const float *mean, const float *rstd, float eps, int64_t M, int64_t N,
                          int32_t dtype, void *dx, void *dgamma, void *dbeta, void *dbias,
                          int32_t dparam_dtype, void *workspace, size_t workspace_bytes,
-                         uint32_t flags, void *stream)
+                         uint32_t flags, void *stream, bool use_static = false)
 {
     if (!dtype_ok(dtype) || !dtype_ok(dparam_dtype))
         return NORM_ERR_DTYPE;
@@ -592,8 +629,16 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
     if (norm_status_t st = bwd_plan(M, N, dtype, vec, nb, kn, &e, &w, &lay))
         return st;
     const size_t need = lay.bytes;
-    if (need > 0 && (!workspace || workspace_bytes < need))
+    if (use_static) {
+        if (need > size_t(NORM_STATIC_SCRATCH_BYTES))
+            return NORM_ERR_WORKSPACE;
+        workspace = nullptr;
+        if (need > 0)
+            if (norm_status_t st = static_scratch(&workspace))
+                return st;
+    } else if (need > 0 && (!workspace || workspace_bytes < need)) {
         return NORM_ERR_WORKSPACE;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     float *ws = static_cast<float *>(workspace);
 
@@ -836,6 +881,15 @@ norm_status_t rms_bwd(const void *dy, const void *x, const void *gamma, const fl
 {
     return bwd_common(true, dy, x, gamma, nullptr, rstd, eps, M, N, dtype, dx, dgamma, dbeta,
                       dbias, dparam_dtype, workspace, workspace_bytes, flags, stream);
+}
+
+norm_status_t ln_bwd_noalloc(const void *dy, const void *x, const void *gamma, const float *mean,
+                             const float *rstd, int64_t M, int64_t N, int32_t dtype, void *dx,
+                             void *dgamma, void *dbeta, void *dbias, int32_t dparam_dtype,
+                             uint32_t flags, void *stream)
+{
+    return bwd_common(false, dy, x, gamma, mean, rstd, 0.f, M, N, dtype, dx, dgamma, dbeta,
+                      dbias, dparam_dtype, nullptr, 0, flags, stream, true);
 }
 
 const char *norm_status_string(norm_status_t st)

@@ -170,10 +170,21 @@ def bwd_args(fn, **over):
              dgamma=P, dbeta=P, dbias=None, pdtype=0, ws=P, ws_bytes=1 << 20, flags=0,
              stream=None)
     a.update(over)
-    keys = ["dy", "x", "gamma"] + (["mean", "rstd"] if fn == "ln_bwd" else ["rstd", "eps"]) + [
-        "M", "N", "dtype", "dx", "dgamma", "dbeta", "dbias", "pdtype", "ws", "ws_bytes",
-        "flags", "stream"]
+    keys = ["dy", "x", "gamma"] + (["rstd", "eps"] if fn == "rms_bwd" else ["mean", "rstd"]) + [
+        "M", "N", "dtype", "dx", "dgamma", "dbeta", "dbias", "pdtype"] + \
+        ([] if fn == "ln_bwd_noalloc" else ["ws", "ws_bytes"]) + ["flags", "stream"]
     return [a[k] for k in keys]
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=3), 4), (dict(pdtype=7), 4), (dict(dy=None), 1), (dict(mean=None), 1),
+    (dict(M=-1), 2), (dict(N=16385), 2), (dict(flags=4), 3), (dict(dx=BAD1), 5),
+    (dict(rstd=BAD2), 5),
+])
+def test_noalloc_backward_rejects(lib, over, code):
+    """ln_bwd_noalloc checks its arguments as ln_bwd does, before touching a
+    device (it takes no workspace)."""
+    assert lib.ln_bwd_noalloc(*bwd_args("ln_bwd_noalloc", **over)) == code
 
 
 @pytest.mark.parametrize("fn", ["ln_bwd", "rms_bwd"])
