@@ -36,7 +36,12 @@ def header_defines():
 
 @pytest.fixture(scope="module")
 def lib():
+    # NORMFUSE_TEST_LIB: run these checks on another build of the library
+    # (the sanitizer test's host-instrumented build)
+    path = os.environ.get("NORMFUSE_TEST_LIB")
     try:
+        if path:
+            nf._lib = nf.load(path)
         return nf.library()
     except nf.NormLibraryMissing as e:
         pytest.fail(str(e))
