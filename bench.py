@@ -36,7 +36,7 @@ CALIB_BYTES = 512 << 20
 # every source that decides what the measured kernels do (the kernels, the
 # host code that picks their shapes, grids and cache policies, the header)
 KERNEL_SOURCE_DIRS = ("normalization_ln_fwd_amd/csrc", "include")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_ln_bf16_576000x384_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_576000x384_8192x4096.md")
 
 
 def log(*a):
