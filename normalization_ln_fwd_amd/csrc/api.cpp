@@ -49,7 +49,10 @@ norm_status_t check_device()
 // NORMFUSE_{FWD,BWD}_GROUPS_PER_WG  : row groups per workgroup (K)
 // NORMFUSE_{FWD,BWD}_INTERLEAVE     : workgroups per interleave block (A)
 // NORMFUSE_WT_BYTES                 : output bytes, counted from the end,
-//                                     stored write-through (see wt_group)
+//                                     stored write-through (see wt_group);
+//                                     NORMFUSE_{FWD,BWD}_WT_BYTES for one
+//                                     direction (the forward's also applies
+//                                     to softmax)
 // NORMFUSE_BWD_SPLIT                : 0 never splits backward rows along N,
 //                                     1 splits them wherever the kernel can
 //                                     (see bwd_plan)
@@ -82,7 +85,7 @@ struct Knobs {
     int fwd_lpr = 0, fwd_vpl = 0, bwd_lpr = 0, bwd_vpl = 0, fwd_teams = 0, bwd_teams = 0;
     int fwd_k = kFwdGroupsPerWg, bwd_k = kBwdGroupsPerWg;
     int fwd_a = kFwdInterleave, bwd_a = kBwdInterleave;
-    double wt_bytes = kWtBytes;
+    double fwd_wt_bytes = kWtBytes, bwd_wt_bytes = kWtBytes;
     int bwd_split = -1; // -1: chosen per shape
 };
 
@@ -123,11 +126,17 @@ Knobs knobs()
     parse_positive(std::getenv("NORMFUSE_BWD_INTERLEAVE"), &r.bwd_a);
     if (const char *v = std::getenv("NORMFUSE_BWD_SPLIT"))
         r.bwd_split = std::atoi(v) != 0 ? 1 : 0;
-    if (const char *v = std::getenv("NORMFUSE_WT_BYTES")) {
-        const double b = std::atof(v);
-        if (b >= 0.0)
-            r.wt_bytes = b;
-    }
+    auto bytes = [](const char *name, double *out) {
+        if (const char *v = std::getenv(name)) {
+            const double b = std::atof(v);
+            if (b >= 0.0)
+                *out = b;
+        }
+    };
+    bytes("NORMFUSE_WT_BYTES", &r.fwd_wt_bytes);
+    bytes("NORMFUSE_WT_BYTES", &r.bwd_wt_bytes);
+    bytes("NORMFUSE_FWD_WT_BYTES", &r.fwd_wt_bytes);
+    bytes("NORMFUSE_BWD_WT_BYTES", &r.bwd_wt_bytes);
 
     return r;
 }
@@ -233,7 +242,7 @@ norm_status_t plan_walk(int64_t M, int teams, int K, int A, Walk *w)
 }
 
 // First row group of a walk whose stores are write-through: the groups
-// from it on write the last kn.wt_bytes (or more) of the call's output, given
+// from it on write the last the write-through byte count (or more) of the call's output, given
 // `out_bytes` bytes written per element of a row.  Row groups are visited in
 // about ascending order (the walk's blocks of workgroups are dispatched in
 // order and step through their groups together), so these are the last
@@ -375,7 +384,7 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     a.K = w.K;
     a.A = w.A;
     a.wt_group = wt_group(w, e->shape.teams, N,
-                          double(y ? (f8 ? 1 : es) : 0) + double(residual_out ? es : 0), kn.wt_bytes);
+                          double(y ? (f8 ? 1 : es) : 0) + double(residual_out ? es : 0), kn.fwd_wt_bytes);
     a.eps = eps;
     a.zero_centred = (flags & NORM_ZERO_CENTERED_GAMMA) != 0;
     const FwdLaunch run = f8 ? (rms ? e->rms_f8 : e->ln_f8) : (rms ? e->rms : e->ln);
@@ -441,7 +450,7 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
     a.N = int(N);
     a.K = w.K;
     a.A = w.A;
-    a.wt_group = wt_group(w, e->shape.teams, N, double(es), kn.wt_bytes);
+    a.wt_group = wt_group(w, e->shape.teams, N, double(es), kn.fwd_wt_bytes);
     return launched(e->run(a, int(w.grid), static_cast<hipStream_t>(stream)));
 }
 
@@ -656,14 +665,14 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         a.N = int(N);
         a.K = w.K;
         a.A = w.A;
-        a.wt_group = wt_group(w, e->shape.teams, N, double(es), kn.wt_bytes);
+        a.wt_group = wt_group(w, e->shape.teams, N, double(es), kn.bwd_wt_bytes);
         a.eps = eps;
         a.zero_centred = (flags & NORM_ZERO_CENTERED_GAMMA) != 0;
         a.rowsums = nullptr;
         a.chunks = 0;
         if (lay.split) {
             // rows, not row groups, from which dx is stored write-through
-            const double rows_wt = std::ceil(kn.wt_bytes / (double(N) * double(es)));
+            const double rows_wt = std::ceil(kn.bwd_wt_bytes / (double(N) * double(es)));
             a.wt_group = rows_wt >= double(M) ? 0 : M - int64_t(rows_wt);
             a.K = lay.split_k;
             a.rowsums = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.rowsums_off);
