@@ -74,7 +74,8 @@
  *              (results stay within the same tolerances, but column sums
  *              may round differently), NORMFUSE_WT_BYTES (output bytes,
  *              counted from the end of a call, stored write-through: a cache
- *              policy, values do not change) and NORMFUSE_BWD_SPLIT=0 / 1
+ *              policy, values do not change; NORMFUSE_FWD_WT_BYTES /
+ *              _BWD_WT_BYTES for one direction) and NORMFUSE_BWD_SPLIT=0 / 1
  *              (turns off / forces the backward's split of rows along N).
  *   Alignment: pointers must be aligned to their element size.  Each call
  *              takes the widest vector access of 16, 8 or 4 bytes (fp32: 16

@@ -376,8 +376,9 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     };
     const GroupWalk walk(a.K, a.A);
 
-    // Parameters: their loads first, then the first row group's, so that the
-    // wait for the parameters does not include the rows.
+    // Parameters: their loads first, then the first row group's (every
+    // kernel: the rows' latency then overlaps the parameters' staging), so
+    // that the wait for the parameters does not include the rows.
     constexpr int PR = PLDS ? 1 : VPL;
     Raw pbias[PR], pgam[PR], pbeta[PR];
     if constexpr (PLDS) {
@@ -385,8 +386,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         sb.fetch(a.bias, N, tid);
         sg.fetch(a.gamma, N, tid);
         se.fetch(a.beta, N, tid);
-        if (PREFETCH)
-            issue(walk.group(0));
+        issue(walk.group(0));
         sb.put(par, a.bias, N, 0.f, tid);
         sg.put(par + CAP, a.gamma, N, 1.f, tid, a.zero_centred);
         se.put(par + 2 * CAP, a.beta, N, 0.f, tid);
@@ -399,8 +399,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         load_param_regs<T, VEC, VPL>(pbias, a.bias, N, poff, false);
         load_param_regs<T, VEC, VPL>(pgam, a.gamma, N, poff, true, a.zero_centred);
         load_param_regs<T, VEC, VPL>(pbeta, a.beta, N, poff, false);
-        if (PREFETCH)
-            issue(walk.group(0));
+        issue(walk.group(0));
     }
 
     float lane_max = 0.f;
@@ -416,8 +415,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         const uint32_t bytes = rgp.bytes;
         const int64_t gbyte = rgp.byte0;
         const bool wt = grp >= a.wt_group; // store policy (see BUF_WT)
-        if (!PREFETCH)
-            issue(grp);
+        if (!PREFETCH && kk > 0)
+            issue(grp); // group 0 was issued before the parameters were staged
         if constexpr (!PLDS) {
             // keep the parameters packed: unpacking them once for the whole
             // walk would cost more registers than the unpacking per group
@@ -733,14 +732,13 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     // group into slot B meanwhile (the two alternate).
     Slot A, B;
 
-    // gamma's loads first, then the first row groups' (see the forward)
+    // gamma's loads first, then the first row group's (see the forward)
     constexpr int PR = PLDS ? 1 : VPL;
     Raw pgam[PR];
     if constexpr (PLDS) {
         ParamStage<T, VEC, CAP, WG> sg;
         sg.fetch(a.gamma, N, tid);
-        if (PIPE)
-            issue(walk.group(0), A);
+        issue(walk.group(0), A);
         sg.put(par, a.gamma, N, 1.f, tid, a.zero_centred);
         __syncthreads();
     } else {
@@ -749,8 +747,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
         for (int k = 0; k < VPL; ++k)
             poff[k] = cvalid[k] ? uint32_t((k * LPR + tl) * VEC) * uint32_t(sizeof(T)) : BUF_OOB;
         load_param_regs<T, VEC, VPL>(pgam, a.gamma, N, poff, true, a.zero_centred);
-        if (PIPE)
-            issue(walk.group(0), A);
+        issue(walk.group(0), A);
     }
 
     float acc_g[E], acc_b[E], acc_d[DB ? E : 1];
@@ -899,7 +896,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
             const int64_t grp = walk.group(kk);
             if (grp >= a.n_groups)
                 break; // uniform over the workgroup; later groups are larger
-            issue(grp, A);
+            if (kk > 0)
+                issue(grp, A); // group 0 was issued before gamma was staged
             work(grp, A, false);
         }
     }
