@@ -133,6 +133,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--no-alt-sets", action="store_true",
+                    help="skip the step timed on two alternating buffer sets")
     ap.add_argument("--cases", default="",
                     help="comma-separated breakdown cases to run (name prefixes; default all)")
     args = ap.parse_args()
@@ -214,6 +216,36 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
     log(f"timed {K} steps: {ms_step:.4f} ms/step (wall {wall / K * 1e3:.4f} ms/step), "
         f"{value:.1f} GB/s")
+    # The same steps alternating between this buffer set and a second one
+    # (same shapes, seed 1), reported beside the value: a step on one set
+    # measures slightly faster than steps that alternate sets, although
+    # either moves far more than the last-level cache between two uses of a
+    # buffer.
+    alt_ms = None
+    if not args.no_alt_sets:
+        h1 = synth.make_inputs(M, N, dtype=synth.BF16, seed=1,
+                               names=("x", "residual", "bias", "gamma", "beta", "dy"))
+        d1 = {k: to_dev(v) for k, v in h1.items()}
+        del h1
+        fo1 = {k: torch.empty_like(v) for k, v in fwd_out.items()}
+        bo1 = {k: torch.empty_like(v) for k, v in bwd_out.items()}
+        ws1 = torch.empty_like(ws)
+        aws1 = nf.amax_workspace(dev)
+
+        def step1():
+            nf.ln_fwd(d1["x"], d1["bias"], d1["residual"], d1["gamma"], d1["beta"], 1e-5,
+                      want_amax=True, amax_workspace=aws1, out=fo1)
+            nf.ln_bwd(d1["dy"], fo1["residual_out"], d1["gamma"], fo1["mean"], fo1["rstd"],
+                      dparam_dtype=torch.bfloat16, workspace=ws1, out=bo1)
+
+        def step0():
+            fwd()
+            bwd()
+
+        alt_ms = time_calls([step0, step1], K, torch)[0] * 1e-3
+        del d1, fo1, bo1, ws1
+        log(f"steps alternating two buffer sets: {alt_ms:.4f} ms/step, "
+            f"{step_bytes / (alt_ms * 1e-3) / 1e9:.1f} GB/s")
 
     # Per-launch durations of the two halves of the step: K forward calls back
     # to back between two events, then K backward calls.  A forward call is
@@ -238,7 +270,10 @@ def main():
                                "M=576000 (1152x500) x N=384",
                    "M": M, "N": N, "io_dtype": "bf16", "compute_dtype": "f32",
                    "step_bytes": step_bytes, "frac_of_peak": round(value / PEAK_GBS, 4),
-                   "fwd_us": round(fwd_avg, 2), "bwd_us": round(bwd_avg, 2)},
+                   "fwd_us": round(fwd_avg, 2), "bwd_us": round(bwd_avg, 2),
+                   "ms_per_step_two_sets": round(alt_ms, 5) if alt_ms else None,
+                   "frac_of_peak_two_sets": (round(step_bytes / (alt_ms * 1e-3) / 1e9 / PEAK_GBS, 4)
+                                             if alt_ms else None)},
         "roofline": roofline,
     }
 
