@@ -12,7 +12,7 @@ namespace nf {
      &launch_bwd<T, VEC, LPR, VPL, TEAMS, true, true>},
 
 static const BwdEntry k_vec[] = {NF_SHAPES_BF16_BWD_VEC(NF_ENTRY)};
-static const BwdEntry k_vec4[] = {NF_SHAPES_BF16_VEC4(NF_ENTRY)};
+static const BwdEntry k_vec4[] = {NF_SHAPES_BF16_VEC4_FINE(NF_ENTRY)};
 static const BwdEntry k_vec2[] = {NF_SHAPES_SHORT_VEC(NF_ENTRY, bf16, 2)};
 static const BwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, bf16)};
 

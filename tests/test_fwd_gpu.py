@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520), (64, 1000),
           (33, 1024), (17, 1536), (9, 2000), (40, 4096), (43, 4096), (30, 3000), (5, 5000),
           (3, 16384), (2, 16383), (21, 2560), (11, 2304), (13, 1200),
-          (45, 1002), (19, 4100), (7, 6002), (6, 12004),
+          (45, 1002), (19, 4100), (7, 6002), (6, 12004), (301, 4100), (23, 6140), (70, 5004),
           (5, 2), (6, 4), (7, 6), (9, 12)]
 
 
@@ -54,11 +54,19 @@ def check_fwd(rms, inp, dtype, eps, out, parts=("x", "bias", "residual", "gamma"
         assert np.all(np.abs(f64(out["mean"]) - st["mean"]) <= 1e-5 * s), "mean"
     rel = np.abs(f64(out["rstd"]) - st["rstd"]) / st["rstd"]
     assert np.all(rel <= 1e-5), f"rstd: max rel err {rel.max():.3e}"
-    # 3. amax: bit-exact against max |stored y|; and within an ulp of the oracle's
+    # 3. amax: bit-exact against max |stored y|; and against the oracle's
+    # within the bound y itself meets: one ulp of bf16, and for fp32 one ulp
+    # or 1e-5 of amax (fp32 y is within 1e-5 of its row scale, and amax is
+    # the max over y, so it is no further from the oracle's amax)
     if out["amax"] is not None:
         brute = float(np.max(np.abs(y_gpu))) if y_gpu.size else 0.0
         assert float(out["amax"].item()) == brute, (out["amax"].item(), brute)
-        assert_within_ulps(np.array([brute]), np.array([ref["amax"]]), dtype, "amax vs oracle")
+        if dtype == F32:
+            assert abs(brute - ref["amax"]) <= max(float(np.spacing(np.float32(ref["amax"]))),
+                                                   1e-5 * ref["amax"]), (brute, ref["amax"])
+        else:
+            assert_within_ulps(np.array([brute]), np.array([ref["amax"]]), dtype,
+                               "amax vs oracle")
     # end to end
     assert_rows_close(y_gpu, ref["y"], dtype, "y (end to end)", ulps=2.0)
 
