@@ -180,20 +180,24 @@ constexpr int64_t kFwdFewGroups = 4096;
 // Row groups per forward workgroup.  Measured on MI355X: one workgroup per
 // CU walking up to kFwdGroupsWide groups suits wide rows and, up to
 // kFwdFewGroups groups, narrow ones too (16384 x 1024: 35 -> 25 us);
-// narrow rows in larger numbers run one group per workgroup, or two with
-// an FP8 y (576000 x 384: 268 -> 259 us, 262144 x 768: 238 -> 233 us,
-// 65536 x 2048: 162 -> 151 us; 131072 x 1024 is 3% slower) -- or as many
-// as make kFwdMinGroupBytes of each tensor per workgroup: small groups pay
-// their workgroup's set-up (staging the parameters, the final amax) too
-// often (524288 x 256 bf16, 16 KiB per group: 225 -> 174 us with two;
-// 4-byte vectors at 65536 x 386, 3 KiB: 195 -> 54 us with eight).  With
-// amax, at most kMaxAmaxWgs workgroups.
+// narrow rows in larger numbers run one group per workgroup -- two with an
+// FP8 y from kFwdF8PairCols columns on (65536 x 2048: 155 -> 152 us,
+// 131072 x 1024: 155 -> 153 us; below, one is faster since the first
+// group's loads overlap the parameters' staging: 576000 x 384 258 -> 248
+// us, 262144 x 768 233 -> 223 us) -- or as many as make kFwdMinGroupBytes
+// of each tensor per workgroup: small groups pay their workgroup's set-up
+// (staging the parameters, the final amax) too often (524288 x 256 bf16,
+// 16 KiB per group: 225 -> 174 us with two; 4-byte vectors at 65536 x 386,
+// 3 KiB: 195 -> 54 us with eight).  With amax, at most kMaxAmaxWgs
+// workgroups.
 constexpr double kFwdMinGroupBytes = 24.0 * 1024;
+constexpr int64_t kFwdF8PairCols = 1024;
 int fwd_groups_per_wg(int64_t M, int64_t N, int32_t dtype, const RowShape &sh, bool amax, bool f8)
 {
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
     const double group_bytes = double(sh.teams) * double(N) * double(elem_size(dtype));
-    int64_t k = std::max<int64_t>(f8 ? 2 : 1, int64_t(std::ceil(kFwdMinGroupBytes / group_bytes)));
+    const int64_t kmin = f8 && N >= kFwdF8PairCols ? 2 : 1;
+    int64_t k = std::max<int64_t>(kmin, int64_t(std::ceil(kFwdMinGroupBytes / group_bytes)));
     if (sh.lpr >= WIDE_LPR || groups <= kFwdFewGroups)
         k = std::min<int64_t>(kFwdGroupsWide, std::max<int64_t>(1, (groups + kCUs - 1) / kCUs));
     if (amax)
