@@ -345,7 +345,7 @@ static void bwd_dx_rows(void *vctx, int64_t r0, int64_t r1)
 }
 
 /* dgamma_j = sum_i dy_ij * xhat_ij,  dbeta_j = sum_i dy_ij, rows in order.
- * Also the 2-norm of the summed terms, the scale the column sums are judged
+ * Also the 2-norm of the summed terms, the scale the column sums are compared
  * against. */
 static void bwd_col_sums(void *vctx, int64_t j0, int64_t j1)
 {

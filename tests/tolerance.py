@@ -14,7 +14,7 @@
     an absolute floor where cancellation makes an element tiny next to its row;
   * column sums (dgamma, dbeta, dbias): |got - ref| <= rel * max(|ref|,
     ||terms||_2), ||terms||_2 being the 2-norm of the summed terms (the scale a
-    zero-mean sum is judged against); for dbias, whose terms are dx, at least
+    zero-mean sum is compared against); for dbias, whose terms are dx, at least
     the 2-norm of dx's own terms rstd * |dy * gamma| (dbias_term_l2); bf16
     outputs additionally may be one bf16 ulp off.
 The reference ``ref`` is the oracle's exact (double) value.
