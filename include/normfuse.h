@@ -279,7 +279,8 @@ norm_status_t rms_bwd(const void *dy, const void *x, const void *gamma, const fl
  *     exceeds it returns NORM_ERR_WORKSPACE and enqueues nothing.
  *   - The call allocates nothing; on its first call on a device it looks up
  *     that device's scratch address (hipGetSymbolAddress; NORM_ERR_DEVICE if
- *     that fails).
+ *     that fails).  The scratch is the current device's: `stream` must be
+ *     NULL or a stream of the current device (NORM_ERR_DEVICE otherwise).
  *   - Every call on a device shares that device's scratch: calls that may
  *     run at the same time on one device (different streams, or different
  *     threads' streams) race and give wrong results; order them on one

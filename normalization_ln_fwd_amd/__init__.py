@@ -100,8 +100,8 @@ def load(path):
     lib.norm_describe.argtypes = [i32, i64, i64, i32, u32, ctypes.c_char_p, sz]
     lib.ln_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, i32, u32,
                                    vp]
-    for name in ("ln_fwd", "rms_fwd", "ln_bwd", "rms_bwd", "norm_bwd_workspace_size",
-                 "norm_describe", "ln_bwd_noalloc"):
+    for name in ("ln_fwd", "rms_fwd", "ln_fwd_fp8", "rms_fwd_fp8", "ln_bwd", "rms_bwd",
+                 "softmax_fwd", "norm_bwd_workspace_size", "norm_describe", "ln_bwd_noalloc"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -143,12 +143,16 @@ def _ptr(t, name, dtype=None, numel=None):
 _current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
-def _stream(stream):
+def _stream(stream, device):
+    """The raw stream handle: ``stream``'s, else the current stream of the
+    tensors' device (kernels run on the stream's device, so that the
+    tensors need not be on the current device)."""
     if stream is not None:
         return stream.cuda_stream
     if _current_raw_stream is not None:
-        return _current_raw_stream(torch.cuda.current_device())
-    return torch.cuda.current_stream().cuda_stream
+        return _current_raw_stream(device.index if device.index is not None
+                                   else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def amax_workspace(device=None):
@@ -196,7 +200,7 @@ def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, 
         *head, _ptr(res_out, "residual_out", dt, M * N),
         _ptr(mean, "mean", torch.float32, M), _ptr(rstd, "rstd", torch.float32, M),
         _ptr(amax, "amax", torch.float32, 1), _ws_ptr(amax_workspace),
-        ZERO_CENTERED_GAMMA if zero_centered_gamma else 0, _stream(stream))
+        ZERO_CENTERED_GAMMA if zero_centered_gamma else 0, _stream(stream, x.device))
     _check(fn, st)
     return {"y": y, "residual_out": res_out, "mean": mean, "rstd": rstd, "amax": amax}
 
@@ -272,8 +276,25 @@ def softmax_fwd(x, *, stream=None, out=None):
     M = x.numel() // N if N else 0
     y = out if out is not None else torch.empty_like(x)
     _check("softmax_fwd", lib.softmax_fwd(_ptr(x, "x"), M, N, _dtype_code(x),
-                                          _ptr(y, "y", x.dtype, M * N), 0, _stream(stream)))
+                                          _ptr(y, "y", x.dtype, M * N), 0,
+                                          _stream(stream, x.device)))
     return y
+
+
+_DTYPE_NAMES = {"f32": F32, "fp32": F32, "float32": F32, "bf16": BF16, "bfloat16": BF16}
+
+
+def _code_of(dtype):
+    """The library's dtype code of ``dtype``: a code, a torch dtype or a name."""
+    if isinstance(dtype, int) and dtype in (F32, BF16):
+        return dtype
+    if dtype == torch.float32:
+        return F32
+    if dtype == torch.bfloat16:
+        return BF16
+    if isinstance(dtype, str) and dtype in _DTYPE_NAMES:
+        return _DTYPE_NAMES[dtype]
+    raise TypeError(f"unsupported dtype {dtype!r}; use float32 or bfloat16")
 
 
 def describe(op, M, N, dtype, *, amax=False, fp8=False, dbias=False, amax_ws=False):
@@ -282,7 +303,7 @@ def describe(op, M, N, dtype, *, amax=False, fp8=False, dbias=False, amax_ws=Fal
     ``fp8=True``) on an [M, N] problem would launch, for 16-byte aligned
     tensors.  Touches no device."""
     lib = library()
-    code = dtype if isinstance(dtype, int) else (F32 if dtype == torch.float32 else BF16)
+    code = _code_of(dtype)
     opts = (DESCRIBE_AMAX if amax else 0) | (DESCRIBE_FP8 if fp8 else 0) | \
         (DESCRIBE_DBIAS if dbias else 0) | (DESCRIBE_AMAX_WS if amax_ws else 0)
     buf = ctypes.create_string_buffer(512)
@@ -294,7 +315,7 @@ def bwd_workspace_size(M, N, dtype):
     """Workspace bytes ln_bwd / rms_bwd need for an [M, N] problem."""
     lib = library()
     n = ctypes.c_size_t(0)
-    code = dtype if isinstance(dtype, int) else (F32 if dtype == torch.float32 else BF16)
+    code = _code_of(dtype)
     _check("norm_bwd_workspace_size", lib.norm_bwd_workspace_size(M, N, code, ctypes.byref(n)))
     return n.value
 
@@ -336,8 +357,13 @@ def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbet
              _ptr(dbias, "dbias", pdt, N), pcode]
     if not noalloc:
         args += [_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()]
-    args += [flags, _stream(stream)]
-    _check(fn, getattr(lib, fn)(*args))
+    args += [flags, _stream(stream, x.device)]
+    if noalloc and x.device.index is not None and x.device.index != torch.cuda.current_device():
+        # the static scratch is the current device's: make x's device current
+        with torch.cuda.device(x.device):
+            _check(fn, getattr(lib, fn)(*args))
+    else:
+        _check(fn, getattr(lib, fn)(*args))
     return {"dx": dx, "dgamma": dgamma, "dbeta": dbeta, "dbias": dbias}
 
 

@@ -577,14 +577,21 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, int nb, con
 
 constexpr int kMaxDevices = 64;
 
-// The address of the current device's scratch.
-norm_status_t static_scratch(void **ptr)
+// The address of the current device's scratch.  A stream other than the
+// null stream must belong to the current device: hipGetSymbolAddress answers
+// for the current device, and the kernels run on the stream's.
+norm_status_t static_scratch(hipStream_t stream, void **ptr)
 {
     static std::atomic<void *> addr[kMaxDevices];
     static std::mutex mu;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return NORM_ERR_DEVICE;
+    if (stream != nullptr) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev)
+            return NORM_ERR_DEVICE;
+    }
     void *p = addr[dev].load(std::memory_order_acquire);
     if (!p) {
         std::lock_guard<std::mutex> lock(mu);
@@ -647,7 +654,7 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
             return NORM_ERR_WORKSPACE;
         workspace = nullptr;
         if (need > 0)
-            if (norm_status_t st = static_scratch(&workspace))
+            if (norm_status_t st = static_scratch(static_cast<hipStream_t>(stream), &workspace))
                 return st;
     } else if (need > 0 && (!workspace || workspace_bytes < need)) {
         return NORM_ERR_WORKSPACE;

@@ -318,3 +318,18 @@ def test_describe_rejects(lib):
     small = ctypes.create_string_buffer(8)
     assert lib.norm_describe(0, 4, 64, 1, 0, small, 8) == 0
     assert small.value == b"fwd_ker"
+
+
+def test_binding_dtype_arguments(lib):
+    """describe / bwd_workspace_size take a dtype code, a torch dtype or its
+    name, and refuse any other type instead of mapping it to bf16."""
+    import torch
+    for bf in ("bf16", "bfloat16", torch.bfloat16):
+        assert nf.describe("ln_fwd", 4096, 384, bf) == nf.describe("ln_fwd", 4096, 384, nf.BF16)
+    for f in ("f32", "fp32", "float32", torch.float32):
+        assert nf.describe("ln_fwd", 64, 384, f) == nf.describe("ln_fwd", 64, 384, nf.F32)
+    for bad in (torch.float16, "fp16", 7, None):
+        with pytest.raises(TypeError, match="unsupported dtype"):
+            nf.describe("ln_fwd", 64, 384, bad)
+        with pytest.raises(TypeError, match="unsupported dtype"):
+            nf.bwd_workspace_size(64, 384, bad)
