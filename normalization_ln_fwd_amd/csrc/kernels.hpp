@@ -11,13 +11,15 @@
 //
 // The whole row stays in registers between the statistics and the
 // normalisation (or between the two reductions of the backward): every
-// [M, N] tensor crosses HBM exactly once, with nontemporal loads and stores.
+// [M, N] tensor crosses HBM exactly once, with nontemporal loads and stores
+// (the stores of a call's last output bytes write through, see BUF_WT).
 //
 // Grid.  Streaming on this GPU is fastest when each workgroup covers a small
 // contiguous piece and exits, so that the workgroups in flight always sweep
 // one compact window of memory: the forward gives each workgroup one row
-// group.  The backward gives each workgroup K row groups (GroupWalk) so that
-// its dgamma / dbeta column partials are written once per K groups.
+// group when there are many (a few when wide rows or few groups would leave
+// CUs idle).  The backward gives each workgroup K row groups (GroupWalk), so
+// that its dgamma / dbeta column partials are written once per K groups.
 #pragma once
 
 #include <type_traits>
