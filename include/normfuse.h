@@ -58,7 +58,13 @@
  *              enqueues nothing.  NORM_ERR_LAUNCH reports a failed launch;
  *              faults during execution appear at the caller's next
  *              synchronisation, as in HIP.
- *   Aliasing : outputs must not overlap inputs or each other.
+ *   Aliasing : an [M, N] output may be the very tensor (same pointer) of an
+ *              [M, N] input of the same call: y or residual_out over x or
+ *              residual, dx over dy or x, softmax's y over x (every row group
+ *              is loaded before the same workgroup stores its outputs, and no
+ *              other workgroup reads those rows).  FP8 codes may not overlap
+ *              an input.  No other overlap between tensors is allowed, nor
+ *              between outputs.
  *   Threads  : calls are thread-safe; the library keeps no state between
  *              calls.
  *   Results  : deterministic: the same inputs give bit-identical outputs.
