@@ -137,6 +137,8 @@ def main():
                     help="skip the step timed on two alternating buffer sets")
     ap.add_argument("--cases", default="",
                     help="comma-separated breakdown cases to run (name prefixes; default all)")
+    ap.add_argument("--large-m", action="store_true",
+                    help="also time the forward and backward at 2, 4 and 8 times the rows")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -290,6 +292,10 @@ def main():
         cases = [c for c in args.cases.split(",") if c]
         result["breakdown"] = breakdown(args.breakdown_iters, nf, torch, np, synth, d, h, dev,
                                         fwd_out, ws, cases, amax_ws)
+
+    if args.large_m:
+        cases = [c for c in args.cases.split(",") if c]
+        result["large_m"] = large_m(args.breakdown_iters, nf, torch, d, dev, cases)
 
     # free the device copies before the CPU leg
     del d
@@ -565,6 +571,59 @@ def breakdown(iters, nf, torch, np, synth, d, h, dev, fwd_out, ws, cases=(), ama
     rec("ln_fwd_8192x4096_2sets", fwd5[:2], fwd_bytes(M5, N5), False)
     rec("ln_bwd_8192x4096_2sets", bwd5[:2], bwd_bytes(M5, N5), False)
     torch.cuda.synchronize()
+    return out
+
+
+LARGE_M = (2 * M_BIG, 4 * M_BIG, 8 * M_BIG)
+
+
+def large_m(iters, nf, torch, d, dev, cases=()):
+    """Per-call time of the forward (amax workspace) and of the backward at
+    2, 4 and 8 times the benchmark's rows (its 576000-row inputs repeated),
+    each timed back to back like the breakdown: how the kernels follow the
+    HBM's sustained rate as transfers grow.  Cases as in the breakdown,
+    named ln_fwd_{M}x384 / ln_bwd_{M}x384."""
+    out = {}
+    N = N_BIG
+    for M in LARGE_M:
+        names = (f"ln_fwd_{M}x{N}", f"ln_bwd_{M}x{N}")
+        todo = [n for n in names if not cases or any(n.startswith(c) for c in cases)]
+        if not todo:
+            continue
+        r = M // M_BIG
+        x, res, dy = (d[k].repeat(r, 1) for k in ("x", "residual", "dy"))
+        fo = {"y": torch.empty_like(x), "residual_out": torch.empty_like(x),
+              "mean": torch.empty(M, dtype=torch.float32, device=dev),
+              "rstd": torch.empty(M, dtype=torch.float32, device=dev),
+              "amax": torch.empty(1, dtype=torch.float32, device=dev)}
+        bo = {"dx": torch.empty_like(x),
+              "dgamma": torch.empty(N, dtype=torch.bfloat16, device=dev),
+              "dbeta": torch.empty(N, dtype=torch.bfloat16, device=dev)}
+        aws = nf.amax_workspace(dev)
+        ws = torch.empty(max(4, nf.bwd_workspace_size(M, N, torch.bfloat16)), dtype=torch.uint8,
+                         device=dev)
+
+        def fwd():
+            nf.ln_fwd(x, d["bias"], res, d["gamma"], d["beta"], 1e-5, want_amax=True,
+                      amax_workspace=aws, out=fo)
+
+        def bwd():
+            nf.ln_bwd(dy, fo["residual_out"], d["gamma"], fo["mean"], fo["rstd"],
+                      dparam_dtype=torch.bfloat16, workspace=ws, out=bo)
+
+        fwd()
+        for name, fn, nbytes in ((names[0], fwd, fwd_bytes(M, N)), (names[1], bwd, bwd_bytes(M, N))):
+            if name not in todo:
+                continue
+            med, mn, _ = time_calls([fn], iters, torch)
+            gbs = nbytes / (med * 1e-6) / 1e9
+            out[name] = {"us_per_call": round(med, 2), "us_best_slice": round(mn, 2),
+                         "bytes": nbytes, "GB_s": round(gbs, 1),
+                         "frac_peak": round(gbs / PEAK_GBS, 4)}
+            log(f"  {name}: {med:.1f} us, {gbs:.0f} GB/s ({100 * gbs / PEAK_GBS:.1f}% of peak)")
+        del x, res, dy, fo, bo, ws
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     return out
 
 
