@@ -607,14 +607,17 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     }
 }
 
-// Whether the backward pipelines its row walk (wide teams of 16-byte
-// vectors, see bwd_kernel): two groups' packed rows, one group's packed dx,
-// the column accumulators and the unpacked working values (about 4E + 24
-// registers) must fit the wave's share of the 512 VGPRs of a SIMD, less 16.
-// Narrow teams hold several rows per wave and keep enough loads in flight
-// without it; fp32 rows (twice the registers per element) and the shorter
-// vectors of unaligned rows do not pipeline (in 1024-thread workgroups,
-// capped at 128 registers, they spilled).
+// Whether the backward pipelines its row walk (wide teams of bf16 in 16- or
+// 8-byte vectors, see bwd_kernel): two groups' packed rows, one group's
+// packed dx, the column accumulators and the unpacked working values (about
+// 4E + 24 registers) must fit the wave's share of the 512 VGPRs of a SIMD,
+// less 16.  Narrow teams hold several rows per wave and keep enough loads in
+// flight without it; fp32 rows (twice the registers per element) and the
+// 4-byte and single-element paths do not pipeline (in 1024-thread
+// workgroups, capped at 128 registers, they spilled).  The 8-byte bf16 rows
+// gained from it, measured on MI355X: 16384 x 4100 122.2 -> 99.5 us,
+// 16384 x 6140 150.7 -> 118.7 us, 32768 x 1500 97.5 -> 69.5 us,
+// 16384 x 8188 186.1 -> 160.2 us.
 template <typename T, int VEC, int LPR, int VPL, int TEAMS>
 constexpr bool bwd_pipelined()
 {
@@ -624,7 +627,7 @@ constexpr bool bwd_pipelined()
     constexpr int waves_per_simd = (LPR * TEAMS / 64 + 3) / 4;
     constexpr int share = 512 / waves_per_simd;
     constexpr int budget = share - 16;
-    return sizeof(T) == 2 && VEC * int(sizeof(T)) == 16 && LPR >= WIDE_LPR &&
+    return sizeof(T) == 2 && VEC * int(sizeof(T)) >= 8 && LPR >= WIDE_LPR &&
            2 * slot + VPL * raw + 4 * E + 24 <= budget;
 }
 
