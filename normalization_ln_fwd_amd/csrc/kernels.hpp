@@ -149,7 +149,9 @@ __device__ __forceinline__ double team_sum_f64(double v, double *lds, int &parit
 // them with LDS loads and no unpacking or selects.  For wider rows each lane
 // keeps its own columns in registers in the packed I/O form, loaded once per
 // workgroup (zeros beyond N or where absent, ones for an absent gamma), so
-// the row walk issues no memory reads besides its rows.
+// the row walk issues no memory reads besides its rows -- except the
+// backward's 1024-thread workgroups of the widest rows, which are short of
+// registers and stage gamma in LDS up to 16384 elements (see bwd_kernel).
 // ---------------------------------------------------------------------------
 constexpr int PARAMS_LDS_MAX = 4096;
 
@@ -678,7 +680,16 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     constexpr int WG = LPR * TEAMS;
     constexpr int NW = WG / 64;
     constexpr int CAP = LPR * VPL * VEC;
-    constexpr bool PLDS = CAP <= PARAMS_LDS_MAX;
+    // 1024-thread workgroups of 16 or more elements per lane (the widest
+    // rows) get 128 registers per lane: they stage gamma in LDS, like the
+    // narrower rows, and keep the dbias sums in LDS too (each lane its own
+    // slots, so no barrier).  Held in registers these spilled to scratch;
+    // measured on MI355X, backward with dbias: 8192 x 16384 fp32 312 ->
+    // 284 us, 8192 x 16380 bf16 233 -> 188 us, 8192 x 16383 bf16 711 ->
+    // 235 us (without dbias 345 -> 217 us).
+    constexpr bool TIGHT = WG >= 1024 && E >= 16;
+    constexpr bool PLDS = CAP <= PARAMS_LDS_MAX || TIGHT;
+    constexpr bool DLDS = DB && TIGHT;
     constexpr bool PIPE = bwd_pipelined<T, VEC, LPR, VPL, TEAMS>();
     // partial slots to fold in LDS: waves (LPR <= 64) or teams (LPR > 64)
     constexpr int SLOTS = LPR <= 64 ? NW : TEAMS;
@@ -688,6 +699,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
     constexpr int NB = DB ? 3 : 2; // column sums: dgamma, dbeta (, dbias)
     __shared__ float col_lds[SLOTS > 1 ? NB * CAP : 1];
     __shared__ __attribute__((aligned(16))) float par[PLDS ? CAP : 4];
+    __shared__ float dacc[DLDS ? E * WG : 1];
+    static_assert(!DLDS || SLOTS == 1, "LDS dbias sums only for one-team workgroups");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -755,12 +768,14 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
         issue(walk.group(0), A);
     }
 
-    float acc_g[E], acc_b[E], acc_d[DB ? E : 1];
+    float acc_g[E], acc_b[E], acc_d[DB && !DLDS ? E : 1];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         acc_g[e] = 0.f;
         acc_b[e] = 0.f;
-        if constexpr (DB)
+        if constexpr (DLDS)
+            dacc[e * WG + tid] = 0.f;
+        else if constexpr (DB)
             acc_d[e] = 0.f;
     }
     int parity = 0;
@@ -839,7 +854,10 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
                     acc_g[i] = fmaf(dv[e], xh, acc_g[i]);
                     acc_b[i] += dv[e];
                     if constexpr (DB)
-                        acc_d[i] += dxv[e]; // dbias: column sums of dx
+                        if constexpr (DLDS)
+                            dacc[i * WG + tid] += dxv[e]; // this lane's own slots
+                        else
+                            acc_d[i] += dxv[e]; // dbias: column sums of dx
                 }
             }
             if (hold)
@@ -919,7 +937,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
         for (int e = 0; e < E; ++e) {
             acc_g[e] = fold_teams_sum<LPR>(acc_g[e]);
             acc_b[e] = fold_teams_sum<LPR>(acc_b[e]);
-            if constexpr (DB)
+            if constexpr (DB && !DLDS)
                 acc_d[e] = fold_teams_sum<LPR>(acc_d[e]);
         }
     }
@@ -927,9 +945,18 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_kernel(const BwdArgs a)
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
             const int c0 = (k * LPR + tl) * VEC;
-            if (cvalid[k] && (LPR >= 64 || lane < LPR))
-                store_partial<VEC, DB>(pg, pb, pd, c0, N, acc_g + k * VEC, acc_b + k * VEC,
-                                       acc_d + (DB ? k * VEC : 0));
+            if (cvalid[k] && (LPR >= 64 || lane < LPR)) {
+                if constexpr (DLDS) {
+                    float vd[VEC];
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        vd[e] = dacc[(k * VEC + e) * WG + tid];
+                    store_partial<VEC, DB>(pg, pb, pd, c0, N, acc_g + k * VEC, acc_b + k * VEC, vd);
+                } else {
+                    store_partial<VEC, DB>(pg, pb, pd, c0, N, acc_g + k * VEC, acc_b + k * VEC,
+                                           acc_d + (DB ? k * VEC : 0));
+                }
+            }
         }
     } else {
         // slots 0 .. SLOTS-2 add their sums into LDS in slot order; the last

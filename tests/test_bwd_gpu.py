@@ -25,7 +25,10 @@ SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520),
           (2500, 384), (1100, 1024), (301, 4096), (93, 3000), (21, 2560), (11, 2304), (13, 1200),
           (9, 6000), (35, 4608),
           (45, 1002), (19, 4100), (7, 6002), (6, 12004), (301, 4100), (23, 6140), (70, 5004),
-          (5, 2), (6, 4), (7, 6), (9, 12)]
+          (5, 2), (6, 4), (7, 6), (9, 12),
+          # the widest rows in 1024-thread workgroups (gamma and the dbias
+          # sums in LDS), walking several row groups per workgroup
+          (600, 16383), (300, 16380)]
 # column sums over at most a few thousand rows in fp32: far inside 1e-5 of
 # the terms' 2-norm
 COLSUM_REL_SMALL = 1e-5
