@@ -187,6 +187,27 @@ struct ParamStage {
                                                           : BUF_OOB);
         }
     }
+    // bf16 rows: the same values as put() in their 16-bit patterns (bf16
+    // values convert to fp32 and back exactly)
+    __device__ __forceinline__ void put_raw(uint16_t *dst, const void *src, int N, float neutral,
+                                            int tid, bool zero_centred = false) const
+    {
+        static_assert(sizeof(T) == 2, "16-bit elements");
+#pragma unroll
+        for (int i = 0; i < SI; ++i) {
+            const int c = (tid + i * WG) * VEC;
+            if (c < CAP) {
+                float v[VEC];
+                VecIO<T, VEC>::unpack(r[i], v);
+                if (zero_centred)
+                    VecIO<T, VEC>::unpack(plus_one<T, VEC>(v), v);
+                const bool ok = src != nullptr && c < N;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    dst[c + e] = uint16_t(__float_as_uint(ok ? v[e] : neutral) >> 16);
+            }
+        }
+    }
     // zero_centred: store round_T(1 + v) (the weight of a zero-centred
     // gamma; 1 where absent)
     __device__ __forceinline__ void put(float *dst, const void *src, int N, float neutral,
@@ -334,7 +355,17 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     using Raw = typename IO::Raw;
     constexpr int WG = LPR * TEAMS;
     constexpr int CAP = LPR * VPL * VEC;
-    constexpr bool PLDS = CAP <= PARAMS_LDS_MAX;
+    // 1024-thread workgroups of 8 or more elements per lane in 4-byte or
+    // single-element accesses (128 registers, one per element or pair)
+    // stage bias, gamma and beta in LDS: as fp32 up to 8192 columns (96 KiB),
+    // beyond that bf16 rows as their 16-bit patterns, unpacked at each use
+    // (fp32 rows that wide keep them in registers).  Held in registers they
+    // spilled to scratch; measured on MI355X: 8192 x 16383 bf16 474 -> 295
+    // us, 16384 x 8191 fp32 471 -> 432 us.  (8-byte vectors hold them packed
+    // in few registers: in LDS, 8192 x 16380 bf16 took 211 against 206 us.)
+    constexpr bool TIGHT = WG >= 1024 && VPL * VEC >= 8 && VEC * int(sizeof(T)) <= 4;
+    constexpr bool PLDS = CAP <= PARAMS_LDS_MAX || (TIGHT && CAP <= 2 * PARAMS_LDS_MAX);
+    constexpr bool PRAW = !PLDS && TIGHT && sizeof(T) == 2;
     constexpr bool PREFETCH = fwd_prefetch<T, VEC, LPR, VPL, TEAMS>();
     static_assert(WG % 64 == 0, "workgroup of whole waves");
 
@@ -342,6 +373,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     __shared__ double red_lds_f64[TeamLds<LPR, TEAMS, 1>::size];
     __shared__ float max_lds[WG / 64];
     __shared__ __attribute__((aligned(16))) float par[PLDS ? 3 * CAP : 4];
+    __shared__ __attribute__((aligned(16))) uint16_t praw[PRAW ? 3 * CAP : 8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -383,7 +415,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
     // Parameters: their loads first, then the first row group's (every
     // kernel: the rows' latency then overlaps the parameters' staging), so
     // that the wait for the parameters does not include the rows.
-    constexpr int PR = PLDS ? 1 : VPL;
+    constexpr int PR = PLDS || PRAW ? 1 : VPL;
     Raw pbias[PR], pgam[PR], pbeta[PR];
     if constexpr (PLDS) {
         ParamStage<T, VEC, CAP, WG> sb, sg, se;
@@ -395,6 +427,16 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         sg.put(par + CAP, a.gamma, N, 1.f, tid, a.zero_centred);
         se.put(par + 2 * CAP, a.beta, N, 0.f, tid);
         __syncthreads();
+    } else if constexpr (PRAW) {
+        ParamStage<T, VEC, CAP, WG> sb, sg, se;
+        sb.fetch(a.bias, N, tid);
+        sg.fetch(a.gamma, N, tid);
+        se.fetch(a.beta, N, tid);
+        issue(walk.group(0));
+        sb.put_raw(praw, a.bias, N, 0.f, tid);
+        sg.put_raw(praw + CAP, a.gamma, N, 1.f, tid, a.zero_centred);
+        se.put_raw(praw + 2 * CAP, a.beta, N, 0.f, tid);
+        __syncthreads();
     } else {
         uint32_t poff[VPL];
 #pragma unroll
@@ -405,6 +447,15 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         load_param_regs<T, VEC, VPL>(pbeta, a.beta, N, poff, false);
         issue(walk.group(0));
     }
+
+    // VEC values of per-column vector `which` (0 bias, 1 gamma, 2 beta) at
+    // column c0; `reg`: this lane's packed registers when not staged
+    auto pvec = [&](int which, const Raw &reg, int c0, float *out) {
+        if constexpr (PRAW)
+            IO::unpack(*reinterpret_cast<const Raw *>(praw + which * CAP + c0), out);
+        else
+            param_vec<T, VEC, PLDS>(par + which * CAP, reg, c0, out);
+    };
 
     float lane_max = 0.f;
     int parity = 0;
@@ -421,7 +472,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
         const bool wt = grp >= a.wt_group; // store policy (see BUF_WT)
         if (!PREFETCH && kk > 0)
             issue(grp); // group 0 was issued before the parameters were staged
-        if constexpr (!PLDS) {
+        if constexpr (!PLDS && !PRAW) {
             // keep the parameters packed: unpacking them once for the whole
             // walk would cost more registers than the unpacking per group
 #pragma unroll
@@ -457,7 +508,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
             IO::unpack(ur[k], t);
             if (fused_add) {
                 float bv[VEC], rv_[VEC];
-                param_vec<T, VEC, PLDS>(par, pbias[PLDS ? 0 : k], c0, bv);
+                pvec(0, pbias[PR == 1 ? 0 : k], c0, bv);
                 IO::unpack(rr[k], rv_);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
@@ -546,8 +597,8 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_kernel(const FwdArgs a)
             const int c0 = (k * LPR + tl) * VEC;
             float u[VEC], gv[VEC], bv[VEC], yv[VEC];
             IO::unpack(ur[k], u);
-            param_vec<T, VEC, PLDS>(par + CAP, pgam[PLDS ? 0 : k], c0, gv);
-            param_vec<T, VEC, PLDS>(par + 2 * CAP, pbeta[PLDS ? 0 : k], c0, bv);
+            pvec(1, pgam[PR == 1 ? 0 : k], c0, gv);
+            pvec(2, pbeta[PR == 1 ? 0 : k], c0, bv);
 #pragma unroll
             for (int e = 0; e < VEC; ++e)
                 yv[e] = fmaf(fmaf(u[e] - mean, rstd, lo_r), gv[e], bv[e]);

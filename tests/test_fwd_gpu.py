@@ -24,7 +24,10 @@ SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520),
           (33, 1024), (17, 1536), (9, 2000), (40, 4096), (43, 4096), (30, 3000), (5, 5000),
           (3, 16384), (2, 16383), (21, 2560), (11, 2304), (13, 1200),
           (45, 1002), (19, 4100), (7, 6002), (6, 12004), (301, 4100), (23, 6140), (70, 5004),
-          (5, 2), (6, 4), (7, 6), (9, 12)]
+          (5, 2), (6, 4), (7, 6), (9, 12),
+          # 1024-thread workgroups of the widest short-vector rows (parameters
+          # staged in LDS), several row groups per workgroup
+          (600, 16383), (700, 8191), (300, 16382)]
 
 
 def run_fwd(rms, inp, dtype, eps, misalign=False, want_amax=True, parts=None):
