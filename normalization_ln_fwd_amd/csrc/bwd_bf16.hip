@@ -13,7 +13,7 @@ namespace nf {
 
 static const BwdEntry k_vec[] = {NF_SHAPES_BF16_BWD_VEC(NF_ENTRY)};
 static const BwdEntry k_vec4[] = {NF_SHAPES_BF16_VEC4_FINE(NF_ENTRY)};
-static const BwdEntry k_vec2[] = {NF_SHAPES_SHORT_VEC(NF_ENTRY, bf16, 2)};
+static const BwdEntry k_vec2[] = {NF_SHAPES_SHORT_VEC_FINE(NF_ENTRY, bf16, 2)};
 static const BwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, bf16)};
 
 const BwdEntry *bwd_table_bf16(int vec, int *count)

@@ -13,7 +13,7 @@
 // aligned, take the widest of 8-byte vectors (bf16, N % 4 == 0, the fp32
 // layouts), 4-byte vectors of 2 elements (N even) or single elements that
 // N and the alignment allow.  Element-wise capacities: 256 512 1024 2048
-// 4096 8192 16384.  (Steps of 2x capacity and 8 elements per lane beyond 1024 columns:
+// 4096 5120 6144 8192 16384.  (Steps of 2x capacity and 8 elements per lane beyond 1024 columns:
 // with steps of 4x and 16 per lane, 32768 x 1500 bf16 took 205 / 254 us
 // forward / backward, now 117 / 164 us.)
 #pragma once
@@ -78,7 +78,7 @@
     X(T, VEC, 64, 4, 8)
 
 #define NF_SHAPES_ELEM(X, T)                                                                     \
-    NF_SHAPES_SHORT_VEC(X, T, 1)                                                                 \
+    NF_SHAPES_SHORT_VEC_FINE(X, T, 1)                                                            \
     X(T, 1, 1024, 16, 1)
 // Element-wise-like layouts for 4-byte vectors of 2 elements (bf16 rows of
 // an even N, fp32 rows of an even N on 8-byte alignment): capacities 512 to
@@ -89,6 +89,23 @@
     X(T, VEC, 64, 16, 4)                                                                         \
     X(T, VEC, 256, 8, 1)                                                                         \
     X(T, VEC, 512, 8, 1)                                                                         \
+    X(T, VEC, 1024, 8, 1)
+// The same with teams of 640 and 768 lanes between 512 and 1024, for the
+// single-element path and bf16 pairs: rows just past a power of two no
+// longer leave up to half of the lanes idle.  Measured on MI355X (forward /
+// backward): 16384 x 4097 bf16 252 / 166 -> 204 / 142 us, 16384 x 6001 bf16
+// 270 / 186 -> 229 / 174 us, 8192 x 9002 bf16 160 / 120 -> 137 / 112 us,
+// 16384 x 4097 fp32 272 / 185 -> 233 / 179 us.  (fp32 pairs are left out:
+// their forward with the next group's loads in flight spilled on these
+// teams.)
+#define NF_SHAPES_SHORT_VEC_FINE(X, T, VEC)                                                       \
+    X(T, VEC, 64, 4, 4)                                                                          \
+    X(T, VEC, 64, 8, 4)                                                                          \
+    X(T, VEC, 64, 16, 4)                                                                         \
+    X(T, VEC, 256, 8, 1)                                                                         \
+    X(T, VEC, 512, 8, 1)                                                                         \
+    X(T, VEC, 640, 8, 1)                                                                         \
+    X(T, VEC, 768, 8, 1)                                                                         \
     X(T, VEC, 1024, 8, 1)
 // bf16 rows of a multiple of 4 elements on 8-byte alignment: the fp32
 // layouts (4 elements per vector).

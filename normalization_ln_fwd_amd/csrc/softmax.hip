@@ -8,7 +8,7 @@ namespace nf {
 
 static const SoftmaxEntry k_vec_bf16[] = {NF_SHAPES_BF16_VEC(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, bf16, 8)};
 static const SoftmaxEntry k_vec4_bf16[] = {NF_SHAPES_BF16_VEC4(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, bf16, 4)};
-static const SoftmaxEntry k_vec2_bf16[] = {NF_SHAPES_SHORT_VEC(NF_ENTRY, bf16, 2)};
+static const SoftmaxEntry k_vec2_bf16[] = {NF_SHAPES_SHORT_VEC_FINE(NF_ENTRY, bf16, 2)};
 static const SoftmaxEntry k_elem_bf16[] = {NF_SHAPES_ELEM(NF_ENTRY, bf16)};
 static const SoftmaxEntry k_vec_f32[] = {NF_SHAPES_F32_VEC(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, float, 4)};
 static const SoftmaxEntry k_vec2_f32[] = {NF_SHAPES_SHORT_VEC(NF_ENTRY, float, 2)};

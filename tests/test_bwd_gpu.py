@@ -28,7 +28,9 @@ SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520),
           (5, 2), (6, 4), (7, 6), (9, 12),
           # the widest rows in 1024-thread workgroups (gamma and the dbias
           # sums in LDS), walking several row groups per workgroup
-          (600, 16383), (300, 16380)]
+          (600, 16383), (300, 16380),
+          # bf16 pairs on teams of 640 and 768 lanes
+          (5, 10002), (4, 12002)]
 # column sums over at most a few thousand rows in fp32: far inside 1e-5 of
 # the terms' 2-norm
 COLSUM_REL_SMALL = 1e-5

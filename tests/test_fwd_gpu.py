@@ -27,7 +27,9 @@ SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520),
           (5, 2), (6, 4), (7, 6), (9, 12),
           # 1024-thread workgroups of the widest short-vector rows (parameters
           # staged in LDS), several row groups per workgroup
-          (600, 16383), (700, 8191), (300, 16382)]
+          (600, 16383), (700, 8191), (300, 16382),
+          # bf16 pairs on teams of 640 and 768 lanes
+          (5, 10002), (4, 12002)]
 
 
 def run_fwd(rms, inp, dtype, eps, misalign=False, want_amax=True, parts=None):
