@@ -84,6 +84,54 @@ def _gpu():
 
 @pytest.mark.parametrize("c", FWD_CASES, ids=_id)
 def test_random_forward(c):
+    _check_forward(c)
+
+
+@pytest.mark.parametrize("c", BWD_CASES, ids=_id)
+def test_random_backward(c):
+    _check_backward(c)
+
+
+def _walk_knobs(rng, direction):
+    """Forced row groups per workgroup, interleave block and write-through
+    bytes for the test build (and, backward, the split along N on or off)."""
+    env = {f"NORMFUSE_{direction}_GROUPS_PER_WG": str(int(rng.integers(1, 9))),
+           f"NORMFUSE_{direction}_INTERLEAVE": str(int(rng.choice([1, 3, 7, 64, 256, 1000]))),
+           f"NORMFUSE_{direction}_WT_BYTES": str(int(rng.choice([0, 4096, 1 << 20, 1 << 30])))}
+    if direction == "BWD" and rng.random() < 0.5:
+        env["NORMFUSE_BWD_SPLIT"] = str(int(rng.integers(0, 2)))
+    return env
+
+
+def _walk_cases(cases, direction, seed):
+    rng = np.random.default_rng(seed)
+    return [dict(c, env=_walk_knobs(rng, direction)) for c in cases]
+
+
+FWD_WALK_CASES = _walk_cases(_fwd_cases(60, seed=20245), "FWD", 20246)
+BWD_WALK_CASES = _walk_cases(_bwd_cases(60, seed=20247), "BWD", 20248)
+
+
+@pytest.mark.parametrize("c", FWD_WALK_CASES, ids=_id)
+def test_random_forward_walks(c, tuning):
+    """The same checks on the test build with the walk forced: row groups per
+    workgroup, interleave blocks that need not divide the grid, and where the
+    write-through tail starts."""
+    for k, v in c["env"].items():
+        tuning.setenv(k, v)
+    _check_forward(c)
+
+
+@pytest.mark.parametrize("c", BWD_WALK_CASES, ids=_id)
+def test_random_backward_walks(c, tuning):
+    """As above for the backward (more or fewer partial rows, the two-level
+    column sums, the split along N forced on or off where it applies)."""
+    for k, v in c["env"].items():
+        tuning.setenv(k, v)
+    _check_backward(c)
+
+
+def _check_forward(c):
     M, N, dtype, rms = c["M"], c["N"], c["dtype"], c["rms"]
     eps = 1e-6 if rms else 1e-5
     inp = synth.make_inputs(M, N, dtype=dtype, seed=c["seed"])
@@ -119,8 +167,7 @@ def test_random_forward(c):
         assert torch.count_nonzero(ws).item() == 0, "amax workspace not left zero-filled"
 
 
-@pytest.mark.parametrize("c", BWD_CASES, ids=_id)
-def test_random_backward(c):
+def _check_backward(c):
     M, N, dtype, rms = c["M"], c["N"], c["dtype"], c["rms"]
     eps = 1e-6 if rms else 1e-5
     inp = synth.make_inputs(M, N, dtype=dtype, seed=c["seed"], names=("x", "dy", "gamma"))
