@@ -81,13 +81,19 @@
  *              may round differently), NORMFUSE_WT_BYTES (output bytes,
  *              counted from the end of a call, stored write-through: a cache
  *              policy, values do not change; NORMFUSE_FWD_WT_BYTES /
- *              _BWD_WT_BYTES for one direction) and NORMFUSE_BWD_SPLIT=0 / 1
- *              (turns off / forces the backward's split of rows along N).
+ *              _BWD_WT_BYTES for one direction), NORMFUSE_BWD_SPLIT=0 / 1
+ *              (turns off / forces the backward's split of rows along N)
+ *              and NORMFUSE_PAIRS=0 (keeps rows of an odd length on the
+ *              single-element kernels).
  *   Alignment: pointers must be aligned to their element size.  Each call
  *              takes the widest vector access of 16, 8 or 4 bytes (fp32: 16
  *              or 8) that N is a multiple of (in elements) and that every
- *              [M, N] / [N] pointer is aligned to, else single elements;
- *              all give results within the same tolerances, fastest with
+ *              [M, N] / [N] pointer is aligned to, else single elements.
+ *              Rows of an odd N whose [M, N] pointers are aligned to two
+ *              elements (an FP8 output to two bytes) are read two rows at
+ *              a time in aligned pairs of elements (forward and softmax, N
+ *              up to 8191 bf16 / 4095 fp32).  All give results within the
+ *              same tolerances, fastest with
  *              16-byte aligned tensors and N a multiple of 8 (bf16) or 4
  *              (fp32).
  *   Sizes    : 0 <= M; 1 <= N <= NORM_N_MAX.  M = 0 enqueues only what

@@ -56,6 +56,8 @@ norm_status_t check_device()
 // NORMFUSE_BWD_SPLIT                : 0 never splits backward rows along N,
 //                                     1 splits them wherever the kernel can
 //                                     (see bwd_plan)
+// NORMFUSE_PAIRS                    : 0 keeps rows of an odd length on the
+//                                     single-element kernels
 constexpr int kFwdGroupsPerWg = 0; // 0: chosen per call (see fwd_common)
 constexpr int kBwdGroupsPerWg = 0; // 0: chosen per shape (see bwd_plan)
 // Row groups per workgroup.  Teams of several waves (wide rows) have few
@@ -87,6 +89,7 @@ struct Knobs {
     int fwd_a = kFwdInterleave, bwd_a = kBwdInterleave;
     double fwd_wt_bytes = kWtBytes, bwd_wt_bytes = kWtBytes;
     int bwd_split = -1; // -1: chosen per shape
+    bool pairs = true;  // odd rows on the odd-row kernels where they apply
 };
 
 #ifdef NORMFUSE_TUNING
@@ -126,6 +129,8 @@ Knobs knobs()
     parse_positive(std::getenv("NORMFUSE_BWD_INTERLEAVE"), &r.bwd_a);
     if (const char *v = std::getenv("NORMFUSE_BWD_SPLIT"))
         r.bwd_split = std::atoi(v) != 0 ? 1 : 0;
+    if (const char *v = std::getenv("NORMFUSE_PAIRS"))
+        r.pairs = std::atoi(v) != 0;
     auto bytes = [](const char *name, double *out) {
         if (const char *v = std::getenv(name)) {
             const double b = std::atof(v);
@@ -232,6 +237,7 @@ const BwdEntry *bwd_entry(int dtype, int vec, int N, const Knobs &k)
 struct Walk {
     int64_t n_groups = 0, grid = 0;
     int K = 1, A = 1;
+    bool pair = false; // odd-row kernel (odd.hpp)
 };
 
 norm_status_t plan_walk(int64_t M, int teams, int K, int A, Walk *w)
@@ -301,20 +307,48 @@ int vec_width(int64_t N, int32_t dtype, std::initializer_list<const void *> ptrs
 
 int full_width(int32_t dtype) { return int(16 / elem_size(dtype)); }
 
+// Rows of an odd length whose streamed [M, N] tensors are all aligned to two
+// elements (an FP8 output to two bytes) can be read in aligned pairs from
+// each row's first even element (odd.hpp); the per-column vectors need only
+// their element alignment.
+bool pair_aligned(int64_t N, int32_t dtype, std::initializer_list<const void *> ptrs,
+                  const void *f8_y = nullptr)
+{
+    if (N % 2 == 0)
+        return false;
+    const size_t pair_bytes = 2 * elem_size(dtype);
+    bool ok = f8_y == nullptr || aligned(f8_y, 2);
+    for (const void *p : ptrs)
+        ok = ok && (p == nullptr || aligned(p, pair_bytes));
+    return ok;
+}
+
 norm_status_t launched(hipError_t e) { return e == hipSuccess ? NORM_OK : NORM_ERR_LAUNCH; }
 
 // ------------------------------------------------------------------ forward
 // Kernel shape and walk of a forward call (shared by the call and by
 // norm_describe, so that a description names what a call launches).
-norm_status_t fwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool amax, bool f8,
-                       const Knobs &kn, const FwdEntry **entry, Walk *w)
+// `pair`: the rows may take the odd-row kernels (pair_aligned), used when
+// one of their shapes holds the row's pairs.
+norm_status_t fwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pair, bool amax,
+                       bool f8, const Knobs &kn, const FwdEntry **entry, Walk *w)
 {
-    const FwdEntry *e = fwd_entry(dtype, vec, M, int(N), kn);
+    const FwdEntry *e = nullptr;
+    pair = pair && kn.pairs;
+    if (pair) {
+        int n = 0;
+        const FwdEntry *tab = dtype == NORM_F32 ? fwd_odd_table_f32(&n) : fwd_odd_table_bf16(&n);
+        e = pick_shape(tab, n, int(N - 1), kn.fwd_lpr, kn.fwd_vpl, kn.fwd_teams);
+        pair = e != nullptr;
+    }
+    if (!e)
+        e = fwd_entry(dtype, vec, M, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
     const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, amax, f8);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
         return st;
+    w->pair = pair;
     *entry = e;
     return NORM_OK;
 }
@@ -353,9 +387,12 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     const int vec = vec_width(N, dtype, {x, bias, residual, gamma, beta, f8 ? nullptr : y,
                                          residual_out},
                               f8 ? y : nullptr);
+    const bool pair = vec == 1 && pair_aligned(N, dtype, {x, residual, f8 ? nullptr : y,
+                                                         residual_out},
+                                                   f8 ? y : nullptr);
     const FwdEntry *e = nullptr;
     Walk w;
-    if (norm_status_t st = fwd_plan(M, N, dtype, vec, amax != nullptr, f8, kn, &e, &w))
+    if (norm_status_t st = fwd_plan(M, N, dtype, vec, pair, amax != nullptr, f8, kn, &e, &w))
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -396,13 +433,28 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
 }
 
 // ------------------------------------------------------------------ softmax
-norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, const Knobs &kn,
-                           const SoftmaxEntry **entry, Walk *w)
+norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pair,
+                           const Knobs &kn, const SoftmaxEntry **entry, Walk *w)
 {
     int n = 0;
+    const SoftmaxEntry *e = nullptr;
+    if (pair && kn.pairs) {
+        const SoftmaxEntry *tab =
+            dtype == NORM_F32 ? softmax_odd_table_f32(&n) : softmax_odd_table_bf16(&n);
+        e = pick_shape(tab, n, int(N - 1), 0, 0, 0);
+        if (e) {
+            const int K =
+                kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, false, false);
+            if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
+                return st;
+            w->pair = true;
+            *entry = e;
+            return NORM_OK;
+        }
+    }
     const SoftmaxEntry *tab =
         dtype == NORM_F32 ? softmax_table_f32(vec, &n) : softmax_table_bf16(vec, &n);
-    const SoftmaxEntry *e = pick_shape(tab, n, int(N), 0, 0, 0);
+    e = pick_shape(tab, n, int(N), 0, 0, 0);
     if (!e)
         return NORM_ERR_SHAPE;
     // the 512-thread variant of a narrow shape when rows are plentiful
@@ -442,9 +494,10 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
         return NORM_OK;
     const Knobs kn = knobs();
     const int vec = vec_width(N, dtype, {x, y});
+    const bool pair = vec == 1 && pair_aligned(N, dtype, {x, y});
     const SoftmaxEntry *e = nullptr;
     Walk w;
-    if (norm_status_t st = softmax_plan(M, N, dtype, vec, kn, &e, &w))
+    if (norm_status_t st = softmax_plan(M, N, dtype, vec, pair, kn, &e, &w))
         return st;
     SoftmaxArgs a;
     a.x = x;
@@ -744,6 +797,13 @@ void describe_shape(Text &t, const char *kernel, int32_t dtype, const RowShape &
           sh.vpl, sh.teams);
 }
 
+// Odd-row kernels: VPL pairs per lane plus the row's leftover element.
+void describe_pair_shape(Text &t, const char *kernel, int32_t dtype, const RowShape &sh)
+{
+    t.add("%s<%s, pairs, LPR %d, VPL %d, TEAMS %d", kernel, dtype_name(dtype), sh.lpr, sh.vpl,
+          sh.teams);
+}
+
 } // namespace
 
 extern "C" {
@@ -769,9 +829,12 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
     if (op == NORM_OP_LN_FWD || op == NORM_OP_RMS_FWD) {
         const bool amax = opts & NORM_DESCRIBE_AMAX, f8 = opts & NORM_DESCRIBE_FP8;
         const FwdEntry *e = nullptr;
-        if (norm_status_t st = fwd_plan(M, N, dtype, vec, amax, f8, kn, &e, &w))
+        if (norm_status_t st = fwd_plan(M, N, dtype, vec, N % 2 == 1, amax, f8, kn, &e, &w))
             return st;
-        describe_shape(t, "fwd_kernel", dtype, e->shape);
+        if (w.pair)
+            describe_pair_shape(t, "fwd_odd_kernel", dtype, e->shape);
+        else
+            describe_shape(t, "fwd_kernel", dtype, e->shape);
         t.add(", %s%s>; grid %lld x %d threads, %d row group(s) of %d rows per workgroup",
               op == NORM_OP_RMS_FWD ? "RMSNorm" : "LayerNorm", f8 ? ", FP8 y" : "",
               (long long)w.grid, e->shape.threads(), w.K, e->shape.teams);
@@ -783,9 +846,12 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
     }
     if (op == NORM_OP_SOFTMAX) {
         const SoftmaxEntry *e = nullptr;
-        if (norm_status_t st = softmax_plan(M, N, dtype, vec, kn, &e, &w))
+        if (norm_status_t st = softmax_plan(M, N, dtype, vec, N % 2 == 1, kn, &e, &w))
             return st;
-        describe_shape(t, "softmax_kernel", dtype, e->shape);
+        if (w.pair)
+            describe_pair_shape(t, "softmax_odd_kernel", dtype, e->shape);
+        else
+            describe_shape(t, "softmax_kernel", dtype, e->shape);
         t.add(">; grid %lld x %d threads, %d row group(s) of %d rows per workgroup",
               (long long)w.grid, e->shape.threads(), w.K, e->shape.teams);
         return NORM_OK;

@@ -99,6 +99,15 @@ const FwdEntry *fwd_table_bf16(int vec, int *count);
 const BwdEntry *bwd_table_f32(int vec, int *count);
 const BwdEntry *bwd_table_bf16(int vec, int *count);
 
+// Kernels for rows of an odd number of elements whose [M, N] tensors are
+// aligned to two elements (odd.hpp): each row read in aligned pairs from its
+// first even element, plus one element by itself; shape capacity = the
+// pairs' elements, N - 1.
+const FwdEntry *fwd_odd_table_f32(int *count);
+const FwdEntry *fwd_odd_table_bf16(int *count);
+const SoftmaxEntry *softmax_odd_table_f32(int *count);
+const SoftmaxEntry *softmax_odd_table_bf16(int *count);
+
 template <class E, size_t n>
 const E *table_of(const E (&t)[n], int *count)
 {
