@@ -194,15 +194,18 @@ constexpr int64_t kFwdFewGroups = 4096;
 // (staging the parameters, the final amax) too often (524288 x 256 bf16,
 // 16 KiB per group: 225 -> 174 us with two; 4-byte vectors at 65536 x 386,
 // 3 KiB: 195 -> 54 us with eight).  With amax, at most kMaxAmaxWgs
-// workgroups.
+// workgroups.  The odd-row kernels (`odd`) run narrow rows one group per
+// workgroup at any group size: measured on MI355X, 576000 x 385 bf16 445
+// -> 366 us, 262144 x 767 376 -> 331 us, 1048576 x 127 500 -> 386 us.
 constexpr double kFwdMinGroupBytes = 24.0 * 1024;
 constexpr int64_t kFwdF8PairCols = 1024;
-int fwd_groups_per_wg(int64_t M, int64_t N, int32_t dtype, const RowShape &sh, bool amax, bool f8)
+int fwd_groups_per_wg(int64_t M, int64_t N, int32_t dtype, const RowShape &sh, bool amax, bool f8,
+                      bool odd = false)
 {
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
     const double group_bytes = double(sh.teams) * double(N) * double(elem_size(dtype));
-    const int64_t kmin = f8 && N >= kFwdF8PairCols ? 2 : 1;
-    int64_t k = std::max<int64_t>(kmin, int64_t(std::ceil(kFwdMinGroupBytes / group_bytes)));
+    const int64_t kmin = f8 && N >= kFwdF8PairCols && !odd ? 2 : 1;
+    int64_t k = odd ? 1 : std::max<int64_t>(kmin, int64_t(std::ceil(kFwdMinGroupBytes / group_bytes)));
     if (sh.lpr >= WIDE_LPR || groups <= kFwdFewGroups)
         k = std::min<int64_t>(kFwdGroupsWide, std::max<int64_t>(1, (groups + kCUs - 1) / kCUs));
     if (amax)
@@ -345,7 +348,8 @@ norm_status_t fwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pair, 
         e = fwd_entry(dtype, vec, M, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
-    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, amax, f8);
+    const int K =
+        kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, amax, f8, pair);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
         return st;
     w->pair = pair;
@@ -443,8 +447,8 @@ norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pa
             dtype == NORM_F32 ? softmax_odd_table_f32(&n) : softmax_odd_table_bf16(&n);
         e = pick_shape(tab, n, int(N - 1), 0, 0, 0);
         if (e) {
-            const int K =
-                kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, false, false);
+            const int K = kn.fwd_k > 0 ? kn.fwd_k
+                                       : fwd_groups_per_wg(M, N, dtype, e->shape, false, false, true);
             if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
                 return st;
             w->pair = true;
@@ -572,7 +576,14 @@ int bwd_groups_per_wg(int64_t M, int64_t N, const RowShape &sh, int32_t dtype)
 {
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
     if (sh.lpr >= WIDE_LPR) {
-        const int64_t per_cu = dtype == NORM_F32 && sh.capacity() <= 8192 ? 2 : 1;
+        int64_t per_cu = dtype == NORM_F32 && sh.capacity() <= 8192 ? 2 : 1;
+        // bf16 rows of 4-byte or single-element accesses (and the odd-row
+        // pairs) in workgroups of 256 or 512 threads: 1024 threads per CU.
+        // Measured on MI355X, one per CU left them idle: 32768 x 1499
+        // odd-row 147 -> 66 us, single-element 209 -> 84 us; 16384 x 4097
+        // odd-row 113 -> 82 us; 16384 x 2047 odd-row 88 -> 51 us.
+        if (dtype == NORM_BF16 && sh.vec <= 2)
+            per_cu = std::max<int64_t>(per_cu, 1024 / sh.threads());
         const int64_t kmax = std::max(1, kBwdRowsWide / sh.teams);
         const int64_t kmin = groups <= kBwdFewGroups
                                  ? 1
@@ -585,21 +596,33 @@ int bwd_groups_per_wg(int64_t M, int64_t N, const RowShape &sh, int32_t dtype)
     return int(std::max<int64_t>(1, (groups + slots - 1) / slots));
 }
 
-norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, int nb, const Knobs &kn,
-                       const BwdEntry **entry, Walk *w, BwdLayout *lay)
+// `pair`: the rows may take the odd-row kernel (pair_aligned), used when one
+// of its shapes holds the row's pairs.
+norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pair, int nb,
+                       const Knobs &kn, const BwdEntry **entry, Walk *w, BwdLayout *lay)
 {
-    const BwdEntry *e = bwd_entry(dtype, vec, int(N), kn);
+    const BwdEntry *e = nullptr;
+    pair = pair && kn.pairs;
+    if (pair) {
+        int n = 0;
+        const BwdEntry *tab = dtype == NORM_F32 ? bwd_odd_table_f32(&n) : bwd_odd_table_bf16(&n);
+        e = pick_shape(tab, n, int(N - 1), kn.bwd_lpr, kn.bwd_vpl, kn.bwd_teams);
+        pair = e != nullptr;
+    }
+    if (!e)
+        e = bwd_entry(dtype, vec, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
     const int K = kn.bwd_k > 0 ? kn.bwd_k : bwd_groups_per_wg(M, N, e->shape, dtype);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.bwd_a, w))
         return st;
+    w->pair = pair;
     *entry = e;
     // Split the rows along N where whole-row workgroups of wide rows leave
     // CUs idle (fewer workgroups than CUs) and a row spans two chunks or more.
     const int chunk = split_chunk_cols(dtype);
     const int64_t chunks = (N + chunk - 1) / chunk;
-    lay->split = vec == full_width(dtype) && M > 0 && e->shape.lpr >= WIDE_LPR && chunks >= 2 &&
+    lay->split = !pair && vec == full_width(dtype) && M > 0 && e->shape.lpr >= WIDE_LPR && chunks >= 2 &&
                  (kn.bwd_split == 1 ||
                   (kn.bwd_split < 0 && dtype == NORM_BF16 && chunks >= kSplitMinChunks &&
                    w->n_groups >= kSplitMinGroups && w->grid < kCUs));
@@ -695,11 +718,12 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         return st;
     const Knobs kn = knobs();
     const int vec = vec_width(N, dtype, {dy, x, gamma, dx});
+    const bool pair = vec == 1 && pair_aligned(N, dtype, {dy, x, dx});
     const BwdEntry *e = nullptr;
     Walk w;
     BwdLayout lay;
     const int nb = dbias ? 3 : 2;
-    if (norm_status_t st = bwd_plan(M, N, dtype, vec, nb, kn, &e, &w, &lay))
+    if (norm_status_t st = bwd_plan(M, N, dtype, vec, pair, nb, kn, &e, &w, &lay))
         return st;
     const size_t need = lay.bytes;
     if (use_static) {
@@ -859,7 +883,7 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
     const bool dbias = opts & NORM_DESCRIBE_DBIAS;
     const BwdEntry *e = nullptr;
     BwdLayout lay;
-    if (norm_status_t st = bwd_plan(M, N, dtype, vec, dbias ? 3 : 2, kn, &e, &w, &lay))
+    if (norm_status_t st = bwd_plan(M, N, dtype, vec, N % 2 == 1, dbias ? 3 : 2, kn, &e, &w, &lay))
         return st;
     const char *norm = op == NORM_OP_RMS_BWD ? "RMSNorm" : "LayerNorm";
     if (lay.split) {
@@ -867,7 +891,10 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
               "x %d threads", dtype_name(dtype), vec, norm, dbias ? ", dbias" : "", lay.chunks,
               lay.blocks, 64 * SPLIT_ROWS_PER_GROUP);
     } else {
-        describe_shape(t, "bwd_kernel", dtype, e->shape);
+        if (w.pair)
+            describe_pair_shape(t, "bwd_odd_kernel", dtype, e->shape);
+        else
+            describe_shape(t, "bwd_kernel", dtype, e->shape);
         t.add(", %s%s>; grid %lld x %d threads, %d row group(s) of %d rows per workgroup", norm,
               dbias ? ", dbias" : "", (long long)w.grid, e->shape.threads(), w.K,
               e->shape.teams);
@@ -933,20 +960,24 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
     if (norm_status_t st = check_device())
         return st;
     // Largest need over the kernels a call of this shape may take (any
-    // vector width N allows, with dbias).
+    // vector width N allows, the odd-row kernel for odd N, with dbias).
     const Knobs kn = knobs();
     size_t best = 0;
-    for (int v = full_width(dtype); v >= 1; v /= 2) {
-        if (N % v != 0)
-            continue;
+    auto need = [&](int v, bool pair) {
         const BwdEntry *e = nullptr;
         Walk w;
         BwdLayout lay;
-        if (norm_status_t st = bwd_plan(M, N, dtype, v, 3, kn, &e, &w, &lay))
+        const norm_status_t st = bwd_plan(M, N, dtype, v, pair, 3, kn, &e, &w, &lay);
+        best = std::max(best, lay.bytes);
+        return st;
+    };
+    for (int v = full_width(dtype); v >= 1; v /= 2)
+        if (N % v == 0)
+            if (norm_status_t st = need(v, false))
+                return st;
+    if (N % 2 == 1)
+        if (norm_status_t st = need(1, true))
             return st;
-        if (lay.bytes > best)
-            best = lay.bytes;
-    }
     *bytes = best;
     return NORM_OK;
 }

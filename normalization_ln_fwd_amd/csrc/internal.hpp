@@ -105,6 +105,8 @@ const BwdEntry *bwd_table_bf16(int vec, int *count);
 // pairs' elements, N - 1.
 const FwdEntry *fwd_odd_table_f32(int *count);
 const FwdEntry *fwd_odd_table_bf16(int *count);
+const BwdEntry *bwd_odd_table_f32(int *count);
+const BwdEntry *bwd_odd_table_bf16(int *count);
 const SoftmaxEntry *softmax_odd_table_f32(int *count);
 const SoftmaxEntry *softmax_odd_table_bf16(int *count);
 

@@ -1,5 +1,5 @@
-// odd.hpp -- forward and softmax kernels for rows of an odd number of
-// elements, read in aligned pairs.
+// odd.hpp -- forward, softmax and backward kernels for rows of an odd
+// number of elements, read in aligned pairs.
 //
 // Row r of an odd length N starts at element r*N, which is even for even r
 // and odd for odd r.  With the tensors aligned to two elements, a row's
@@ -460,6 +460,232 @@ hipError_t launch_softmax_odd(const SoftmaxArgs &a, int grid, hipStream_t s)
 {
     hipLaunchKernelGGL((softmax_odd_kernel<T, LPR, VPL, TEAMS>), dim3(grid), dim3(LPR * TEAMS),
                        0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Backward stage 1 on rows of an odd length: as bwd_kernel (one load of dy
+// and x per row, the row sums give dx, the column sums are accumulated over
+// the workgroup's rows and written as its partial row), on pairs plus the
+// leftover element.  Workgroups hold an even number of teams and row groups
+// start on even rows, so each team keeps one row parity and with it one set
+// of columns for its whole walk: its column sums stay in registers, one per
+// element as in bwd_kernel (plus the leftover's on the team's first lane).
+// The teams' sums meet in LDS by column, added in team order, and the
+// workgroup stores the partial row from there.
+// ---------------------------------------------------------------------------
+template <typename T, int LPR, int VPL, int TEAMS, bool RMS, bool DB>
+__global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
+{
+    using IO = VecIO<T, 2>;
+    using BIO = BufIO<T, 2>;
+    using IO1 = VecIO<T, 1>;
+    using BIO1 = BufIO<T, 1>;
+    using Raw = typename IO::Raw;
+    using Raw1 = typename IO1::Raw;
+    constexpr int WG = LPR * TEAMS;
+    constexpr int PE = 2 * LPR * VPL + 1; // columns staged: the longest row
+    constexpr int NB = DB ? 3 : 2;        // column sums: dgamma, dbeta (, dbias)
+    using Stage = OddStage<T, PE, WG>;
+    using S = typename Stage::S;
+    static_assert(TEAMS % 2 == 0, "each team keeps one row parity");
+    static_assert(LPR % 64 == 0, "teams of whole waves");
+
+    __shared__ float red_lds[TeamLds<LPR, TEAMS, 2>::size];
+    __shared__ __attribute__((aligned(16))) S par[PE];
+    __shared__ float col_lds[NB * PE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int team = tid / LPR;
+    const int tl = tid % LPR;
+    const int wave_in_team = LPR > 64 ? tl / 64 : 0;
+    const int N = a.N;
+    const int np = (N - 1) / 2;
+    const bool recompute = RMS && a.rstd == nullptr;
+    // rows r0 + team with r0 even: the team's parity is its own
+    const OddRow<T, LPR, VPL> o(team, tl, N, team);
+
+    Raw xr[VPL], dr[VPL];
+    Raw1 x1, d1;
+    float mean = 0.f, rstd = 0.f;
+    auto issue = [&](int64_t g) {
+        const RowGroup rg(g, TEAMS, a.M, N, sizeof(T));
+        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + rg.byte0, rg.bytes);
+        const rsrc_t ds = make_rsrc(static_cast<const char *>(a.dy) + rg.byte0, rg.bytes);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            xr[k] = BIO::load(xs, o.off[k]);
+            dr[k] = BIO::load(ds, o.off[k]);
+        }
+        x1 = BIO1::load(xs, o.off1);
+        d1 = BIO1::load(ds, o.off1);
+        mean = RMS ? 0.f : row_stat(a.mean, rg, team);
+        rstd = recompute ? 0.f : row_stat(a.rstd, rg, team);
+    };
+    const GroupWalk walk(a.K, a.A);
+    {
+        Stage sg;
+        sg.fetch(a.gamma, N, tid);
+        issue(walk.group(0));
+        sg.put(par, a.gamma, N, 1.f, tid, a.zero_centred);
+        __syncthreads();
+    }
+
+    float ag[VPL][2], ab[VPL][2], ad[DB ? VPL : 1][2];
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            ag[k][e] = 0.f;
+            ab[k][e] = 0.f;
+            if constexpr (DB)
+                ad[k][e] = 0.f;
+        }
+    }
+    float a1g = 0.f, a1b = 0.f, a1d = 0.f; // the leftover's column (team's first lane)
+    int parity = 0;
+
+    for (int kk = 0; kk < a.K; ++kk) {
+        const int64_t grp = walk.group(kk);
+        if (grp >= a.n_groups)
+            break; // uniform over the workgroup; later groups are larger
+        if (kk > 0)
+            issue(grp); // group 0 was issued before gamma was staged
+        const RowGroup rg(grp, TEAMS, a.M, N, sizeof(T));
+        const bool rv = rg.r0 + team < a.M;
+        // this lane's columns, opaque to the compiler on each group: gamma
+        // is read from LDS where it is used, not hoisted out of the walk
+        // into registers (32 more for 16 pairs per lane)
+        int cb = o.c0, cl = o.c1;
+        reload_barrier(cb);
+        reload_barrier(cl);
+
+        // Row sums, g = dy * gamma (pairs past the row and the leftover
+        // outside the first lane read dy = 0, so g = 0):
+        //   LN : s0 = sum g (x - mean), s1 = sum g
+        //   RMS: s0 = sum g x; without rstd also s1 = sum x^2
+        float s[2] = {0.f, 0.f};
+        auto row_sums = [&](float xv, float dv, float gm) {
+            const float g = dv * gm;
+            if constexpr (!RMS) {
+                s[0] = fmaf(g, xv - mean, s[0]);
+                s[1] += g;
+            } else {
+                s[0] = fmaf(g, xv, s[0]);
+                if (recompute)
+                    s[1] = fmaf(xv, xv, s[1]);
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int c = cb + 2 * k * LPR;
+            float xv[2], dv[2];
+            IO::unpack(xr[k], xv);
+            IO::unpack(dr[k], dv);
+            row_sums(xv[0], dv[0], odd_param(par, c));
+            row_sums(xv[1], dv[1], odd_param(par, c + 1));
+        }
+        {
+            float xv[1], dv[1];
+            IO1::unpack(x1, xv);
+            IO1::unpack(d1, dv);
+            row_sums(xv[0], dv[0], odd_param(par, cl));
+        }
+        team_sum<LPR, TEAMS, 2>(s, red_lds, parity, team, wave_in_team, lane);
+        if (recompute)
+            rstd = rsqrtf(s[1] / float(N) + a.eps);
+        // dx = rstd (g - c2 - xhat c1) = fma(xhat, -rstd c1, fma(g, rstd, -rstd c2))
+        const float c1 = rstd * (s[0] / float(N));
+        const float c2 = RMS ? 0.f : s[1] / float(N);
+        const float k1 = -rstd * c1, k2 = -rstd * c2;
+        // dx of one element; its column sums when the row is valid (the
+        // sums of pairs past the row are never stored)
+        auto grad = [&](float xv, float dv, float gm, float &sg, float &sb, float &sd) {
+            const float xh = RMS ? xv * rstd : (xv - mean) * rstd;
+            const float dxv = fmaf(xh, k1, fmaf(dv * gm, rstd, k2));
+            if (rv) {
+                sg = fmaf(dv, xh, sg);
+                sb += dv;
+                if constexpr (DB)
+                    sd += dxv;
+            }
+            return dxv;
+        };
+
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            reload_barrier(xr[k]);
+            reload_barrier(dr[k]);
+        }
+        const rsrc_t dxs = make_rsrc(static_cast<char *>(a.dx) + rg.byte0, rg.bytes);
+        const bool wt = grp >= a.wt_group;
+#pragma unroll
+        for (int k = 0; k < VPL; ++k) {
+            const int c = cb + 2 * k * LPR;
+            float xv[2], dv[2], dxv[2], unused = 0.f;
+            IO::unpack(xr[k], xv);
+            IO::unpack(dr[k], dv);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                dxv[e] = grad(xv[e], dv[e], odd_param(par, c + e), ag[k][e], ab[k][e],
+                              DB ? ad[DB ? k : 0][e] : unused);
+            BIO::store(dxs, o.off[k], IO::pack(dxv), wt);
+        }
+        {
+            float xv[1], dv[1], dxv[1];
+            IO1::unpack(x1, xv);
+            IO1::unpack(d1, dv);
+            dxv[0] = grad(xv[0], dv[0], odd_param(par, cl), a1g, a1b, a1d);
+            BIO1::store(dxs, o.off1, IO1::pack(dxv), wt);
+        }
+    }
+
+    // ---- fold the teams' column sums in LDS by column, in team order ----
+    // Every team covers every column (its pairs and its leftover), so team
+    // 0 writes each column and the others add to it.
+    for (int t = 0; t < TEAMS; ++t) {
+        if (team == t) {
+            auto put = [&](int b, int c, float v) {
+                float &dst = col_lds[b * PE + c];
+                dst = t == 0 ? v : dst + v;
+            };
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                if (k * LPR + tl < np) {
+                    const int c = o.c0 + 2 * k * LPR;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        put(0, c + e, ag[k][e]);
+                        put(1, c + e, ab[k][e]);
+                        if constexpr (DB)
+                            put(2, c + e, ad[k][e]);
+                    }
+                }
+            }
+            if (tl == 0) {
+                put(0, o.c1, a1g);
+                put(1, o.c1, a1b);
+                if constexpr (DB)
+                    put(2, o.c1, a1d);
+            }
+        }
+        __syncthreads();
+    }
+    // Block b of the workspace (dgamma, dbeta, dbias) holds row blockIdx.x.
+    const int64_t ld = colsum_ld(N);
+    for (int c = tid; c < N; c += WG) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            a.ws[((int64_t)b * gridDim.x + blockIdx.x) * ld + c] = col_lds[b * PE + c];
+    }
+}
+
+template <typename T, int LPR, int VPL, int TEAMS, bool RMS, bool DB>
+hipError_t launch_bwd_odd(const BwdArgs &a, int grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((bwd_odd_kernel<T, LPR, VPL, TEAMS, RMS, DB>), dim3(grid),
+                       dim3(LPR * TEAMS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -27,3 +27,23 @@
     X(T, 2, 640, 8, 1)                                                                           \
     X(T, 2, 768, 8, 1)                                                                           \
     X(T, 2, 1024, 8, 1)
+
+// The backward's: an even number of teams per workgroup (each team keeps
+// one row parity), teams of whole waves, up to 8193 columns in workgroups
+// of at most 1024 threads.  Beyond 8 pairs per lane, two teams of 128
+// lanes instead of four of 64: 16 pairs per lane took 256 registers with
+// dbias (one wave per SIMD).
+#define NF_SHAPES_ODD_BWD(X, T)                                                                  \
+    X(T, 2, 64, 1, 4)                                                                            \
+    X(T, 2, 64, 2, 4)                                                                            \
+    X(T, 2, 64, 3, 4)                                                                            \
+    X(T, 2, 64, 4, 4)                                                                            \
+    X(T, 2, 64, 6, 4)                                                                            \
+    X(T, 2, 64, 8, 4)                                                                            \
+    X(T, 2, 128, 6, 2)                                                                           \
+    X(T, 2, 128, 8, 2)                                                                           \
+    X(T, 2, 192, 8, 2)                                                                           \
+    X(T, 2, 256, 8, 2)                                                                           \
+    X(T, 2, 320, 8, 2)                                                                           \
+    X(T, 2, 384, 8, 2)                                                                           \
+    X(T, 2, 512, 8, 2)

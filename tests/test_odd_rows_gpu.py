@@ -1,7 +1,7 @@
 """GPU parity of the odd-row kernels: rows of an odd length whose [M, N]
 tensors are aligned to two elements, each row read in aligned pairs from
 its first even element plus its one leftover element (forward, FP8
-forward, softmax).
+forward, softmax, and the backward, whose teams each keep one row parity).
 
 Every shape the odd-row tables hold (bf16 rows up to 16383 columns, fp32
 forward rows up to 8193), N = 1, row counts of both parities and around the
@@ -58,7 +58,7 @@ def _odd_taken(op, M, N, dtype):
 
 def test_describe_names_the_odd_row_kernels():
     """Odd rows take the odd-row kernels up to the longest row their tables
-    hold; even rows and the backward do not."""
+    hold; even rows do not."""
     for dt in (BF16, F32):
         for op in ("ln_fwd", "rms_fwd", "softmax_fwd"):
             longest = 8193 if dt == F32 and op != "softmax_fwd" else 16383
@@ -67,7 +67,6 @@ def test_describe_names_the_odd_row_kernels():
             if longest + 2 <= 16384:
                 assert not _odd_taken(op, 1000, longest + 2, dt)
             assert not _odd_taken(op, 1000, 1000, dt)
-        assert not _odd_taken("ln_bwd", 1000, 1001, dt)
 
 
 @pytest.mark.parametrize("c", CASES, ids=_id)
@@ -226,3 +225,109 @@ def test_odd_softmax_matches_oracle(c):
     y = nf.softmax_fwd(to_dev(x, dtype))
     torch.cuda.synchronize()
     assert_rows_close(f64(y), oracle.softmax_fwd(x, dtype=dtype), dtype, "softmax")
+
+
+# ---------------------------------------------------------------- backward
+from test_bwd_gpu import COLSUM_REL_SMALL, make_case, oracle_bwd, run_bwd  # noqa: E402
+from tolerance import assert_colsums_close, dbias_term_l2, dx_term_scale  # noqa: E402
+
+# each backward table entry at its longest row (two or four teams per
+# workgroup, each keeping one row parity), row counts of both parities and
+# around the group sizes (2 and 4 rows), a few thousand rows; 8195 leaves
+# the table
+BWD_SHAPES = [(1, 1), (2, 1), (3, 3), (5, 7), (8, 7), (37, 129), (17, 257), (12, 385), (40, 513),
+              (9, 769), (33, 1025), (10, 1537), (31, 2049), (7, 3073), (20, 4097), (7, 5121),
+              (11, 6145), (9, 8193), (6, 8191), (2001, 385), (1025, 4097), (5, 8195)]
+BWD_CASES = [(M, N, BF16) for M, N in BWD_SHAPES] + [(M, N, F32) for M, N in BWD_SHAPES]
+
+
+def _check_bwd(inp, out, ref, dtype, dbias):
+    assert_rows_close(f64(out["dx"]), ref["dx"], dtype, "dx",
+                      scale=dx_term_scale(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+    assert_colsums_close(f64(out["dgamma"]), ref["dgamma"], ref["dgamma_l2"], COLSUM_REL_SMALL,
+                         "dgamma")
+    assert_colsums_close(f64(out["dbeta"]), ref["dbeta"], ref["dbeta_l2"], COLSUM_REL_SMALL,
+                         "dbeta")
+    if dbias:
+        l2 = np.maximum(ref["dbias_l2"], dbias_term_l2(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+        assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
+
+
+def test_describe_names_the_odd_row_backward():
+    for dt in (BF16, F32):
+        assert _odd_taken("ln_bwd", 1000, 8193, dt)
+        assert _odd_taken("rms_bwd", 3, 1, dt)
+        assert not _odd_taken("ln_bwd", 1000, 8195, dt)
+        assert not _odd_taken("ln_bwd", 1000, 1000, dt)
+
+
+@pytest.mark.parametrize("c", BWD_CASES, ids=_id)
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+def test_odd_backward_matches_oracle(c, rms):
+    """dx row by row, dgamma / dbeta / dbias against the oracle's column
+    sums; dx, dgamma and dbeta identical without dbias."""
+    M, N, dtype = c
+    inp, eps = make_case(M, N, dtype, rms, seed=M * 41 + N)
+    out = run_bwd(rms, inp, dtype, eps, dparam_dtype=torch.float32, want_dbias=True)
+    _check_bwd(inp, out, oracle_bwd(rms, inp, dtype, eps, want_dbias=True), dtype, True)
+    plain = run_bwd(rms, inp, dtype, eps, dparam_dtype=torch.float32)
+    for k in ("dx", "dgamma", "dbeta"):
+        assert torch.equal(out[k], plain[k]), k
+
+
+@pytest.mark.parametrize("c", [(3, 7, BF16), (2001, 385, F32), (9, 8193, BF16), (10, 1537, F32)],
+                         ids=_id)
+def test_odd_backward_rms_recomputes_rstd(c):
+    M, N, dtype = c
+    inp, eps = make_case(M, N, dtype, True, seed=M + 5 * N)
+    out = run_bwd(True, inp, dtype, eps, recompute=True, dparam_dtype=torch.float32)
+    _check_bwd(inp, out, oracle_bwd(True, inp, dtype, eps, recompute=True), dtype, False)
+
+
+@pytest.mark.parametrize("c", [(3, 7, BF16), (9, 8193, BF16), (2001, 385, BF16), (1025, 4097, F32),
+                               (31, 2049, F32)], ids=_id)
+@pytest.mark.parametrize("rms", [False, True], ids=["ln", "rms"])
+def test_odd_backward_matches_single_element_kernels(c, rms, tuning):
+    """The same call with the odd-row kernels turned off: both within the
+    oracle's bar, and dx within one ulp (or its row scale) of each other."""
+    M, N, dtype = c
+    inp, eps = make_case(M, N, dtype, rms, seed=M + 9 * N)
+    a = run_bwd(rms, inp, dtype, eps, dparam_dtype=torch.float32, want_dbias=True)
+    tuning.setenv("NORMFUSE_PAIRS", "0")
+    assert not _odd_taken("rms_bwd" if rms else "ln_bwd", M, N, dtype)
+    b = run_bwd(rms, inp, dtype, eps, dparam_dtype=torch.float32, want_dbias=True)
+    ref = oracle_bwd(rms, inp, dtype, eps, want_dbias=True)
+    _check_bwd(inp, a, ref, dtype, True)
+    _check_bwd(inp, b, ref, dtype, True)
+    assert_rows_close(f64(a["dx"]), f64(b["dx"]), dtype, "dx pairs vs elements",
+                      scale=dx_term_scale(inp["dy"], inp["gamma"], ref["rstd"], dtype))
+
+
+@pytest.mark.parametrize("groups", [1, 2, 3, 7])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 63, 64, 65, 257])
+def test_odd_backward_walks(M, groups, tuning):
+    """Row groups per workgroup and interleave blocks forced (more or fewer
+    partial rows), row counts around the group size of four."""
+    tuning.setenv("NORMFUSE_BWD_GROUPS_PER_WG", str(groups))
+    tuning.setenv("NORMFUSE_BWD_INTERLEAVE", "3")
+    N = 1001
+    inp, eps = make_case(M, N, BF16, False, seed=M * 13 + groups)
+    out = run_bwd(False, inp, BF16, eps, dparam_dtype=torch.float32, want_dbias=True)
+    _check_bwd(inp, out, oracle_bwd(False, inp, BF16, eps, want_dbias=True), BF16, True)
+
+
+@pytest.mark.parametrize("M,N,dtype", [(3, 7, BF16), (5, 1, F32), (9, 8193, BF16),
+                                       (65, 1001, F32)])
+def test_odd_backward_dx_stays_in_bounds(M, N, dtype):
+    inp, eps = make_case(M, N, dtype, False, seed=M + 7 * N)
+    tdt = TORCH_DT[dtype]
+    buf = torch.full((M * N + 2 + 32,), 7.0, dtype=tdt, device="cuda")
+    dx = buf[2:2 + M * N].view(M, N)
+    nf.ln_bwd(to_dev(inp["dy"], dtype), to_dev(inp["x"], dtype), to_dev(inp["gamma"], dtype),
+              torch.from_numpy(inp["mean"]).cuda(), torch.from_numpy(inp["rstd"]).cuda(),
+              dparam_dtype=torch.float32, out={"dx": dx})
+    torch.cuda.synchronize()
+    assert torch.all(buf[:2] == 7.0) and torch.all(buf[2 + M * N:] == 7.0)
+    ref = oracle_bwd(False, inp, dtype, eps)
+    assert_rows_close(f64(dx), ref["dx"], dtype, "dx",
+                      scale=dx_term_scale(inp["dy"], inp["gamma"], ref["rstd"], dtype))
