@@ -60,13 +60,14 @@ class NormError(RuntimeError):
 
 
 _lib = None
+_product_lib = None  # the product build, once loaded
 
 
 def library():
     """The loaded ``libnormfuse.so`` (ctypes), with argument types set."""
-    global _lib
+    global _lib, _product_lib
     if _lib is None:
-        _lib = load(_LIB_PATH)
+        _lib = _product_lib = load(_LIB_PATH)
     return _lib
 
 
@@ -127,7 +128,7 @@ def _ptr(t, name, dtype=None, numel=None):
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -136,6 +137,20 @@ def _ptr(t, name, dtype=None, numel=None):
     if numel is not None and t.numel() != numel:
         raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
     return t.data_ptr()
+
+
+def _fresh_views(device, *sizes, dtype=torch.float32):
+    """Fresh tensors of the given sizes (None for 0), carved from one
+    allocation: per call, one allocator round trip instead of several."""
+    total = sum(sizes)
+    if total == 0:
+        return [None] * len(sizes)
+    buf = torch.empty(total, dtype=dtype, device=device)
+    views, at = [], 0
+    for n in sizes:
+        views.append(buf[at:at + n] if n else None)
+        at += n
+    return views
 
 
 # The raw handle of the current stream without building a Stream object
@@ -170,36 +185,45 @@ def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, 
     M = x.numel() // N if N else 0
     dt = x.dtype
     fp8 = fn.endswith("_fp8")
-    out = dict(out or {})
+    out = out or {}
+    # outputs not given are allocated here (and need no checks); mean, rstd
+    # and amax share one allocation
     y = out.get("y")
     if y is None:
         y = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device) if fp8 \
             else torch.empty_like(x)
-    if fp8 and y.dtype not in (torch.float8_e4m3fn, torch.uint8):
-        raise TypeError(f"y: expected float8_e4m3fn or uint8, got {y.dtype}")
+        y_p = y.data_ptr()
+    else:
+        if fp8 and y.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError(f"y: expected float8_e4m3fn or uint8, got {y.dtype}")
+        y_p = _ptr(y, "y", y.dtype if fp8 else dt, M * N)
     res_out = out.get("residual_out")
     if res_out is None and want_residual_out:
         res_out = torch.empty_like(x)
-    mean = out.get("mean")
-    if mean is None and want_mean:
-        mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    rstd = out.get("rstd")
-    if rstd is None and want_rstd:
-        rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    amax = out.get("amax")
-    if amax is None and want_amax:
-        amax = torch.empty(1, dtype=torch.float32, device=x.device)
+        res_p = res_out.data_ptr()
+    else:
+        res_p = _ptr(res_out, "residual_out", dt, M * N)
+    mean, rstd, amax = out.get("mean"), out.get("rstd"), out.get("amax")
+    new_mean, new_rstd, new_amax = _fresh_views(
+        x.device, M if mean is None and want_mean else 0, M if rstd is None and want_rstd else 0,
+        1 if amax is None and want_amax else 0)
+    stat_shape = x.shape[:-1]
+    mean_p = _ptr(mean, "mean", torch.float32, M)
+    if new_mean is not None:
+        mean, mean_p = new_mean.view(stat_shape), new_mean.data_ptr()
+    rstd_p = _ptr(rstd, "rstd", torch.float32, M)
+    if new_rstd is not None:
+        rstd, rstd_p = new_rstd.view(stat_shape), new_rstd.data_ptr()
+    amax_p = _ptr(amax, "amax", torch.float32, 1)
+    if new_amax is not None:
+        amax, amax_p = new_amax, new_amax.data_ptr()
     head = [_ptr(x, "x"), _ptr(bias, "bias", dt, N), _ptr(residual, "residual", dt, M * N),
             _ptr(gamma, "gamma", dt, N), _ptr(beta, "beta", dt, N), float(eps), M, N,
             _dtype_code(x)]
     if fp8:
-        head += [_ptr(y_scale, "y_scale", torch.float32, 1), _ptr(y, "y", y.dtype, M * N)]
-    else:
-        head += [_ptr(y, "y", dt, M * N)]
+        head.append(_ptr(y_scale, "y_scale", torch.float32, 1))
     st = getattr(lib, fn)(
-        *head, _ptr(res_out, "residual_out", dt, M * N),
-        _ptr(mean, "mean", torch.float32, M), _ptr(rstd, "rstd", torch.float32, M),
-        _ptr(amax, "amax", torch.float32, 1), _ws_ptr(amax_workspace),
+        *head, y_p, res_p, mean_p, rstd_p, amax_p, _ws_ptr(amax_workspace),
         ZERO_CENTERED_GAMMA if zero_centered_gamma else 0, _stream(stream, x.device))
     _check(fn, st)
     return {"y": y, "residual_out": res_out, "mean": mean, "rstd": rstd, "amax": amax}
@@ -208,7 +232,7 @@ def _fwd(fn, x, bias, residual, gamma, beta, eps, want_residual_out, want_mean, 
 def _ws_ptr(ws):
     if ws is None:
         return None
-    if not isinstance(ws, torch.Tensor) or ws.device.type != "cuda" or not ws.is_contiguous():
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
         raise ValueError("amax_workspace must be a contiguous GPU tensor")
     if ws.numel() * ws.element_size() < AMAX_WS_BYTES:
         raise ValueError(f"amax_workspace must hold at least {AMAX_WS_BYTES} bytes")
@@ -320,6 +344,24 @@ def bwd_workspace_size(M, N, dtype):
     return n.value
 
 
+# Workspace sizes the product library gave, by (M, N, dtype): a pure
+# function of them there (the test build's depends on its overrides too,
+# and is asked every time).
+_ws_bytes = {}
+
+
+def _workspace_bytes(lib, M, N, dtype):
+    if lib is not _product_lib:
+        return bwd_workspace_size(M, N, dtype)
+    key = (M, N, dtype)
+    n = _ws_bytes.get(key)
+    if n is None:
+        if len(_ws_bytes) >= 1024:
+            _ws_bytes.clear()
+        n = _ws_bytes[key] = bwd_workspace_size(M, N, dtype)
+    return n
+
+
 def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbeta, want_dbias,
          workspace, stream, out, flags=0):
     dt = x.dtype
@@ -329,22 +371,21 @@ def _bwd(fn, dy, x, gamma, mean, rstd, eps, dparam_dtype, want_dgamma, want_dbet
     lib = library()
     N = x.shape[-1]
     M = x.numel() // N if N else 0
-    out = dict(out or {})
+    out = out or {}
     dx = out.get("dx")
     if dx is None:
         dx = torch.empty_like(x)
-    dgamma = out.get("dgamma")
-    if dgamma is None and want_dgamma:
-        dgamma = torch.empty(N, dtype=pdt, device=x.device)
-    dbeta = out.get("dbeta")
-    if dbeta is None and want_dbeta:
-        dbeta = torch.empty(N, dtype=pdt, device=x.device)
-    dbias = out.get("dbias")
-    if dbias is None and want_dbias:
-        dbias = torch.empty(N, dtype=pdt, device=x.device)
+    # the parameter gradients not given share one allocation
+    dgamma, dbeta, dbias = out.get("dgamma"), out.get("dbeta"), out.get("dbias")
+    new = _fresh_views(x.device, N if dgamma is None and want_dgamma else 0,
+                     N if dbeta is None and want_dbeta else 0,
+                     N if dbias is None and want_dbias else 0, dtype=pdt)
+    dgamma = dgamma if new[0] is None else new[0]
+    dbeta = dbeta if new[1] is None else new[1]
+    dbias = dbias if new[2] is None else new[2]
     noalloc = fn == "ln_bwd_noalloc"
     if workspace is None and not noalloc:
-        need = bwd_workspace_size(M, N, dt)
+        need = _workspace_bytes(lib, M, N, dt)
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
     pcode = F32 if pdt == torch.float32 else BF16
     args = [_ptr(dy, "dy", dt, M * N), _ptr(x, "x"), _ptr(gamma, "gamma", dt, N)]
