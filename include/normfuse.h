@@ -90,10 +90,11 @@
  *              or 8) that N is a multiple of (in elements) and that every
  *              [M, N] / [N] pointer is aligned to, else single elements.
  *              Rows of an odd N whose [M, N] pointers are aligned to two
- *              elements (an FP8 output to two bytes) are read two rows at
- *              a time in aligned pairs of elements (forward and softmax, N
- *              up to 8191 bf16 / 4095 fp32).  All give results within the
- *              same tolerances, fastest with
+ *              elements (an FP8 output to two bytes) are read in aligned
+ *              pairs of elements from each row's first even element, plus
+ *              one element by itself (forward and softmax up to N = 16383,
+ *              the fp32 forward up to 8193; the backward up to 8193).  All
+ *              give results within the same tolerances, fastest with
  *              16-byte aligned tensors and N a multiple of 8 (bf16) or 4
  *              (fp32).
  *   Sizes    : 0 <= M; 1 <= N <= NORM_N_MAX.  M = 0 enqueues only what

@@ -195,19 +195,27 @@ constexpr int64_t kFwdFewGroups = 4096;
 // 16 KiB per group: 225 -> 174 us with two; 4-byte vectors at 65536 x 386,
 // 3 KiB: 195 -> 54 us with eight).  With amax, at most kMaxAmaxWgs
 // workgroups.  The odd-row kernels (`odd`) run narrow rows one group per
-// workgroup at any group size: measured on MI355X, 576000 x 385 bf16 445
-// -> 366 us, 262144 x 767 376 -> 331 us, 1048576 x 127 500 -> 386 us.
+// workgroup at any group size (measured on MI355X, 576000 x 385 bf16 445
+// -> 366 us, 262144 x 767 376 -> 331 us, 1048576 x 127 500 -> 386 us),
+// and the forward's wide bf16 rows up to kFwdOddGroupsWide groups per
+// workgroup, their next group's loads in flight
+// (8192 x 16383 301 -> 279 us, 8192 x 8191 138 -> 132 us, 16384 x 6001
+// 240 -> 233 us; fp32 rows gained nothing from it).
+constexpr int64_t kFwdOddGroupsWide = 8;
 constexpr double kFwdMinGroupBytes = 24.0 * 1024;
 constexpr int64_t kFwdF8PairCols = 1024;
 int fwd_groups_per_wg(int64_t M, int64_t N, int32_t dtype, const RowShape &sh, bool amax, bool f8,
-                      bool odd = false)
+                      bool odd = false, bool softmax = false)
 {
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
     const double group_bytes = double(sh.teams) * double(N) * double(elem_size(dtype));
     const int64_t kmin = f8 && N >= kFwdF8PairCols && !odd ? 2 : 1;
     int64_t k = odd ? 1 : std::max<int64_t>(kmin, int64_t(std::ceil(kFwdMinGroupBytes / group_bytes)));
-    if (sh.lpr >= WIDE_LPR || groups <= kFwdFewGroups)
-        k = std::min<int64_t>(kFwdGroupsWide, std::max<int64_t>(1, (groups + kCUs - 1) / kCUs));
+    if (sh.lpr >= WIDE_LPR || groups <= kFwdFewGroups) {
+        const bool odd_wide = odd && !softmax && dtype == NORM_BF16 && sh.lpr >= WIDE_LPR;
+        const int64_t kmax = odd_wide ? kFwdOddGroupsWide : kFwdGroupsWide;
+        k = std::min<int64_t>(kmax, std::max<int64_t>(1, (groups + kCUs - 1) / kCUs));
+    }
     if (amax)
         k = std::max(k, (groups + kMaxAmaxWgs - 1) / kMaxAmaxWgs);
     return int(std::max<int64_t>(1, k));
@@ -448,7 +456,8 @@ norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pa
         e = pick_shape(tab, n, int(N - 1), 0, 0, 0);
         if (e) {
             const int K = kn.fwd_k > 0 ? kn.fwd_k
-                                       : fwd_groups_per_wg(M, N, dtype, e->shape, false, false, true);
+                                       : fwd_groups_per_wg(M, N, dtype, e->shape, false, false,
+                                                           true, true);
             if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
                 return st;
             w->pair = true;
