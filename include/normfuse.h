@@ -83,20 +83,25 @@
  *              policy, values do not change; NORMFUSE_FWD_WT_BYTES /
  *              _BWD_WT_BYTES for one direction), NORMFUSE_BWD_SPLIT=0 / 1
  *              (turns off / forces the backward's split of rows along N)
- *              and NORMFUSE_PAIRS=0 (keeps rows of an odd length on the
- *              single-element kernels).
+ *              and NORMFUSE_PAIRS=0 (turns the odd-row kernels below off:
+ *              such rows then take the narrower vectors N allows).
  *   Alignment: pointers must be aligned to their element size.  Each call
  *              takes the widest vector access of 16, 8 or 4 bytes (fp32: 16
  *              or 8) that N is a multiple of (in elements) and that every
  *              [M, N] / [N] pointer is aligned to, else single elements.
- *              Rows of an odd N whose [M, N] pointers are aligned to two
- *              elements (an FP8 output to two bytes) are read in aligned
- *              pairs of elements from each row's first even element, plus
- *              one element by itself (forward and softmax up to N = 16383,
- *              the fp32 forward up to 8193; the backward up to 8193).  All
- *              give results within the same tolerances, fastest with
- *              16-byte aligned tensors and N a multiple of 8 (bf16) or 4
- *              (fp32).
+ *              Rows whose N is an odd multiple of a unit U of 1, 2 or
+ *              (bf16) 4 elements, with [M, N] pointers aligned to 2U
+ *              elements (an FP8 output to 2U bytes), are read in aligned
+ *              vectors of 2U elements from each row's first such element,
+ *              plus one unit by itself ("odd-row" kernels; 2U elements are
+ *              wider than the rule above allows).  The forward and softmax
+ *              take them up to NORM_N_MAX (the fp32 forward up to 8193 /
+ *              8194 for U = 1 / 2), the backward up to 8193 (U = 1), 8194
+ *              (U = 2; fp32 4098) or 8196 (U = 4); for U = 2 and 4 the
+ *              backward takes a row across several waves only where that
+ *              leaves fewer lanes idle than the vector kernel.  All give
+ *              results within the same tolerances, fastest with 16-byte
+ *              aligned tensors and N a multiple of 8 (bf16) or 4 (fp32).
  *   Sizes    : 0 <= M; 1 <= N <= NORM_N_MAX.  M = 0 enqueues only what
  *              defines the outputs (amax = 0, dgamma = dbeta = dbias = 0), and then
  *              the [M, N] and [M] pointers may be NULL.

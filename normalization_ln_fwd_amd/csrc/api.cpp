@@ -46,6 +46,7 @@ norm_status_t check_device()
 // can sweep them:
 // NORMFUSE_{FWD,BWD}_SHAPE          : "LPRxVPL" or "LPRxVPLxTEAMS" -- use that
 //                                     instantiated shape when it covers the row
+//                                     (the FWD one for softmax too)
 // NORMFUSE_{FWD,BWD}_GROUPS_PER_WG  : row groups per workgroup (K)
 // NORMFUSE_{FWD,BWD}_INTERLEAVE     : workgroups per interleave block (A)
 // NORMFUSE_WT_BYTES                 : output bytes, counted from the end,
@@ -89,7 +90,7 @@ struct Knobs {
     int fwd_a = kFwdInterleave, bwd_a = kBwdInterleave;
     double fwd_wt_bytes = kWtBytes, bwd_wt_bytes = kWtBytes;
     int bwd_split = -1; // -1: chosen per shape
-    bool pairs = true;  // odd rows on the odd-row kernels where they apply
+    bool pairs = true;  // rows of an odd multiple of a unit on the odd-row kernels
 };
 
 #ifdef NORMFUSE_TUNING
@@ -248,7 +249,7 @@ const BwdEntry *bwd_entry(int dtype, int vec, int N, const Knobs &k)
 struct Walk {
     int64_t n_groups = 0, grid = 0;
     int K = 1, A = 1;
-    bool pair = false; // odd-row kernel (odd.hpp)
+    int unit = 0;      // the odd-row kernel's unit (odd.hpp), 0 for the others
 };
 
 norm_status_t plan_walk(int64_t M, int teams, int K, int A, Walk *w)
@@ -318,49 +319,95 @@ int vec_width(int64_t N, int32_t dtype, std::initializer_list<const void *> ptrs
 
 int full_width(int32_t dtype) { return int(16 / elem_size(dtype)); }
 
-// Rows of an odd length whose streamed [M, N] tensors are all aligned to two
-// elements (an FP8 output to two bytes) can be read in aligned pairs from
-// each row's first even element (odd.hpp); the per-column vectors need only
-// their element alignment.
-bool pair_aligned(int64_t N, int32_t dtype, std::initializer_list<const void *> ptrs,
-                  const void *f8_y = nullptr)
+// Rows whose length is an odd multiple of a unit U (a power of two, at most
+// half a 16-byte vector: U = 1 for odd N) and whose streamed [M, N] tensors
+// are all aligned to 2U elements (an FP8 output to 2U bytes) can be read in
+// aligned vectors of 2U elements from each row's first such element (the
+// odd-row kernels, odd.hpp); the per-column vectors need only their element
+// alignment.  Returns U, or 0 where that does not hold.
+int odd_unit(int64_t N, int32_t dtype, std::initializer_list<const void *> ptrs,
+             const void *f8_y = nullptr)
 {
-    if (N % 2 == 0)
-        return false;
-    const size_t pair_bytes = 2 * elem_size(dtype);
-    bool ok = f8_y == nullptr || aligned(f8_y, 2);
+    const int half = full_width(dtype) / 2;
+    int u = 1;
+    while (u < half && N % (2 * u) == 0)
+        u *= 2;
+    if (N % (2 * u) != u)
+        return 0; // a multiple of a whole vector: the vector layouts
+    const size_t vector_bytes = size_t(2 * u) * elem_size(dtype);
+    bool ok = f8_y == nullptr || aligned(f8_y, size_t(2 * u));
     for (const void *p : ptrs)
-        ok = ok && (p == nullptr || aligned(p, pair_bytes));
-    return ok;
+        ok = ok && (p == nullptr || aligned(p, vector_bytes));
+    return ok ? u : 0;
 }
+
+// The odd-row kernel tables of a dtype and unit (empty where there are
+// none).
+const FwdEntry *fwd_odd_table(int32_t dtype, int unit, int *count)
+{
+    *count = 0;
+    if (dtype == NORM_F32)
+        return unit == 1 ? fwd_odd_table_f32_u1(count)
+                         : unit == 2 ? fwd_odd_table_f32_u2(count) : nullptr;
+    return unit == 1   ? fwd_odd_table_bf16_u1(count)
+           : unit == 2 ? fwd_odd_table_bf16_u2(count)
+           : unit == 4 ? fwd_odd_table_bf16_u4(count)
+                       : nullptr;
+}
+const BwdEntry *bwd_odd_table(int32_t dtype, int unit, int *count)
+{
+    *count = 0;
+    if (dtype == NORM_F32)
+        return unit == 1 ? bwd_odd_table_f32_u1(count)
+                         : unit == 2 ? bwd_odd_table_f32_u2(count) : nullptr;
+    return unit == 1   ? bwd_odd_table_bf16_u1(count)
+           : unit == 2 ? bwd_odd_table_bf16_u2(count)
+           : unit == 4 ? bwd_odd_table_bf16_u4(count)
+                       : nullptr;
+}
+const SoftmaxEntry *softmax_odd_table(int32_t dtype, int unit, int *count)
+{
+    *count = 0;
+    if (dtype == NORM_F32)
+        return unit == 1 ? softmax_odd_table_f32_u1(count)
+                         : unit == 2 ? softmax_odd_table_f32_u2(count) : nullptr;
+    return unit == 1   ? softmax_odd_table_bf16_u1(count)
+           : unit == 2 ? softmax_odd_table_bf16_u2(count)
+           : unit == 4 ? softmax_odd_table_bf16_u4(count)
+                       : nullptr;
+}
+
+// The unit a call takes the odd-row kernels with: theirs when their vectors
+// are wider than the vector layout's `vec`, else 0.
+int odd_unit_for(int unit, int vec) { return unit > 0 && 2 * unit > vec ? unit : 0; }
 
 norm_status_t launched(hipError_t e) { return e == hipSuccess ? NORM_OK : NORM_ERR_LAUNCH; }
 
 // ------------------------------------------------------------------ forward
 // Kernel shape and walk of a forward call (shared by the call and by
 // norm_describe, so that a description names what a call launches).
-// `pair`: the rows may take the odd-row kernels (pair_aligned), used when
-// one of their shapes holds the row's pairs.
-norm_status_t fwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pair, bool amax,
+// `unit`: the rows may take the odd-row kernels of that unit (odd_unit_for;
+// 0: not), used when one of their shapes holds the row's vectors.
+norm_status_t fwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, int unit, bool amax,
                        bool f8, const Knobs &kn, const FwdEntry **entry, Walk *w)
 {
     const FwdEntry *e = nullptr;
-    pair = pair && kn.pairs;
-    if (pair) {
+    unit = kn.pairs ? unit : 0;
+    if (unit) {
         int n = 0;
-        const FwdEntry *tab = dtype == NORM_F32 ? fwd_odd_table_f32(&n) : fwd_odd_table_bf16(&n);
-        e = pick_shape(tab, n, int(N - 1), kn.fwd_lpr, kn.fwd_vpl, kn.fwd_teams);
-        pair = e != nullptr;
+        const FwdEntry *tab = fwd_odd_table(dtype, unit, &n);
+        e = pick_shape(tab, n, int(N - unit), kn.fwd_lpr, kn.fwd_vpl, kn.fwd_teams);
+        unit = e != nullptr ? unit : 0;
     }
     if (!e)
         e = fwd_entry(dtype, vec, M, int(N), kn);
     if (!e)
         return NORM_ERR_SHAPE;
     const int K =
-        kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, amax, f8, pair);
+        kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, amax, f8, unit > 0);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
         return st;
-    w->pair = pair;
+    w->unit = unit;
     *entry = e;
     return NORM_OK;
 }
@@ -399,12 +446,11 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
     const int vec = vec_width(N, dtype, {x, bias, residual, gamma, beta, f8 ? nullptr : y,
                                          residual_out},
                               f8 ? y : nullptr);
-    const bool pair = vec == 1 && pair_aligned(N, dtype, {x, residual, f8 ? nullptr : y,
-                                                         residual_out},
-                                                   f8 ? y : nullptr);
+    const int unit = odd_unit_for(
+        odd_unit(N, dtype, {x, residual, f8 ? nullptr : y, residual_out}, f8 ? y : nullptr), vec);
     const FwdEntry *e = nullptr;
     Walk w;
-    if (norm_status_t st = fwd_plan(M, N, dtype, vec, pair, amax != nullptr, f8, kn, &e, &w))
+    if (norm_status_t st = fwd_plan(M, N, dtype, vec, unit, amax != nullptr, f8, kn, &e, &w))
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -445,33 +491,32 @@ norm_status_t fwd_common(bool rms, const void *x, const void *bias, const void *
 }
 
 // ------------------------------------------------------------------ softmax
-norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pair,
+norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, int unit,
                            const Knobs &kn, const SoftmaxEntry **entry, Walk *w)
 {
     int n = 0;
     const SoftmaxEntry *e = nullptr;
-    if (pair && kn.pairs) {
-        const SoftmaxEntry *tab =
-            dtype == NORM_F32 ? softmax_odd_table_f32(&n) : softmax_odd_table_bf16(&n);
-        e = pick_shape(tab, n, int(N - 1), 0, 0, 0);
+    if (unit && kn.pairs) {
+        const SoftmaxEntry *tab = softmax_odd_table(dtype, unit, &n);
+        e = pick_shape(tab, n, int(N - unit), kn.fwd_lpr, kn.fwd_vpl, kn.fwd_teams);
         if (e) {
             const int K = kn.fwd_k > 0 ? kn.fwd_k
                                        : fwd_groups_per_wg(M, N, dtype, e->shape, false, false,
                                                            true, true);
             if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
                 return st;
-            w->pair = true;
+            w->unit = unit;
             *entry = e;
             return NORM_OK;
         }
     }
     const SoftmaxEntry *tab =
         dtype == NORM_F32 ? softmax_table_f32(vec, &n) : softmax_table_bf16(vec, &n);
-    e = pick_shape(tab, n, int(N), 0, 0, 0);
+    e = pick_shape(tab, n, int(N), kn.fwd_lpr, kn.fwd_vpl, kn.fwd_teams);
     if (!e)
         return NORM_ERR_SHAPE;
     // the 512-thread variant of a narrow shape when rows are plentiful
-    for (int i = 0; i < n; ++i) {
+    for (int i = 0; i < n && kn.fwd_lpr == 0; ++i) {
         const RowShape &ws = tab[i].shape;
         if (ws.lpr == e->shape.lpr && ws.vpl == e->shape.vpl && ws.teams == 2 * e->shape.teams &&
             (M + ws.teams - 1) / ws.teams >= kMinWideGroups) {
@@ -507,10 +552,10 @@ norm_status_t softmax_common(const void *x, int64_t M, int64_t N, int32_t dtype,
         return NORM_OK;
     const Knobs kn = knobs();
     const int vec = vec_width(N, dtype, {x, y});
-    const bool pair = vec == 1 && pair_aligned(N, dtype, {x, y});
+    const int unit = odd_unit_for(odd_unit(N, dtype, {x, y}), vec);
     const SoftmaxEntry *e = nullptr;
     Walk w;
-    if (norm_status_t st = softmax_plan(M, N, dtype, vec, pair, kn, &e, &w))
+    if (norm_status_t st = softmax_plan(M, N, dtype, vec, unit, kn, &e, &w))
         return st;
     SoftmaxArgs a;
     a.x = x;
@@ -605,18 +650,30 @@ int bwd_groups_per_wg(int64_t M, int64_t N, const RowShape &sh, int32_t dtype)
     return int(std::max<int64_t>(1, (groups + slots - 1) / slots));
 }
 
-// `pair`: the rows may take the odd-row kernel (pair_aligned), used when one
-// of its shapes holds the row's pairs.
-norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pair, int nb,
+// `unit`: the rows may take the odd-row kernel of that unit (odd_unit_for;
+// 0: not), used when one of its shapes holds the row's vectors.
+norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, int unit, int nb,
                        const Knobs &kn, const BwdEntry **entry, Walk *w, BwdLayout *lay)
 {
     const BwdEntry *e = nullptr;
-    pair = pair && kn.pairs;
-    if (pair) {
+    unit = kn.pairs ? unit : 0;
+    if (unit) {
         int n = 0;
-        const BwdEntry *tab = dtype == NORM_F32 ? bwd_odd_table_f32(&n) : bwd_odd_table_bf16(&n);
-        e = pick_shape(tab, n, int(N - 1), kn.bwd_lpr, kn.bwd_vpl, kn.bwd_teams);
-        pair = e != nullptr;
+        const BwdEntry *tab = bwd_odd_table(dtype, unit, &n);
+        e = pick_shape(tab, n, int(N - unit), kn.bwd_lpr, kn.bwd_vpl, kn.bwd_teams);
+        // Rows of 2- or 4-element units also fit the vector kernel on 4- or
+        // 8-byte vectors.  On a wide team (two rows per workgroup, each across
+        // several waves) the odd-row backward takes it only where it leaves
+        // fewer lanes idle: at the same fill the vector kernel is 4-10% faster
+        // (measured on MI355X, 8192 x 6004 bf16: 70.6 against 63.8 us; 16384 x
+        // 3076: 79.3 against 75.2 us), and with fewer idle lanes it is slower
+        // (16384 x 4100: 92.1 against 99.6 us, 8192 x 8196: 87.4 against 126.8).
+        if (e && vec > 1 && e->shape.lpr >= WIDE_LPR && kn.bwd_lpr == 0) {
+            const BwdEntry *v = bwd_entry(dtype, vec, int(N), kn);
+            if (v && (N - unit) * int64_t(v->shape.capacity()) <= N * int64_t(e->shape.capacity()))
+                e = nullptr;
+        }
+        unit = e != nullptr ? unit : 0;
     }
     if (!e)
         e = bwd_entry(dtype, vec, int(N), kn);
@@ -625,13 +682,13 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, bool pair, 
     const int K = kn.bwd_k > 0 ? kn.bwd_k : bwd_groups_per_wg(M, N, e->shape, dtype);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.bwd_a, w))
         return st;
-    w->pair = pair;
+    w->unit = unit;
     *entry = e;
     // Split the rows along N where whole-row workgroups of wide rows leave
     // CUs idle (fewer workgroups than CUs) and a row spans two chunks or more.
     const int chunk = split_chunk_cols(dtype);
     const int64_t chunks = (N + chunk - 1) / chunk;
-    lay->split = !pair && vec == full_width(dtype) && M > 0 && e->shape.lpr >= WIDE_LPR && chunks >= 2 &&
+    lay->split = !unit && vec == full_width(dtype) && M > 0 && e->shape.lpr >= WIDE_LPR && chunks >= 2 &&
                  (kn.bwd_split == 1 ||
                   (kn.bwd_split < 0 && dtype == NORM_BF16 && chunks >= kSplitMinChunks &&
                    w->n_groups >= kSplitMinGroups && w->grid < kCUs));
@@ -727,12 +784,12 @@ norm_status_t bwd_common(bool rms, const void *dy, const void *x, const void *ga
         return st;
     const Knobs kn = knobs();
     const int vec = vec_width(N, dtype, {dy, x, gamma, dx});
-    const bool pair = vec == 1 && pair_aligned(N, dtype, {dy, x, dx});
+    const int unit = odd_unit_for(odd_unit(N, dtype, {dy, x, dx}), vec);
     const BwdEntry *e = nullptr;
     Walk w;
     BwdLayout lay;
     const int nb = dbias ? 3 : 2;
-    if (norm_status_t st = bwd_plan(M, N, dtype, vec, pair, nb, kn, &e, &w, &lay))
+    if (norm_status_t st = bwd_plan(M, N, dtype, vec, unit, nb, kn, &e, &w, &lay))
         return st;
     const size_t need = lay.bytes;
     if (use_static) {
@@ -830,11 +887,12 @@ void describe_shape(Text &t, const char *kernel, int32_t dtype, const RowShape &
           sh.vpl, sh.teams);
 }
 
-// Odd-row kernels: VPL pairs per lane plus the row's leftover element.
-void describe_pair_shape(Text &t, const char *kernel, int32_t dtype, const RowShape &sh)
+// Odd-row kernels: VPL vectors of 2U elements per lane plus the row's
+// leftover unit of U.
+void describe_odd_shape(Text &t, const char *kernel, int32_t dtype, int unit, const RowShape &sh)
 {
-    t.add("%s<%s, pairs, LPR %d, VPL %d, TEAMS %d", kernel, dtype_name(dtype), sh.lpr, sh.vpl,
-          sh.teams);
+    t.add("%s<%s, unit %d, LPR %d, VPL %d, TEAMS %d", kernel, dtype_name(dtype), unit, sh.lpr,
+          sh.vpl, sh.teams);
 }
 
 } // namespace
@@ -862,10 +920,11 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
     if (op == NORM_OP_LN_FWD || op == NORM_OP_RMS_FWD) {
         const bool amax = opts & NORM_DESCRIBE_AMAX, f8 = opts & NORM_DESCRIBE_FP8;
         const FwdEntry *e = nullptr;
-        if (norm_status_t st = fwd_plan(M, N, dtype, vec, N % 2 == 1, amax, f8, kn, &e, &w))
+        if (norm_status_t st = fwd_plan(M, N, dtype, vec, odd_unit_for(odd_unit(N, dtype, {}), vec),
+                                        amax, f8, kn, &e, &w))
             return st;
-        if (w.pair)
-            describe_pair_shape(t, "fwd_odd_kernel", dtype, e->shape);
+        if (w.unit)
+            describe_odd_shape(t, "fwd_odd_kernel", dtype, w.unit, e->shape);
         else
             describe_shape(t, "fwd_kernel", dtype, e->shape);
         t.add(", %s%s>; grid %lld x %d threads, %d row group(s) of %d rows per workgroup",
@@ -879,10 +938,11 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
     }
     if (op == NORM_OP_SOFTMAX) {
         const SoftmaxEntry *e = nullptr;
-        if (norm_status_t st = softmax_plan(M, N, dtype, vec, N % 2 == 1, kn, &e, &w))
+        if (norm_status_t st = softmax_plan(M, N, dtype, vec,
+                                            odd_unit_for(odd_unit(N, dtype, {}), vec), kn, &e, &w))
             return st;
-        if (w.pair)
-            describe_pair_shape(t, "softmax_odd_kernel", dtype, e->shape);
+        if (w.unit)
+            describe_odd_shape(t, "softmax_odd_kernel", dtype, w.unit, e->shape);
         else
             describe_shape(t, "softmax_kernel", dtype, e->shape);
         t.add(">; grid %lld x %d threads, %d row group(s) of %d rows per workgroup",
@@ -892,7 +952,8 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
     const bool dbias = opts & NORM_DESCRIBE_DBIAS;
     const BwdEntry *e = nullptr;
     BwdLayout lay;
-    if (norm_status_t st = bwd_plan(M, N, dtype, vec, N % 2 == 1, dbias ? 3 : 2, kn, &e, &w, &lay))
+    if (norm_status_t st = bwd_plan(M, N, dtype, vec, odd_unit_for(odd_unit(N, dtype, {}), vec),
+                                    dbias ? 3 : 2, kn, &e, &w, &lay))
         return st;
     const char *norm = op == NORM_OP_RMS_BWD ? "RMSNorm" : "LayerNorm";
     if (lay.split) {
@@ -900,8 +961,8 @@ norm_status_t norm_describe(int32_t op, int64_t M, int64_t N, int32_t dtype, uin
               "x %d threads", dtype_name(dtype), vec, norm, dbias ? ", dbias" : "", lay.chunks,
               lay.blocks, 64 * SPLIT_ROWS_PER_GROUP);
     } else {
-        if (w.pair)
-            describe_pair_shape(t, "bwd_odd_kernel", dtype, e->shape);
+        if (w.unit)
+            describe_odd_shape(t, "bwd_odd_kernel", dtype, w.unit, e->shape);
         else
             describe_shape(t, "bwd_kernel", dtype, e->shape);
         t.add(", %s%s>; grid %lld x %d threads, %d row group(s) of %d rows per workgroup", norm,
@@ -969,24 +1030,28 @@ norm_status_t norm_bwd_workspace_size(int64_t M, int64_t N, int32_t dtype, size_
     if (norm_status_t st = check_device())
         return st;
     // Largest need over the kernels a call of this shape may take (any
-    // vector width N allows, the odd-row kernel for odd N, with dbias).
+    // vector width N allows, the odd-row kernel of N's unit on any such
+    // width, with dbias).
     const Knobs kn = knobs();
     size_t best = 0;
-    auto need = [&](int v, bool pair) {
+    const int unit = odd_unit(N, dtype, {});
+    auto need = [&](int v, int u) {
         const BwdEntry *e = nullptr;
         Walk w;
         BwdLayout lay;
-        const norm_status_t st = bwd_plan(M, N, dtype, v, pair, 3, kn, &e, &w, &lay);
+        const norm_status_t st = bwd_plan(M, N, dtype, v, u, 3, kn, &e, &w, &lay);
         best = std::max(best, lay.bytes);
         return st;
     };
-    for (int v = full_width(dtype); v >= 1; v /= 2)
-        if (N % v == 0)
-            if (norm_status_t st = need(v, false))
-                return st;
-    if (N % 2 == 1)
-        if (norm_status_t st = need(1, true))
+    for (int v = full_width(dtype); v >= 1; v /= 2) {
+        if (N % v != 0)
+            continue;
+        if (norm_status_t st = need(v, 0))
             return st;
+        if (odd_unit_for(unit, v))
+            if (norm_status_t st = need(v, unit))
+                return st;
+    }
     *bytes = best;
     return NORM_OK;
 }

@@ -99,16 +99,26 @@ const FwdEntry *fwd_table_bf16(int vec, int *count);
 const BwdEntry *bwd_table_f32(int vec, int *count);
 const BwdEntry *bwd_table_bf16(int vec, int *count);
 
-// Kernels for rows of an odd number of elements whose [M, N] tensors are
-// aligned to two elements (odd.hpp): each row read in aligned pairs from its
-// first even element, plus one element by itself; shape capacity = the
-// pairs' elements, N - 1.
-const FwdEntry *fwd_odd_table_f32(int *count);
-const FwdEntry *fwd_odd_table_bf16(int *count);
-const BwdEntry *bwd_odd_table_f32(int *count);
-const BwdEntry *bwd_odd_table_bf16(int *count);
-const SoftmaxEntry *softmax_odd_table_f32(int *count);
-const SoftmaxEntry *softmax_odd_table_bf16(int *count);
+// Kernels for rows whose length is an odd multiple of a unit of U elements
+// (U = 1: odd N; 2: N = 2 mod 4; 4: bf16 N = 4 mod 8) and whose [M, N]
+// tensors are aligned to 2U elements (odd.hpp): each row read in aligned
+// vectors of 2U from its first such element, plus one unit by itself; shape
+// capacity = the vectors' elements, N - U.  One table per dtype and unit.
+const FwdEntry *fwd_odd_table_bf16_u1(int *count);
+const FwdEntry *fwd_odd_table_bf16_u2(int *count);
+const FwdEntry *fwd_odd_table_bf16_u4(int *count);
+const FwdEntry *fwd_odd_table_f32_u1(int *count);
+const FwdEntry *fwd_odd_table_f32_u2(int *count);
+const BwdEntry *bwd_odd_table_bf16_u1(int *count);
+const BwdEntry *bwd_odd_table_bf16_u2(int *count);
+const BwdEntry *bwd_odd_table_bf16_u4(int *count);
+const BwdEntry *bwd_odd_table_f32_u1(int *count);
+const BwdEntry *bwd_odd_table_f32_u2(int *count);
+const SoftmaxEntry *softmax_odd_table_bf16_u1(int *count);
+const SoftmaxEntry *softmax_odd_table_bf16_u2(int *count);
+const SoftmaxEntry *softmax_odd_table_bf16_u4(int *count);
+const SoftmaxEntry *softmax_odd_table_f32_u1(int *count);
+const SoftmaxEntry *softmax_odd_table_f32_u2(int *count);
 
 template <class E, size_t n>
 const E *table_of(const E (&t)[n], int *count)

@@ -1,36 +1,47 @@
-// odd.hpp -- forward, softmax and backward kernels for rows of an odd
-// number of elements, read in aligned pairs.
+// odd.hpp -- forward, softmax and backward kernels for rows whose length is
+// an odd multiple of a unit of U elements (U = 1: odd N; U = 2: N = 2 mod 4;
+// U = 4: N = 4 mod 8), read in aligned vectors of 2U elements.
 //
-// Row r of an odd length N starts at element r*N, which is even for even r
-// and odd for odd r.  With the tensors aligned to two elements, a row's
-// elements from its first even one on pair up into aligned two-element
-// accesses (4 bytes for bf16, 8 for fp32): columns 0..N-2 of an even row and
-// columns 1..N-1 of an odd one, (N - 1) / 2 pairs either way.  The one
-// element left over -- column N-1 of an even row, column 0 of an odd one --
-// is read and written by itself, by the team's first lane.  A team of LPR
-// lanes owns a row as in kernels.hpp: lane tl holds pairs j = k*LPR + tl,
-// k < VPL, starting at the row's parity (its first even element), so every
-// access instruction of a wave covers one contiguous span.  Every access
-// lies inside its row: no range check is relied on beyond the matrix's end.
+// Row r of such an N starts at element r*N, a multiple of 2U for even r and
+// an odd multiple of U for odd r.  With the tensors aligned to 2U elements,
+// a row's elements from its first 2U-aligned one on group into aligned
+// vectors of 2U: columns 0..N-U-1 of an even row, U..N-1 of an odd one,
+// (N - U) / (2U) vectors either way.  The unit left over -- columns N-U..N-1
+// of an even row, 0..U-1 of an odd one -- is read and written by itself, by
+// the team's first lane.  The vectors are twice the width the row's length
+// alone allows (bf16: 4, 8 or 16 bytes for U = 1, 2, 4; fp32: 8 or 16 for
+// U = 1, 2).  A team of LPR lanes owns a row as in kernels.hpp: lane tl holds
+// vectors j = k*LPR + tl, k < VPL, from the row's first aligned element on,
+// so every access instruction of a wave covers one contiguous span.  Every
+// access lies inside its row: no range check is relied on beyond the
+// matrix's end.
 //
-// Against the single-element kernels this halves the access instructions
-// and keeps the per-element work of the paired (4-byte) kernels; the price
-// is the per-row parity of the columns a lane holds, so the per-column
-// vectors are staged in LDS, read per column (two 16-bit or 32-bit LDS
-// reads per pair, the pair's first column being odd in odd rows).
+// The columns a lane holds move by U with the row's parity, so the
+// per-column vectors are staged in LDS per column and read U columns at a
+// time (one aligned LDS read each: the columns of a unit start on a multiple
+// of U).
 #pragma once
 
 #include "kernels.hpp"
 
 namespace nf {
 
-// One per-column vector staged in LDS, one entry per column (neutral past N
-// or where absent): bf16 vectors as their 16-bit patterns, fp32 ones as
-// floats.  fetch() issues this thread's loads, put() converts and stores
-// them (two phases, so that the first rows' loads go out between).
-template <typename T, int PE, int WG>
+// Columns staged as fp32 up to this many (12 bytes a column for the three
+// vectors); bf16 vectors past it, and those of the U = 1 kernels, as their
+// 16-bit patterns (6 bytes a column).
+constexpr int ODD_F32_STAGE_MAX = 4096;
+
+template <typename T, int U, int PE>
+using odd_stage_t =
+    typename std::conditional<sizeof(T) == 2 && (U == 1 || PE > ODD_F32_STAGE_MAX + U), uint16_t,
+                              float>::type;
+
+// One per-column vector staged in LDS as S, one entry per column (neutral
+// past N or where absent).  fetch() issues this thread's loads, put()
+// converts and stores them (two phases, so that the first rows' loads go
+// out between).
+template <typename T, typename S, int PE, int WG>
 struct OddStage {
-    using S = typename std::conditional<sizeof(T) == 2, uint16_t, float>::type;
     static constexpr int SI = (PE + WG - 1) / WG;
     typename VecIO<T, 1>::Raw r[SI];
 
@@ -56,7 +67,7 @@ struct OddStage {
                 if (zero_centred)
                     VecIO<T, 1>::unpack(plus_one<T, 1>(&v), &v);
                 v = src != nullptr && c < N ? v : neutral;
-                if constexpr (sizeof(T) == 2)
+                if constexpr (sizeof(S) == 2)
                     dst[c] = uint16_t(__float_as_uint(v) >> 16); // exact: v is a bf16 value
                 else
                     dst[c] = v;
@@ -65,76 +76,115 @@ struct OddStage {
     }
 };
 
-// The staged value of column c.
-template <typename S>
-__device__ __forceinline__ float odd_param(const S *base, int c)
+// The staged values of columns c .. c+U-1 (c a multiple of U), in one LDS
+// read.
+template <int U, typename S>
+__device__ __forceinline__ void odd_params(const S *base, int c, float *out)
 {
-    if constexpr (sizeof(S) == 2)
-        return __uint_as_float(uint32_t(base[c]) << 16);
-    else
-        return base[c];
+    if constexpr (sizeof(S) == 4) {
+        if constexpr (U == 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(base + c);
+            out[0] = v.x;
+            out[1] = v.y;
+            out[2] = v.z;
+            out[3] = v.w;
+        } else if constexpr (U == 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(base + c);
+            out[0] = v.x;
+            out[1] = v.y;
+        } else {
+            out[0] = base[c];
+        }
+    } else {
+        if constexpr (U == 4) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(base + c);
+            out[0] = bf16_lo(w.x);
+            out[1] = bf16_hi(w.x);
+            out[2] = bf16_lo(w.y);
+            out[3] = bf16_hi(w.y);
+        } else if constexpr (U == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(base + c);
+            out[0] = bf16_lo(w);
+            out[1] = bf16_hi(w);
+        } else {
+            out[0] = __uint_as_float(uint32_t(base[c]) << 16);
+        }
+    }
 }
 
-// Whether the odd-row forward keeps the next row group's loads in flight
-// (wide teams, as fwd_prefetch; the per-column vectors are always in LDS).
-template <typename T, int LPR, int VPL, int TEAMS>
+// Whether the forward keeps the next row group's loads in flight (wide
+// teams, as fwd_prefetch; the per-column vectors are always in LDS).
+template <typename T, int U, int LPR, int VPL, int TEAMS>
 constexpr bool odd_prefetch()
 {
-    constexpr int raw = 2 * int(sizeof(T)) / 4;
+    constexpr int raw = 2 * U * int(sizeof(T)) / 4;
     constexpr int waves_per_simd = (LPR * TEAMS / 64 + 3) / 4;
     constexpr int share = 512 / waves_per_simd;
     return LPR >= WIDE_LPR && 4 * VPL * raw + 28 <= share;
 }
 
-// Where a lane's accesses of one row group go: the byte offsets of its pairs
-// and of the leftover element (lane 0 of the team only; BUF_OOB elsewhere)
-// inside the group, and the column of its pair k = 0 and of the leftover.
-template <typename T, int LPR, int VPL>
+// Where a lane's accesses of one row group go: the byte offsets of its
+// vectors and of the leftover unit (lane 0 of the team only; BUF_OOB
+// elsewhere) inside the group, and the first column of its vector k = 0
+// and of the leftover.
+template <typename T, int U, int LPR, int VPL>
 struct OddRow {
     uint32_t off[VPL], off1;
     int c0, c1;
     __device__ __forceinline__ OddRow(int team, int tl, int N, int64_t row)
     {
         const int par = int(row & 1);
-        const int np = (N - 1) / 2;
-        c0 = par + 2 * tl;
-        c1 = par ? 0 : N - 1;
+        const int nv = (N - U) / (2 * U);
+        c0 = par * U + 2 * U * tl;
+        c1 = par ? 0 : N - U;
         const uint32_t base = uint32_t(team) * uint32_t(N);
 #pragma unroll
         for (int k = 0; k < VPL; ++k)
-            off[k] = k * LPR + tl < np ? (base + uint32_t(c0 + 2 * k * LPR)) * uint32_t(sizeof(T))
-                                       : BUF_OOB;
+            off[k] = k * LPR + tl < nv
+                         ? (base + uint32_t(c0 + 2 * U * k * LPR)) * uint32_t(sizeof(T))
+                         : BUF_OOB;
         off1 = tl == 0 ? (base + uint32_t(c1)) * uint32_t(sizeof(T)) : BUF_OOB;
     }
 };
 
+// LDS rows of the three staged per-column vectors, each on a 16-byte
+// boundary (the U = 4 reads of fp32 are 16 bytes).
+template <typename S, int PE>
+struct OddRows {
+    static constexpr int STRIDE = (PE + 7) & ~7;
+    static constexpr int SIZE = 3 * STRIDE;
+};
+
 // ---------------------------------------------------------------------------
-// Forward on rows of an odd length: as fwd_kernel -- t = (x + bias) +
-// residual, u = round(t) -> residual_out, two-pass statistics of u from
-// registers (the mean as an fp32 pair), y = normalise(u) * gamma + beta -> y
-// (or FP8 codes), running max |y| -- on pairs plus the leftover element.
+// Forward: as fwd_kernel -- t = (x + bias) + residual, u = round(t) ->
+// residual_out, two-pass statistics of u from registers (the mean as an
+// fp32 pair), y = normalise(u) * gamma + beta -> y (or FP8 codes), running
+// max |y| -- on the row's vectors plus its leftover unit.
 // ---------------------------------------------------------------------------
-template <typename T, int LPR, int VPL, int TEAMS, bool RMS, bool F8>
+template <typename T, int U, int LPR, int VPL, int TEAMS, bool RMS, bool F8>
 __global__ void __launch_bounds__(LPR *TEAMS) fwd_odd_kernel(const FwdArgs a)
 {
-    using IO = VecIO<T, 2>;
-    using BIO = BufIO<T, 2>;
-    using IO1 = VecIO<T, 1>;
-    using BIO1 = BufIO<T, 1>;
+    constexpr int VE = 2 * U; // elements per vector
+    using IO = VecIO<T, VE>;
+    using BIO = BufIO<T, VE>;
+    using IO1 = VecIO<T, U>;
+    using BIO1 = BufIO<T, U>;
     using Raw = typename IO::Raw;
     using Raw1 = typename IO1::Raw;
     using Acc = typename std::conditional<std::is_same<T, float>::value, double, float>::type;
     constexpr int WG = LPR * TEAMS;
-    constexpr int PE = 2 * LPR * VPL + 1; // columns staged: the longest row
-    constexpr bool PREFETCH = odd_prefetch<T, LPR, VPL, TEAMS>();
-    using Stage = OddStage<T, PE, WG>;
-    using S = typename Stage::S;
+    constexpr int PE = VE * LPR * VPL + U; // columns staged: the longest row
+    constexpr bool PREFETCH = odd_prefetch<T, U, LPR, VPL, TEAMS>();
+    using S = odd_stage_t<T, U, PE>;
+    using Stage = OddStage<T, S, PE, WG>;
+    using Rows = OddRows<S, PE>;
     static_assert(WG % 64 == 0, "workgroup of whole waves");
 
     __shared__ float red_lds[TeamLds<LPR, TEAMS, 1>::size];
     __shared__ double red_lds_f64[TeamLds<LPR, TEAMS, 1>::size];
     __shared__ float max_lds[WG / 64];
-    __shared__ __attribute__((aligned(16))) S par[3 * PE];
+    __shared__ __attribute__((aligned(16))) S par[Rows::SIZE];
+    S *const pb = par, *const pg = par + Rows::STRIDE, *const pe = par + 2 * Rows::STRIDE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -150,7 +200,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_odd_kernel(const FwdArgs a)
     Raw1 xn1, rn1;
     auto issue = [&](int64_t g) {
         const RowGroup rg(g, TEAMS, a.M, N, sizeof(T));
-        const OddRow<T, LPR, VPL> o(team, tl, N, rg.r0 + team);
+        const OddRow<T, U, LPR, VPL> o(team, tl, N, rg.r0 + team);
         const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + rg.byte0, rg.bytes);
         const rsrc_t rs = make_rsrc(has_res ? static_cast<const char *>(a.res) + rg.byte0 : nullptr,
                                     has_res ? rg.bytes : 0u);
@@ -160,7 +210,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_odd_kernel(const FwdArgs a)
             rn[k] = has_res ? BIO::load(rs, o.off[k]) : IO::zero();
         }
         xn1 = BIO1::load(xs, o.off1);
-        rn1 = has_res ? BIO1::load(rs, o.off1) : Raw1(0);
+        rn1 = has_res ? BIO1::load(rs, o.off1) : IO1::zero();
     };
     const GroupWalk walk(a.K, a.A);
     {
@@ -169,12 +219,12 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_odd_kernel(const FwdArgs a)
         sg.fetch(a.gamma, N, tid);
         se.fetch(a.beta, N, tid);
         issue(walk.group(0));
-        sb.put(par, a.bias, N, 0.f, tid);
-        sg.put(par + PE, a.gamma, N, 1.f, tid, a.zero_centred);
-        se.put(par + 2 * PE, a.beta, N, 0.f, tid);
+        sb.put(pb, a.bias, N, 0.f, tid);
+        sg.put(pg, a.gamma, N, 1.f, tid, a.zero_centred);
+        se.put(pe, a.beta, N, 0.f, tid);
         __syncthreads();
     }
-    const int np = (N - 1) / 2;
+    const int nv = (N - U) / (2 * U);
 
     float lane_max = 0.f;
     int parity = 0;
@@ -199,42 +249,56 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_odd_kernel(const FwdArgs a)
         const int64_t next = walk.group(kk + 1);
         if (PREFETCH && kk + 1 < a.K && next < a.n_groups)
             issue(next);
-        const OddRow<T, LPR, VPL> o(team, tl, N, row);
+        const OddRow<T, U, LPR, VPL> o(team, tl, N, row);
 
         // fused add and the row sum (fp64 for fp32 rows, as fwd_kernel);
-        // pairs past the row and the leftover outside lane 0 take no part
+        // vectors past the row and the leftover outside lane 0 take no part
         // (their x and residual read as zeros, but not the bias)
         Acc sum = Acc(0);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            float t[2];
+            float t[VE];
             IO::unpack(ur[k], t);
             if (fused_add) {
-                const int c = o.c0 + 2 * k * LPR;
-                float r[2];
+                const int c = o.c0 + VE * k * LPR;
+                float r[VE], bv[VE];
                 IO::unpack(rr[k], r);
-                t[0] = (t[0] + odd_param(par, c)) + r[0];
-                t[1] = (t[1] + odd_param(par, c + 1)) + r[1];
+                odd_params<U>(pb, c, bv);
+                odd_params<U>(pb, c + U, bv + U);
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    t[e] = (t[e] + bv[e]) + r[e];
                 ur[k] = IO::pack(t);
                 IO::unpack(ur[k], t);
             }
-            if constexpr (!RMS)
-                if (k * LPR + tl < np)
-                    sum += Acc(t[0]) + Acc(t[1]);
+            if constexpr (!RMS) {
+                if (k * LPR + tl < nv) {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e)
+                        sum += Acc(t[e]);
+                }
+            }
         }
         {
-            float t[1];
+            float t[U];
             IO1::unpack(ur1, t);
             if (fused_add) {
-                float r[1];
+                float r[U], bv[U];
                 IO1::unpack(rr1, r);
-                t[0] = (t[0] + odd_param(par, o.c1)) + r[0];
+                odd_params<U>(pb, o.c1, bv);
+#pragma unroll
+                for (int e = 0; e < U; ++e)
+                    t[e] = (t[e] + bv[e]) + r[e];
                 ur1 = IO1::pack(t);
                 IO1::unpack(ur1, t);
             }
-            if constexpr (!RMS)
-                if (tl == 0)
-                    sum += Acc(t[0]);
+            if constexpr (!RMS) {
+                if (tl == 0) {
+#pragma unroll
+                    for (int e = 0; e < U; ++e)
+                        sum += Acc(t[e]);
+                }
+            }
         }
         if (a.res_out) {
             const rsrc_t os = make_rsrc(static_cast<char *>(a.res_out) + rg.byte0, rg.bytes);
@@ -267,18 +331,24 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_odd_kernel(const FwdArgs a)
         float d2[1] = {0.f};
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            if (k * LPR + tl < np) {
-                float u[2];
+            if (k * LPR + tl < nv) {
+                float u[VE];
                 IO::unpack(ur[k], u);
-                const float e0 = u[0] - mean, e1 = u[1] - mean;
-                d2[0] = fmaf(e0, e0, fmaf(e1, e1, d2[0]));
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    const float d = u[e] - mean;
+                    d2[0] = fmaf(d, d, d2[0]);
+                }
             }
         }
         if (tl == 0) {
-            float u[1];
+            float u[U];
             IO1::unpack(ur1, u);
-            const float e = u[0] - mean;
-            d2[0] = fmaf(e, e, d2[0]);
+#pragma unroll
+            for (int e = 0; e < U; ++e) {
+                const float d = u[e] - mean;
+                d2[0] = fmaf(d, d, d2[0]);
+            }
         }
         team_sum<LPR, TEAMS, 1>(d2, red_lds, parity, team, wave_in_team, lane);
         if constexpr (RMS)
@@ -297,42 +367,55 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_odd_kernel(const FwdArgs a)
                              : make_rsrc(static_cast<char *>(a.y) + rg.byte0, rg.bytes);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            const int c = o.c0 + 2 * k * LPR;
-            float u[2], yv[2];
+            const int c = o.c0 + VE * k * LPR;
+            float u[VE], gv[VE], bv[VE], yv[VE];
             IO::unpack(ur[k], u);
+            odd_params<U>(pg, c, gv);
+            odd_params<U>(pg, c + U, gv + U);
+            odd_params<U>(pe, c, bv);
+            odd_params<U>(pe, c + U, bv + U);
 #pragma unroll
-            for (int e = 0; e < 2; ++e)
-                yv[e] = fmaf(fmaf(u[e] - mean, rstd, lo_r), odd_param(par + PE, c + e),
-                             odd_param(par + 2 * PE, c + e));
+            for (int e = 0; e < VE; ++e)
+                yv[e] = fmaf(fmaf(u[e] - mean, rstd, lo_r), gv[e], bv[e]);
             if constexpr (F8) {
-                float q[2];
+                float q[VE];
                 IO::unpack(IO::pack(yv), q);
-                q[0] *= y_scale;
-                q[1] *= y_scale;
-                store_e4m3<2>(ys, o.off[k] == BUF_OOB ? BUF_OOB : o.off[k] / uint32_t(sizeof(T)), q,
-                              wt);
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    q[e] *= y_scale;
+                store_e4m3<VE>(ys, o.off[k] == BUF_OOB ? BUF_OOB : o.off[k] / uint32_t(sizeof(T)),
+                               q, wt);
             } else {
                 BIO::store(ys, o.off[k], IO::pack(yv), wt);
             }
-            if (rv && k * LPR + tl < np)
-                lane_max = fmaxf(lane_max, fmaxf(fabsf(yv[0]), fabsf(yv[1])));
+            if (rv && k * LPR + tl < nv) {
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    lane_max = fmaxf(lane_max, fabsf(yv[e]));
+            }
         }
         if (tl == 0) {
-            float u[1], yv[1];
+            float u[U], gv[U], bv[U], yv[U];
             IO1::unpack(ur1, u);
-            yv[0] = fmaf(fmaf(u[0] - mean, rstd, lo_r), odd_param(par + PE, o.c1),
-                         odd_param(par + 2 * PE, o.c1));
+            odd_params<U>(pg, o.c1, gv);
+            odd_params<U>(pe, o.c1, bv);
+#pragma unroll
+            for (int e = 0; e < U; ++e)
+                yv[e] = fmaf(fmaf(u[e] - mean, rstd, lo_r), gv[e], bv[e]);
             if constexpr (F8) {
-                float q[1];
+                float q[U];
                 IO1::unpack(IO1::pack(yv), q);
-                q[0] *= y_scale;
-                store_e4m3<1>(ys, o.off1 / uint32_t(sizeof(T)), q, wt);
+#pragma unroll
+                for (int e = 0; e < U; ++e)
+                    q[e] *= y_scale;
+                store_e4m3<U>(ys, o.off1 / uint32_t(sizeof(T)), q, wt);
             } else {
                 BIO1::store(ys, o.off1, IO1::pack(yv), wt);
             }
-            if (rv)
-                lane_max = fmaxf(lane_max, fabsf(yv[0]));
             if (rv) {
+#pragma unroll
+                for (int e = 0; e < U; ++e)
+                    lane_max = fmaxf(lane_max, fabsf(yv[e]));
                 if (a.mean)
                     a.mean[row] = mean;
                 if (a.rstd)
@@ -353,7 +436,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_odd_kernel(const FwdArgs a)
             for (int w = 1; w < WG / 64; ++w)
                 mm = fmaxf(mm, max_lds[w]);
             float r[1] = {mm};
-            IO1::unpack(IO1::pack(r), r); // max of the stored y
+            VecIO<T, 1>::unpack(VecIO<T, 1>::pack(r), r); // max of the stored y
             const unsigned bits = __float_as_uint(r[0]);
             if (a.amax_ws == nullptr)
                 atomicMax(a.amax, bits); // *amax was zeroed by a kernel before this one
@@ -363,25 +446,26 @@ __global__ void __launch_bounds__(LPR *TEAMS) fwd_odd_kernel(const FwdArgs a)
     }
 }
 
-template <typename T, int LPR, int VPL, int TEAMS, bool RMS, bool F8>
+template <typename T, int U, int LPR, int VPL, int TEAMS, bool RMS, bool F8>
 hipError_t launch_fwd_odd(const FwdArgs &a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((fwd_odd_kernel<T, LPR, VPL, TEAMS, RMS, F8>), dim3(grid),
+    hipLaunchKernelGGL((fwd_odd_kernel<T, U, LPR, VPL, TEAMS, RMS, F8>), dim3(grid),
                        dim3(LPR * TEAMS), 0, s, a);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Row softmax on rows of an odd length: as softmax_kernel, on pairs plus the
-// leftover element.
+// Row softmax: as softmax_kernel, on the row's vectors plus its leftover
+// unit.
 // ---------------------------------------------------------------------------
-template <typename T, int LPR, int VPL, int TEAMS>
+template <typename T, int U, int LPR, int VPL, int TEAMS>
 __global__ void __launch_bounds__(LPR *TEAMS) softmax_odd_kernel(const SoftmaxArgs a)
 {
-    using IO = VecIO<T, 2>;
-    using BIO = BufIO<T, 2>;
-    using IO1 = VecIO<T, 1>;
-    using BIO1 = BufIO<T, 1>;
+    constexpr int VE = 2 * U;
+    using IO = VecIO<T, VE>;
+    using BIO = BufIO<T, VE>;
+    using IO1 = VecIO<T, U>;
+    using BIO1 = BufIO<T, U>;
     using Raw = typename IO::Raw;
     constexpr int WG = LPR * TEAMS;
     static_assert(WG % 64 == 0, "workgroup of whole waves");
@@ -394,7 +478,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) softmax_odd_kernel(const SoftmaxAr
     const int tl = tid % LPR;
     const int wave_in_team = LPR > 64 ? tl / 64 : 0;
     const int N = a.N;
-    const int np = (N - 1) / 2;
+    const int nv = (N - U) / (2 * U);
 
     int parity = 0;
     const GroupWalk walk(a.K, a.A);
@@ -403,39 +487,50 @@ __global__ void __launch_bounds__(LPR *TEAMS) softmax_odd_kernel(const SoftmaxAr
         if (grp >= a.n_groups)
             break; // uniform over the workgroup
         const RowGroup rg(grp, TEAMS, a.M, N, sizeof(T));
-        const OddRow<T, LPR, VPL> o(team, tl, N, rg.r0 + team);
+        const OddRow<T, U, LPR, VPL> o(team, tl, N, rg.r0 + team);
         const bool wt = grp >= a.wt_group;
         const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + rg.byte0, rg.bytes);
         Raw xr[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k)
             xr[k] = BIO::load(xs, o.off[k]);
-        float x1[1];
+        float x1[U];
         IO1::unpack(BIO1::load(xs, o.off1), x1);
 
-        // row max (pairs past the row and the leftover outside lane 0 take
-        // no part)
-        float m[1] = {tl == 0 ? x1[0] : -INFINITY};
+        // row max (vectors past the row and the leftover outside lane 0
+        // take no part)
+        float m[1] = {-INFINITY};
+        if (tl == 0) {
+#pragma unroll
+            for (int e = 0; e < U; ++e)
+                m[0] = fmaxf(m[0], x1[e]);
+        }
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            if (k * LPR + tl < np) {
-                float v[2];
+            if (k * LPR + tl < nv) {
+                float v[VE];
                 IO::unpack(xr[k], v);
-                m[0] = fmaxf(m[0], fmaxf(v[0], v[1]));
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    m[0] = fmaxf(m[0], v[e]);
             }
         }
         team_reduce<LPR, TEAMS, 1, OpMax>(m, red_lds, parity, team, wave_in_team, lane);
 
-        float ev[VPL][2];
-        float e1 = tl == 0 ? __expf(x1[0] - m[0]) : 0.f;
-        float sum[1] = {e1};
+        float ev[VPL][VE], e1[U];
+        float sum[1] = {0.f};
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+            e1[e] = tl == 0 ? __expf(x1[e] - m[0]) : 0.f;
+            sum[0] += e1[e];
+        }
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            float v[2];
+            float v[VE];
             IO::unpack(xr[k], v);
-            const bool ok = k * LPR + tl < np;
+            const bool ok = k * LPR + tl < nv;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
+            for (int e = 0; e < VE; ++e) {
                 ev[k][e] = ok ? __expf(v[e] - m[0]) : 0.f;
                 sum[0] += ev[k][e];
             }
@@ -446,53 +541,57 @@ __global__ void __launch_bounds__(LPR *TEAMS) softmax_odd_kernel(const SoftmaxAr
         const rsrc_t ys = make_rsrc(static_cast<char *>(a.y) + rg.byte0, rg.bytes);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            ev[k][0] *= inv;
-            ev[k][1] *= inv;
+#pragma unroll
+            for (int e = 0; e < VE; ++e)
+                ev[k][e] *= inv;
             BIO::store(ys, o.off[k], IO::pack(ev[k]), wt);
         }
-        e1 *= inv;
-        BIO1::store(ys, o.off1, IO1::pack(&e1), wt);
+#pragma unroll
+        for (int e = 0; e < U; ++e)
+            e1[e] *= inv;
+        BIO1::store(ys, o.off1, IO1::pack(e1), wt);
     }
 }
 
-template <typename T, int LPR, int VPL, int TEAMS>
+template <typename T, int U, int LPR, int VPL, int TEAMS>
 hipError_t launch_softmax_odd(const SoftmaxArgs &a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((softmax_odd_kernel<T, LPR, VPL, TEAMS>), dim3(grid), dim3(LPR * TEAMS),
+    hipLaunchKernelGGL((softmax_odd_kernel<T, U, LPR, VPL, TEAMS>), dim3(grid), dim3(LPR * TEAMS),
                        0, s, a);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Backward stage 1 on rows of an odd length: as bwd_kernel (one load of dy
-// and x per row, the row sums give dx, the column sums are accumulated over
-// the workgroup's rows and written as its partial row), on pairs plus the
-// leftover element.  Workgroups hold an even number of teams and row groups
-// start on even rows, so each team keeps one row parity and with it one set
-// of columns for its whole walk: its column sums stay in registers, one per
+// Backward stage 1: as bwd_kernel (one load of dy and x per row, the row
+// sums give dx, the column sums are accumulated over the workgroup's rows
+// and written as its partial row), on the row's vectors plus its leftover
+// unit.  Workgroups hold an even number of teams and row groups start on
+// even rows, so each team keeps one row parity and with it one set of
+// columns for its whole walk: its column sums stay in registers, one per
 // element as in bwd_kernel (plus the leftover's on the team's first lane).
 // The teams' sums meet in LDS by column, added in team order, and the
 // workgroup stores the partial row from there.
 // ---------------------------------------------------------------------------
-template <typename T, int LPR, int VPL, int TEAMS, bool RMS, bool DB>
+template <typename T, int U, int LPR, int VPL, int TEAMS, bool RMS, bool DB>
 __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
 {
-    using IO = VecIO<T, 2>;
-    using BIO = BufIO<T, 2>;
-    using IO1 = VecIO<T, 1>;
-    using BIO1 = BufIO<T, 1>;
+    constexpr int VE = 2 * U;
+    using IO = VecIO<T, VE>;
+    using BIO = BufIO<T, VE>;
+    using IO1 = VecIO<T, U>;
+    using BIO1 = BufIO<T, U>;
     using Raw = typename IO::Raw;
     using Raw1 = typename IO1::Raw;
     constexpr int WG = LPR * TEAMS;
-    constexpr int PE = 2 * LPR * VPL + 1; // columns staged: the longest row
-    constexpr int NB = DB ? 3 : 2;        // column sums: dgamma, dbeta (, dbias)
-    using Stage = OddStage<T, PE, WG>;
-    using S = typename Stage::S;
+    constexpr int PE = VE * LPR * VPL + U; // columns staged: the longest row
+    constexpr int NB = DB ? 3 : 2;         // column sums: dgamma, dbeta (, dbias)
+    using S = odd_stage_t<T, U, PE>;
+    using Stage = OddStage<T, S, PE, WG>;
     static_assert(TEAMS % 2 == 0, "each team keeps one row parity");
-    static_assert(LPR % 64 == 0, "teams of whole waves");
+    static_assert(WG % 64 == 0, "workgroup of whole waves");
 
     __shared__ float red_lds[TeamLds<LPR, TEAMS, 2>::size];
-    __shared__ __attribute__((aligned(16))) S par[PE];
+    __shared__ __attribute__((aligned(16))) S par[(PE + 7) & ~7];
     __shared__ float col_lds[NB * PE];
 
     const int tid = threadIdx.x;
@@ -501,10 +600,10 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
     const int tl = tid % LPR;
     const int wave_in_team = LPR > 64 ? tl / 64 : 0;
     const int N = a.N;
-    const int np = (N - 1) / 2;
+    const int nv = (N - U) / (2 * U);
     const bool recompute = RMS && a.rstd == nullptr;
     // rows r0 + team with r0 even: the team's parity is its own
-    const OddRow<T, LPR, VPL> o(team, tl, N, team);
+    const OddRow<T, U, LPR, VPL> o(team, tl, N, team);
 
     Raw xr[VPL], dr[VPL];
     Raw1 x1, d1;
@@ -532,18 +631,21 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
         __syncthreads();
     }
 
-    float ag[VPL][2], ab[VPL][2], ad[DB ? VPL : 1][2];
+    float ag[VPL][VE], ab[VPL][VE], ad[DB ? VPL : 1][VE];
 #pragma unroll
     for (int k = 0; k < VPL; ++k) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < VE; ++e) {
             ag[k][e] = 0.f;
             ab[k][e] = 0.f;
             if constexpr (DB)
                 ad[k][e] = 0.f;
         }
     }
-    float a1g = 0.f, a1b = 0.f, a1d = 0.f; // the leftover's column (team's first lane)
+    float a1g[U], a1b[U], a1d[U]; // the leftover's columns (team's first lane)
+#pragma unroll
+    for (int e = 0; e < U; ++e)
+        a1g[e] = a1b[e] = a1d[e] = 0.f;
     int parity = 0;
 
     for (int kk = 0; kk < a.K; ++kk) {
@@ -561,7 +663,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
         reload_barrier(cb);
         reload_barrier(cl);
 
-        // Row sums, g = dy * gamma (pairs past the row and the leftover
+        // Row sums, g = dy * gamma (vectors past the row and the leftover
         // outside the first lane read dy = 0, so g = 0):
         //   LN : s0 = sum g (x - mean), s1 = sum g
         //   RMS: s0 = sum g x; without rstd also s1 = sum x^2
@@ -579,18 +681,24 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
         };
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            const int c = cb + 2 * k * LPR;
-            float xv[2], dv[2];
+            const int c = cb + VE * k * LPR;
+            float xv[VE], dv[VE], gv[VE];
             IO::unpack(xr[k], xv);
             IO::unpack(dr[k], dv);
-            row_sums(xv[0], dv[0], odd_param(par, c));
-            row_sums(xv[1], dv[1], odd_param(par, c + 1));
+            odd_params<U>(par, c, gv);
+            odd_params<U>(par, c + U, gv + U);
+#pragma unroll
+            for (int e = 0; e < VE; ++e)
+                row_sums(xv[e], dv[e], gv[e]);
         }
         {
-            float xv[1], dv[1];
+            float xv[U], dv[U], gv[U];
             IO1::unpack(x1, xv);
             IO1::unpack(d1, dv);
-            row_sums(xv[0], dv[0], odd_param(par, cl));
+            odd_params<U>(par, cl, gv);
+#pragma unroll
+            for (int e = 0; e < U; ++e)
+                row_sums(xv[e], dv[e], gv[e]);
         }
         team_sum<LPR, TEAMS, 2>(s, red_lds, parity, team, wave_in_team, lane);
         if (recompute)
@@ -600,7 +708,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
         const float c2 = RMS ? 0.f : s[1] / float(N);
         const float k1 = -rstd * c1, k2 = -rstd * c2;
         // dx of one element; its column sums when the row is valid (the
-        // sums of pairs past the row are never stored)
+        // sums of vectors past the row are never stored)
         auto grad = [&](float xv, float dv, float gm, float &sg, float &sb, float &sd) {
             const float xh = RMS ? xv * rstd : (xv - mean) * rstd;
             const float dxv = fmaf(xh, k1, fmaf(dv * gm, rstd, k2));
@@ -622,28 +730,33 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
         const bool wt = grp >= a.wt_group;
 #pragma unroll
         for (int k = 0; k < VPL; ++k) {
-            const int c = cb + 2 * k * LPR;
-            float xv[2], dv[2], dxv[2], unused = 0.f;
+            const int c = cb + VE * k * LPR;
+            float xv[VE], dv[VE], gv[VE], dxv[VE], unused = 0.f;
             IO::unpack(xr[k], xv);
             IO::unpack(dr[k], dv);
+            odd_params<U>(par, c, gv);
+            odd_params<U>(par, c + U, gv + U);
 #pragma unroll
-            for (int e = 0; e < 2; ++e)
-                dxv[e] = grad(xv[e], dv[e], odd_param(par, c + e), ag[k][e], ab[k][e],
+            for (int e = 0; e < VE; ++e)
+                dxv[e] = grad(xv[e], dv[e], gv[e], ag[k][e], ab[k][e],
                               DB ? ad[DB ? k : 0][e] : unused);
             BIO::store(dxs, o.off[k], IO::pack(dxv), wt);
         }
         {
-            float xv[1], dv[1], dxv[1];
+            float xv[U], dv[U], gv[U], dxv[U];
             IO1::unpack(x1, xv);
             IO1::unpack(d1, dv);
-            dxv[0] = grad(xv[0], dv[0], odd_param(par, cl), a1g, a1b, a1d);
+            odd_params<U>(par, cl, gv);
+#pragma unroll
+            for (int e = 0; e < U; ++e)
+                dxv[e] = grad(xv[e], dv[e], gv[e], a1g[e], a1b[e], a1d[e]);
             BIO1::store(dxs, o.off1, IO1::pack(dxv), wt);
         }
     }
 
     // ---- fold the teams' column sums in LDS by column, in team order ----
-    // Every team covers every column (its pairs and its leftover), so team
-    // 0 writes each column and the others add to it.
+    // Every team covers every column (its vectors and its leftover), so
+    // team 0 writes each column and the others add to it.
     for (int t = 0; t < TEAMS; ++t) {
         if (team == t) {
             auto put = [&](int b, int c, float v) {
@@ -652,10 +765,10 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
             };
 #pragma unroll
             for (int k = 0; k < VPL; ++k) {
-                if (k * LPR + tl < np) {
-                    const int c = o.c0 + 2 * k * LPR;
+                if (k * LPR + tl < nv) {
+                    const int c = o.c0 + VE * k * LPR;
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
+                    for (int e = 0; e < VE; ++e) {
                         put(0, c + e, ag[k][e]);
                         put(1, c + e, ab[k][e]);
                         if constexpr (DB)
@@ -664,10 +777,13 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
                 }
             }
             if (tl == 0) {
-                put(0, o.c1, a1g);
-                put(1, o.c1, a1b);
-                if constexpr (DB)
-                    put(2, o.c1, a1d);
+#pragma unroll
+                for (int e = 0; e < U; ++e) {
+                    put(0, o.c1 + e, a1g[e]);
+                    put(1, o.c1 + e, a1b[e]);
+                    if constexpr (DB)
+                        put(2, o.c1 + e, a1d[e]);
+                }
             }
         }
         __syncthreads();
@@ -681,10 +797,10 @@ __global__ void __launch_bounds__(LPR *TEAMS) bwd_odd_kernel(const BwdArgs a)
     }
 }
 
-template <typename T, int LPR, int VPL, int TEAMS, bool RMS, bool DB>
+template <typename T, int U, int LPR, int VPL, int TEAMS, bool RMS, bool DB>
 hipError_t launch_bwd_odd(const BwdArgs &a, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((bwd_odd_kernel<T, LPR, VPL, TEAMS, RMS, DB>), dim3(grid),
+    hipLaunchKernelGGL((bwd_odd_kernel<T, U, LPR, VPL, TEAMS, RMS, DB>), dim3(grid),
                        dim3(LPR * TEAMS), 0, s, a);
     return hipGetLastError();
 }

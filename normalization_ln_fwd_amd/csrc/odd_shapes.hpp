@@ -1,10 +1,15 @@
-// odd_shapes.hpp -- shapes of the odd-row kernels (odd.hpp), as
-// X(T, 2, LPR, VPL, TEAMS) lists ordered by capacity LPR * VPL * 2, the
-// elements of a row's pairs (N - 1).  Steps of a third to a half: a row
-// just past one capacity leaves at most a third of the lanes of the next
-// idle (16384 x 6001 bf16 on 512 lanes holding 8 pairs each, 73% of them
-// busy: 250 us against 230 us on the single-element kernels).
+// odd_shapes.hpp -- shapes of the kernels for rows of an odd multiple of a
+// unit of U elements (odd.hpp), as X(T, 2U, LPR, VPL, TEAMS) lists ordered
+// by capacity LPR * VPL * 2U, the elements of a row's vectors (N - U).
+// Unit 1 (odd N) below, in steps of a third to a half: a row just past one
+// capacity leaves at most a third of the lanes of the next idle (16384 x
+// 6001 bf16 on 512 lanes holding 8 pairs each, 73% of them busy: 250 us
+// against 230 us on the single-element kernels).  Units 2 and 4 take the
+// vector layouts of shapes.hpp for their vector width, the backward's with
+// an even number of teams.
 #pragma once
+
+#include "shapes.hpp"
 
 #define NF_SHAPES_ODD(X, T)                                                                      \
     X(T, 2, 16, 4, 16)                                                                           \
@@ -47,3 +52,64 @@
     X(T, 2, 320, 8, 2)                                                                           \
     X(T, 2, 384, 8, 2)                                                                           \
     X(T, 2, 512, 8, 2)
+
+// Units 2 and 4 (vectors of 4 or 8 elements): the narrow layouts of
+// shapes.hpp, wide teams holding one vector per lane, then one team of 512,
+// 640 or 768 lanes holding 2 or 4 vectors.  Measured on MI355X (bf16, us):
+// one vector per lane on 640 or 768 lanes is slower than two on 512
+// (8192 x 5124 forward 78 against 67, 8192 x 6004 softmax 43 against 35),
+// and so are 1024 lanes holding 4 (8192 x 9002 forward 163 against 139 on
+// 640 lanes).  The softmax, with no parameters to stage, prefers 4 vectors
+// on 512 lanes to 2 on 768 (8192 x 6002: 36 against 43 us).
+#define NF_SHAPES_ODD_U4_BF16(X)                                                                 \
+    NF_SHAPES_NARROW(X, bf16, 8)                                                                 \
+    NF_SHAPES_WIDE_ONE_VEC(X, bf16, 8)                                                           \
+    X(bf16, 8, 512, 2, 1)                                                                        \
+    X(bf16, 8, 640, 2, 1)                                                                        \
+    X(bf16, 8, 768, 2, 1)                                                                        \
+    X(bf16, 8, 512, 4, 1)
+#define NF_SHAPES_ODD_U2_FWD(X, T)                                                               \
+    NF_SHAPES_NARROW(X, T, 4)                                                                    \
+    NF_SHAPES_WIDE_ONE_VEC(X, T, 4)                                                              \
+    X(T, 4, 512, 2, 1)                                                                           \
+    X(T, 4, 640, 2, 1)                                                                           \
+    X(T, 4, 768, 2, 1)                                                                           \
+    X(T, 4, 512, 4, 1)
+#define NF_SHAPES_ODD_U2_SOFTMAX(X, T)                                                           \
+    NF_SHAPES_NARROW(X, T, 4)                                                                    \
+    NF_SHAPES_WIDE_ONE_VEC(X, T, 4)                                                              \
+    X(T, 4, 512, 2, 1)                                                                           \
+    X(T, 4, 512, 4, 1)
+// beyond 8192 columns (bf16 forward, softmax of either dtype)
+#define NF_SHAPES_ODD_U2_WIDE(X, T)                                                              \
+    X(T, 4, 640, 4, 1)                                                                           \
+    X(T, 4, 768, 4, 1)                                                                           \
+    X(T, 4, 1024, 4, 1)
+// The backward: the narrow layouts, then two teams of 512 lanes per
+// workgroup (each team keeps one row parity) holding 1, 2 or (unit 2) 4
+// vectors; narrower wide teams measured slower than the vector kernel.
+#define NF_SHAPES_ODD_U4_BF16_BWD(X)                                                             \
+    NF_SHAPES_NARROW(X, bf16, 8)                                                                 \
+    X(bf16, 8, 512, 1, 2)                                                                        \
+    X(bf16, 8, 512, 2, 2)
+#define NF_SHAPES_ODD_U2_BWD(X, T)                                                               \
+    NF_SHAPES_NARROW(X, T, 4)                                                                    \
+    X(T, 4, 512, 1, 2)                                                                           \
+    X(T, 4, 512, 2, 2)
+
+// Table entries (FwdEntry / BwdEntry / SoftmaxEntry) of one shape: the unit
+// is half the vector width VEC.
+#define NF_FWD_ODD(T, VEC, LPR, VPL, TEAMS)                                                        \
+    {{LPR, VPL, TEAMS, VEC},                                                                     \
+     &launch_fwd_odd<T, VEC / 2, LPR, VPL, TEAMS, false, false>,                                  \
+     &launch_fwd_odd<T, VEC / 2, LPR, VPL, TEAMS, true, false>,                                   \
+     &launch_fwd_odd<T, VEC / 2, LPR, VPL, TEAMS, false, true>,                                   \
+     &launch_fwd_odd<T, VEC / 2, LPR, VPL, TEAMS, true, true>},
+#define NF_BWD_ODD(T, VEC, LPR, VPL, TEAMS)                                                        \
+    {{LPR, VPL, TEAMS, VEC},                                                                     \
+     &launch_bwd_odd<T, VEC / 2, LPR, VPL, TEAMS, false, false>,                                  \
+     &launch_bwd_odd<T, VEC / 2, LPR, VPL, TEAMS, true, false>,                                   \
+     &launch_bwd_odd<T, VEC / 2, LPR, VPL, TEAMS, false, true>,                                   \
+     &launch_bwd_odd<T, VEC / 2, LPR, VPL, TEAMS, true, true>},
+#define NF_SOFTMAX_ODD(T, VEC, LPR, VPL, TEAMS)                                                    \
+    {{LPR, VPL, TEAMS, VEC}, &launch_softmax_odd<T, VEC / 2, LPR, VPL, TEAMS>},

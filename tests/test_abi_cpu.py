@@ -306,6 +306,55 @@ def test_describe_names_the_planned_kernels(lib):
     assert "bwd_split_kernel" in nf.describe("ln_bwd", 64, 16384, nf.BF16)
 
 
+def _odd_unit(op, M, N, dtype):
+    """The odd-row unit a call would take (0: another kernel)."""
+    m = re.search(r"odd_kernel<\w+, unit (\d+),", nf.describe(op, M, N, dtype))
+    return int(m.group(1)) if m else 0
+
+
+def test_describe_names_the_odd_row_kernels(lib):
+    """Rows of an odd multiple of a unit (1, 2 or, bf16, 4 elements) take the
+    odd-row kernels of that unit up to the longest row their tables hold;
+    rows of whole 16-byte vectors do not."""
+    BF16, F32 = nf.BF16, nf.F32
+    for dt in (BF16, F32):
+        for op in ("ln_fwd", "rms_fwd", "softmax_fwd"):
+            longest = 8193 if dt == F32 and op != "softmax_fwd" else 16383
+            assert _odd_unit(op, 1000, longest, dt) == 1
+            assert _odd_unit(op, 3, 1, dt) == 1
+            if longest + 2 <= 16384:
+                assert _odd_unit(op, 1000, longest + 2, dt) == 0
+            assert _odd_unit(op, 1000, 1002, dt) == 2
+            assert _odd_unit(op, 1000, 2, dt) == 2
+            assert _odd_unit(op, 1000, 1004, dt) == (4 if dt == BF16 else 0)
+            assert _odd_unit(op, 1000, 1024, dt) == 0
+    assert _odd_unit("ln_fwd", 10, 8194, F32) == 2 and _odd_unit("ln_fwd", 10, 8198, F32) == 0
+    assert _odd_unit("softmax_fwd", 10, 16382, F32) == 2
+    assert _odd_unit("ln_fwd", 10, 16380, BF16) == 4 and _odd_unit("ln_fwd", 10, 16382, BF16) == 2
+
+
+def test_describe_names_the_odd_row_backward(lib):
+    """The backward takes the odd-row kernels for odd N up to 8193 columns;
+    for units of 2 and 4 elements it takes a wide odd-row shape only where
+    that leaves fewer lanes idle than the vector kernel would."""
+    BF16, F32 = nf.BF16, nf.F32
+    for dt in (BF16, F32):
+        assert _odd_unit("ln_bwd", 1000, 8193, dt) == 1
+        assert _odd_unit("rms_bwd", 3, 1, dt) == 1
+        assert _odd_unit("ln_bwd", 1000, 8195, dt) == 0
+        assert _odd_unit("ln_bwd", 1000, 1024, dt) == 0
+        assert _odd_unit("ln_bwd", 1000, 4098, dt) == 2
+        assert _odd_unit("ln_bwd", 1000, 1002, dt) == 2      # narrow: always
+    assert _odd_unit("ln_bwd", 1000, 8194, BF16) == 2 and _odd_unit("ln_bwd", 1000, 8198, BF16) == 0
+    assert _odd_unit("ln_bwd", 1000, 4100, BF16) == 4 and _odd_unit("ln_bwd", 1000, 8196, BF16) == 4
+    assert _odd_unit("ln_bwd", 1000, 8204, BF16) == 0 and _odd_unit("ln_bwd", 1000, 4102, F32) == 0
+    # the same fill as the vector kernel's (6000 of 6144 lanes' columns)
+    assert _odd_unit("ln_bwd", 1000, 6004, BF16) == 0
+    assert _odd_unit("ln_bwd", 1000, 6002, BF16) == 0
+    # more idle lanes than the vector kernel's
+    assert _odd_unit("ln_bwd", 1000, 5124, BF16) == 0
+
+
 def test_describe_rejects(lib):
     buf = ctypes.create_string_buffer(64)
     assert lib.norm_describe(0, 4, 64, 1, 0, None, 64) == 1

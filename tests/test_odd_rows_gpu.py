@@ -1,7 +1,9 @@
-"""GPU parity of the odd-row kernels: rows of an odd length whose [M, N]
-tensors are aligned to two elements, each row read in aligned pairs from
-its first even element plus its one leftover element (forward, FP8
-forward, softmax, and the backward, whose teams each keep one row parity).
+"""GPU parity of the odd-row kernels: rows whose length is an odd multiple
+of a unit U (U = 1: odd N; U = 2: N = 2 mod 4; U = 4: bf16 N = 4 mod 8)
+and whose [M, N] tensors are aligned to 2U elements, each row read in
+aligned vectors of 2U from its first such element plus its one leftover
+unit (forward, FP8 forward, softmax, and the backward, whose teams each
+keep one row parity).
 
 Every shape the odd-row tables hold (bf16 rows up to 16383 columns, fp32
 forward rows up to 8193), N = 1, row counts of both parities and around the
@@ -13,6 +15,8 @@ off (residual_out bit-identical: the same fused-add rounding), and for
 writes outside the outputs (guard elements around each output stay
 untouched).
 """
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -38,8 +42,23 @@ SHAPES_BF16 = [(1, 1), (2, 1), (5, 1), (3, 3), (3, 7), (8, 7), (37, 129), (17, 2
                (2001, 385), (1025, 4097), (65, 1001)]
 SHAPES_F32 = [(1, 1), (2, 1), (3, 7), (8, 7), (37, 129), (17, 257), (12, 385), (40, 513),
               (9, 769), (33, 1025), (10, 1537), (31, 2049), (7, 3073), (20, 4097), (7, 5121),
-              (11, 6145), (7, 8193), (2001, 385), (5, 8195), (3, 16383)]
-CASES = [(M, N, BF16) for M, N in SHAPES_BF16] + [(M, N, F32) for M, N in SHAPES_F32]
+              (11, 6145), (7, 8193), (2001, 385), (5, 8195), (3, 16383), (3, 10243)]
+# units 2 and 4: each table's narrow and wide entries, the longest rows,
+# rows of a single leftover unit (N = 2, 4) and the same row parities
+SHAPES_BF16_U2 = [(3, 2), (5, 6), (8, 10), (37, 130), (17, 258), (12, 386), (40, 514), (33, 1026),
+                  (10, 1538), (31, 2050), (7, 3074), (20, 4098), (7, 5122), (11, 6146),
+                  (9, 8194), (5, 10242), (4, 12290), (3, 16382), (2001, 386), (1025, 4098),
+                  (9, 38), (5, 134), (7, 518), (6, 1030)]
+SHAPES_BF16_U4 = [(3, 4), (5, 12), (8, 20), (37, 132), (17, 260), (12, 388), (40, 516), (33, 1028),
+                  (10, 1540), (31, 2052), (7, 3076), (20, 4100), (7, 5124), (11, 6148),
+                  (9, 8196), (5, 10244), (4, 12292), (3, 16380), (2001, 388), (1025, 4100),
+                  (7, 524), (6, 2060)]
+SHAPES_F32_U2 = [(3, 2), (5, 6), (8, 10), (37, 130), (17, 258), (40, 514), (33, 1026),
+                 (31, 2050), (20, 4098), (7, 8194), (5, 8198), (3, 16382), (2001, 386),
+                 (9, 38), (5, 134), (7, 518), (6, 1030), (5, 1286), (4, 4102), (3, 5126),
+                 (3, 10246)]
+CASES = ([(M, N, BF16) for M, N in SHAPES_BF16 + SHAPES_BF16_U2 + SHAPES_BF16_U4] +
+         [(M, N, F32) for M, N in SHAPES_F32 + SHAPES_F32_U2])
 
 
 def _id(c):
@@ -52,21 +71,10 @@ def _gpu():
     require_gpu()
 
 
-def _odd_taken(op, M, N, dtype):
-    return "odd_kernel" in nf.describe(op, M, N, dtype)
-
-
-def test_describe_names_the_odd_row_kernels():
-    """Odd rows take the odd-row kernels up to the longest row their tables
-    hold; even rows do not."""
-    for dt in (BF16, F32):
-        for op in ("ln_fwd", "rms_fwd", "softmax_fwd"):
-            longest = 8193 if dt == F32 and op != "softmax_fwd" else 16383
-            assert _odd_taken(op, 1000, longest, dt)
-            assert _odd_taken(op, 3, 1, dt)
-            if longest + 2 <= 16384:
-                assert not _odd_taken(op, 1000, longest + 2, dt)
-            assert not _odd_taken(op, 1000, 1000, dt)
+def _unit(op, M, N, dtype):
+    """The odd-row unit a call would take (0: another kernel)."""
+    m = re.search(r"odd_kernel<\w+, unit (\d+),", nf.describe(op, M, N, dtype))
+    return int(m.group(1)) if m else 0
 
 
 @pytest.mark.parametrize("c", CASES, ids=_id)
@@ -113,7 +121,7 @@ def test_odd_forward_matches_single_element_kernels(c, rms, tuning):
     eps = 1e-6 if rms else 1e-5
     a = run_fwd(rms, inp, dtype, eps)
     tuning.setenv("NORMFUSE_PAIRS", "0")
-    assert not _odd_taken("rms_fwd" if rms else "ln_fwd", M, N, dtype)
+    assert not _unit("rms_fwd" if rms else "ln_fwd", M, N, dtype)
     b = run_fwd(rms, inp, dtype, eps)
     assert torch.equal(a["residual_out"], b["residual_out"])
     assert_rows_close(f64(a["y"]), f64(b["y"]), dtype, "y pairs vs elements", ulps=1.0)
@@ -238,7 +246,15 @@ from tolerance import assert_colsums_close, dbias_term_l2, dx_term_scale  # noqa
 BWD_SHAPES = [(1, 1), (2, 1), (3, 3), (5, 7), (8, 7), (37, 129), (17, 257), (12, 385), (40, 513),
               (9, 769), (33, 1025), (10, 1537), (31, 2049), (7, 3073), (20, 4097), (7, 5121),
               (11, 6145), (9, 8193), (6, 8191), (2001, 385), (1025, 4097), (5, 8195)]
-BWD_CASES = [(M, N, BF16) for M, N in BWD_SHAPES] + [(M, N, F32) for M, N in BWD_SHAPES]
+BWD_SHAPES_U2 = [(3, 2), (5, 6), (8, 10), (37, 130), (12, 386), (33, 1026), (31, 2050),
+                 (20, 4098), (11, 6146), (9, 8194), (2001, 386), (1025, 4098), (5, 8198),
+                 (9, 38), (5, 134), (7, 198), (6, 390), (7, 518), (6, 1030), (5, 1286),
+                 (4, 4102)]
+BWD_SHAPES_U4 = [(3, 4), (5, 12), (8, 20), (37, 132), (12, 388), (33, 1028), (31, 2052),
+                 (20, 4100), (11, 6148), (9, 8196), (2001, 388), (1025, 4100), (5, 8204),
+                 (9, 140), (7, 396), (7, 524), (6, 1036), (6, 2060), (5, 2572), (4, 4108)]
+BWD_CASES = ([(M, N, BF16) for M, N in BWD_SHAPES + BWD_SHAPES_U2 + BWD_SHAPES_U4] +
+             [(M, N, F32) for M, N in BWD_SHAPES + BWD_SHAPES_U2])
 
 
 def _check_bwd(inp, out, ref, dtype, dbias):
@@ -251,14 +267,6 @@ def _check_bwd(inp, out, ref, dtype, dbias):
     if dbias:
         l2 = np.maximum(ref["dbias_l2"], dbias_term_l2(inp["dy"], inp["gamma"], ref["rstd"], dtype))
         assert_colsums_close(f64(out["dbias"]), ref["dbias"], l2, COLSUM_REL_SMALL, "dbias")
-
-
-def test_describe_names_the_odd_row_backward():
-    for dt in (BF16, F32):
-        assert _odd_taken("ln_bwd", 1000, 8193, dt)
-        assert _odd_taken("rms_bwd", 3, 1, dt)
-        assert not _odd_taken("ln_bwd", 1000, 8195, dt)
-        assert not _odd_taken("ln_bwd", 1000, 1000, dt)
 
 
 @pytest.mark.parametrize("c", BWD_CASES, ids=_id)
@@ -294,7 +302,7 @@ def test_odd_backward_matches_single_element_kernels(c, rms, tuning):
     inp, eps = make_case(M, N, dtype, rms, seed=M + 9 * N)
     a = run_bwd(rms, inp, dtype, eps, dparam_dtype=torch.float32, want_dbias=True)
     tuning.setenv("NORMFUSE_PAIRS", "0")
-    assert not _odd_taken("rms_bwd" if rms else "ln_bwd", M, N, dtype)
+    assert not _unit("rms_bwd" if rms else "ln_bwd", M, N, dtype)
     b = run_bwd(rms, inp, dtype, eps, dparam_dtype=torch.float32, want_dbias=True)
     ref = oracle_bwd(rms, inp, dtype, eps, want_dbias=True)
     _check_bwd(inp, a, ref, dtype, True)
