@@ -499,6 +499,20 @@ norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, int uni
     if (unit && kn.pairs) {
         const SoftmaxEntry *tab = softmax_odd_table(dtype, unit, &n);
         e = pick_shape(tab, n, int(N - unit), kn.fwd_lpr, kn.fwd_vpl, kn.fwd_teams);
+        // As in the backward: on a wide team a row of 2- or 4-element units
+        // takes the odd-row softmax only where that leaves fewer lanes idle
+        // than the vector kernel (measured on MI355X, bf16, us, odd-row /
+        // vector: at the same fill 16384 x 2562 41.7 / 33.1, 16384 x 3074
+        // 42.2 / 38.2; with fewer idle lanes 16384 x 4100 51.7 / 55.1,
+        // 8192 x 12292 67.9 / 78.2).
+        if (e && vec > 1 && e->shape.lpr >= WIDE_LPR && kn.fwd_lpr == 0) {
+            int nv = 0;
+            const SoftmaxEntry *vt =
+                dtype == NORM_F32 ? softmax_table_f32(vec, &nv) : softmax_table_bf16(vec, &nv);
+            const SoftmaxEntry *v = pick_shape(vt, nv, int(N), 0, 0, 0);
+            if (v && (N - unit) * int64_t(v->shape.capacity()) <= N * int64_t(e->shape.capacity()))
+                e = nullptr;
+        }
         if (e) {
             const int K = kn.fwd_k > 0 ? kn.fwd_k
                                        : fwd_groups_per_wg(M, N, dtype, e->shape, false, false,

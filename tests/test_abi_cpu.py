@@ -329,7 +329,12 @@ def test_describe_names_the_odd_row_kernels(lib):
             assert _odd_unit(op, 1000, 1004, dt) == (4 if dt == BF16 else 0)
             assert _odd_unit(op, 1000, 1024, dt) == 0
     assert _odd_unit("ln_fwd", 10, 8194, F32) == 2 and _odd_unit("ln_fwd", 10, 8198, F32) == 0
-    assert _odd_unit("softmax_fwd", 10, 16382, F32) == 2
+    # softmax of 2- and 4-element units on a wide team only where that
+    # leaves fewer lanes idle than the vector kernel
+    assert _odd_unit("softmax_fwd", 10, 10242, F32) == 2      # 10240 of 10240 vs 12288
+    assert _odd_unit("softmax_fwd", 10, 16382, F32) == 0      # 16380 of 16384 vs 16382 of 16384
+    assert _odd_unit("softmax_fwd", 10, 4100, BF16) == 4 and _odd_unit("softmax_fwd", 10, 3076, BF16) == 0
+    assert _odd_unit("softmax_fwd", 10, 3074, BF16) == 0 and _odd_unit("ln_fwd", 10, 3074, BF16) == 2
     assert _odd_unit("ln_fwd", 10, 16380, BF16) == 4 and _odd_unit("ln_fwd", 10, 16382, BF16) == 2
 
 

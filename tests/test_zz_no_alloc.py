@@ -47,9 +47,10 @@ def _noalloc_abi(d, M, N, dbias):
 
 
 @pytest.mark.parametrize("shapes", [((8192, 4096), (3000, 4096)), ((20000, 384), (5000, 384)),
-                                    ((301, 1024), (7, 1024)), ((2001, 1001), (7, 1001))],
+                                    ((301, 1024), (7, 1024)), ((2001, 1001), (7, 1001)),
+                                    ((1025, 4100), (9, 4100)), ((2001, 386), (5, 386))],
                          ids=["8192x4096-then-3000", "20000x384-then-5000", "301x1024-then-7",
-                              "2001x1001-then-7"])
+                              "2001x1001-then-7", "1025x4100-then-9", "2001x386-then-5"])
 def test_noalloc_matches_workspace_entry_point(shapes):
     for i, ((M, N), dbias) in enumerate(zip(shapes, (True, False))):
         inp = _case(M, N, seed=M + i)
