@@ -1242,6 +1242,19 @@ __global__ void __launch_bounds__(64 * SPLIT_ROWS_PER_GROUP) bwd_split_kernel(co
 // the team takes the row max, then sum_j exp(x_j - max) with the exponentials
 // kept in registers, and stores exp(x_j - max) / sum.
 // ---------------------------------------------------------------------------
+// Whether the softmax walk keeps the next row group's loads in flight: on
+// wide teams whose lanes hold at most 16 bytes of a row, whose one load per
+// lane otherwise leaves the memory system idle through the two team
+// reductions.  Measured on MI355X (bf16, us, without / with): 26214 x 2560
+// 55.9 / 51.9, 21845 x 3072 51.4 / 46.6, 16384 x 4096 46.9 / 45.1, fp32
+// 16384 x 2048 44.7 / 43.3; lanes holding more lost up to 3% with it
+// (8192 x 12288: 66.3 / 68.2).
+template <typename T, int VEC, int LPR, int VPL, int TEAMS>
+constexpr bool softmax_prefetch()
+{
+    return LPR >= WIDE_LPR && VPL * VEC * int(sizeof(T)) <= 16;
+}
+
 template <typename T, int VEC, int LPR, int VPL, int TEAMS>
 __global__ void __launch_bounds__(LPR *TEAMS) softmax_kernel(const SoftmaxArgs a)
 {
@@ -1249,6 +1262,7 @@ __global__ void __launch_bounds__(LPR *TEAMS) softmax_kernel(const SoftmaxArgs a
     using BIO = BufIO<T, VEC>;
     using Raw = typename IO::Raw;
     constexpr int WG = LPR * TEAMS;
+    constexpr bool PREFETCH = softmax_prefetch<T, VEC, LPR, VPL, TEAMS>();
     static_assert(WG % 64 == 0, "workgroup of whole waves");
 
     __shared__ float red_lds[TeamLds<LPR, TEAMS, 1>::size];
@@ -1269,18 +1283,34 @@ __global__ void __launch_bounds__(LPR *TEAMS) softmax_kernel(const SoftmaxArgs a
                            : BUF_OOB;
     }
 
+    // x of row group g (zeros outside the matrix)
+    Raw xn[VPL];
+    auto issue = [&](int64_t g) {
+        const RowGroup rg(g, TEAMS, a.M, N, sizeof(T));
+        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + rg.byte0, rg.bytes);
+#pragma unroll
+        for (int k = 0; k < VPL; ++k)
+            xn[k] = BIO::load(xs, off[k]);
+    };
+
     int parity = 0;
     const GroupWalk walk(a.K, a.A);
+    if (PREFETCH)
+        issue(walk.group(0));
     for (int kk = 0; kk < a.K; ++kk) {
         const int64_t grp = walk.group(kk);
         if (grp >= a.n_groups)
             break; // uniform over the workgroup; later groups are larger
         const RowGroup rg(grp, TEAMS, a.M, N, sizeof(T));
-        const rsrc_t xs = make_rsrc(static_cast<const char *>(a.x) + rg.byte0, rg.bytes);
+        if (!PREFETCH)
+            issue(grp);
         Raw xr[VPL];
 #pragma unroll
         for (int k = 0; k < VPL; ++k)
-            xr[k] = BIO::load(xs, off[k]);
+            xr[k] = xn[k];
+        const int64_t next = walk.group(kk + 1);
+        if (PREFETCH && kk + 1 < a.K && next < a.n_groups)
+            issue(next); // in flight during this group's work
 
         // row max (columns past N do not take part)
         float m[1] = {-INFINITY};
