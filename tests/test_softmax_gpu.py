@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520), (64, 1000),
           (33, 1024), (17, 1536), (9, 2000), (43, 4096), (5, 5000), (3, 16384), (2, 16383),
           (5000, 384), (21, 2560), (13, 1200), (45, 1002), (19, 4100),
-          (5, 2), (6, 4), (7, 6)]
+          (5, 2), (6, 4), (7, 6), (6, 8192), (4, 6152), (1000, 3072), (700, 2304), (900, 1280)]
 
 
 @pytest.fixture(autouse=True)
