@@ -57,8 +57,9 @@ norm_status_t check_device()
 // NORMFUSE_BWD_SPLIT                : 0 never splits backward rows along N,
 //                                     1 splits them wherever the kernel can
 //                                     (see bwd_plan)
-// NORMFUSE_PAIRS                    : 0 keeps rows of an odd length on the
-//                                     single-element kernels
+// NORMFUSE_PAIRS                    : 0 turns the odd-row kernels off (rows
+//                                     of an odd number of units then take
+//                                     the narrower vectors N allows)
 constexpr int kFwdGroupsPerWg = 0; // 0: chosen per call (see fwd_common)
 constexpr int kBwdGroupsPerWg = 0; // 0: chosen per shape (see bwd_plan)
 // Row groups per workgroup.  Teams of several waves (wide rows) have few
@@ -67,7 +68,6 @@ constexpr int kBwdGroupsPerWg = 0; // 0: chosen per shape (see bwd_plan)
 // sets how many rows one column partial covers, i.e. how finely the column
 // reduction is split over the rows (see bwd_groups_per_wg).
 constexpr int kFwdGroupsWide = 4;
-constexpr int kBwdRowsWide = 128;
 constexpr int64_t kBwdFewGroups = 64;
 // Compute units of the gfx950 parts.  A constant rather than a device query,
 // so that the grid (and with it every summation order, and the workspace
@@ -201,8 +201,17 @@ constexpr int64_t kFwdFewGroups = 4096;
 // and the forward's wide bf16 rows up to kFwdOddGroupsWide groups per
 // workgroup, their next group's loads in flight
 // (8192 x 16383 301 -> 279 us, 8192 x 8191 138 -> 132 us, 16384 x 6001
-// 240 -> 233 us; fp32 rows gained nothing from it).
+// 240 -> 233 us; fp32 rows gained nothing from it).  Beyond kFwdFewGroups
+// groups, wide rows on the 16-byte path whose lanes hold one or two vectors
+// walk two groups per workgroup.  Measured on MI355X against walks of four
+// (us): bf16 43690 x 3072 175.6 -> 170.4, 26214 x 5120 188.4 -> 182.9,
+// 21845 x 6144 180.8 -> 173.6, 131072 x 4096 725.7 -> 702.1, 32768 x 8192
+// 355.0 -> 350.0; fp32 65536 x 4096 730.6 -> 708.0.  (At 8192 x 4096 bf16,
+// 4096 groups, walks of two took 48.7 us against 47.0.)  Lanes holding four
+// vectors showed no rule: walks of four, eight or one workgroup per CU each
+// won somewhere by up to 8%, so they keep walks of four.
 constexpr int64_t kFwdOddGroupsWide = 8;
+constexpr int64_t kFwdGroupsWideShort = 2;
 constexpr double kFwdMinGroupBytes = 24.0 * 1024;
 constexpr int64_t kFwdF8PairCols = 1024;
 int fwd_groups_per_wg(int64_t M, int64_t N, int32_t dtype, const RowShape &sh, bool amax, bool f8,
@@ -214,7 +223,10 @@ int fwd_groups_per_wg(int64_t M, int64_t N, int32_t dtype, const RowShape &sh, b
     int64_t k = odd ? 1 : std::max<int64_t>(kmin, int64_t(std::ceil(kFwdMinGroupBytes / group_bytes)));
     if (sh.lpr >= WIDE_LPR || groups <= kFwdFewGroups) {
         const bool odd_wide = odd && !softmax && dtype == NORM_BF16 && sh.lpr >= WIDE_LPR;
-        const int64_t kmax = odd_wide ? kFwdOddGroupsWide : kFwdGroupsWide;
+        int64_t kmax = odd_wide ? kFwdOddGroupsWide : kFwdGroupsWide;
+        if (!odd && !softmax && sh.lpr >= WIDE_LPR && sh.vec * elem_size(dtype) == 16 &&
+            sh.vpl <= 2 && groups > kFwdFewGroups)
+            kmax = kFwdGroupsWideShort;
         k = std::min<int64_t>(kmax, std::max<int64_t>(1, (groups + kCUs - 1) / kCUs));
     }
     if (amax)
@@ -538,7 +550,8 @@ norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, int uni
             break;
         }
     }
-    const int K = kn.fwd_k > 0 ? kn.fwd_k : fwd_groups_per_wg(M, N, dtype, e->shape, false, false);
+    const int K = kn.fwd_k > 0 ? kn.fwd_k
+                               : fwd_groups_per_wg(M, N, dtype, e->shape, false, false, false, true);
     if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
         return st;
     *entry = e;
@@ -617,11 +630,15 @@ constexpr int64_t kSplitMinGroups = 64;
 //  - wide rows (teams of 320 to 1024 lanes): as many workgroups as the CUs
 //    hold at once -- one per CU, two for the fp32 shapes up to 8192
 //    columns, whose registers leave room for a second -- each walking at
-//    least 2 and at most kBwdRowsWide rows (below 2 rows the partials
-//    outweigh the rows themselves).  A fixed 32-row walk left most CUs idle
-//    at small M (64 x 16384 bf16: 102 us, now 18 us) and cut large M into
-//    more partials than needed (32768 x 4096 bf16: 141 us, now 129 us;
-//    8192 x 4096 fp32: 92 us, now 68 us).  Up to kBwdFewGroups row groups
+//    least 2 rows (below 2 rows the partials outweigh the rows themselves)
+//    and as many as it takes, so that no second round of workgroups runs
+//    behind the first.  A fixed 32-row walk left most CUs idle at small M
+//    (64 x 16384 bf16: 102 us, now 18 us) and cut large M into more
+//    partials than needed (32768 x 4096 bf16: 141 us, now 129 us; 8192 x
+//    4096 fp32: 92 us, now 68 us); walks capped at 128 rows left a partial
+//    second round at larger M (52428 x 2560 bf16: 160 us, now 132 us;
+//    43690 x 3072: 170 -> 129 us; 131072 x 4096: 556 -> 527 us; 65536 x
+//    8192: 549 -> 515 us).  Up to kBwdFewGroups row groups
 //    take one workgroup each: their partials are a few MiB at most, the
 //    call is latency-bound, and a second row per workgroup adds its memory
 //    round trip (4 x 16384 bf16: 11.7 us with two rows per workgroup, 9.0 us
@@ -652,12 +669,9 @@ int bwd_groups_per_wg(int64_t M, int64_t N, const RowShape &sh, int32_t dtype)
         // odd-row 113 -> 82 us; 16384 x 2047 odd-row 88 -> 51 us.
         if (dtype == NORM_BF16 && sh.vec <= 2)
             per_cu = std::max<int64_t>(per_cu, 1024 / sh.threads());
-        const int64_t kmax = std::max(1, kBwdRowsWide / sh.teams);
-        const int64_t kmin = groups <= kBwdFewGroups
-                                 ? 1
-                                 : std::min<int64_t>(kmax, (2 + sh.teams - 1) / sh.teams);
+        const int64_t kmin = groups <= kBwdFewGroups ? 1 : (2 + sh.teams - 1) / sh.teams;
         const int64_t slots = kCUs * per_cu;
-        return int(std::min(kmax, std::max(kmin, (groups + slots - 1) / slots)));
+        return int(std::min<int64_t>(INT32_MAX, std::max(kmin, (groups + slots - 1) / slots)));
     }
     const double group_bytes = double(sh.teams) * double(N) * double(elem_size(dtype));
     const int64_t slots = (group_bytes < kBwdSmallGroupBytes ? 4 : 2) * kCUs;

@@ -11,7 +11,7 @@ namespace nf {
      &launch_fwd<T, VEC, LPR, VPL, TEAMS, false, true>,                                           \
      &launch_fwd<T, VEC, LPR, VPL, TEAMS, true, true>},
 
-static const FwdEntry k_vec[] = {NF_SHAPES_F32_VEC(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, float, 4)};
+static const FwdEntry k_vec[] = {NF_SHAPES_FWD_VEC(NF_ENTRY, float, 4) NF_ENTRY(float, 4, 1024, 4, 1) NF_SHAPES_NARROW_2X(NF_ENTRY, float, 4)};
 static const FwdEntry k_vec2[] = {NF_SHAPES_SHORT_VEC(NF_ENTRY, float, 2)};
 static const FwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, float)};
 

@@ -4,11 +4,11 @@
 //
 // 16-byte path (VEC = 16 / sizeof(T)); narrow rows in workgroups of 256
 // threads (the forward adds 512-thread variants), wide rows in teams of
-// 320 to 512 threads:
+// 320 to 1024 threads (softmax has tables of its own, in softmax.hip):
 //   bf16 capacities: 64 128 256 384 512 768 1024 1536 2048 2560 3072 4096
-//                    (backward: 5120 6144) 8192 16384
+//                    (backward: 5120 6144) 8192 10240 12288 16384
 //   fp32 capacities: 32 64 128 192 256 384 512 768 1024 1280 1536 2048 4096
-//                    8192 16384
+//                    (forward: 5120 6144) 8192 16384
 // Rows that are not whole 16-byte vectors, or pointers that are not 16-byte
 // aligned, take the widest of 8-byte vectors (bf16, N % 4 == 0, the fp32
 // layouts), 4-byte vectors of 2 elements (N even) or single elements that
@@ -48,8 +48,26 @@
     X(T, VEC, 512, 2, 1)                                                                         \
     X(T, VEC, 512, 4, 1)
 #define NF_SHAPES_WIDE(X, T, VEC) NF_SHAPES_WIDE_ONE_VEC(X, T, VEC) NF_SHAPES_WIDE_MULTI_VEC(X, T, VEC)
+// Teams of 640 and 768 lanes holding two vectors each, between 512 lanes
+// holding two and 512 holding four (up to half of whose lanes would idle).
+// Measured on MI355X, 512 x 4 against these (us): bf16 forward 8192 x 9216
+// 123.9 -> 114.4, 8192 x 10240 130.8 -> 121.2, 32768 x 12288 569.9 ->
+// 546.0; bf16 backward 8192 x 9216 103.9 -> 81.2, 8192 x 10240 104.2 ->
+// 85.2, 32768 x 12288 420.8 -> 392.9; fp32 forward 32768 x 5120 466.5 ->
+// 456.8, 32768 x 6144 559.1 -> 540.8, 10922 x 6144 184.1 -> 178.0.  (The
+// fp32 backward went either way, by up to 15%, and keeps 512 x 4; teams of
+// 1024 lanes holding two lost to 512 holding four at 16384 columns.)
+#define NF_SHAPES_WIDE_TWO_VEC_FINE(X, T, VEC)                                                   \
+    X(T, VEC, 512, 2, 1)                                                                         \
+    X(T, VEC, 640, 2, 1)                                                                         \
+    X(T, VEC, 768, 2, 1)                                                                         \
+    X(T, VEC, 512, 4, 1)
+// The forward's 16-byte tables (fp32 adds 1024 x 4 for 16384 columns).
+#define NF_SHAPES_FWD_VEC(X, T, VEC)                                                             \
+    NF_SHAPES_NARROW(X, T, VEC)                                                                  \
+    NF_SHAPES_WIDE_ONE_VEC(X, T, VEC)                                                            \
+    NF_SHAPES_WIDE_TWO_VEC_FINE(X, T, VEC)
 
-#define NF_SHAPES_BF16_VEC(X) NF_SHAPES_NARROW(X, bf16, 8) NF_SHAPES_WIDE(X, bf16, 8)
 // The bf16 backward also runs rows of 4097-6144 columns on one team of 640
 // or 768 lanes holding one vector each, instead of 512 lanes holding two
 // with idle lanes.  Measured on MI355X: 32768 x 5120 219 -> 180 us,
@@ -60,7 +78,7 @@
     NF_SHAPES_WIDE_ONE_VEC(X, bf16, 8)                                                           \
     X(bf16, 8, 640, 1, 1)                                                                        \
     X(bf16, 8, 768, 1, 1)                                                                        \
-    NF_SHAPES_WIDE_MULTI_VEC(X, bf16, 8)
+    NF_SHAPES_WIDE_TWO_VEC_FINE(X, bf16, 8)
 #define NF_SHAPES_F32_VEC(X)                                                                     \
     NF_SHAPES_NARROW(X, float, 4) NF_SHAPES_WIDE(X, float, 4) X(float, 4, 1024, 4, 1)
 

@@ -24,6 +24,8 @@ SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520),
           (17, 1536), (40, 4096), (43, 4096), (5, 5000), (3, 16384), (2, 16383), (21, 2560),
           (13, 1200), (45, 1002), (19, 4100),
           (5, 2), (6, 4), (7, 6),
+          # teams of 640 and 768 lanes holding two vectors
+          (7, 9216), (129, 10240), (5, 12288), (200, 6144),
           # 1024-thread workgroups with the parameters staged in LDS
           (600, 16383), (300, 16382), (700, 8191)]
 

@@ -25,6 +25,8 @@ SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520),
           (3, 16384), (2, 16383), (21, 2560), (11, 2304), (13, 1200),
           (45, 1002), (19, 4100), (7, 6002), (6, 12004), (301, 4100), (23, 6140), (70, 5004),
           (5, 2), (6, 4), (7, 6), (9, 12),
+          # teams of 640 and 768 lanes holding two vectors
+          (7, 9216), (5, 12288), (129, 10240), (200, 6144),
           # 1024-thread workgroups of the widest short-vector rows (parameters
           # staged in LDS), several row groups per workgroup
           (600, 16383), (700, 8191), (300, 16382),
