@@ -241,6 +241,18 @@ const FwdEntry *fwd_entry(int dtype, int vec, int64_t M, int N, const Knobs &k)
     const FwdEntry *e = pick_shape(tab, n, N, k.fwd_lpr, k.fwd_vpl, k.fwd_teams);
     if (!e || k.fwd_lpr > 0)
         return e;
+    // a narrow 16-byte team holding more than four vectors per lane (one
+    // wave per row, five vectors: bf16 rows of 2049-2560 columns) only where
+    // it leaves kMinWideGroups row groups; otherwise the next shape that
+    // holds the row
+    if (e->shape.lpr < WIDE_LPR && e->shape.vpl > 4 && e->shape.vec * elem_size(dtype) == 16 &&
+        (M + e->shape.teams - 1) / e->shape.teams < kMinWideGroups) {
+        for (const FwdEntry *f = e + 1; f < tab + n; ++f)
+            if (f->shape.capacity() >= N && f->shape.lpr >= WIDE_LPR) {
+                e = f;
+                break;
+            }
+    }
     for (int i = 0; i < n; ++i) {
         const RowShape &w = tab[i].shape;
         if (w.lpr == e->shape.lpr && w.vpl == e->shape.vpl && w.teams == 2 * e->shape.teams &&

@@ -11,7 +11,7 @@ namespace nf {
      &launch_fwd<T, VEC, LPR, VPL, TEAMS, false, true>,                                           \
      &launch_fwd<T, VEC, LPR, VPL, TEAMS, true, true>},
 
-static const FwdEntry k_vec[] = {NF_SHAPES_FWD_VEC(NF_ENTRY, bf16, 8) NF_SHAPES_NARROW_2X(NF_ENTRY, bf16, 8)};
+static const FwdEntry k_vec[] = {NF_SHAPES_FWD_BF16_VEC(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, bf16, 8)};
 static const FwdEntry k_vec4[] = {NF_SHAPES_BF16_VEC4_FINE(NF_ENTRY) NF_SHAPES_NARROW_2X(NF_ENTRY, bf16, 4)};
 static const FwdEntry k_vec2[] = {NF_SHAPES_SHORT_VEC_FINE(NF_ENTRY, bf16, 2)};
 static const FwdEntry k_elem[] = {NF_SHAPES_ELEM(NF_ENTRY, bf16)};

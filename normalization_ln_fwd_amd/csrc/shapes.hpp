@@ -6,7 +6,8 @@
 // threads (the forward adds 512-thread variants), wide rows in teams of
 // 320 to 1024 threads (softmax has tables of its own, in softmax.hip):
 //   bf16 capacities: 64 128 256 384 512 768 1024 1536 2048 2560 3072 4096
-//                    (backward: 5120 6144) 8192 10240 12288 16384
+//                    (backward: 5120 6144) 8192 10240 12288 16384; the forward
+//                    adds 2560 on one wave per row
 //   fp32 capacities: 32 64 128 192 256 384 512 768 1024 1280 1536 2048 4096
 //                    (forward: 5120 6144) 8192 16384
 // Rows that are not whole 16-byte vectors, or pointers that are not 16-byte
@@ -67,16 +68,31 @@
     NF_SHAPES_NARROW(X, T, VEC)                                                                  \
     NF_SHAPES_WIDE_ONE_VEC(X, T, VEC)                                                            \
     NF_SHAPES_WIDE_TWO_VEC_FINE(X, T, VEC)
+// bf16 adds one wave per row holding five vectors for 2049-2560 columns,
+// taken where it leaves at least 2048 row groups (the host's fwd_entry):
+// measured on MI355X against 320 lanes x 1 (us), 16384 x 2560 57.9 ->
+// 53.2, 65536 x 2304 212.0 -> 194.6, 8192 x 2560 28.9 -> 27.8; with fewer
+// rows its 256-thread workgroups hold too few waves (4096 x 2560: 18.3
+// against 16.2).
+#define NF_SHAPES_FWD_BF16_VEC(X)                                                                \
+    NF_SHAPES_NARROW(X, bf16, 8)                                                                 \
+    X(bf16, 8, 64, 5, 4)                                                                         \
+    NF_SHAPES_WIDE_ONE_VEC(X, bf16, 8)                                                           \
+    NF_SHAPES_WIDE_TWO_VEC_FINE(X, bf16, 8)
 
-// The bf16 backward also runs rows of 4097-6144 columns on one team of 640
-// or 768 lanes holding one vector each, instead of 512 lanes holding two
-// with idle lanes.  Measured on MI355X: 32768 x 5120 219 -> 180 us,
-// 32768 x 6144 230 -> 198 us, 8192 x 5120 62 -> 51 us.  The forward gains
-// nothing there (-7% to +2%), nor does either direction in fp32.
+// The bf16 backward also runs rows of 4097-6144 columns on teams that leave
+// fewer lanes idle than 512 lanes holding two vectors: two teams of 320
+// lanes holding two each up to 5120 columns, one team of 768 lanes holding
+// one up to 6144.  Measured on MI355X against 512 x 2: 32768 x 5120 219 ->
+// 158 us, 32768 x 6144 230 -> 193 us, 8192 x 5120 62 -> 45 us; 320 x 2 x 2
+// against 640 lanes holding one: 32768 x 5120 176 -> 158 us, 16384 x 4608
+// 92.5 -> 77.0 us (at 6144 columns 384 x 2 x 2 and 768 x 1 were within 2%
+// either way).  The forward gains nothing from 640 or 768 lanes holding
+// one vector (-7% to +2%), nor does either direction in fp32.
 #define NF_SHAPES_BF16_BWD_VEC(X)                                                                \
     NF_SHAPES_NARROW(X, bf16, 8)                                                                 \
     NF_SHAPES_WIDE_ONE_VEC(X, bf16, 8)                                                           \
-    X(bf16, 8, 640, 1, 1)                                                                        \
+    X(bf16, 8, 320, 2, 2)                                                                        \
     X(bf16, 8, 768, 1, 1)                                                                        \
     NF_SHAPES_WIDE_TWO_VEC_FINE(X, bf16, 8)
 #define NF_SHAPES_F32_VEC(X)                                                                     \

@@ -304,6 +304,13 @@ def test_describe_names_the_planned_kernels(lib):
     assert nf.describe("softmax_fwd", 576000, 384, nf.BF16).startswith(
         "softmax_kernel<bf16, VEC 8, LPR 16, VPL 3, TEAMS 32>")
     assert "bwd_split_kernel" in nf.describe("ln_bwd", 64, 16384, nf.BF16)
+    # one wave per row holding five vectors only from 2048 row groups on
+    assert nf.describe("ln_fwd", 8192, 2560, nf.BF16).startswith(
+        "fwd_kernel<bf16, VEC 8, LPR 64, VPL 5, TEAMS 4,")
+    assert nf.describe("ln_fwd", 8188, 2560, nf.BF16).startswith(
+        "fwd_kernel<bf16, VEC 8, LPR 320, VPL 1, TEAMS 2,")
+    assert nf.describe("ln_bwd", 8192, 5120, nf.BF16).startswith(
+        "bwd_kernel<bf16, VEC 8, LPR 320, VPL 2, TEAMS 2,")
 
 
 def _odd_unit(op, M, N, dtype):

@@ -28,6 +28,8 @@ SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520),
           (5, 2), (6, 4), (7, 6), (9, 12),
           # teams of 640 and 768 lanes holding two vectors
           (7, 9216), (5, 12288), (129, 10240), (200, 6144),
+          # two teams of 320 lanes holding two vectors, several groups each
+          (700, 4800),
           # the widest rows in 1024-thread workgroups (gamma and the dbias
           # sums in LDS), walking several row groups per workgroup
           (600, 16383), (300, 16380),

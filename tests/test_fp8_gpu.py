@@ -26,6 +26,8 @@ SHAPES = [(1, 1), (3, 7), (37, 8), (130, 64), (257, 100), (300, 384), (77, 520),
           (5, 2), (6, 4), (7, 6),
           # teams of 640 and 768 lanes holding two vectors
           (7, 9216), (129, 10240), (5, 12288), (200, 6144),
+          # one wave per row holding five vectors (taken from 2048 row groups on)
+          (8198, 2312),
           # 1024-thread workgroups with the parameters staged in LDS
           (600, 16383), (300, 16382), (700, 8191)]
 
