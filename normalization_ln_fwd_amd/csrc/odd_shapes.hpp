@@ -53,9 +53,10 @@
     X(T, 2, 384, 8, 2)                                                                           \
     X(T, 2, 512, 8, 2)
 
-// Units 2 and 4 (vectors of 4 or 8 elements): the narrow layouts of
-// shapes.hpp, wide teams holding one vector per lane, then one team of 512,
-// 640 or 768 lanes holding 2 or 4 vectors.  Measured on MI355X (bf16, us):
+// Units 2 and 4 with 16-byte vectors (bf16 unit 4, fp32 unit 2): the
+// narrow layouts of shapes.hpp, wide teams holding one vector per lane,
+// then one team of 512, 640 or 768 lanes holding 2 or 4 vectors (bf16 rows
+// of unit 2 have tables of their own, below).  Measured on MI355X (bf16, us):
 // one vector per lane on 640 or 768 lanes is slower than two on 512
 // (8192 x 5124 forward 78 against 67, 8192 x 6004 softmax 43 against 35),
 // and so are 1024 lanes holding 4 (8192 x 9002 forward 163 against 139 on
@@ -91,6 +92,38 @@
     NF_SHAPES_WIDE_ONE_VEC(X, T, 4)                                                              \
     X(T, 4, 512, 2, 1)                                                                           \
     X(T, 4, 512, 4, 1)
+// bf16 rows of unit 2 (8-byte vectors): one wave per row holding six or
+// eight vectors, then teams of 128 lanes holding six or eight, where the
+// teams above hold 8 or 16 bytes per lane.  Measured on MI355X (us, those
+// teams / these): 65472 x 2050 forward 291.7 / 204.4, softmax 139.1 /
+// 95.0, backward 230.6 / 152.9; 87267 x 1538 forward 238.7 / 209.2,
+// softmax 162.1 / 91.0, backward (on the 4-byte vector kernel) 162.9 /
+// 144.4; 8192 x 3074 forward 59.5 / 51.7.  The backward keeps two teams of
+// 512 lanes past 2048 columns (teams of 128 lanes lost there: 65472 x 2050
+// 334 us) and softmax 512 lanes holding two at 4096 (32752 x 4098: 91.9
+// against 94.9 us).
+#define NF_SHAPES_ODD_U2_BF16_FWD(X)                                                             \
+    NF_SHAPES_NARROW(X, bf16, 4)                                                                 \
+    X(bf16, 4, 64, 6, 4)                                                                         \
+    X(bf16, 4, 64, 8, 4)                                                                         \
+    X(bf16, 4, 128, 6, 2)                                                                        \
+    X(bf16, 4, 128, 8, 2)                                                                        \
+    X(bf16, 4, 640, 2, 1)                                                                        \
+    X(bf16, 4, 768, 2, 1)                                                                        \
+    X(bf16, 4, 512, 4, 1)
+#define NF_SHAPES_ODD_U2_BF16_SOFTMAX(X)                                                         \
+    NF_SHAPES_NARROW(X, bf16, 4)                                                                 \
+    X(bf16, 4, 64, 6, 4)                                                                         \
+    X(bf16, 4, 64, 8, 4)                                                                         \
+    X(bf16, 4, 128, 6, 2)                                                                        \
+    X(bf16, 4, 512, 2, 1)                                                                        \
+    X(bf16, 4, 512, 4, 1)
+#define NF_SHAPES_ODD_U2_BF16_BWD(X)                                                             \
+    NF_SHAPES_NARROW(X, bf16, 4)                                                                 \
+    X(bf16, 4, 64, 6, 4)                                                                         \
+    X(bf16, 4, 64, 8, 4)                                                                         \
+    X(bf16, 4, 512, 2, 2)                                                                        \
+    X(bf16, 4, 512, 4, 2)
 // beyond 8192 columns (bf16 forward, softmax of either dtype)
 #define NF_SHAPES_ODD_U2_WIDE(X, T)                                                              \
     X(T, 4, 640, 4, 1)                                                                           \
