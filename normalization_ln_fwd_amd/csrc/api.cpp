@@ -674,12 +674,13 @@ int bwd_groups_per_wg(int64_t M, int64_t N, const RowShape &sh, int32_t dtype)
     const int64_t groups = (M + sh.teams - 1) / sh.teams;
     if (sh.lpr >= WIDE_LPR) {
         int64_t per_cu = dtype == NORM_F32 && sh.capacity() <= 8192 ? 2 : 1;
-        // bf16 rows of 4-byte or single-element accesses (and the odd-row
-        // pairs) in workgroups of 256 or 512 threads: 1024 threads per CU.
-        // Measured on MI355X, one per CU left them idle: 32768 x 1499
+        // bf16 rows of 8-byte, 4-byte or single-element accesses (and the
+        // odd-row pairs) in workgroups of 256 or 512 threads: 1024 threads per
+        // CU.  Measured on MI355X, one per CU left them idle: 32768 x 1499
         // odd-row 147 -> 66 us, single-element 209 -> 84 us; 16384 x 4097
-        // odd-row 113 -> 82 us; 16384 x 2047 odd-row 88 -> 51 us.
-        if (dtype == NORM_BF16 && sh.vec <= 2)
+        // odd-row 113 -> 82 us; 16384 x 2047 odd-row 88 -> 51 us; 8-byte
+        // vectors 43633 x 3076 187.5 -> 164.9 us, 21831 x 6148 186.8 -> 167.1.
+        if (dtype == NORM_BF16 && sh.vec * elem_size(dtype) < 16)
             per_cu = std::max<int64_t>(per_cu, 1024 / sh.threads());
         const int64_t kmin = groups <= kBwdFewGroups ? 1 : (2 + sh.teams - 1) / sh.teams;
         const int64_t slots = kCUs * per_cu;

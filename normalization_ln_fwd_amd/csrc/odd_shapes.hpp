@@ -62,9 +62,14 @@
 // and so are 1024 lanes holding 4 (8192 x 9002 forward 163 against 139 on
 // 640 lanes).  The softmax, with no parameters to stage, prefers 4 vectors
 // on 512 lanes to 2 on 768 (8192 x 6002: 36 against 43 us).
+// bf16 rows of unit 4 take one wave per row holding five vectors up to
+// 2564 columns instead of 320 lanes holding one (58153 x 2308 forward
+// 225.1 -> 193.8 us, 52347 x 2564 215.6 -> 198.5 us).
 #define NF_SHAPES_ODD_U4_BF16(X)                                                                 \
     NF_SHAPES_NARROW(X, bf16, 8)                                                                 \
-    NF_SHAPES_WIDE_ONE_VEC(X, bf16, 8)                                                           \
+    X(bf16, 8, 64, 5, 4)                                                                         \
+    X(bf16, 8, 384, 1, 2)                                                                        \
+    X(bf16, 8, 512, 1, 2)                                                                        \
     X(bf16, 8, 512, 2, 1)                                                                        \
     X(bf16, 8, 640, 2, 1)                                                                        \
     X(bf16, 8, 768, 2, 1)                                                                        \
@@ -76,13 +81,16 @@
     X(T, 4, 640, 2, 1)                                                                           \
     X(T, 4, 768, 2, 1)                                                                           \
     X(T, 4, 512, 4, 1)
-// Softmax of unit 4 keeps, of the one-vector teams, only the 512-lane one
-// (with the vector kernel taken at the same fill, below); on 320 or 384
-// lanes it measured slower than the vector kernel at full fill (16384 x
-// 3076: 42.7 against 38.7 us).
+// Softmax of unit 4: one wave per row holding five, six or eight vectors
+// up to 4100 columns.  Teams of 320-512 lanes holding one measured slower
+// than the vector kernel, these faster (us, vector or 512 lanes / these):
+// 58153 x 2308 119.2 / 90.1, 43633 x 3076 97.2 / 91.6, 32736 x 4100 100.7
+// / 90.7, 8192 x 2564 20.5 / 15.8.
 #define NF_SHAPES_ODD_U4_BF16_SOFTMAX(X)                                                         \
     NF_SHAPES_NARROW(X, bf16, 8)                                                                 \
-    X(bf16, 8, 512, 1, 2)                                                                        \
+    X(bf16, 8, 64, 5, 4)                                                                         \
+    X(bf16, 8, 64, 6, 4)                                                                         \
+    X(bf16, 8, 64, 8, 4)                                                                         \
     X(bf16, 8, 512, 2, 1)                                                                        \
     X(bf16, 8, 640, 2, 1)                                                                        \
     X(bf16, 8, 768, 2, 1)                                                                        \

@@ -340,8 +340,10 @@ def test_describe_names_the_odd_row_kernels(lib):
     # leaves fewer lanes idle than the vector kernel
     assert _odd_unit("softmax_fwd", 10, 10242, F32) == 2      # 10240 of 10240 vs 12288
     assert _odd_unit("softmax_fwd", 10, 16382, F32) == 0      # 16380 of 16384 vs 16382 of 16384
-    assert _odd_unit("softmax_fwd", 10, 4100, BF16) == 4 and _odd_unit("softmax_fwd", 10, 3076, BF16) == 0
-    assert _odd_unit("softmax_fwd", 10, 3074, BF16) == 0 and _odd_unit("ln_fwd", 10, 3074, BF16) == 2
+    assert _odd_unit("softmax_fwd", 10, 6004, BF16) == 0      # 8192-column teams either way
+    assert _odd_unit("softmax_fwd", 10, 6002, BF16) == 0 and _odd_unit("ln_fwd", 10, 6002, BF16) == 2
+    # one wave per row (a narrow layout) at any fill
+    assert _odd_unit("softmax_fwd", 10, 4100, BF16) == 4 and _odd_unit("softmax_fwd", 10, 3076, BF16) == 4
     assert _odd_unit("ln_fwd", 10, 16380, BF16) == 4 and _odd_unit("ln_fwd", 10, 16382, BF16) == 2
 
 
