@@ -706,12 +706,19 @@ norm_status_t bwd_plan(int64_t M, int64_t N, int32_t dtype, int vec, int unit, i
         // 8-byte vectors.  On a wide team (two rows per workgroup, each across
         // several waves) the odd-row backward takes it only where it leaves
         // fewer lanes idle: at the same fill the vector kernel is 4-10% faster
-        // (measured on MI355X, 8192 x 6004 bf16: 70.6 against 63.8 us; 16384 x
-        // 3076: 79.3 against 75.2 us), and with fewer idle lanes it is slower
-        // (16384 x 4100: 92.1 against 99.6 us, 8192 x 8196: 87.4 against 126.8).
+        // on teams of 320-512 lanes (measured on MI355X, 8192 x 6004 bf16:
+        // 70.6 against 63.8 us; 16384 x 3076: 79.3 against 75.2 us), and with
+        // fewer idle lanes it is slower (16384 x 4100: 92.1 against 99.6 us,
+        // 8192 x 8196: 87.4 against 126.8).  Teams of 256 lanes holding four
+        // vectors also win at the same fill once 70% of their lanes are busy
+        // (43662 x 3074: 159.6 against 164.4 us, 37428 x 3586: 149.1 against
+        // 163.5), not below (52387 x 2562: 180.9 against 172.1 us).
         if (e && vec > 1 && e->shape.lpr >= WIDE_LPR && kn.bwd_lpr == 0) {
             const BwdEntry *v = bwd_entry(dtype, vec, int(N), kn);
-            if (v && (N - unit) * int64_t(v->shape.capacity()) <= N * int64_t(e->shape.capacity()))
+            const int64_t busy = N - unit, cap = e->shape.capacity();
+            const bool fuller = !v || busy * int64_t(v->shape.capacity()) > N * cap;
+            const bool busy_team = e->shape.lpr <= 256 && busy * 10 >= 7 * cap;
+            if (!fuller && !busy_team)
                 e = nullptr;
         }
         unit = e != nullptr ? unit : 0;

@@ -106,10 +106,11 @@
 // teams / these): 65472 x 2050 forward 291.7 / 204.4, softmax 139.1 /
 // 95.0, backward 230.6 / 152.9; 87267 x 1538 forward 238.7 / 209.2,
 // softmax 162.1 / 91.0, backward (on the 4-byte vector kernel) 162.9 /
-// 144.4; 8192 x 3074 forward 59.5 / 51.7.  The backward keeps two teams of
-// 512 lanes past 2048 columns (teams of 128 lanes lost there: 65472 x 2050
-// 334 us) and softmax 512 lanes holding two at 4096 (32752 x 4098: 91.9
-// against 94.9 us).
+// 144.4; 8192 x 3074 forward 59.5 / 51.7.  The backward takes two teams of
+// 256 lanes holding four past 2050 columns (32752 x 4098: 179.8 -> 154.0
+// us against two teams of 512 holding two; teams of 128 lanes lost there:
+// 65472 x 2050 213 us), softmax 512 lanes holding two at 4096 (32752 x
+// 4098: 91.9 against 94.9 us).
 #define NF_SHAPES_ODD_U2_BF16_FWD(X)                                                             \
     NF_SHAPES_NARROW(X, bf16, 4)                                                                 \
     X(bf16, 4, 64, 6, 4)                                                                         \
@@ -130,7 +131,7 @@
     NF_SHAPES_NARROW(X, bf16, 4)                                                                 \
     X(bf16, 4, 64, 6, 4)                                                                         \
     X(bf16, 4, 64, 8, 4)                                                                         \
-    X(bf16, 4, 512, 2, 2)                                                                        \
+    X(bf16, 4, 256, 4, 2)                                                                        \
     X(bf16, 4, 512, 4, 2)
 // beyond 8192 columns (bf16 forward, softmax of either dtype)
 #define NF_SHAPES_ODD_U2_WIDE(X, T)                                                              \
