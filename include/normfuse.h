@@ -75,7 +75,8 @@
  *              also honours tuning overrides read at every call, for tests
  *              that cross-check kernel shapes against each other and for
  *              measurements: NORMFUSE_FWD_SHAPE / _BWD_SHAPE
- *              ("LPRxVPL[xTEAMS]"), NORMFUSE_FWD_GROUPS_PER_WG /
+ *              ("LPRxVPL[xTEAMS]"; the forward's also for softmax),
+ *              NORMFUSE_FWD_GROUPS_PER_WG /
  *              _BWD_GROUPS_PER_WG, NORMFUSE_FWD_INTERLEAVE / _BWD_INTERLEAVE
  *              (results stay within the same tolerances, but column sums
  *              may round differently), NORMFUSE_WT_BYTES (output bytes,
