@@ -538,7 +538,13 @@ norm_status_t softmax_plan(int64_t M, int64_t N, int32_t dtype, int vec, int uni
                 e = nullptr;
         }
         if (e) {
+            // rows of odd N (pairs, eight per lane on the wide teams): one row
+            // group per workgroup, many workgroups deep.  Measured on MI355X
+            // against walks of four (bf16, us): 32760 x 4097 112.3 -> 101.0,
+            // 21841 x 6145 118.6 -> 104.9, 16382 x 8193 113.4 -> 104.9.  (Teams
+            // holding one or two 8- or 16-byte vectors walk four.)
             const int K = kn.fwd_k > 0 ? kn.fwd_k
+                          : unit == 1  ? 1
                                        : fwd_groups_per_wg(M, N, dtype, e->shape, false, false,
                                                            true, true);
             if (norm_status_t st = plan_walk(M, e->shape.teams, K, kn.fwd_a, w))
