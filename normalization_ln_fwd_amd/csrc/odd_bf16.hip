@@ -5,7 +5,7 @@
 
 namespace nf {
 
-static const FwdEntry k_fwd[] = {NF_SHAPES_ODD(NF_FWD_ODD, bf16) NF_SHAPES_ODD_WIDE(NF_FWD_ODD, bf16)};
+static const FwdEntry k_fwd[] = {NF_SHAPES_ODD_FWD_BF16(NF_FWD_ODD) NF_SHAPES_ODD_WIDE(NF_FWD_ODD, bf16)};
 static const BwdEntry k_bwd[] = {NF_SHAPES_ODD_BWD(NF_BWD_ODD, bf16)};
 static const SoftmaxEntry k_softmax[] = {NF_SHAPES_ODD(NF_SOFTMAX_ODD, bf16) NF_SHAPES_ODD_WIDE(NF_SOFTMAX_ODD, bf16)};
 

@@ -25,6 +25,26 @@
     X(T, 2, 320, 8, 1)                                                                           \
     X(T, 2, 384, 8, 1)                                                                           \
     X(T, 2, 512, 8, 1)
+// The bf16 forward's: the wide teams two to a workgroup (they share the
+// staged per-column vectors and hold twice the waves).  Measured on MI355X
+// against one team per workgroup (us): 32760 x 4097 263.7 -> 224.2, 26209 x
+// 5121 331.1 -> 265.3, 21841 x 6145 302.5 -> 256.3, 16382 x 8193 266.2 ->
+// 234.5, 8192 x 4097 84.9 -> 68.6.  (Teams of twice the lanes holding four
+// pairs instead were slower: 16382 x 8193 on 1024 lanes, 296.2 us.)
+#define NF_SHAPES_ODD_FWD_BF16(X)                                                                \
+    X(bf16, 2, 16, 4, 16)                                                                        \
+    X(bf16, 2, 32, 4, 8)                                                                         \
+    X(bf16, 2, 64, 3, 4)                                                                         \
+    X(bf16, 2, 64, 4, 4)                                                                         \
+    X(bf16, 2, 64, 6, 4)                                                                         \
+    X(bf16, 2, 64, 8, 4)                                                                         \
+    X(bf16, 2, 64, 12, 4)                                                                        \
+    X(bf16, 2, 64, 16, 4)                                                                        \
+    X(bf16, 2, 192, 8, 2)                                                                        \
+    X(bf16, 2, 256, 8, 2)                                                                        \
+    X(bf16, 2, 320, 8, 2)                                                                        \
+    X(bf16, 2, 384, 8, 2)                                                                        \
+    X(bf16, 2, 512, 8, 2)
 // Up to 16385 columns (the forward's per-column vectors take 6 bytes per
 // column of LDS for bf16; fp32's 12 would not fit past 8193 columns beside
 // the rows in flight).
