@@ -45,6 +45,23 @@
     X(bf16, 2, 320, 8, 2)                                                                        \
     X(bf16, 2, 384, 8, 2)                                                                        \
     X(bf16, 2, 512, 8, 2)
+// The bf16 softmax's likewise, but for the 320-lane teams (measured (us),
+// one team / two: 43676 x 3073 106.7 / 92.0, 32760 x 4097 101.4 / 89.9,
+// 16382 x 8193 104.9 / 98.0; 26209 x 5121 105.3 / 110.1).
+#define NF_SHAPES_ODD_SOFTMAX_BF16(X)                                                            \
+    X(bf16, 2, 16, 4, 16)                                                                        \
+    X(bf16, 2, 32, 4, 8)                                                                         \
+    X(bf16, 2, 64, 3, 4)                                                                         \
+    X(bf16, 2, 64, 4, 4)                                                                         \
+    X(bf16, 2, 64, 6, 4)                                                                         \
+    X(bf16, 2, 64, 8, 4)                                                                         \
+    X(bf16, 2, 64, 12, 4)                                                                        \
+    X(bf16, 2, 64, 16, 4)                                                                        \
+    X(bf16, 2, 192, 8, 2)                                                                        \
+    X(bf16, 2, 256, 8, 2)                                                                        \
+    X(bf16, 2, 320, 8, 1)                                                                        \
+    X(bf16, 2, 384, 8, 2)                                                                        \
+    X(bf16, 2, 512, 8, 2)
 // Up to 16385 columns (the forward's per-column vectors take 6 bytes per
 // column of LDS for bf16; fp32's 12 would not fit past 8193 columns beside
 // the rows in flight).
