@@ -98,9 +98,10 @@
  *              wider than the rule above allows).  The forward and softmax
  *              take them up to NORM_N_MAX (the fp32 forward up to 8193 /
  *              8194 for U = 1 / 2), the backward up to 8193 (U = 1), 8194
- *              (U = 2; fp32 4098) or 8196 (U = 4); for U = 2 and 4 the
+ *              (U = 2) or 8196 (U = 4); for U = 2 and 4 the
  *              backward takes a row across several waves only where that
- *              leaves fewer lanes idle than the vector kernel.  All give
+ *              leaves fewer lanes idle than the vector kernel (on teams of
+ *              256 lanes, also where 70% of them are busy).  All give
  *              results within the same tolerances, fastest with 16-byte
  *              aligned tensors and N a multiple of 8 (bf16) or 4 (fp32).
  *   Sizes    : 0 <= M; 1 <= N <= NORM_N_MAX.  M = 0 enqueues only what

@@ -170,22 +170,29 @@
     X(bf16, 4, 64, 8, 4)                                                                         \
     X(bf16, 4, 256, 4, 2)                                                                        \
     X(bf16, 4, 512, 4, 2)
+// fp32 rows of unit 2 (16-byte vectors), backward: past 2050 columns two
+// teams of 256 lanes holding four or eight vectors (the vector kernel, on
+// 8-byte vectors, took the rows past 4098).  Measured on MI355X (us):
+// 8190 x 8194 196.3 -> 156.6 (vector kernel before), 16376 x 4098 149.4
+// -> 145.1 (two teams of 512 lanes holding two before), 10919 x 6146
+// 159.0 -> 155.2.  512 lanes holding four spilled registers with dbias.
+#define NF_SHAPES_ODD_U2_F32_BWD(X)                                                              \
+    NF_SHAPES_NARROW(X, float, 4)                                                                \
+    X(float, 4, 512, 1, 2)                                                                       \
+    X(float, 4, 256, 4, 2)                                                                       \
+    X(float, 4, 256, 8, 2)
 // beyond 8192 columns (bf16 forward, softmax of either dtype)
 #define NF_SHAPES_ODD_U2_WIDE(X, T)                                                              \
     X(T, 4, 640, 4, 1)                                                                           \
     X(T, 4, 768, 4, 1)                                                                           \
     X(T, 4, 1024, 4, 1)
-// The backward: the narrow layouts, then two teams of 512 lanes per
-// workgroup (each team keeps one row parity) holding 1, 2 or (unit 2) 4
+// The bf16 backward of unit 4: the narrow layouts, then two teams of 512
+// lanes per workgroup (each team keeps one row parity) holding 1 or 2
 // vectors; narrower wide teams measured slower than the vector kernel.
 #define NF_SHAPES_ODD_U4_BF16_BWD(X)                                                             \
     NF_SHAPES_NARROW(X, bf16, 8)                                                                 \
     X(bf16, 8, 512, 1, 2)                                                                        \
     X(bf16, 8, 512, 2, 2)
-#define NF_SHAPES_ODD_U2_BWD(X, T)                                                               \
-    NF_SHAPES_NARROW(X, T, 4)                                                                    \
-    X(T, 4, 512, 1, 2)                                                                           \
-    X(T, 4, 512, 2, 2)
 
 // Table entries (FwdEntry / BwdEntry / SoftmaxEntry) of one shape: the unit
 // is half the vector width VEC.

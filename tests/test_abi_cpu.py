@@ -360,6 +360,7 @@ def test_describe_names_the_odd_row_backward(lib):
         assert _odd_unit("ln_bwd", 1000, 4098, dt) == 2
         assert _odd_unit("ln_bwd", 1000, 1002, dt) == 2      # narrow: always
     assert _odd_unit("ln_bwd", 1000, 8194, BF16) == 2 and _odd_unit("ln_bwd", 1000, 8198, BF16) == 0
+    assert _odd_unit("ln_bwd", 1000, 8194, F32) == 2 and _odd_unit("ln_bwd", 1000, 8198, F32) == 0
     assert _odd_unit("ln_bwd", 1000, 4100, BF16) == 4 and _odd_unit("ln_bwd", 1000, 8196, BF16) == 4
     assert _odd_unit("ln_bwd", 1000, 8204, BF16) == 0 and _odd_unit("ln_bwd", 1000, 4102, F32) == 0
     # the same fill as the vector kernel's (6000 of 6144 lanes' columns)
