@@ -313,6 +313,28 @@ def test_describe_names_the_planned_kernels(lib):
         "bwd_kernel<bf16, VEC 8, LPR 320, VPL 2, TEAMS 2,")
 
 
+def test_describe_walk_rules(lib):
+    """The walk rules the measurements chose: wide backward rows take as many
+    workgroups as the CUs hold (no second round behind the first), the
+    forward's 16-byte wide rows walk two groups beyond 4096 row groups and
+    four up to them, the 8-byte bf16 backward on 512-thread workgroups runs
+    two per CU."""
+    def grid_k(op, M, N, dtype=nf.BF16):
+        m = re.search(r"grid (\d+) x \d+ threads, (\d+) row group", nf.describe(op, M, N, dtype))
+        return int(m.group(1)), int(m.group(2))
+    assert grid_k("ln_bwd", 52428, 2560) == (255, 103)
+    assert grid_k("ln_bwd", 131072, 4096) == (256, 256)
+    assert grid_k("ln_bwd", 8192, 4096) == (256, 16)
+    assert grid_k("ln_fwd", 43690, 3072) == (10923, 2)
+    assert grid_k("ln_fwd", 8192, 4096) == (1024, 4)
+    assert grid_k("ln_fwd", 10922, 12288) == (5461, 2)     # 768 lanes x 2 vectors
+    assert grid_k("ln_fwd", 8192, 16384) == (2048, 4)      # 512 lanes x 4 vectors
+    assert grid_k("ln_bwd", 43633, 3076)[0] == 508
+    # softmax keeps walks of four; odd-N softmax one group per workgroup
+    assert grid_k("softmax_fwd", 43690, 3072)[1] == 4
+    assert grid_k("softmax_fwd", 32760, 4097)[1] == 1
+
+
 def _odd_unit(op, M, N, dtype):
     """The odd-row unit a call would take (0: another kernel)."""
     m = re.search(r"odd_kernel<\w+, unit (\d+),", nf.describe(op, M, N, dtype))
